@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the heterogeneous LoRA hot path on one MI355X.
+
+Workload (the decode configuration): a Llama-7B-shaped layer, 64 one-token
+rows, d = 4096, q/k/v/o projections, rank-16 adapters.  One step is one pass
+of the whole path over that batch:
+
+  1. fully heterogeneous batch (row i -> adapter i, 64 adapters):
+     segment build + plan (host, C) -> metadata upload -> shrink -> expand
+  2. homogeneous batch (all rows -> adapter 0): the same
+  3. mode switch of the layer: merge adapter 0 into the four W[4096x4096],
+     then unmerge it (one launch each, four matrices per launch)
+
+Inputs are resident in HBM before the timed region.  `value` is the step's
+algorithmic bytes (what the method must move: x rows, each distinct adapter's
+A and B once, v written and read, y read and written in fp32, W read and
+written in bf16) divided by the wall-clock time per step.  Per-kernel times
+come from HIP events recorded on the stream the kernels run on, inside the
+timed steps; `roofline` describes the kernel with the largest share of the
+step time.  `cpu_baseline` times the CPU oracle on a bounded sample of the
+same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "hetero-LoRA shrink+expand µs, GB/s & TFLOP/s vs roofline; merge µs/layer"
+
+
+def delta_cost(W, row_adapter):
+    """Algorithmic bytes/flops of shrink and expand for every projection of W."""
+    ra = np.asarray(row_adapter)
+    act = ra[ra >= 0]
+    distinct = np.unique(act)
+    r_act = W.adapter_rank[act].astype(np.int64)
+    r_dis = W.adapter_rank[distinct].astype(np.int64)
+    cost = {"shrink_bytes": 0, "expand_bytes": 0, "flops": 0}
+    for p in W.projections:
+        cost["shrink_bytes"] += act.size * p.d_in * 2 + int(r_dis.sum()) * p.d_in * 2 + int(r_act.sum()) * 4
+        cost["expand_bytes"] += int(r_act.sum()) * 4 + int(r_dis.sum()) * p.d_out * 2 + act.size * p.d_out * 8
+        cost["flops"] += int(2 * r_act.sum() * (p.d_in + p.d_out))
+    return cost
+
+
+def merge_cost(d_out, d_in, r, n):
+    return {"bytes": n * (4 * d_out * d_in + r * (d_in + d_out) * 2), "flops": n * 2 * r * d_out * d_in}
+
+
+def cpu_baseline(W, batches, merge_w):
+    """The oracle as it stands, on a bounded sample: every row of both batches
+    for all projections, plus merge and unmerge of one of the layer's W."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    nbytes = 0
+    for name, ra in batches.items():
+        for p in W.projections:
+            oracle.apply_ref(ra, W.adapter_rank, p.x, p.y0, W.pool, p.A, p.B, W.scale)
+        c = delta_cost(W, ra)
+        nbytes += c["shrink_bytes"] + c["expand_bytes"]
+    p = W.projections[0]
+    r = int(W.adapter_rank[W.merge.adapter])
+    wm = oracle.merge_ref(merge_w, W.pool, p.A, p.B, W.merge.adapter, r, W.scale)
+    oracle.unmerge_ref(wm, W.pool, p.A, p.B, W.merge.adapter, r, W.scale)
+    nbytes += 2 * merge_cost(p.d_out, p.d_in, r, 1)["bytes"]
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": "oracle delta on all 64 rows x q/k/v/o of the heterogeneous and homogeneous batches, "
+                      "plus merge and unmerge of one W[4096x4096]; %.1f s of CPU time" % dt,
+            "seconds": round(dt, 3), "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path is single-GPU by design (no sharding, no collectives); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from heterogeneous_adapter_batching_amd.session import Batch, Rows, merge, unmerge
+    from workloads.device import bits_to_device, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = workloads.gen_config(1)
+    dw = to_device(W)
+    het, homo = W.batches["hetero"], W.batches["homo"]
+    rows = lambda desc, off: Rows(dw.pool, off, desc.n_adapters, desc.max_rank, desc.row_len, desc.chunk_len)
+    A = [rows(p.A, d.A_off) for p, d in zip(W.projections, dw.projections)]
+    B = [rows(p.B, d.B_off) for p, d in zip(W.projections, dw.projections)]
+    merge_host = [W.merge.weight(0, i) for i in W.merge.projs]
+    Wt = [bits_to_device(w) for w in merge_host]
+    r_m = int(W.adapter_rank[W.merge.adapter])
+    mats = [(Wt[i], A[i], B[i], W.merge.adapter, r_m, W.scale) for i in range(len(Wt))]
+    ldv = 16
+    v = [torch.empty((64, ldv), dtype=torch.float32, device=dev) for _ in W.projections]
+    bh = Batch(64, W.adapter_rank, 4096, 4096)
+    bo = Batch(64, W.adapter_rank, 4096, 4096)
+    stream = torch.cuda.current_stream()
+
+    groups = ["hetero_shrink", "hetero_expand", "homo_shrink", "homo_expand", "merge", "unmerge"]
+
+    def step(ev):
+        for b, ra, g in ((bh, het, 0), (bo, homo, 2)):
+            b.refresh(ra)
+            ev[g][0].record(stream)
+            b.shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)])
+            ev[g][1].record(stream)
+            ev[g + 1][0].record(stream)
+            b.expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
+            ev[g + 1][1].record(stream)
+        ev[4][0].record(stream)
+        merge(mats)
+        ev[4][1].record(stream)
+        ev[5][0].record(stream)
+        unmerge(mats)
+        ev[5][1].record(stream)
+
+    def new_events():
+        return [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in groups]
+
+    for _ in range(args.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+    evs = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    us = {g: [] for g in groups}
+    for ev in evs:
+        for gi, g in enumerate(groups):
+            us[g].append(ev[gi][0].elapsed_time(ev[gi][1]) * 1e3)
+    med = {g: float(np.median(us[g])) for g in groups}
+
+    ch, co = delta_cost(W, het), delta_cost(W, homo)
+    mc = merge_cost(4096, 4096, r_m, len(Wt))
+    alg = {"hetero_shrink": (ch["shrink_bytes"], ch["flops"] * 0.5),
+           "hetero_expand": (ch["expand_bytes"], ch["flops"] * 0.5),
+           "homo_shrink": (co["shrink_bytes"], co["flops"] * 0.5),
+           "homo_expand": (co["expand_bytes"], co["flops"] * 0.5),
+           "merge": (mc["bytes"], mc["flops"]), "unmerge": (mc["bytes"], mc["flops"])}
+    step_bytes = sum(b for b, _ in alg.values())
+    kernels = {}
+    for g in groups:
+        b, f = alg[g]
+        gbs = b / (med[g] * 1e-6) / 1e9
+        kernels[g] = {"us_median": round(med[g], 3), "us_p10": round(float(np.percentile(us[g], 10)), 3),
+                      "us_p90": round(float(np.percentile(us[g], 90)), 3), "alg_bytes": int(b),
+                      "GB_s": round(gbs, 1), "TFLOP_s": round(f / (med[g] * 1e-6) / 1e12, 3),
+                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    # dominant kernel: largest share of GPU time; merge and unmerge are the same kernel
+    mavg = (med["merge"] + med["unmerge"]) / 2
+    share = {"merge": med["merge"] + med["unmerge"], "hetero_expand": med["hetero_expand"],
+             "hetero_shrink": med["hetero_shrink"]}
+    dom = max(share, key=share.get)
+    if dom == "merge":
+        d_us, d_bytes, name = mavg, mc["bytes"], "merge_kernel (merge/unmerge, 4 x W[4096x4096], rank 16)"
+    else:
+        d_us, d_bytes, name = med[dom], alg[dom][0], dom
+    achieved = d_bytes / (d_us * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(step_bytes / (dt / args.steps) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode BGMV, Llama-7B-shaped layer: 64 one-token rows, d 4096, q/k/v/o, "
+                               "rank 16; hetero (64 adapters) + homo (1 adapter) batches, then merge+unmerge "
+                               "of one adapter into the layer's 4 W[4096x4096]",
+                   "rows": 64, "d": 4096, "rank": 16, "adapters": 64, "projections": 4},
+        "roofline": {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "us_per_launch": round(d_us, 3), "alg_bytes_per_launch": int(d_bytes)},
+        "kernels": kernels,
+        "hetero_over_homo": round((med["hetero_shrink"] + med["hetero_expand"]) /
+                                  (med["homo_shrink"] + med["homo_expand"]), 3),
+        "merge_us_per_layer": round(mavg, 3),
+        "step_alg_bytes": int(step_bytes),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W, {"hetero": het, "homo": homo}, merge_host[0])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+"""Heterogeneous LoRA adapter batching on MI355X (gfx950).
+
+Thin Python binding of ``libhetlora.so`` (declared in ``include/hetlora.h``):
+the functions below carry the C entry points' names and only marshal
+arguments -- numpy arrays for host inputs, raw device addresses (e.g.
+``tensor.data_ptr()``) for device buffers, an integer ``hipStream_t`` for the
+stream.  Every step of the path runs in the library.  There is no fallback:
+importing this package fails loudly when the library is not built.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhetlora.so")
+
+LORA_ABI_VERSION = 1
+LORA_MAX_RANK = 128
+LORA_MAX_PROJ = 8
+LORA_MAX_RANGES = 16
+LORA_MAX_MERGE = 8
+LORA_OK, LORA_EINVAL, LORA_EADAPTER, LORA_ERANK, LORA_ESHAPE, LORA_ECAPACITY, LORA_EHIP = 0, -1, -2, -3, -4, -5, -6
+LORA_OP_SHRINK, LORA_OP_EXPAND = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python __graft_entry__.py` (build()) first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+_P = ctypes.POINTER
+
+
+class lora_rows_t(ctypes.Structure):
+    _fields_ = [("pool", _vp), ("row_off", _vp), ("n_adapters", _i32), ("max_rank", _i32),
+                ("row_len", _i32), ("chunk_len", _i32)]
+
+
+class lora_work_t(ctypes.Structure):
+    _fields_ = [("row0", _i32), ("nrows", _i32), ("adapter", _i32), ("rank", _i32)]
+
+
+class lora_range_t(ctypes.Structure):
+    _fields_ = [("variant", _i32), ("begin", _i32), ("count", _i32), ("rows_per_item", _i32)]
+
+
+class lora_plan_info_t(ctypes.Structure):
+    _fields_ = [("op", _i32), ("n_work", _i32), ("n_active", _i32), ("max_rank", _i32),
+                ("max_adapter", _i32), ("n_ranges", _i32), ("ranges", lora_range_t * LORA_MAX_RANGES)]
+
+    def range_list(self):
+        return [(r.variant, r.begin, r.count, r.rows_per_item) for r in self.ranges[:self.n_ranges]]
+
+
+class lora_launch_t(ctypes.Structure):
+    _fields_ = [("row_index", _vp), ("work", _vp), ("info", lora_plan_info_t)]
+
+
+class lora_shrink_proj_t(ctypes.Structure):
+    _fields_ = [("x", _vp), ("ldx", _i64), ("d_in", _i32), ("A", lora_rows_t), ("v", _vp), ("ldv", _i64)]
+
+
+class lora_expand_proj_t(ctypes.Structure):
+    _fields_ = [("v", _vp), ("ldv", _i64), ("B", lora_rows_t), ("d_out", _i32), ("y", _vp),
+                ("ldy", _i64), ("scale", _f32)]
+
+
+class lora_merge_mat_t(ctypes.Structure):
+    _fields_ = [("W", _vp), ("ldw", _i64), ("d_out", _i32), ("d_in", _i32), ("A", lora_rows_t),
+                ("B", lora_rows_t), ("adapter", _i32), ("rank", _i32), ("scale", _f32)]
+
+
+_sig = {
+    "lora_abi_version": (_i32, []),
+    "lora_status_string": (ctypes.c_char_p, [_i32]),
+    "lora_build_segments": (_i32, [_i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _P(_i32), _P(_i32)]),
+    "lora_plan": (_i32, [_i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _P(lora_plan_info_t)]),
+    "lora_shrink": (_i32, [_P(lora_launch_t), _i32, _P(lora_shrink_proj_t), _vp]),
+    "lora_expand": (_i32, [_P(lora_launch_t), _i32, _P(lora_expand_proj_t), _vp]),
+    "lora_merge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
+    "lora_unmerge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
+    "lora_rows_dense_offsets": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _P(_i64)]),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype, _fn.argtypes = _res, _args
+
+
+class LoraError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__(f"{where}: {lora_status_string(code)} ({code})")
+
+
+def _check(code, where):
+    if code != LORA_OK:
+        raise LoraError(code, where)
+
+
+def _ptr(a):
+    return a.ctypes.data if a is not None and a.size else None
+
+
+def lora_abi_version():
+    return _lib.lora_abi_version()
+
+
+def lora_status_string(code):
+    return _lib.lora_status_string(int(code)).decode()
+
+
+class Segments:
+    """Host result of lora_build_segments."""
+
+    def __init__(self, row_index, seg_start, seg_adapter, seg_rank):
+        self.row_index, self.seg_start, self.seg_adapter, self.seg_rank = row_index, seg_start, seg_adapter, seg_rank
+
+    @property
+    def n_seg(self):
+        return int(self.seg_adapter.shape[0])
+
+    @property
+    def n_active(self):
+        return int(self.row_index.shape[0])
+
+
+def lora_build_segments(row_adapter, adapter_rank, seg_capacity=None, raw=False):
+    """Segment table of a batch (host).  Returns Segments; with raw=True returns
+    (status, n_seg, n_active) instead of raising, for error-path tests."""
+    ra = np.ascontiguousarray(row_adapter, dtype=np.int32)
+    rk = np.ascontiguousarray(adapter_rank, dtype=np.int32)
+    n_rows, n_ad = ra.shape[0], rk.shape[0]
+    cap = min(n_ad, n_rows) if seg_capacity is None else int(seg_capacity)
+    row_index = np.empty(max(n_rows, 1), np.int32)
+    seg_start = np.empty(cap + 1, np.int32)
+    seg_adapter = np.empty(max(cap, 1), np.int32)
+    seg_rank = np.empty(max(cap, 1), np.int32)
+    n_seg, n_act = _i32(-7), _i32(-7)
+    st = _lib.lora_build_segments(n_rows, _ptr(ra), n_ad, _ptr(rk), cap, row_index.ctypes.data,
+                                  seg_start.ctypes.data, seg_adapter.ctypes.data, seg_rank.ctypes.data,
+                                  ctypes.byref(n_seg), ctypes.byref(n_act))
+    if raw:
+        return st, n_seg.value, n_act.value
+    _check(st, "lora_build_segments")
+    ns, na = n_seg.value, n_act.value
+    return Segments(row_index[:na].copy(), seg_start[:ns + 1].copy(), seg_adapter[:ns].copy(),
+                    seg_rank[:ns].copy())
+
+
+def lora_plan(op, segs, d_in, d_out, work_capacity=None):
+    """Launch plan (host).  Returns (work int32 [n_work, 4], lora_plan_info_t)."""
+    cap = segs.n_active if work_capacity is None else int(work_capacity)
+    work = np.zeros((max(cap, 1), 4), np.int32)
+    info = lora_plan_info_t()
+    st = _lib.lora_plan(int(op), segs.n_seg, segs.seg_start.ctypes.data, _ptr(segs.seg_adapter),
+                        _ptr(segs.seg_rank), int(d_in), int(d_out), cap, work.ctypes.data, ctypes.byref(info))
+    _check(st, "lora_plan")
+    return work[:info.n_work].copy(), info
+
+
+def make_rows(pool_ptr, row_off_ptr, n_adapters, max_rank, row_len, chunk_len):
+    return lora_rows_t(pool_ptr, row_off_ptr, int(n_adapters), int(max_rank), int(row_len), int(chunk_len))
+
+
+def make_launch(row_index_ptr, work_ptr, info):
+    return lora_launch_t(row_index_ptr, work_ptr, info)
+
+
+def lora_shrink(launch, projs, stream):
+    arr = (lora_shrink_proj_t * len(projs))(*projs)
+    _check(_lib.lora_shrink(ctypes.byref(launch), len(projs), arr, stream), "lora_shrink")
+
+
+def lora_expand(launch, projs, stream):
+    arr = (lora_expand_proj_t * len(projs))(*projs)
+    _check(_lib.lora_expand(ctypes.byref(launch), len(projs), arr, stream), "lora_expand")
+
+
+def lora_merge(mats, stream):
+    arr = (lora_merge_mat_t * len(mats))(*mats)
+    _check(_lib.lora_merge(len(mats), arr, stream), "lora_merge")
+
+
+def lora_unmerge(mats, stream):
+    arr = (lora_merge_mat_t * len(mats))(*mats)
+    _check(_lib.lora_unmerge(len(mats), arr, stream), "lora_unmerge")
+
+
+def lora_rows_dense_offsets(rank, max_rank, row_len, chunk_len):
+    """Dense packed row-offset table (host).  Returns (row_off int64, pool_elems)."""
+    rk = np.ascontiguousarray(rank, dtype=np.int32)
+    chunks = -(-int(row_len) // int(chunk_len)) if chunk_len > 0 else 1
+    off = np.empty(max(1, rk.shape[0] * int(max_rank) * chunks), np.int64)
+    pe = _i64(0)
+    _check(_lib.lora_rows_dense_offsets(rk.shape[0], int(max_rank), _ptr(rk), int(row_len), int(chunk_len),
+                                        off.ctypes.data, ctypes.byref(pe)), "lora_rows_dense_offsets")
+    return off[:rk.shape[0] * int(max_rank) * chunks].copy(), pe.value

@@ -1,0 +1,187 @@
+// Host core of the library: segment metadata, launch planning, dense row
+// offsets, status strings.  Plain C++17 with no HIP dependency, so every path
+// here runs and is tested on a CPU-only machine.
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/hetlora.h"
+#include "variants.h"
+
+namespace {
+#include "tile_table.inc"
+}
+
+extern "C" int32_t lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+extern "C" const char* lora_status_string(int32_t status) {
+    switch (status) {
+        case LORA_OK: return "ok";
+        case LORA_EINVAL: return "invalid argument (null pointer, negative count, stride or alignment)";
+        case LORA_EADAPTER: return "adapter id out of range";
+        case LORA_ERANK: return "rank out of range [1, 128]";
+        case LORA_ESHAPE: return "dimension or chunk length not a positive multiple of 64";
+        case LORA_ECAPACITY: return "output capacity too small";
+        case LORA_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+// Segment table: counting sort of the active rows by adapter id.  Rows keep
+// their input order inside an adapter (stable), adapters come in ascending id,
+// and one segment is emitted per adapter that has at least one row.
+extern "C" int32_t lora_build_segments(int32_t n_rows, const int32_t* row_adapter,
+                                       int32_t n_adapters, const int32_t* adapter_rank,
+                                       int32_t seg_capacity, int32_t* row_index,
+                                       int32_t* seg_start, int32_t* seg_adapter,
+                                       int32_t* seg_rank, int32_t* n_seg, int32_t* n_active) {
+    if (n_rows < 0 || n_adapters < 0 || seg_capacity < 0) return LORA_EINVAL;
+    if ((n_rows > 0 && (row_adapter == nullptr || row_index == nullptr)) ||
+        (n_adapters > 0 && adapter_rank == nullptr) || seg_start == nullptr ||
+        (seg_capacity > 0 && (seg_adapter == nullptr || seg_rank == nullptr)) ||
+        n_seg == nullptr || n_active == nullptr)
+        return LORA_EINVAL;
+    for (int32_t i = 0; i < n_rows; ++i)
+        if (row_adapter[i] < -1 || row_adapter[i] >= n_adapters) return LORA_EADAPTER;
+    for (int32_t a = 0; a < n_adapters; ++a)
+        if (adapter_rank[a] < 1 || adapter_rank[a] > LORA_MAX_RANK) return LORA_ERANK;
+
+    std::vector<int32_t> count((size_t)n_adapters + 1, 0);
+    int32_t active = 0;
+    for (int32_t i = 0; i < n_rows; ++i)
+        if (row_adapter[i] >= 0) { ++count[(size_t)row_adapter[i] + 1]; ++active; }
+    int32_t segs = 0;
+    for (int32_t a = 0; a < n_adapters; ++a) segs += count[(size_t)a + 1] > 0;
+    *n_seg = segs;
+    *n_active = active;
+    if (segs > seg_capacity) return LORA_ECAPACITY;
+
+    for (int32_t a = 0; a < n_adapters; ++a) count[(size_t)a + 1] += count[(size_t)a];
+    // count[a] is now the first slot of adapter a in row_index
+    std::vector<int32_t> next(count.begin(), count.end() - 1);
+    for (int32_t i = 0; i < n_rows; ++i) {
+        const int32_t a = row_adapter[i];
+        if (a >= 0) row_index[next[(size_t)a]++] = i;
+    }
+    int32_t s = 0;
+    for (int32_t a = 0; a < n_adapters; ++a) {
+        if (count[(size_t)a + 1] == count[(size_t)a]) continue;
+        seg_start[s] = count[(size_t)a];
+        seg_adapter[s] = a;
+        seg_rank[s] = adapter_rank[a];
+        ++s;
+    }
+    seg_start[segs] = active;
+    return LORA_OK;
+}
+
+namespace {
+
+int pick_shape(int32_t op, int32_t len, int32_t rank, int32_t d) {
+    const int lb = lv_len_bucket(len), rb = lv_rank_bucket(rank), db = lv_d_bucket(d);
+    return op == LORA_OP_SHRINK ? kShrinkShape[lb][rb][db] : kExpandShape[lb][rb][db];
+}
+
+}  // namespace
+
+// Launch plan: every segment is cut into ceil(len / rows_per_item) work items
+// whose sizes differ by at most one row; items are grouped by variant (in
+// ascending variant id, segments in order inside a variant) so that each
+// variant is one launch over a contiguous range.
+extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
+                             const int32_t* seg_adapter, const int32_t* seg_rank,
+                             int32_t d_in, int32_t d_out, int32_t work_capacity,
+                             lora_work_t* work, lora_plan_info_t* info) {
+    if ((op != LORA_OP_SHRINK && op != LORA_OP_EXPAND) || n_seg < 0 || work_capacity < 0 ||
+        info == nullptr || seg_start == nullptr)
+        return LORA_EINVAL;
+    if (n_seg > 0 && (seg_adapter == nullptr || seg_rank == nullptr)) return LORA_EINVAL;
+    if (d_in <= 0 || d_out <= 0 || d_in % 64 != 0 || d_out % 64 != 0) return LORA_ESHAPE;
+    if (seg_start[0] != 0) return LORA_EINVAL;
+    for (int32_t s = 0; s < n_seg; ++s) {
+        if (seg_start[s + 1] <= seg_start[s]) return LORA_EINVAL;
+        if (seg_adapter[s] < 0) return LORA_EADAPTER;
+        if (seg_rank[s] < 1 || seg_rank[s] > LORA_MAX_RANK) return LORA_ERANK;
+    }
+    const int n_variants = LV_RANK_CLASSES * (op == LORA_OP_SHRINK ? LV_S_SHAPES : LV_E_SHAPES);
+    const int32_t d = op == LORA_OP_SHRINK ? d_in : d_out;
+
+    std::vector<int> seg_variant((size_t)n_seg);
+    std::vector<int32_t> seg_items((size_t)n_seg), per_variant((size_t)n_variants, 0);
+    int64_t total = 0;
+    for (int32_t s = 0; s < n_seg; ++s) {
+        const int32_t len = seg_start[s + 1] - seg_start[s];
+        const int shape = pick_shape(op, len, seg_rank[s], d);
+        const int cls = op == LORA_OP_SHRINK ? lv_shrink_class(seg_rank[s]) : lv_expand_class(seg_rank[s]);
+        const int32_t mt = op == LORA_OP_SHRINK ? lv_shrink_rows(shape) : lv_expand_rows(shape);
+        seg_variant[(size_t)s] = shape * LV_RANK_CLASSES + cls;
+        seg_items[(size_t)s] = (len + mt - 1) / mt;
+        per_variant[(size_t)seg_variant[(size_t)s]] += seg_items[(size_t)s];
+        total += seg_items[(size_t)s];
+    }
+    info->n_work = (int32_t)total;
+    if (total > work_capacity) return LORA_ECAPACITY;
+    if (total > 0 && work == nullptr) return LORA_EINVAL;
+
+    lora_plan_info_t out;
+    memset(&out, 0, sizeof(out));
+    out.op = op;
+    out.n_work = (int32_t)total;
+    out.n_active = seg_start[n_seg];
+    out.max_rank = 0;
+    out.max_adapter = -1;
+    int32_t begin = 0;
+    for (int v = 0; v < n_variants; ++v) {
+        if (per_variant[(size_t)v] == 0) continue;
+        lora_range_t& r = out.ranges[out.n_ranges++];
+        r.variant = v;
+        r.begin = begin;
+        r.count = per_variant[(size_t)v];
+        const int shape = v / LV_RANK_CLASSES;
+        r.rows_per_item = op == LORA_OP_SHRINK ? lv_shrink_rows(shape) : lv_expand_rows(shape);
+        int32_t w = begin;
+        for (int32_t s = 0; s < n_seg; ++s) {
+            if (seg_variant[(size_t)s] != v) continue;
+            const int32_t len = seg_start[s + 1] - seg_start[s];
+            const int32_t k = seg_items[(size_t)s];
+            const int32_t base = len / k, extra = len % k;
+            int32_t row = seg_start[s];
+            for (int32_t t = 0; t < k; ++t) {
+                const int32_t n = base + (t < extra ? 1 : 0);
+                work[w++] = lora_work_t{row, n, seg_adapter[s], seg_rank[s]};
+                row += n;
+            }
+            if (seg_rank[s] > out.max_rank) out.max_rank = seg_rank[s];
+            if (seg_adapter[s] > out.max_adapter) out.max_adapter = seg_adapter[s];
+        }
+        begin = w;
+    }
+    *info = out;
+    return LORA_OK;
+}
+
+extern "C" int32_t lora_rows_dense_offsets(int32_t n_adapters, int32_t max_rank,
+                                           const int32_t* rank, int32_t row_len,
+                                           int32_t chunk_len, int64_t* row_off,
+                                           int64_t* pool_elems) {
+    if (n_adapters < 0 || pool_elems == nullptr || (n_adapters > 0 && (rank == nullptr || row_off == nullptr)))
+        return LORA_EINVAL;
+    if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERANK;
+    if (row_len <= 0 || chunk_len <= 0 || chunk_len % 64 != 0) return LORA_ESHAPE;
+    for (int32_t a = 0; a < n_adapters; ++a)
+        if (rank[a] < 1 || rank[a] > max_rank) return LORA_ERANK;
+    const int64_t chunks = (row_len + chunk_len - 1) / chunk_len;
+    const int64_t stride = ((int64_t)row_len + 7) / 8 * 8;
+    int64_t row = 0;
+    for (int32_t a = 0; a < n_adapters; ++a) {
+        for (int32_t j = 0; j < max_rank; ++j)
+            for (int64_t c = 0; c < chunks; ++c) {
+                const int64_t idx = ((int64_t)a * max_rank + j) * chunks + c;
+                row_off[idx] = j < rank[a] ? (row + j) * stride + c * chunk_len : -1;
+            }
+        row += rank[a];
+    }
+    *pool_elems = row * stride;
+    return LORA_OK;
+}

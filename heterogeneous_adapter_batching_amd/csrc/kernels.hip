@@ -1,0 +1,566 @@
+// gfx950 kernels of the heterogeneous LoRA path and their C-ABI launchers.
+//
+//   shrink  v[p][j]  = sum_k x[row_index[p]][k] * A_a[j][k]       (j < r_a)
+//   expand  y[row_index[p]][n] += s * sum_j v[p][j] * B_a[j][n]
+//   merge   W[n][k]  = RNE_bf16(W[n][k] + s * sum_j B_a[j][n] * A_a[j][k])
+//
+// (BEE-30060 "Multi-LoRA serving", Punica paragraph: per-request delta
+// x_i A_i B_i, requests grouped by adapter; VaLoRA blog section 4.4.1:
+// Delta W = B x A added once; S-LoRA article, Unified Paging: adapter rows are
+// hidden-size vectors gathered from a pool.)
+//
+// All three use the bf16 MFMA v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation.  Operand convention relied upon: in the first operand lane l
+// supplies row (l % 16), in the second operand column (l % 16); both take the
+// same 8 reduction elements from lane group (l / 16); the fp32 result of lane l
+// is column (l % 16), rows 4*(l / 16) + 0..3.  Because both operands use the
+// same lane-group pairing, any fixed assignment of memory positions to the 32
+// reduction slots gives the exact dot product; the kernels use that freedom to
+// load 16 or 32 contiguous bytes per lane.
+//
+// Rows whose reduction index runs along memory (x and A in the shrink) load
+// straight into operands.  Where the reduction index (the rank j) is the slow
+// memory index (B in the expand, A and B in the merge), each lane loads 8
+// rows x 8 consecutive columns and transposes that 8x8 bf16 block in
+// registers; output column slot i of MFMA c then stands for memory column
+// base + 8*i + c, so each lane still ends up owning 8 consecutive outputs.
+//
+// No float atomics and a fixed reduction order everywhere: results do not
+// depend on a row's position in a work item or on the launch order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hetlora.h"
+#include "variants.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define WG 256
+
+namespace {
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ f32x4_t ldf4(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+__device__ __forceinline__ void stf4(float* p, f32x4_t v) { *reinterpret_cast<f32x4_t*>(p) = v; }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// 8 rows (r[e] = 8 consecutive bf16 columns of row e) -> 8 columns
+// (out[c] = the 8 rows' values in column c).
+__device__ __forceinline__ void transpose8x8(const u32x4_t r[8], u32x4_t out[8]) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int d = c >> 1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t a = r[2 * q][d], b = r[2 * q + 1][d];
+            out[c][q] = (c & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+        }
+    }
+}
+
+// Address of element `col` of row j of adapter a in a row table.
+struct Rows {
+    const uint16_t* pool;
+    const int64_t* row_off;
+    int32_t max_rank, chunk_len, chunks;
+};
+__device__ __forceinline__ const uint16_t* row_ptr(const Rows& t, int32_t a, int32_t j, int32_t col) {
+    const int32_t c = col / t.chunk_len;
+    return t.pool + t.row_off[((int64_t)a * t.max_rank + j) * t.chunks + c] + (col - c * t.chunk_len);
+}
+
+// ------------------------------------------------------------------ shrink
+struct ShrinkProj {
+    const uint16_t* x;
+    int64_t ldx;
+    Rows A;
+    int32_t d_in;
+    float* v;
+    int64_t ldv;
+};
+struct ShrinkArgs {
+    const int32_t* row_index;
+    const lora_work_t* work;
+    int32_t begin;
+    ShrinkProj p[LORA_MAX_PROJ];
+};
+
+// One workgroup = one work item of one projection.
+//   KSPLIT = 4: the four waves share the item's 16 rows and take every 4th
+//               64-wide K block; partial sums are added in LDS in wave order.
+//   KSPLIT = 1: wave w owns rows [16*MTW*w, 16*MTW*(w+1)) of the item.
+// NT = number of 16-wide rank tiles; U = K blocks loaded ahead per step.
+template <int KSPLIT, int MTW, int NT, int U>
+__global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
+    const lora_work_t it = args.work[args.begin + blockIdx.x];
+    const ShrinkProj& P = args.p[blockIdx.y];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int mbase = KSPLIT > 1 ? 0 : wave * 16 * MTW;
+    if (KSPLIT == 1 && mbase >= it.nrows) return;  // no barrier in this configuration
+
+    const uint16_t* xrow[MTW];
+#pragma unroll
+    for (int t = 0; t < MTW; ++t) {
+        const int m = mbase + 16 * t + li;
+        xrow[t] = m < it.nrows ? P.x + (int64_t)args.row_index[it.row0 + m] * P.ldx + 16 * lg : nullptr;
+    }
+    f32x4_t acc[MTW][NT];
+#pragma unroll
+    for (int t = 0; t < MTW; ++t)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const int kblocks = P.d_in / 64;
+    const int cblocks = P.A.chunk_len / 64;
+    for (int c = 0; c < P.A.chunks; ++c) {
+        const uint16_t* arow[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int j = 16 * n + li;
+            arow[n] = j < it.rank
+                          ? P.A.pool + P.A.row_off[((int64_t)it.adapter * P.A.max_rank + j) * P.A.chunks + c] + 16 * lg
+                          : nullptr;
+        }
+        const int kb0 = c * cblocks;
+        const int kb1 = min(kblocks, kb0 + cblocks);
+        // first block of this chunk owned by this wave (blocks are dealt round-robin by global index)
+        int kb = KSPLIT > 1 ? kb0 + ((wave - kb0 % KSPLIT) + KSPLIT) % KSPLIT : kb0;
+        for (; kb < kb1; kb += KSPLIT * U) {
+            u32x4_t xa[U][MTW][2], aa[U][NT][2];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = kb + u * KSPLIT;
+                const bool ok = k < kb1;
+                const int64_t kx = (int64_t)k * 64, ka = (int64_t)(k - kb0) * 64;
+#pragma unroll
+                for (int t = 0; t < MTW; ++t) {
+                    xa[u][t][0] = (ok && xrow[t]) ? ld16(xrow[t] + kx) : zero;
+                    xa[u][t][1] = (ok && xrow[t]) ? ld16(xrow[t] + kx + 8) : zero;
+                }
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    aa[u][n][0] = (ok && arow[n]) ? ld16(arow[n] + ka) : zero;
+                    aa[u][n][1] = (ok && arow[n]) ? ld16(arow[n] + ka + 8) : zero;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (kb + u * KSPLIT >= kb1) break;
+#pragma unroll
+                for (int t = 0; t < MTW; ++t)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        if (16 * n >= it.rank) continue;
+                        acc[t][n] = mfma_bf16(xa[u][t][0], aa[u][n][0], acc[t][n]);
+                        acc[t][n] = mfma_bf16(xa[u][t][1], aa[u][n][1], acc[t][n]);
+                    }
+            }
+        }
+    }
+
+    if constexpr (KSPLIT > 1) {
+        __shared__ f32x4_t red[KSPLIT - 1][NT][64];
+        if (wave > 0)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) red[wave - 1][n][lane] = acc[0][n];
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int w = 0; w < KSPLIT - 1; ++w)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[0][n] += red[w][n][lane];
+    }
+    // result lane layout: column j = 16n + li, rows 4*lg + e of tile t
+#pragma unroll
+    for (int t = 0; t < MTW; ++t)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int j = 16 * n + li;
+            if (j >= it.rank) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = mbase + 16 * t + 4 * lg + e;
+                if (m < it.nrows) P.v[(int64_t)(it.row0 + m) * P.ldv + j] = acc[t][n][e];
+            }
+        }
+}
+
+// ------------------------------------------------------------------ expand
+struct ExpandProj {
+    const float* v;
+    int64_t ldv;
+    Rows B;
+    int32_t d_out;
+    float* y;
+    int64_t ldy;
+    float scale;
+    int32_t cg_begin;  // first column group (grid.y) of this projection
+};
+struct ExpandArgs {
+    const int32_t* row_index;
+    const lora_work_t* work;
+    int32_t begin;
+    int32_t n_proj;
+    ExpandProj p[LORA_MAX_PROJ];
+};
+
+// One workgroup = one work item x one 512-column group of one projection;
+// wave w owns columns [128w, 128w+128) of the group.  The wave loads and
+// transposes its B strip once (KS steps of 32 ranks), then walks the item's
+// rows 16 at a time.  v is split as hi + lo bf16 (two MFMAs) so the product
+// keeps ~16 mantissa bits of v; y is read, updated and written in fp32.
+template <int KS>
+__global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
+    const lora_work_t it = args.work[args.begin + blockIdx.x];
+    int pi = 0;
+    while (pi + 1 < args.n_proj && (int)blockIdx.y >= args.p[pi + 1].cg_begin) ++pi;
+    const ExpandProj& P = args.p[pi];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int col0 = ((int)blockIdx.y - P.cg_begin) * 512 + wave * 128;
+    if (col0 >= P.d_out) return;  // no barrier in this kernel
+    const int n0 = col0 + 8 * li;
+    const bool col_ok = n0 < P.d_out;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+    u32x4_t bop[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t rows[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = 32 * ks + 8 * lg + e;
+            rows[e] = (col_ok && j < it.rank) ? ld16(row_ptr(P.B, it.adapter, j, n0)) : zero;
+        }
+        transpose8x8(rows, bop[ks]);
+    }
+
+    for (int mt = 0; mt * 16 < it.nrows; ++mt) {
+        // first operand: v rows, split into hi/lo bf16
+        const int m = 16 * mt + li;
+        const bool row_ok = m < it.nrows;
+        const float* vrow = P.v + (int64_t)(it.row0 + m) * P.ldv;
+        u32x4_t vhi[KS], vlo[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int j0 = 32 * ks + 8 * lg;
+            f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+            if (row_ok && j0 < it.rank) a = ldf4(vrow + j0);
+            if (row_ok && j0 + 4 < it.rank) b = ldf4(vrow + j0 + 4);
+            float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (j0 + e >= it.rank) f[e] = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t h = pack_bf16(f[2 * q], f[2 * q + 1]);
+                vhi[ks][q] = h;
+                vlo[ks][q] = pack_bf16(f[2 * q] - bf16_lo(h), f[2 * q + 1] - bf16_hi(h));
+            }
+        }
+        // output rows owned by this lane: 4*lg + e of this tile
+        float* yrow[4];
+        f32x4_t y0[4], y1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int mm = 16 * mt + 4 * lg + e;
+            yrow[e] = (col_ok && mm < it.nrows) ? P.y + (int64_t)args.row_index[it.row0 + mm] * P.ldy + n0 : nullptr;
+            if (yrow[e]) {
+                y0[e] = ldf4(yrow[e]);
+                y1[e] = ldf4(yrow[e] + 4);
+            }
+        }
+        f32x4_t acc[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (32 * ks >= it.rank) continue;
+                acc[c] = mfma_bf16(vhi[ks], bop[ks][c], acc[c]);
+                acc[c] = mfma_bf16(vlo[ks], bop[ks][c], acc[c]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (!yrow[e]) continue;
+            f32x4_t o0, o1;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                o0[c] = __builtin_fmaf(P.scale, acc[c][e], y0[e][c]);
+                o1[c] = __builtin_fmaf(P.scale, acc[c + 4][e], y1[e][c]);
+            }
+            stf4(yrow[e], o0);
+            stf4(yrow[e] + 4, o1);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ merge
+struct MergeMat {
+    uint16_t* W;
+    int64_t ldw;
+    int32_t d_out, d_in;
+    Rows A, B;
+    int32_t adapter, rank;
+    float scale;
+    int32_t tiles_k;  // 512-column tiles along d_in
+    int32_t tiles;    // total tiles of this matrix
+};
+struct MergeArgs {
+    MergeMat m[LORA_MAX_MERGE];
+};
+
+// One workgroup = a 128 (rows n of W) x 512 (columns k) tile; wave w owns
+// columns [128w, 128w+128).  First operand: B rows (rank x n) transposed so
+// row slot i of MFMA c2 is n = nbase + 8*i + c2; second operand: A rows
+// transposed so column slot i of MFMA c is k = kbase + 8*i + c.  Lane (li,lg)
+// then owns W rows nbase + 8*(4*lg+e) + c2 at columns kbase + 8*li .. +7.
+template <int KS>
+__global__ __launch_bounds__(WG) void merge_kernel(MergeArgs args) {
+    const MergeMat& M = args.m[blockIdx.y];
+    if ((int)blockIdx.x >= M.tiles) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int tn = blockIdx.x / M.tiles_k, tk = blockIdx.x % M.tiles_k;
+    const int nbase = tn * 128, kbase = tk * 512 + wave * 128;
+    if (kbase >= M.d_in) return;  // no barrier in this kernel
+    const int k0 = kbase + 8 * li;
+    const bool k_ok = k0 < M.d_in;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+    // W values this lane updates: 8 row sub-slots x 4 rows x 8 columns
+    uint16_t* wrow[8][4];
+    u32x4_t wv[8][4];
+#pragma unroll
+    for (int c2 = 0; c2 < 8; ++c2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int n = nbase + 8 * (4 * lg + e) + c2;
+            wrow[c2][e] = (k_ok && n < M.d_out) ? M.W + (int64_t)n * M.ldw + k0 : nullptr;
+            wv[c2][e] = wrow[c2][e] ? ld16(wrow[c2][e]) : zero;
+        }
+
+    u32x4_t aop[KS][8], bop[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t rows[8];
+        const int nn = nbase + 8 * li;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = 32 * ks + 8 * lg + e;
+            rows[e] = (nn < M.d_out && j < M.rank) ? ld16(row_ptr(M.B, M.adapter, j, nn)) : zero;
+        }
+        transpose8x8(rows, aop[ks]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = 32 * ks + 8 * lg + e;
+            rows[e] = (k_ok && j < M.rank) ? ld16(row_ptr(M.A, M.adapter, j, k0)) : zero;
+        }
+        transpose8x8(rows, bop[ks]);
+    }
+
+#pragma unroll
+    for (int c2 = 0; c2 < 8; ++c2) {
+        f32x4_t acc[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (32 * ks >= M.rank) continue;
+                acc[c] = mfma_bf16(aop[ks][c2], bop[ks][c], acc[c]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (!wrow[c2][e]) continue;
+            u32x4_t o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w = wv[c2][e][q];
+                const float lo = __builtin_fmaf(M.scale, acc[2 * q][e], bf16_lo(w));
+                const float hi = __builtin_fmaf(M.scale, acc[2 * q + 1][e], bf16_hi(w));
+                o[q] = pack_bf16(lo, hi);
+            }
+            *reinterpret_cast<u32x4_t*>(wrow[c2][e]) = o;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host side
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int32_t check_rows(const lora_rows_t& r, int32_t d, int32_t max_rank, int32_t max_adapter) {
+    if (!r.pool || !r.row_off || !aligned16(r.pool)) return LORA_EINVAL;
+    if (r.row_len != d) return LORA_ESHAPE;
+    if (r.chunk_len <= 0 || r.chunk_len % 64 != 0) return LORA_ESHAPE;
+    if (r.max_rank < 1 || r.max_rank > LORA_MAX_RANK || max_rank > r.max_rank) return LORA_ERANK;
+    if (max_adapter >= r.n_adapters) return LORA_EADAPTER;
+    return LORA_OK;
+}
+
+Rows to_rows(const lora_rows_t& r) {
+    return Rows{r.pool, r.row_off, r.max_rank, r.chunk_len, (r.row_len + r.chunk_len - 1) / r.chunk_len};
+}
+
+int32_t check_launch(const lora_launch_t* L, int32_t op, int32_t n_proj) {
+    if (!L || n_proj < 1 || n_proj > LORA_MAX_PROJ) return LORA_EINVAL;
+    const lora_plan_info_t& I = L->info;
+    if (I.op != op || I.n_work < 0 || I.n_ranges < 0 || I.n_ranges > LORA_MAX_RANGES) return LORA_EINVAL;
+    if (I.n_work > 0 && (!L->row_index || !L->work)) return LORA_EINVAL;
+    if (I.max_rank > LORA_MAX_RANK) return LORA_ERANK;
+    const int n_variants = LV_RANK_CLASSES * (op == LORA_OP_SHRINK ? LV_S_SHAPES : LV_E_SHAPES);
+    for (int r = 0; r < I.n_ranges; ++r) {
+        const lora_range_t& R = I.ranges[r];
+        if (R.variant < 0 || R.variant >= n_variants || R.begin < 0 || R.count < 0 || R.begin + R.count > I.n_work)
+            return LORA_EINVAL;
+    }
+    return LORA_OK;
+}
+
+typedef void (*shrink_fn)(ShrinkArgs);
+template <int KSPLIT, int MTW, int NT>
+constexpr int unroll_for() {
+    return KSPLIT > 1 ? (NT == 1 ? 8 : NT == 2 ? 4 : NT == 4 ? 2 : 1) : ((MTW + NT) <= 2 ? 4 : (MTW + NT) <= 4 ? 2 : 1);
+}
+template <int KSPLIT, int MTW, int NT>
+shrink_fn shrink_inst() {
+    return shrink_kernel<KSPLIT, MTW, NT, unroll_for<KSPLIT, MTW, NT>()>;
+}
+shrink_fn shrink_table(int variant) {
+    static const shrink_fn t[LV_S_SHAPES * LV_RANK_CLASSES] = {
+        shrink_inst<4, 1, 1>(), shrink_inst<4, 1, 2>(), shrink_inst<4, 1, 4>(), shrink_inst<4, 1, 8>(),
+        shrink_inst<1, 1, 1>(), shrink_inst<1, 1, 2>(), shrink_inst<1, 1, 4>(), shrink_inst<1, 1, 8>(),
+        shrink_inst<1, 2, 1>(), shrink_inst<1, 2, 2>(), shrink_inst<1, 2, 4>(), shrink_inst<1, 2, 8>(),
+    };
+    return t[variant];
+}
+
+typedef void (*expand_fn)(ExpandArgs);
+expand_fn expand_table(int rank_class) {
+    static const expand_fn t[3] = {expand_kernel<1>, expand_kernel<2>, expand_kernel<4>};
+    return t[rank_class];
+}
+
+}  // namespace
+
+extern "C" int32_t lora_shrink(const lora_launch_t* L, int32_t n_proj, const lora_shrink_proj_t* projs,
+                               void* hip_stream) {
+    int32_t st = check_launch(L, LORA_OP_SHRINK, n_proj);
+    if (st != LORA_OK) return st;
+    if (!projs) return LORA_EINVAL;
+    ShrinkArgs args;
+    args.row_index = L->row_index;
+    args.work = L->work;
+    for (int i = 0; i < n_proj; ++i) {
+        const lora_shrink_proj_t& p = projs[i];
+        if (!p.x || !p.v || !aligned16(p.x) || !aligned16(p.v)) return LORA_EINVAL;
+        if (p.d_in <= 0 || p.d_in % 64 != 0) return LORA_ESHAPE;
+        if (p.ldx < p.d_in || p.ldx % 8 != 0 || p.ldv % 4 != 0 || p.ldv < L->info.max_rank) return LORA_EINVAL;
+        if ((st = check_rows(p.A, p.d_in, L->info.max_rank, L->info.max_adapter)) != LORA_OK) return st;
+        args.p[i] = ShrinkProj{p.x, p.ldx, to_rows(p.A), p.d_in, p.v, p.ldv};
+    }
+    if (L->info.n_work == 0) return LORA_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    for (int r = 0; r < L->info.n_ranges; ++r) {
+        const lora_range_t& R = L->info.ranges[r];
+        if (R.count == 0) continue;
+        args.begin = R.begin;
+        hipLaunchKernelGGL(shrink_table(R.variant), dim3((unsigned)R.count, (unsigned)n_proj), dim3(WG), 0, s, args);
+    }
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
+extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lora_expand_proj_t* projs,
+                               void* hip_stream) {
+    int32_t st = check_launch(L, LORA_OP_EXPAND, n_proj);
+    if (st != LORA_OK) return st;
+    if (!projs) return LORA_EINVAL;
+    ExpandArgs args;
+    args.row_index = L->row_index;
+    args.work = L->work;
+    args.n_proj = n_proj;
+    int32_t groups = 0;
+    for (int i = 0; i < n_proj; ++i) {
+        const lora_expand_proj_t& p = projs[i];
+        if (!p.v || !p.y || !aligned16(p.v) || !aligned16(p.y)) return LORA_EINVAL;
+        if (p.d_out <= 0 || p.d_out % 64 != 0) return LORA_ESHAPE;
+        if (p.ldy < p.d_out || p.ldy % 4 != 0 || p.ldv % 4 != 0 || p.ldv < L->info.max_rank) return LORA_EINVAL;
+        if ((st = check_rows(p.B, p.d_out, L->info.max_rank, L->info.max_adapter)) != LORA_OK) return st;
+        args.p[i] = ExpandProj{p.v, p.ldv, to_rows(p.B), p.d_out, p.y, p.ldy, p.scale, groups};
+        groups += (p.d_out + 511) / 512;
+    }
+    if (L->info.n_work == 0) return LORA_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    for (int r = 0; r < L->info.n_ranges; ++r) {
+        const lora_range_t& R = L->info.ranges[r];
+        if (R.count == 0) continue;
+        args.begin = R.begin;
+        hipLaunchKernelGGL(expand_table(R.variant % LV_RANK_CLASSES), dim3((unsigned)R.count, (unsigned)groups),
+                           dim3(WG), 0, s, args);
+    }
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
+namespace {
+int32_t merge_impl(int32_t n_mats, const lora_merge_mat_t* mats, float sign, void* hip_stream) {
+    if (n_mats < 1 || n_mats > LORA_MAX_MERGE || !mats) return LORA_EINVAL;
+    MergeArgs args;
+    int32_t max_tiles = 0, max_rank = 0;
+    for (int i = 0; i < n_mats; ++i) {
+        const lora_merge_mat_t& m = mats[i];
+        if (!m.W || !aligned16(m.W)) return LORA_EINVAL;
+        if (m.d_out <= 0 || m.d_in <= 0 || m.d_out % 64 != 0 || m.d_in % 64 != 0) return LORA_ESHAPE;
+        if (m.ldw < m.d_in || m.ldw % 8 != 0) return LORA_EINVAL;
+        if (m.rank < 1 || m.rank > LORA_MAX_RANK) return LORA_ERANK;
+        if (m.adapter < 0) return LORA_EADAPTER;
+        int32_t st;
+        if ((st = check_rows(m.A, m.d_in, m.rank, m.adapter)) != LORA_OK) return st;
+        if ((st = check_rows(m.B, m.d_out, m.rank, m.adapter)) != LORA_OK) return st;
+        const int32_t tk = (m.d_in + 511) / 512, tn = (m.d_out + 127) / 128;
+        args.m[i] = MergeMat{m.W, m.ldw, m.d_out, m.d_in, to_rows(m.A), to_rows(m.B), m.adapter, m.rank,
+                             sign * m.scale, tk, tk * tn};
+        if (tk * tn > max_tiles) max_tiles = tk * tn;
+        if (m.rank > max_rank) max_rank = m.rank;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    const dim3 grid((unsigned)max_tiles, (unsigned)n_mats);
+    if (max_rank <= 32)
+        hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(WG), 0, s, args);
+    else if (max_rank <= 64)
+        hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(WG), 0, s, args);
+    else
+        hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(WG), 0, s, args);
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+}  // namespace
+
+extern "C" int32_t lora_merge(int32_t n_mats, const lora_merge_mat_t* mats, void* hip_stream) {
+    return merge_impl(n_mats, mats, 1.0f, hip_stream);
+}
+
+extern "C" int32_t lora_unmerge(int32_t n_mats, const lora_merge_mat_t* mats, void* hip_stream) {
+    return merge_impl(n_mats, mats, -1.0f, hip_stream);
+}

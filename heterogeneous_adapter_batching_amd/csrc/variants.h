@@ -1,0 +1,54 @@
+// Kernel variants shared by the planner (host) and the launchers (HIP).
+//
+// A variant is (shape, rank class).  The shape fixes how many rows one work
+// item may hold and how a workgroup splits the work; the rank class fixes how
+// many 16-wide MFMA tiles the rank dimension needs, so registers are padded,
+// never memory.  variant = shape * LV_RANK_CLASSES + rank_class.
+#pragma once
+
+#include <stdint.h>
+
+#define LV_RANK_CLASSES 4
+
+// Shrink shapes (rows per work item): 4 waves split K over one 16-row tile,
+// or 4 waves each own 16 / 32 rows over the full K.
+#define LV_S_SPLITK16 0
+#define LV_S_ROWS64 1
+#define LV_S_ROWS128 2
+#define LV_S_SHAPES 3
+
+// Expand shapes: the same kernel, work items of 16 / 64 / 128 / 256 rows
+// (more rows reuse each B column strip more, fewer rows give more workgroups).
+#define LV_E_ROWS16 0
+#define LV_E_ROWS64 1
+#define LV_E_ROWS128 2
+#define LV_E_ROWS256 3
+#define LV_E_SHAPES 4
+
+static inline int32_t lv_shrink_rows(int shape) {
+    return shape == LV_S_SPLITK16 ? 16 : shape == LV_S_ROWS64 ? 64 : 128;
+}
+static inline int32_t lv_expand_rows(int shape) {
+    return shape == LV_E_ROWS16 ? 16 : shape == LV_E_ROWS64 ? 64 : shape == LV_E_ROWS128 ? 128 : 256;
+}
+
+// Shrink rank classes: N tiles of 16 ranks -> 1, 2, 4, 8 (rank <= 16, 32, 64, 128).
+static inline int lv_shrink_class(int32_t rank) {
+    return rank <= 16 ? 0 : rank <= 32 ? 1 : rank <= 64 ? 2 : 3;
+}
+// Expand rank classes: K steps of 32 ranks -> 1, 2, 4 (rank <= 32, 64, 128);
+// class 3 is unused.
+static inline int lv_expand_class(int32_t rank) {
+    return rank <= 32 ? 0 : rank <= 64 ? 1 : 2;
+}
+
+// Bucket keys of the tile-config table.
+#define LV_LEN_BUCKETS 8
+#define LV_RANK_BUCKETS 4
+#define LV_D_BUCKETS 4
+static inline int lv_len_bucket(int32_t len) {
+    return len <= 1 ? 0 : len <= 4 ? 1 : len <= 8 ? 2 : len <= 16 ? 3 : len <= 32 ? 4 : len <= 64 ? 5
+         : len <= 256 ? 6 : 7;
+}
+static inline int lv_rank_bucket(int32_t r) { return r <= 16 ? 0 : r <= 32 ? 1 : r <= 64 ? 2 : 3; }
+static inline int lv_d_bucket(int32_t d) { return d <= 1024 ? 0 : d <= 4096 ? 1 : d <= 8192 ? 2 : 3; }

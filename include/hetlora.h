@@ -1,0 +1,262 @@
+/*
+ * hetlora.h -- C ABI of the heterogeneous LoRA batching library for MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * A batch of token rows, each either released (adapter id -1) or tied to one
+ * LoRA adapter a of rank r_a, receives the low-rank delta
+ *
+ *     v_i    = x_i . A_a^T                  (shrink, d_in -> r_a)
+ *     y_i   += s * v_i . B_a                (expand, r_a -> d_out)
+ *
+ * with no padding of ranks or rows (BEE-30060 "Multi-LoRA serving and adapter
+ * management", Punica paragraph: every request adds its own x_i A_i B_i; SGMV
+ * groups requests by adapter, BGMV serves one-token decode rows; S-LoRA
+ * article, "Batching": adapters are computed without padding).  The mode
+ * switch folds one adapter into a base weight and back out again,
+ *
+ *     W <- RNE_bf16(W + s * B_a^T . A_a)    (merge)
+ *     W <- RNE_bf16(W - s * B_a^T . A_a)    (unmerge)
+ *
+ * (VaLoRA blog, section 4.4.1 "Swift Inference Mode Switch": Delta W = B x A is
+ * computed at run time and added to / subtracted from the weights once).
+ *
+ * Layouts (all row-major, element strides "ld*" in elements)
+ * ---------------------------------------------------------
+ *   x  bf16 [n_rows][ldx]   token rows (input)
+ *   y  fp32 [n_rows][ldy]   outputs, updated in place (y += ...)
+ *   v  fp32 [n_active][ldv] rank-r intermediate; row p belongs to row_index[p]
+ *   W  bf16 [d_out][ldw]    base weight (nn.Linear orientation, y = x W^T)
+ *   A  r_a rows of d_in bf16 per adapter, B  r_a rows of d_out bf16 per adapter.
+ * A and B are both stored as r "hidden-size vectors" (S-LoRA article, "Unified
+ * Paging": a rank-R adapter weight occupies R pages of H-vectors), addressed
+ * through a row-offset table, lora_rows_t, that covers both a dense packing
+ * and a paged pool:
+ *
+ *   chunk c of row j of adapter a starts at
+ *       pool + row_off[(a * max_rank + j) * chunks + c]      (bf16 elements)
+ *   where chunks = ceil(row_len / chunk_len); the chunk holds chunk_len
+ *   elements, the last one only up to row_len.
+ *
+ * bf16 values are passed as uint16_t bit patterns.
+ *
+ * Ownership, streams, errors
+ * --------------------------
+ * Every buffer belongs to the caller.  Pointers documented "device" must be
+ * device memory of the current HIP device; "host" pointers are ordinary host
+ * memory.  The library allocates no memory and keeps no pointer after a call
+ * returns.  GPU work is enqueued on the given hipStream_t (passed as void*;
+ * NULL = the null stream) and is asynchronous: no call synchronises.  All
+ * functions are re-entrant; the only global state is constant tables.
+ * Arguments are validated before anything is launched; on error nothing is
+ * launched and no output is written, except that the counts of
+ * lora_build_segments / lora_plan are written on LORA_ECAPACITY so the caller
+ * can resize.  An empty batch (no active rows) is LORA_OK and launches nothing.
+ * Device array contents (row_index, work, row_off) are trusted: they must be
+ * what lora_build_segments / lora_plan / the caller's page table produced for
+ * the host-side summary passed alongside.  x must not alias y; v must not
+ * alias x or y.
+ */
+#ifndef HETLORA_H
+#define HETLORA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+#define LORA_MAX_RANK 128   /* ranks are 1..128                              */
+#define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
+#define LORA_MAX_RANGES 16  /* kernel variants in one plan                   */
+#define LORA_MAX_MERGE 8    /* weight matrices per merge/unmerge call        */
+
+/* Status codes (int32_t return value of every call except the two getters). */
+#define LORA_OK         0  /* success                                                  */
+#define LORA_EINVAL    -1  /* null pointer, negative count, ld < d, misaligned pointer */
+#define LORA_EADAPTER  -2  /* adapter id outside [-1, n_adapters)                     */
+#define LORA_ERANK     -3  /* rank outside [1, LORA_MAX_RANK]                          */
+#define LORA_ESHAPE    -4  /* d_in / d_out / chunk_len not a positive multiple of 64   */
+#define LORA_ECAPACITY -5  /* an output capacity is too small                          */
+#define LORA_EHIP      -6  /* a HIP launch reported an error                           */
+
+#define LORA_OP_SHRINK 0
+#define LORA_OP_EXPAND 1
+
+/* Adapter rows of one matrix kind (A or B of one projection).
+ *   pool      device, bf16 elements; 16-byte aligned
+ *   row_off   device, int64 [n_adapters * max_rank * chunks]; every offset a
+ *             multiple of 8 (16 bytes); entries for j >= r_a are never read
+ *   max_rank  row-slot stride of the table (>= every rank used with it)
+ *   row_len   elements per row (d_in for A, d_out for B)
+ *   chunk_len elements per chunk, a positive multiple of 64              */
+typedef struct lora_rows {
+    const uint16_t* pool;
+    const int64_t* row_off;
+    int32_t n_adapters;
+    int32_t max_rank;
+    int32_t row_len;
+    int32_t chunk_len;
+} lora_rows_t;
+
+/* One unit of kernel work: rows row_index[row0 .. row0+nrows) of one segment,
+ * all on `adapter` of rank `rank`. */
+typedef struct lora_work {
+    int32_t row0;
+    int32_t nrows;
+    int32_t adapter;
+    int32_t rank;
+} lora_work_t;
+
+/* Work items [begin, begin+count) of the plan run kernel `variant`; no item
+ * has more than rows_per_item rows. */
+typedef struct lora_range {
+    int32_t variant;
+    int32_t begin;
+    int32_t count;
+    int32_t rows_per_item;
+} lora_range_t;
+
+/* Host-side summary of a plan, written by lora_plan. */
+typedef struct lora_plan_info {
+    int32_t op;           /* LORA_OP_SHRINK or LORA_OP_EXPAND            */
+    int32_t n_work;       /* work items written                          */
+    int32_t n_active;     /* rows covered (= seg_start[n_seg])           */
+    int32_t max_rank;     /* largest rank among the items                */
+    int32_t max_adapter;  /* largest adapter id among the items (-1 if none) */
+    int32_t n_ranges;
+    lora_range_t ranges[LORA_MAX_RANGES];
+} lora_plan_info_t;
+
+/* What lora_shrink / lora_expand need to launch one plan. */
+typedef struct lora_launch {
+    const int32_t* row_index;   /* device int32 [info.n_active] (lora_build_segments) */
+    const lora_work_t* work;    /* device [info.n_work] (lora_plan, same op)           */
+    lora_plan_info_t info;      /* host copy of the plan summary                      */
+} lora_launch_t;
+
+/* One projection of a shrink: v[p][j] = sum_k x[row_index[p]][k] * A_a[j][k].
+ *   x  device bf16 [*][ldx], 16-byte aligned, ldx % 8 == 0, ldx >= d_in
+ *   v  device fp32 [n_active][ldv], 16-byte aligned, ldv % 4 == 0,
+ *      ldv >= info.max_rank; columns j >= r_a of a row are not written      */
+typedef struct lora_shrink_proj {
+    const uint16_t* x;
+    int64_t ldx;
+    int32_t d_in;
+    lora_rows_t A;
+    float* v;
+    int64_t ldv;
+} lora_shrink_proj_t;
+
+/* One projection of an expand: y[row_index[p]][n] += scale * sum_j v[p][j] * B_a[j][n].
+ *   v  device fp32 as written by lora_shrink (same ldv rules)
+ *   y  device fp32 [*][ldy], 16-byte aligned, ldy % 4 == 0, ldy >= d_out;
+ *      rows not listed in row_index are not touched                         */
+typedef struct lora_expand_proj {
+    const float* v;
+    int64_t ldv;
+    lora_rows_t B;
+    int32_t d_out;
+    float* y;
+    int64_t ldy;
+    float scale;
+} lora_expand_proj_t;
+
+/* One weight matrix of a merge/unmerge.
+ *   W  device bf16 [d_out][ldw], 16-byte aligned, ldw % 8 == 0, ldw >= d_in
+ *   A  rows of d_in (A.row_len == d_in), B rows of d_out (B.row_len == d_out)
+ *   adapter, rank: which adapter's rows 0..rank-1 to fold in            */
+typedef struct lora_merge_mat {
+    uint16_t* W;
+    int64_t ldw;
+    int32_t d_out;
+    int32_t d_in;
+    lora_rows_t A;
+    lora_rows_t B;
+    int32_t adapter;
+    int32_t rank;
+    float scale;
+} lora_merge_mat_t;
+
+/* ABI version (LORA_ABI_VERSION of the built library). */
+int32_t lora_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* lora_status_string(int32_t status);
+
+/* Segment metadata of a batch (host only, deterministic).
+ * Active rows are those with row_adapter[i] >= 0 (LoRazor article: a released
+ * row gets no LoRA work); they are listed in row_index ordered by
+ * (adapter id, row index), and grouped into one segment per distinct adapter,
+ * in ascending adapter id (BEE-30060 page, Punica paragraph: requests are
+ * grouped by adapter identity).
+ *   row_adapter   host int32 [n_rows], each in [-1, n_adapters)
+ *   adapter_rank  host int32 [n_adapters], each in [1, LORA_MAX_RANK]
+ *   row_index     host int32 [n_rows] (capacity n_rows; n_active written)
+ *   seg_start     host int32 [seg_capacity + 1]; seg_start[n_seg] == n_active
+ *   seg_adapter, seg_rank  host int32 [seg_capacity]
+ * Errors: LORA_EINVAL, LORA_EADAPTER, LORA_ERANK, LORA_ECAPACITY (n_seg and
+ * n_active are written, nothing else). */
+int32_t lora_build_segments(int32_t n_rows, const int32_t* row_adapter,
+                            int32_t n_adapters, const int32_t* adapter_rank,
+                            int32_t seg_capacity, int32_t* row_index,
+                            int32_t* seg_start, int32_t* seg_adapter,
+                            int32_t* seg_rank, int32_t* n_seg, int32_t* n_active);
+
+/* Launch plan for one op (host only).  Every segment is cut into work items of
+ * at most rows_per_item rows, where the kernel variant and rows_per_item come
+ * from a compiled-in table keyed by (op, segment length, rank, d) buckets
+ * (VaLoRA blog, section 4.3.2: the best tiling per input shape is found offline
+ * and looked up at run time).  Items cover only active rows and are grouped by
+ * variant.  At most n_active items are written (work_capacity >= n_active is
+ * always enough).
+ *   seg_*  as written by lora_build_segments
+ *   d_in, d_out  positive multiples of 64 (the largest over the projections
+ *                that will share this plan)
+ * Errors: LORA_EINVAL, LORA_ERANK, LORA_ESHAPE, LORA_ECAPACITY (info->n_work
+ * written). */
+int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
+                  const int32_t* seg_adapter, const int32_t* seg_rank,
+                  int32_t d_in, int32_t d_out, int32_t work_capacity,
+                  lora_work_t* work, lora_plan_info_t* info);
+
+/* Shrink for n_proj projections (1..LORA_MAX_PROJ) sharing one plan
+ * (launch->info.op == LORA_OP_SHRINK): one kernel launch per variant range.
+ * Errors: LORA_EINVAL, LORA_ESHAPE, LORA_EADAPTER / LORA_ERANK (summary does
+ * not fit the row tables), LORA_EHIP. */
+int32_t lora_shrink(const lora_launch_t* launch, int32_t n_proj,
+                    const lora_shrink_proj_t* projs, void* hip_stream);
+
+/* Expand for n_proj projections sharing one plan
+ * (launch->info.op == LORA_OP_EXPAND).  Same errors as lora_shrink. */
+int32_t lora_expand(const lora_launch_t* launch, int32_t n_proj,
+                    const lora_expand_proj_t* projs, void* hip_stream);
+
+/* Merge n_mats (1..LORA_MAX_MERGE) adapters into their weights in place, one
+ * launch: W <- RNE_bf16(W + scale * B_a^T A_a), with Delta W accumulated in
+ * fp32 and a single rounding to bf16.  Matrices must not overlap.
+ * Errors: LORA_EINVAL, LORA_ESHAPE, LORA_EADAPTER, LORA_ERANK, LORA_EHIP. */
+int32_t lora_merge(int32_t n_mats, const lora_merge_mat_t* mats, void* hip_stream);
+
+/* Unmerge: identical to lora_merge with every scale negated. */
+int32_t lora_unmerge(int32_t n_mats, const lora_merge_mat_t* mats, void* hip_stream);
+
+/* Row-offset table of the packed dense layout (host only): adapters in id
+ * order, rows j = 0..rank[a]-1 back to back, each row taking
+ * ceil(row_len/8)*8 elements; chunk c of a row sits c*chunk_len elements after
+ * the row start; slots j >= rank[a] are set to -1.
+ *   rank      host int32 [n_adapters], each in [1, max_rank]
+ *   row_off   host int64 [n_adapters * max_rank * ceil(row_len/chunk_len)]
+ *   pool_elems  host, receives the pool size in elements the layout needs
+ * Errors: LORA_EINVAL, LORA_ERANK, LORA_ESHAPE. */
+int32_t lora_rows_dense_offsets(int32_t n_adapters, int32_t max_rank,
+                                const int32_t* rank, int32_t row_len,
+                                int32_t chunk_len, int64_t* row_off,
+                                int64_t* pool_elems);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HETLORA_H */

@@ -1,0 +1,93 @@
+"""Shared code of the GPU parity tests: run the HIP path through the C ABI and
+compare with the oracle on the same seeded inputs."""
+import numpy as np
+import torch
+
+import oracle
+from heterogeneous_adapter_batching_amd.session import Batch, Rows, merge, unmerge
+from workloads.device import bits_to_device, to_device
+
+REL_F_TOL = 4e-3      # contract bound (relative Frobenius of the delta)
+ABS_TOL = 2e-2        # contract bound (max abs error of y)
+REL_F_EXPECT = 1e-4   # fp32 sums of exact bf16 products with a hi+lo split v land near 1e-6
+
+
+def rows_of(pool, desc, off):
+    return Rows(pool, off, desc.n_adapters, desc.max_rank, desc.row_len, desc.chunk_len)
+
+
+def run_delta(W, row_adapter=None, dw=None, scale=None, ldv=None):
+    """Shrink + expand for every projection of W; returns (batch, v list, y list) on the host."""
+    dw = dw if dw is not None else to_device(W)
+    ra = W.row_adapter if row_adapter is None else np.asarray(row_adapter, np.int32)
+    d_in = max(p.d_in for p in W.projections)
+    d_out = max(p.d_out for p in W.projections)
+    batch = Batch(max(1, W.n_rows), W.adapter_rank, d_in, d_out).refresh(ra)
+    ldv = ldv or -(-int(W.adapter_rank.max()) // 4) * 4
+    vs = [torch.full((max(1, batch.n_active), ldv), float("nan"), dtype=torch.float32, device="cuda")
+          for _ in W.projections]
+    s = W.scale if scale is None else scale
+    batch.shrink([(dp.x, rows_of(dw.pool, p.A, dp.A_off), v)
+                  for p, dp, v in zip(W.projections, dw.projections, vs)])
+    batch.expand([(v, rows_of(dw.pool, p.B, dp.B_off), dp.y, s)
+                  for p, dp, v in zip(W.projections, dw.projections, vs)])
+    torch.cuda.synchronize()
+    return batch, [v.cpu().numpy() for v in vs], [dp.y.cpu().numpy() for dp in dw.projections]
+
+
+def check_delta(W, batch, vs, ys, row_adapter=None, rows=None, scale=None, check_v=True):
+    """Compare GPU y (and v) with the oracle on `rows` (default: all rows)."""
+    ra = W.row_adapter if row_adapter is None else np.asarray(row_adapter, np.int32)
+    s = W.scale if scale is None else scale
+    rows = list(range(W.n_rows)) if rows is None else list(rows)
+    pos = {int(r): p for p, r in enumerate(batch.segs.row_index)}
+    report = []
+    for pi, p in enumerate(W.projections):
+        yref, vref = oracle.apply_ref(ra, W.adapter_rank, p.x, p.y0, W.pool, p.A, p.B, s, rows=rows)
+        num = den = 0.0
+        amax = 0.0
+        for i in rows:
+            y_gpu = ys[pi][i].astype(np.float64)
+            if ra[i] < 0:
+                assert np.array_equal(ys[pi][i], p.y0[i]), f"released row {i} touched"
+                continue
+            d_ref = yref[i] - p.y0[i].astype(np.float64)
+            d_gpu = y_gpu - p.y0[i].astype(np.float64)
+            num += float(np.sum((d_gpu - d_ref) ** 2))
+            den += float(np.sum(d_ref ** 2))
+            amax = max(amax, float(np.max(np.abs(y_gpu - yref[i]))))
+            if check_v:
+                r = int(W.adapter_rank[ra[i]])
+                vg = vs[pi][pos[i]]
+                np.testing.assert_allclose(vg[:r], vref[i], rtol=1e-4, atol=1e-4 * (1 + np.abs(vref[i]).max()))
+                assert np.all(np.isnan(vg[r:])), "v columns beyond the rank were written"
+        relF = (num / den) ** 0.5 if den > 0 else 0.0
+        assert np.isfinite(relF) and relF <= REL_F_TOL, (p.name, relF)
+        assert amax <= ABS_TOL, (p.name, amax)
+        assert relF <= REL_F_EXPECT, (p.name, relF)
+        report.append((p.name, relF, amax))
+    return report
+
+
+def ulp_compare(got_bits, ref_bits):
+    """Fraction of bf16 elements equal, and max |bit difference| of the rest."""
+    g = got_bits.astype(np.int32).reshape(-1)
+    r = ref_bits.astype(np.int32).reshape(-1)
+    eq = g == r
+    return float(eq.mean()), int(np.max(np.abs(g - r))) if not eq.all() else 0
+
+
+def run_merge(W_bits_list, dw, descs, adapter, rank, scale, unmerge_too=False):
+    """Merge adapter into each W (list of uint16 arrays) on the GPU; returns merged (and restored) bits."""
+    Ws = [bits_to_device(w) for w in W_bits_list]
+    mats = [(Wt, rows_of(dw.pool, A, Aoff), rows_of(dw.pool, B, Boff), adapter, rank, scale)
+            for Wt, (A, Aoff, B, Boff) in zip(Ws, descs)]
+    merge(mats)
+    torch.cuda.synchronize()
+    merged = [w.cpu().numpy().view(np.uint16).copy() for w in Ws]
+    restored = None
+    if unmerge_too:
+        unmerge(mats)
+        torch.cuda.synchronize()
+        restored = [w.cpu().numpy().view(np.uint16).copy() for w in Ws]
+    return merged, restored

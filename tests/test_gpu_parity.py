@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerances: relative Frobenius error of the delta <= 4e-3 and max abs error of
+y <= 2e-2 (the contract), plus a precision check relF <= 1e-4 (the kernels add
+exact bf16 products in fp32 with v split into two bf16 terms, so ~1e-6 is
+expected; a single-bf16 v would show up near 1e-3).  Metadata and the
+structural invariants (released rows, permutation, dense vs paged storage,
+s = 0, repeat runs) are bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import Projection, RowsDesc, Workload, build_pool, to_bf16_bits
+from workloads.device import to_device
+
+from gpu_helpers import check_delta, run_delta, run_merge, ulp_compare, rows_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _explicit_workload(x, A_list, B_list, row_adapter, y0, scale=2.0, layout="dense", page=64):
+    ranks = np.array([a.shape[0] for a in A_list], np.int32)
+    mr = int(ranks.max())
+    bits = lambda m: to_bf16_bits(np.asarray(m, np.float32))
+    pool, d = build_pool([("A", x.shape[1], [bits(a) for a in A_list]),
+                          ("B", y0.shape[1], [bits(b) for b in B_list])],
+                         len(A_list), mr, layout, page, np.random.default_rng(0))
+    proj = Projection("p", x.shape[1], y0.shape[1], bits(x), np.asarray(y0, np.float32), d["A"], d["B"])
+    ra = np.asarray(row_adapter, np.int32)
+    return Workload("explicit", 0, len(ra), ra, ranks, pool, [proj], scale, {"main": ra})
+
+
+# ------------------------------------------------------------------ workloads 0 and 1
+def test_tiny_sgmv_parity():
+    W = workloads.gen_config(0)
+    _say("tiny: rows", W.n_rows, "segments", oracle.build_segments_ref(W.row_adapter, W.adapter_rank).n_seg)
+    batch, vs, ys = run_delta(W)
+    ref = oracle.build_segments_ref(W.row_adapter, W.adapter_rank)
+    assert np.array_equal(batch.segs.row_index, ref.row_index)
+    _say(check_delta(W, batch, vs, ys))
+
+
+@pytest.mark.parametrize("which", ["hetero", "homo"])
+def test_decode_bgmv_parity(which):
+    W = workloads.gen_config(1)
+    ra = W.batches[which]
+    _say("decode", which)
+    batch, vs, ys = run_delta(W, ra)
+    _say(check_delta(W, batch, vs, ys, row_adapter=ra))
+
+
+def test_tiny_merge_parity_and_restore():
+    W = workloads.gen_config(0)
+    dw = to_device(W)
+    p = W.projections[0]
+    Wb = W.merge.weight(0, 0)
+    r = int(W.adapter_rank[W.merge.adapter])
+    merged, restored = run_merge([Wb], dw, [(p.A, dw.projections[0].A_off, p.B, dw.projections[0].B_off)],
+                                 W.merge.adapter, r, W.scale, unmerge_too=True)
+    ref = oracle.merge_ref(Wb, W.pool, p.A, p.B, W.merge.adapter, r, W.scale)
+    frac, maxd = ulp_compare(merged[0], ref)
+    _say("tiny merge: equal fraction", frac, "max ulp", maxd)
+    assert frac >= 0.9999 and maxd <= 1
+    # restore after unmerge, against the oracle's own unmerge of the GPU result and against W
+    ref_r = oracle.unmerge_ref(merged[0], W.pool, p.A, p.B, W.merge.adapter, r, W.scale)
+    frac_r, maxd_r = ulp_compare(restored[0], ref_r)
+    assert frac_r >= 0.9999 and maxd_r <= 1
+    w0, w2 = oracle.bf16_to_f64(Wb), oracle.bf16_to_f64(restored[0])
+    relF = np.linalg.norm(w2 - w0) / np.linalg.norm(w0)
+    assert relF <= 4e-3 and np.max(np.abs(w2 - w0)) <= 2e-2
+    # merged == unmerged inference (S-LoRA formula 1 vs formula 2)
+    x = oracle.bf16_to_f64(p.x)
+    Aa = oracle.gather_rows_ref(W.pool, p.A.row_off, p.A.max_rank, p.A.row_len, p.A.chunk_len, 0, r)
+    Ba = oracle.gather_rows_ref(W.pool, p.B.row_off, p.B.max_rank, p.B.row_len, p.B.chunk_len, 0, r)
+    f1 = x @ oracle.bf16_to_f64(merged[0]).T
+    f2 = x @ w0.T + W.scale * (x @ Aa.T) @ Ba
+    assert np.linalg.norm(f1 - f2) / np.linalg.norm(f2) <= 4e-3
+
+
+# ------------------------------------------------------------------ exact cases and invariants
+def test_rank1_closed_form_bit_exact():
+    d = 64
+    x = np.zeros((3, d)); x[0, :8] = np.arange(-3, 5); x[1, :8] = np.arange(5, -3, -1); x[2, 2] = 7
+    a = np.zeros((1, d)); a[0, 2] = 1.0
+    b = np.zeros((1, d)); b[0, :4] = [1.0, 0.5, -2.0, 4.0]; b[0, 63] = 0.25
+    W = _explicit_workload(x, [a], [b], [0, 0, -1], np.zeros((3, d)))
+    _, _, ys = run_delta(W)
+    want = np.zeros((3, d), np.float32)
+    for i in range(2):
+        want[i] = 2.0 * x[i, 2] * b[0]
+    assert np.array_equal(ys[0], want)
+    assert ys[0][0, :4].tolist() == [-2.0, -1.0, 4.0, -8.0]
+
+
+def test_scale_zero_keeps_y():
+    W = workloads.gen_custom(21, np.repeat([0, 1, 2, -1], [5, 40, 130, 3]), [7, 33, 64], 256, 320)
+    _, _, ys = run_delta(W, scale=0.0)
+    assert np.array_equal(ys[0], W.projections[0].y0)
+
+
+def test_permutation_bit_identical():
+    ra = np.repeat([0, 1, 2, 3, 1], [1, 20, 70, 300, 9])
+    W = workloads.gen_custom(22, ra, [16, 64, 8, 32], 512, 576, n_proj=2)
+    _, _, ys = run_delta(W)
+    perm = np.random.default_rng(3).permutation(W.n_rows)
+    Wp = Workload(W.name, W.seed, W.n_rows, W.row_adapter[perm], W.adapter_rank, W.pool,
+                  [Projection(p.name, p.d_in, p.d_out, p.x[perm], p.y0[perm], p.A, p.B) for p in W.projections],
+                  W.scale)
+    _, _, ysp = run_delta(Wp)
+    for y, yp in zip(ys, ysp):
+        assert np.array_equal(yp, y[perm])
+
+
+def test_released_rows_untouched_and_active_rows_unchanged():
+    rng = np.random.default_rng(4)
+    ra = np.repeat(rng.integers(0, 6, size=12), rng.integers(1, 60, size=12))
+    W = workloads.gen_custom(23, ra, [4, 16, 24, 40, 64, 128], 384, 448)
+    keep = rng.random(W.n_rows) < 0.6
+    ra_rel = np.where(keep, ra, -1)
+    batch, vs, ys = run_delta(W, ra_rel)
+    p = W.projections[0]
+    assert np.array_equal(ys[0][~keep], p.y0[~keep])
+    # the same batch with the released rows deleted gives bit-identical active rows
+    idx = np.nonzero(keep)[0]
+    Wd = Workload(W.name, W.seed, len(idx), ra[idx], W.adapter_rank, W.pool,
+                  [Projection(p.name, p.d_in, p.d_out, p.x[idx], p.y0[idx], p.A, p.B)], W.scale)
+    _, _, ysd = run_delta(Wd)
+    assert np.array_equal(ysd[0], ys[0][idx])
+    check_delta(W, batch, vs, ys, row_adapter=ra_rel)
+
+
+@pytest.mark.parametrize("page", [64, 192])
+def test_dense_vs_paged_bit_identical(page):
+    ra = np.repeat([2, 0, 1, 2], [3, 100, 17, 260])
+    Wd = workloads.gen_custom(24, ra, [12, 48, 100], 640, 896, layout="dense")
+    Wp = workloads.gen_custom(24, ra, [12, 48, 100], 640, 896, layout="paged", page_elems=page)
+    assert Wp.projections[0].B.chunks > 1
+    _, vd, yd = run_delta(Wd)
+    batch, vp, yp = run_delta(Wp)
+    assert np.array_equal(yd[0], yp[0])
+    assert np.array_equal(np.nan_to_num(vd[0], nan=7.0), np.nan_to_num(vp[0], nan=7.0))
+    check_delta(Wp, batch, vp, yp)
+
+
+def test_repeat_runs_bit_identical():
+    ra = np.repeat([0, 1, 2], [1, 33, 513])
+    W = workloads.gen_custom(25, ra, [16, 96, 64], 1024, 1024, n_proj=3)
+    dw = to_device(W)
+    _, _, y1 = run_delta(W, dw=dw)
+    for _ in range(3):
+        from workloads.device import reset_outputs
+        reset_outputs(W, dw)
+        _, _, y2 = run_delta(W, dw=dw)
+        for a, b in zip(y1, y2):
+            assert np.array_equal(a, b)
+
+
+def test_empty_batch_no_work():
+    W = workloads.gen_custom(26, [-1, -1, -1], [8], 128, 128)
+    batch, vs, ys = run_delta(W)
+    assert batch.n_active == 0 and batch.info_shrink.n_work == 0
+    assert np.array_equal(ys[0], W.projections[0].y0)
+
+
+@pytest.mark.parametrize("seed", range(100, 110))
+def test_random_shapes_parity(seed):
+    """Every kernel variant: segment lengths 1..700, ranks 1..128, d 64..2048 with ragged 64-multiples."""
+    rng = np.random.default_rng(seed)
+    n_ad = int(rng.integers(1, 10))
+    ranks = rng.integers(1, 129, size=n_ad)
+    ranks[0] = int(rng.choice([1, 8, 16, 17, 32, 33, 64, 65, 127, 128]))
+    lens = rng.choice([1, 2, 3, 5, 9, 16, 17, 31, 64, 65, 127, 128, 129, 300, 700], size=int(rng.integers(1, 9)))
+    ra = np.repeat(rng.integers(-1, n_ad, size=len(lens)), lens)
+    d_in = 64 * int(rng.integers(1, 33))
+    d_out = 64 * int(rng.integers(1, 33))
+    layout = "paged" if seed % 3 == 0 else "dense"
+    W = workloads.gen_custom(seed, ra, ranks, d_in, d_out, n_proj=1 + seed % 3, layout=layout,
+                             page_elems=64 * int(rng.integers(1, 5)))
+    _say("random", seed, "rows", W.n_rows, "ranks", ranks.tolist(), "d", d_in, d_out, layout)
+    batch, vs, ys = run_delta(W)
+    _say(check_delta(W, batch, vs, ys))
+
+
+@pytest.mark.parametrize("d_out,d_in,r", [(64, 192, 1), (576, 320, 17), (1024, 512, 64), (256, 704, 128)])
+def test_merge_shapes_parity(d_out, d_in, r):
+    rng = np.random.default_rng(d_out + d_in + r)
+    n_ad = 3
+    ranks = np.array([r, max(1, r // 2), 5])
+    W = workloads.gen_custom(int(d_out + r), [0], ranks, d_in, d_out, layout="paged" if r % 2 else "dense",
+                             page_elems=128)
+    dw = to_device(W)
+    p = W.projections[0]
+    Wb = to_bf16_bits(rng.standard_normal((d_out, d_in)).astype(np.float32) / np.sqrt(d_in))
+    a = int(rng.integers(0, n_ad)) if r > 1 else 0
+    ra_ = int(ranks[a])
+    merged, restored = run_merge([Wb], dw, [(p.A, dw.projections[0].A_off, p.B, dw.projections[0].B_off)],
+                                 a, ra_, 2.0, unmerge_too=True)
+    ref = oracle.merge_ref(Wb, W.pool, p.A, p.B, a, ra_, 2.0)
+    frac, maxd = ulp_compare(merged[0], ref)
+    _say("merge", d_out, d_in, r, "equal", frac, "max ulp", maxd)
+    assert frac >= 0.9999 and maxd <= 1
+    w0, w2 = oracle.bf16_to_f64(Wb), oracle.bf16_to_f64(restored[0])
+    assert np.linalg.norm(w2 - w0) / np.linalg.norm(w0) <= 4e-3

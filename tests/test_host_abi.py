@@ -1,0 +1,267 @@
+"""CPU tests of the C-ABI library: exports, host-side entry points, error paths.
+
+No kernel is launched here.  The library's host functions (segment builder,
+planner, dense offsets) are compared bit-exactly with the oracle's definitions;
+shrink/expand/merge are called only with arguments that fail validation, which
+returns before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import heterogeneous_adapter_batching_amd as hl
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(lora_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 9, names
+    lib = ctypes.CDLL(hl.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert hl.lora_abi_version() == hl.LORA_ABI_VERSION
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert hl.lora_status_string(code) != "unknown status"
+
+
+# ---------------------------------------------------------------- segments
+def _same(a, b):
+    for k in ("row_index", "seg_start", "seg_adapter", "seg_rank"):
+        assert np.array_equal(getattr(a, k), getattr(b, k)), k
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 4])
+def test_build_segments_matches_oracle_on_workloads(k):
+    # structure only: avoid drawing the big tensors of the large workloads
+    rng = np.random.default_rng([k, 0])
+    W = workloads.gen_config(k) if k <= 1 else None
+    if W is not None:
+        batches = list(W.batches.values())
+        ranks = W.adapter_rank
+    else:
+        gen = {2: workloads.gen_prefill, 3: workloads.gen_vision, 4: workloads.gen_mix70b}[k]
+        batches, ranks = _structure_only(gen, k)
+    for ra in batches:
+        _same(hl.lora_build_segments(ra, ranks), oracle.build_segments_ref(ra, ranks))
+
+
+def _structure_only(gen, seed):
+    """Replay a generator's structure draws without drawing tensors."""
+    import math
+    rng = np.random.default_rng([seed, 0])
+    if gen is workloads.gen_prefill:
+        z = rng.standard_normal(16)
+        lens = np.clip(np.rint(np.exp(math.log(512.0) + 0.6 * z)), 32, 2048).astype(np.int64)
+        ranks = rng.choice(np.array([8, 16, 32, 64]), size=16)
+        ad = workloads._zipf_choice(rng, 16, 16)
+        return [np.repeat(ad, lens)], ranks
+    if gen is workloads.gen_vision:
+        lens = rng.integers(256, 1025, size=24) + 32
+        ad = workloads._zipf_choice(rng, 32, 24)
+        return [np.repeat(ad, lens)], np.full(32, 64)
+    ranks = rng.choice(np.array([16, 32, 64]), size=128)
+    dec = rng.integers(0, 128, size=256)
+    released = rng.choice(256, size=128, replace=False)
+    dec[released] = -1
+    pre = np.repeat(rng.integers(0, 128, size=8), 1024)
+    return [np.concatenate([dec, pre])], ranks
+
+
+def test_build_segments_matches_oracle_random():
+    rng = np.random.default_rng(5)
+    for t in range(1000):
+        n = int(rng.integers(0, 50))
+        n_ad = int(rng.integers(1, 12))
+        ranks = rng.integers(1, 129, size=n_ad)
+        mode = t % 4
+        if mode == 0:
+            ra = rng.integers(-1, n_ad, size=n)
+        elif mode == 1:        # all released
+            ra = np.full(n, -1)
+        elif mode == 2:        # one adapter, non-adjacent repeats
+            ra = np.where(rng.random(n) < 0.5, -1, int(rng.integers(0, n_ad)))
+        else:                  # runs of repeated adapters
+            ra = np.repeat(rng.integers(-1, n_ad, size=max(1, n // 5)), 5)[:n]
+        _same(hl.lora_build_segments(ra, ranks), oracle.build_segments_ref(ra, ranks))
+
+
+def test_build_segments_error_codes_and_no_writes():
+    lib = hl._lib
+    sentinel = -12345
+
+    def call(ra, rk, cap):
+        ra = np.asarray(ra, np.int32); rk = np.asarray(rk, np.int32)
+        outs = [np.full(max(1, len(ra)), sentinel, np.int32), np.full(cap + 1, sentinel, np.int32),
+                np.full(max(1, cap), sentinel, np.int32), np.full(max(1, cap), sentinel, np.int32)]
+        ns, na = ctypes.c_int32(sentinel), ctypes.c_int32(sentinel)
+        st = lib.lora_build_segments(len(ra), ra.ctypes.data if len(ra) else None, len(rk),
+                                     rk.ctypes.data if len(rk) else None, cap,
+                                     *[o.ctypes.data for o in outs], ctypes.byref(ns), ctypes.byref(na))
+        return st, outs, ns.value, na.value
+
+    st, outs, ns, na = call([0, 2], [4, 4], 2)
+    assert st == hl.LORA_EADAPTER and all(np.all(o == sentinel) for o in outs) and ns == sentinel
+    st, outs, *_ = call([0, -2], [4], 1)
+    assert st == hl.LORA_EADAPTER
+    st, outs, *_ = call([0], [0], 1)
+    assert st == hl.LORA_ERANK and all(np.all(o == sentinel) for o in outs)
+    st, outs, *_ = call([0], [129], 1)
+    assert st == hl.LORA_ERANK
+    st, outs, ns, na = call([0, 1, 2, 1], [4, 4, 4], 2)           # needs 3 segments
+    assert st == hl.LORA_ECAPACITY and ns == 3 and na == 4
+    assert all(np.all(o == sentinel) for o in outs)
+    st, outs, ns, na = call([], [4], 0)                             # empty batch
+    assert st == hl.LORA_OK and ns == 0 and na == 0 and outs[1][0] == 0
+    st, outs, ns, na = call([-1, -1], [4], 0)                       # all released
+    assert st == hl.LORA_OK and ns == 0 and na == 0
+    assert lib.lora_build_segments(-1, None, 1, None, 0, None, None, None, None, None, None) == hl.LORA_EINVAL
+
+
+# ---------------------------------------------------------------- plan
+def test_plan_coverage_invariants():
+    rng = np.random.default_rng(8)
+    cases = [np.repeat(rng.integers(-1, 20, size=40), rng.integers(1, 400, size=40)) for _ in range(30)]
+    cases += [np.arange(64), np.zeros(64, int), np.full(3000, 2), np.array([5])]
+    for ra in cases:
+        ranks = rng.integers(1, 129, size=int(ra.max()) + 1 if ra.max() >= 0 else 1)
+        segs = hl.lora_build_segments(ra, ranks)
+        for op in (hl.LORA_OP_SHRINK, hl.LORA_OP_EXPAND):
+            for d_in, d_out in ((512, 512), (4096, 4096), (8192, 28672)):
+                work, info = hl.lora_plan(op, segs, d_in, d_out)
+                assert info.n_active == segs.n_active and info.n_work == work.shape[0]
+                oracle.check_plan_coverage(segs, work, info.range_list())
+                if segs.n_seg:
+                    assert info.max_rank == segs.seg_rank.max()
+                    assert info.max_adapter == segs.seg_adapter.max()
+                assert work.shape[0] <= segs.n_active
+
+
+def test_plan_errors():
+    segs = hl.lora_build_segments([0, 0, 1], [8, 16])
+    with pytest.raises(hl.LoraError) as e:
+        hl.lora_plan(hl.LORA_OP_SHRINK, segs, 100, 512)
+    assert e.value.code == hl.LORA_ESHAPE
+    with pytest.raises(hl.LoraError) as e:
+        hl.lora_plan(7, segs, 512, 512)
+    assert e.value.code == hl.LORA_EINVAL
+    with pytest.raises(hl.LoraError) as e:
+        hl.lora_plan(hl.LORA_OP_SHRINK, segs, 512, 512, work_capacity=1)
+    assert e.value.code == hl.LORA_ECAPACITY
+    empty = hl.lora_build_segments([-1, -1], [8])
+    work, info = hl.lora_plan(hl.LORA_OP_EXPAND, empty, 512, 512)
+    assert info.n_work == 0 and info.n_ranges == 0
+
+
+# ---------------------------------------------------------------- dense offsets
+def test_dense_offsets_match_oracle():
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "delta_worked.json")))["dense_offsets"]
+    off, pe = hl.lora_rows_dense_offsets(g["adapter_rank"], g["max_rank"], g["row_len"], g["chunk_len"])
+    assert off.tolist() == g["expected"] and pe == 6 * 104
+    rng = np.random.default_rng(2)
+    for _ in range(50):
+        n_ad = int(rng.integers(1, 9)); mr = int(rng.integers(1, 129))
+        rk = rng.integers(1, mr + 1, size=n_ad)
+        rl = int(rng.integers(1, 5000)); cl = 64 * int(rng.integers(1, 40))
+        off, _ = hl.lora_rows_dense_offsets(rk, mr, rl, cl)
+        assert np.array_equal(off, oracle.dense_offsets_ref(rk, mr, rl, cl))
+    with pytest.raises(hl.LoraError) as e:
+        hl.lora_rows_dense_offsets([4], 4, 512, 100)
+    assert e.value.code == hl.LORA_ESHAPE
+    with pytest.raises(hl.LoraError) as e:
+        hl.lora_rows_dense_offsets([5], 4, 512, 64)
+    assert e.value.code == hl.LORA_ERANK
+
+
+# ---------------------------------------------------------------- launch validation (no launch)
+def _launch(op, n_work=1, max_rank=16, max_adapter=0):
+    info = hl.lora_plan_info_t()
+    info.op, info.n_work, info.n_active, info.max_rank, info.max_adapter = op, n_work, n_work, max_rank, max_adapter
+    info.n_ranges = 1
+    info.ranges[0].variant, info.ranges[0].begin, info.ranges[0].count, info.ranges[0].rows_per_item = 0, 0, n_work, 16
+    return hl.lora_launch_t(0x1000, 0x2000, info)
+
+
+def _rows(row_len=512, chunk_len=512, max_rank=16, n_ad=4, pool=0x10000):
+    return hl.lora_rows_t(pool, 0x20000, n_ad, max_rank, row_len, chunk_len)
+
+
+def test_shrink_expand_merge_validation_errors():
+    lib = hl._lib
+    L = _launch(hl.LORA_OP_SHRINK)
+
+    def shrink(**kw):
+        p = dict(x=0x30000, ldx=512, d_in=512, A=_rows(), v=0x40000, ldv=16)
+        p.update(kw)
+        arr = (hl.lora_shrink_proj_t * 1)(hl.lora_shrink_proj_t(**p))
+        return lib.lora_shrink(ctypes.byref(L), 1, arr, None)
+
+    assert shrink(x=None) == hl.LORA_EINVAL
+    assert shrink(x=0x30008) == hl.LORA_EINVAL                 # misaligned
+    assert shrink(d_in=500, ldx=512, A=_rows(row_len=500)) == hl.LORA_ESHAPE
+    assert shrink(ldx=256) == hl.LORA_EINVAL                   # ld < d
+    assert shrink(ldv=8) == hl.LORA_EINVAL                     # ldv < max rank
+    assert shrink(A=_rows(max_rank=8)) == hl.LORA_ERANK
+    assert shrink(A=_rows(n_ad=0)) == hl.LORA_EADAPTER
+    assert shrink(A=_rows(chunk_len=100)) == hl.LORA_ESHAPE
+    assert shrink(A=_rows(row_len=1024)) == hl.LORA_ESHAPE
+    Lbad = _launch(hl.LORA_OP_EXPAND)
+    arr = (hl.lora_shrink_proj_t * 1)(hl.lora_shrink_proj_t(0x30000, 512, 512, _rows(), 0x40000, 16))
+    assert lib.lora_shrink(ctypes.byref(Lbad), 1, arr, None) == hl.LORA_EINVAL   # wrong op
+    assert lib.lora_shrink(ctypes.byref(L), 0, arr, None) == hl.LORA_EINVAL
+    assert lib.lora_shrink(ctypes.byref(L), 9, arr, None) == hl.LORA_EINVAL
+
+    LE = _launch(hl.LORA_OP_EXPAND)
+
+    def expand(**kw):
+        p = dict(v=0x40000, ldv=16, B=_rows(), d_out=512, y=0x50000, ldy=512, scale=2.0)
+        p.update(kw)
+        arr = (hl.lora_expand_proj_t * 1)(hl.lora_expand_proj_t(**p))
+        return lib.lora_expand(ctypes.byref(LE), 1, arr, None)
+
+    assert expand(y=None) == hl.LORA_EINVAL
+    assert expand(y=0x50004) == hl.LORA_EINVAL
+    assert expand(ldy=510) == hl.LORA_EINVAL
+    assert expand(d_out=96, ldy=96, B=_rows(row_len=96)) == hl.LORA_ESHAPE
+    assert expand(B=_rows(max_rank=4)) == hl.LORA_ERANK
+
+    def merge(**kw):
+        p = dict(W=0x60000, ldw=512, d_out=512, d_in=512, A=_rows(), B=_rows(), adapter=0, rank=16, scale=2.0)
+        p.update(kw)
+        arr = (hl.lora_merge_mat_t * 1)(hl.lora_merge_mat_t(**p))
+        return lib.lora_merge(1, arr, None), lib.lora_unmerge(1, arr, None)
+
+    assert merge(W=None) == (hl.LORA_EINVAL,) * 2
+    assert merge(rank=0) == (hl.LORA_ERANK,) * 2
+    assert merge(rank=32) == (hl.LORA_ERANK,) * 2              # beyond the tables' max_rank
+    assert merge(adapter=4) == (hl.LORA_EADAPTER,) * 2
+    assert merge(adapter=-1) == (hl.LORA_EADAPTER,) * 2
+    assert merge(d_in=100) == (hl.LORA_ESHAPE,) * 2
+    assert merge(ldw=256) == (hl.LORA_EINVAL,) * 2
+    assert lib.lora_merge(0, None, None) == hl.LORA_EINVAL
+    assert lib.lora_merge(9, None, None) == hl.LORA_EINVAL
+
+
+def test_empty_batch_launches_nothing():
+    # n_work == 0 returns OK before any HIP call (works without a GPU)
+    lib = hl._lib
+    L = _launch(hl.LORA_OP_SHRINK, n_work=0)
+    L.info.n_ranges = 0
+    arr = (hl.lora_shrink_proj_t * 1)(hl.lora_shrink_proj_t(0x30000, 512, 512, _rows(), 0x40000, 16))
+    assert lib.lora_shrink(ctypes.byref(L), 1, arr, None) == hl.LORA_OK
