@@ -81,8 +81,16 @@ __device__ __forceinline__ void transpose8x8(const u32x4_t r[8], u32x4_t out[8])
 struct Rows {
     const uint16_t* pool;
     const int64_t* row_off;
-    int32_t max_rank, chunk_len, chunks;
+    int32_t n_adapters, max_rank, chunk_len, chunks;
 };
+
+// A work item is used only if it lies inside the launch's rows and fits the
+// row tables and the kernel's rank capacity; anything else is skipped, so a
+// corrupted work list cannot index outside the buffers.
+__device__ __forceinline__ bool item_ok(const lora_work_t& it, int32_t n_active, const Rows& t, int32_t rank_cap) {
+    return it.nrows > 0 && it.row0 >= 0 && it.row0 + it.nrows <= n_active && it.adapter >= 0 &&
+           it.adapter < t.n_adapters && it.rank >= 1 && it.rank <= rank_cap && it.rank <= t.max_rank;
+}
 __device__ __forceinline__ const uint16_t* row_ptr(const Rows& t, int32_t a, int32_t j, int32_t col) {
     const int32_t c = col / t.chunk_len;
     return t.pool + t.row_off[((int64_t)a * t.max_rank + j) * t.chunks + c] + (col - c * t.chunk_len);
@@ -101,6 +109,7 @@ struct ShrinkArgs {
     const int32_t* row_index;
     const lora_work_t* work;
     int32_t begin;
+    int32_t n_active;
     ShrinkProj p[LORA_MAX_PROJ];
 };
 
@@ -113,6 +122,7 @@ template <int KSPLIT, int MTW, int NT, int U>
 __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
     const lora_work_t it = args.work[args.begin + blockIdx.x];
     const ShrinkProj& P = args.p[blockIdx.y];
+    if (!item_ok(it, args.n_active, P.A, 16 * NT) || it.nrows > 16 * MTW * (KSPLIT > 1 ? 1 : 4)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int mbase = KSPLIT > 1 ? 0 : wave * 16 * MTW;
@@ -221,6 +231,7 @@ struct ExpandArgs {
     const int32_t* row_index;
     const lora_work_t* work;
     int32_t begin;
+    int32_t n_active;
     int32_t n_proj;
     ExpandProj p[LORA_MAX_PROJ];
 };
@@ -236,6 +247,7 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     int pi = 0;
     while (pi + 1 < args.n_proj && (int)blockIdx.y >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
+    if (!item_ok(it, args.n_active, P.B, 32 * KS)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int col0 = ((int)blockIdx.y - P.cg_begin) * 512 + wave * 128;
@@ -422,7 +434,7 @@ int32_t check_rows(const lora_rows_t& r, int32_t d, int32_t max_rank, int32_t ma
 }
 
 Rows to_rows(const lora_rows_t& r) {
-    return Rows{r.pool, r.row_off, r.max_rank, r.chunk_len, (r.row_len + r.chunk_len - 1) / r.chunk_len};
+    return Rows{r.pool, r.row_off, r.n_adapters, r.max_rank, r.chunk_len, (r.row_len + r.chunk_len - 1) / r.chunk_len};
 }
 
 int32_t check_launch(const lora_launch_t* L, int32_t op, int32_t n_proj) {
@@ -474,6 +486,7 @@ extern "C" int32_t lora_shrink(const lora_launch_t* L, int32_t n_proj, const lor
     ShrinkArgs args;
     args.row_index = L->row_index;
     args.work = L->work;
+    args.n_active = L->info.n_active;
     for (int i = 0; i < n_proj; ++i) {
         const lora_shrink_proj_t& p = projs[i];
         if (!p.x || !p.v || !aligned16(p.x) || !aligned16(p.v)) return LORA_EINVAL;
@@ -501,6 +514,7 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
     ExpandArgs args;
     args.row_index = L->row_index;
     args.work = L->work;
+    args.n_active = L->info.n_active;
     args.n_proj = n_proj;
     int32_t groups = 0;
     for (int i = 0; i < n_proj; ++i) {

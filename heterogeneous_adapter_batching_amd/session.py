@@ -14,6 +14,17 @@ from . import (LORA_OP_EXPAND, LORA_OP_SHRINK, lora_build_segments, lora_expand,
                lora_merge_mat_t, lora_shrink_proj_t)
 
 
+def staging_layout(n_active, n_work_shrink, n_work_expand):
+    """Byte offsets of (row_index, shrink work, expand work) in the staging
+    buffer, and its size in int32 elements: row_index is int32 [n_active],
+    each work item 4 int32 (16 bytes)."""
+    ri = 0
+    ws = 4 * n_active
+    we = ws + 16 * n_work_shrink
+    n = max(1, n_active + 4 * (n_work_shrink + n_work_expand))
+    return ri, ws, we, n
+
+
 def stream_handle(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -60,7 +71,7 @@ class Batch:
         h[:na] = segs.row_index
         h[na:na + 4 * ns] = ws.reshape(-1)
         h[na + 4 * ns:na + 4 * (ns + ne)] = we.reshape(-1)
-        n = max(1, na + 4 * (ns + ne))
+        o_ri, o_ws, o_we, n = staging_layout(na, ns, ne)
         with torch.cuda.stream(stream) if stream is not None else _null():
             self._dev[:n].copy_(self._host[:n], non_blocking=True)
             self._copied = torch.cuda.Event()
@@ -68,8 +79,8 @@ class Batch:
         base = self._dev.data_ptr()
         self.segs, self.work_shrink, self.work_expand = segs, ws, we
         self.info_shrink, self.info_expand = info_s, info_e
-        self.shrink_launch = make_launch(base, base + 4 * na, info_s)
-        self.expand_launch = make_launch(base, base + 4 * (na + ns), info_e)
+        self.shrink_launch = make_launch(base + o_ri, base + o_ws, info_s)
+        self.expand_launch = make_launch(base + o_ri, base + o_we, info_e)
         return self
 
     @property

@@ -77,6 +77,32 @@ def ulp_compare(got_bits, ref_bits):
     return float(eq.mean()), int(np.max(np.abs(g - r))) if not eq.all() else 0
 
 
+def check_merge_bits(got_bits, W_bits, Aa, Ba, scale, min_equal=0.9999):
+    """Merged W from the GPU against the oracle.
+
+    The oracle rounds the exact W + s*B^T A once to bf16.  The kernel rounds
+    W + s*dW once too, but accumulates dW over the rank in fp32, so an element
+    may differ from the oracle's bits where that fp32 error straddles a
+    rounding boundary -- rarely, and by several ulps only where W and s*dW
+    nearly cancel.  Required: >= min_equal of the elements bit-identical, and
+    every element within half a bf16 ulp plus an fp32 accumulation bound of
+    one fp32 ulp per added term, (r + 4) * 2^-23 * |s| * (|B|^T |A|), plus the
+    final fp32 rounding 2^-23 * |exact|, of the exact value."""
+    ref = oracle.merge_dense_ref(W_bits, Aa, Ba, scale)
+    frac, maxd = ulp_compare(got_bits, ref)
+    exact = oracle.bf16_to_f64(W_bits) + scale * (Ba.T @ Aa)
+    got = oracle.bf16_to_f64(got_bits)
+    r = Aa.shape[0]
+    mag = np.abs(Ba).T @ np.abs(Aa)
+    a = np.maximum(np.abs(got), 2.0 ** -126)
+    ulp = np.exp2(np.floor(np.log2(a)) - 7)
+    bound = 0.5 * ulp + (r + 4) * 2.0 ** -23 * abs(scale) * mag + 2.0 ** -23 * np.abs(exact)
+    worst = float(np.max(np.abs(got - exact) / bound))
+    assert frac >= min_equal, (frac, maxd)
+    assert worst <= 1.0, worst
+    return frac, maxd, worst
+
+
 def run_merge(W_bits_list, dw, descs, adapter, rank, scale, unmerge_too=False):
     """Merge adapter into each W (list of uint16 arrays) on the GPU; returns merged (and restored) bits."""
     Ws = [bits_to_device(w) for w in W_bits_list]

@@ -265,3 +265,18 @@ def test_empty_batch_launches_nothing():
     L.info.n_ranges = 0
     arr = (hl.lora_shrink_proj_t * 1)(hl.lora_shrink_proj_t(0x30000, 512, 512, _rows(), 0x40000, 16))
     assert lib.lora_shrink(ctypes.byref(L), 1, arr, None) == hl.LORA_OK
+
+
+def test_staging_layout_matches_host_packing():
+    # the device copy of (row_index, shrink work, expand work) is packed as int32
+    from heterogeneous_adapter_batching_amd.session import staging_layout
+    segs = hl.lora_build_segments(np.repeat([0, 1, 2], [5, 70, 300]), [8, 16, 64])
+    ws, _ = hl.lora_plan(hl.LORA_OP_SHRINK, segs, 512, 512)
+    we, _ = hl.lora_plan(hl.LORA_OP_EXPAND, segs, 512, 512)
+    buf = np.concatenate([segs.row_index, ws.reshape(-1), we.reshape(-1)]).astype(np.int32)
+    o_ri, o_ws, o_we, n = staging_layout(segs.n_active, ws.shape[0], we.shape[0])
+    raw = buf.tobytes()
+    assert n == buf.shape[0]
+    assert np.array_equal(np.frombuffer(raw[o_ri:o_ri + 4 * segs.n_active], np.int32), segs.row_index)
+    assert np.array_equal(np.frombuffer(raw[o_ws:o_ws + 16 * ws.shape[0]], np.int32).reshape(-1, 4), ws)
+    assert np.array_equal(np.frombuffer(raw[o_we:o_we + 16 * we.shape[0]], np.int32).reshape(-1, 4), we)
