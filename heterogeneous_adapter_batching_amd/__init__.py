@@ -15,11 +15,13 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
-LORA_ABI_VERSION = 1
+LORA_ABI_VERSION = 2
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
 LORA_MAX_RANGES = 16
 LORA_MAX_MERGE = 8
+LORA_MAX_SLICES = 16
+WORK_INTS = 8  # int32 fields of lora_work_t
 LORA_OK, LORA_EINVAL, LORA_EADAPTER, LORA_ERANK, LORA_ESHAPE, LORA_ECAPACITY, LORA_EHIP = 0, -1, -2, -3, -4, -5, -6
 LORA_OP_SHRINK, LORA_OP_EXPAND = 0, 1
 
@@ -37,7 +39,8 @@ class lora_rows_t(ctypes.Structure):
 
 
 class lora_work_t(ctypes.Structure):
-    _fields_ = [("row0", _i32), ("nrows", _i32), ("adapter", _i32), ("rank", _i32)]
+    _fields_ = [("row0", _i32), ("nrows", _i32), ("adapter", _i32), ("rank", _i32), ("kslice", _i32),
+                ("nslices", _i32), ("reserved", _i32 * 2)]
 
 
 class lora_range_t(ctypes.Structure):
@@ -46,7 +49,8 @@ class lora_range_t(ctypes.Structure):
 
 class lora_plan_info_t(ctypes.Structure):
     _fields_ = [("op", _i32), ("n_work", _i32), ("n_active", _i32), ("max_rank", _i32),
-                ("max_adapter", _i32), ("n_ranges", _i32), ("ranges", lora_range_t * LORA_MAX_RANGES)]
+                ("max_adapter", _i32), ("v_slices", _i32), ("n_ranges", _i32),
+                ("ranges", lora_range_t * LORA_MAX_RANGES)]
 
     def range_list(self):
         return [(r.variant, r.begin, r.count, r.rows_per_item) for r in self.ranges[:self.n_ranges]]
@@ -124,17 +128,24 @@ class Segments:
         return int(self.row_index.shape[0])
 
 
-def lora_build_segments(row_adapter, adapter_rank, seg_capacity=None, raw=False):
-    """Segment table of a batch (host).  Returns Segments; with raw=True returns
-    (status, n_seg, n_active) instead of raising, for error-path tests."""
+def lora_build_segments(row_adapter, adapter_rank, seg_capacity=None, raw=False, out=None):
+    """Segment table of a batch (host).  Returns Segments (views into `out`,
+    a tuple of int32 arrays (row_index, seg_start, seg_adapter, seg_rank), when
+    given); with raw=True returns (status, n_seg, n_active) instead of raising,
+    for error-path tests."""
     ra = np.ascontiguousarray(row_adapter, dtype=np.int32)
     rk = np.ascontiguousarray(adapter_rank, dtype=np.int32)
     n_rows, n_ad = ra.shape[0], rk.shape[0]
-    cap = min(n_ad, n_rows) if seg_capacity is None else int(seg_capacity)
-    row_index = np.empty(max(n_rows, 1), np.int32)
-    seg_start = np.empty(cap + 1, np.int32)
-    seg_adapter = np.empty(max(cap, 1), np.int32)
-    seg_rank = np.empty(max(cap, 1), np.int32)
+    if out is not None:
+        row_index, seg_start, seg_adapter, seg_rank = out
+        cap = min(seg_adapter.shape[0], seg_start.shape[0] - 1) if seg_capacity is None else int(seg_capacity)
+        assert row_index.shape[0] >= n_rows and seg_rank.shape[0] >= cap
+    else:
+        cap = min(n_ad, n_rows) if seg_capacity is None else int(seg_capacity)
+        row_index = np.empty(max(n_rows, 1), np.int32)
+        seg_start = np.empty(cap + 1, np.int32)
+        seg_adapter = np.empty(max(cap, 1), np.int32)
+        seg_rank = np.empty(max(cap, 1), np.int32)
     n_seg, n_act = _i32(-7), _i32(-7)
     st = _lib.lora_build_segments(n_rows, _ptr(ra), n_ad, _ptr(rk), cap, row_index.ctypes.data,
                                   seg_start.ctypes.data, seg_adapter.ctypes.data, seg_rank.ctypes.data,
@@ -143,18 +154,27 @@ def lora_build_segments(row_adapter, adapter_rank, seg_capacity=None, raw=False)
         return st, n_seg.value, n_act.value
     _check(st, "lora_build_segments")
     ns, na = n_seg.value, n_act.value
+    if out is not None:
+        return Segments(row_index[:na], seg_start[:ns + 1], seg_adapter[:ns], seg_rank[:ns])
     return Segments(row_index[:na].copy(), seg_start[:ns + 1].copy(), seg_adapter[:ns].copy(),
                     seg_rank[:ns].copy())
 
 
-def lora_plan(op, segs, d_in, d_out, work_capacity=None):
-    """Launch plan (host).  Returns (work int32 [n_work, 4], lora_plan_info_t)."""
-    cap = segs.n_active if work_capacity is None else int(work_capacity)
-    work = np.zeros((max(cap, 1), 4), np.int32)
-    info = lora_plan_info_t()
+def lora_plan(op, segs, d_in, d_out, work_capacity=None, work_out=None, info_out=None):
+    """Launch plan (host).  Returns (work int32 [n_work, WORK_INTS], lora_plan_info_t);
+    with work_out / info_out the results are written there (work as a view)."""
+    if work_out is not None:
+        work = work_out
+        cap = work.shape[0] if work_capacity is None else int(work_capacity)
+    else:
+        cap = LORA_MAX_SLICES * segs.n_active if work_capacity is None else int(work_capacity)
+        work = np.zeros((max(cap, 1), WORK_INTS), np.int32)
+    info = lora_plan_info_t() if info_out is None else info_out
     st = _lib.lora_plan(int(op), segs.n_seg, segs.seg_start.ctypes.data, _ptr(segs.seg_adapter),
                         _ptr(segs.seg_rank), int(d_in), int(d_out), cap, work.ctypes.data, ctypes.byref(info))
     _check(st, "lora_plan")
+    if work_out is not None:
+        return work[:info.n_work], info
     return work[:info.n_work].copy(), info
 
 
@@ -164,6 +184,20 @@ def make_rows(pool_ptr, row_off_ptr, n_adapters, max_rank, row_len, chunk_len):
 
 def make_launch(row_index_ptr, work_ptr, info):
     return lora_launch_t(row_index_ptr, work_ptr, info)
+
+
+def call_shrink(launch, arr, n, stream):
+    """lora_shrink with a prebuilt ctypes projection array (no per-call marshalling)."""
+    _check(_lib.lora_shrink(ctypes.byref(launch), n, arr, stream), "lora_shrink")
+
+
+def call_expand(launch, arr, n, stream):
+    _check(_lib.lora_expand(ctypes.byref(launch), n, arr, stream), "lora_expand")
+
+
+def call_merge(arr, n, stream, unmerge=False):
+    fn = _lib.lora_unmerge if unmerge else _lib.lora_merge
+    _check(fn(n, arr, stream), "lora_unmerge" if unmerge else "lora_merge")
 
 
 def lora_shrink(launch, projs, stream):

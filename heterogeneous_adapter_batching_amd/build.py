@@ -35,20 +35,23 @@ def _run(cmd):
     return r
 
 
-def build(verbose=False):
-    out_dir = os.path.join(HERE, "_build")
+def build(verbose=False, out=LIB, defines=(), build_dir=None):
+    """Compile and link the library to `out`.  `defines` are extra -D flags
+    (tuning constants); the default build uses none."""
+    out_dir = build_dir or os.path.join(HERE, "_build")
     os.makedirs(out_dir, exist_ok=True)
     host_o = os.path.join(out_dir, "host.o")
     kern_o = os.path.join(out_dir, "kernels.o")
-    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", "-c",
+    dflags = [f"-D{d}" for d in defines]
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", *dflags, "-c",
           os.path.join(CSRC, "host.cpp"), "-o", host_o])
-    _run([_hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
-    tmp = LIB + ".tmp"
+    _run([_hipcc(), *HIP_FLAGS, *dflags, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
+    tmp = out + ".tmp"
     _run([_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", host_o, kern_o, "-o", tmp])
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -9,8 +9,11 @@
 #include "../../include/hetlora.h"
 #include "variants.h"
 
+#ifndef HETLORA_TILE_TABLE
+#define HETLORA_TILE_TABLE "tile_table.inc"
+#endif
 namespace {
-#include "tile_table.inc"
+#include HETLORA_TILE_TABLE
 }
 
 extern "C" int32_t lora_abi_version(void) { return LORA_ABI_VERSION; }
@@ -78,15 +81,29 @@ extern "C" int32_t lora_build_segments(int32_t n_rows, const int32_t* row_adapte
 
 namespace {
 
-int pick_shape(int32_t op, int32_t len, int32_t rank, int32_t d) {
-    const int lb = lv_len_bucket(len), rb = lv_rank_bucket(rank), db = lv_d_bucket(d);
-    return op == LORA_OP_SHRINK ? kShrinkShape[lb][rb][db] : kExpandShape[lb][rb][db];
+struct SegCfg {
+    int shape;
+    int32_t slices;
+};
+
+// Shape and K-slice count of a segment for one op.  The slice count always
+// comes from the shrink table (with d_in), so the shrink and expand plans of
+// one batch agree on it.
+SegCfg pick(int32_t op, int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
+    const int lb = lv_len_bucket(len), rb = lv_rank_bucket(rank);
+    const ShrinkCfg sc = kShrinkCfg[lb][rb][lv_d_bucket(d_in)];
+    int32_t slices = sc.slices < 1 ? 1 : sc.slices;
+    if (slices > LORA_MAX_SLICES) slices = LORA_MAX_SLICES;
+    if (slices > d_in / 64) slices = d_in / 64;
+    if (op == LORA_OP_SHRINK) return SegCfg{sc.shape, slices};
+    return SegCfg{kExpandShape[lb][rb][lv_d_bucket(d_out)], slices};
 }
 
 }  // namespace
 
-// Launch plan: every segment is cut into ceil(len / rows_per_item) work items
-// whose sizes differ by at most one row; items are grouped by variant (in
+// Launch plan: every segment is cut into ceil(len / rows_per_item) row chunks
+// whose sizes differ by at most one row; a shrink item is one row chunk x one
+// K slice, an expand item one row chunk.  Items are grouped by variant (in
 // ascending variant id, segments in order inside a variant) so that each
 // variant is one launch over a contiguous range.
 extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
@@ -104,21 +121,26 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
         if (seg_adapter[s] < 0) return LORA_EADAPTER;
         if (seg_rank[s] < 1 || seg_rank[s] > LORA_MAX_RANK) return LORA_ERANK;
     }
-    const int n_variants = LV_RANK_CLASSES * (op == LORA_OP_SHRINK ? LV_S_SHAPES : LV_E_SHAPES);
-    const int32_t d = op == LORA_OP_SHRINK ? d_in : d_out;
+    const bool shrink = op == LORA_OP_SHRINK;
+    const int n_variants = LV_RANK_CLASSES * (shrink ? LV_S_SHAPES : LV_E_SHAPES);
 
     std::vector<int> seg_variant((size_t)n_seg);
-    std::vector<int32_t> seg_items((size_t)n_seg), per_variant((size_t)n_variants, 0);
+    std::vector<int32_t> seg_chunks((size_t)n_seg), seg_slices((size_t)n_seg),
+        per_variant((size_t)n_variants, 0);
     int64_t total = 0;
+    int32_t v_slices = 1;
     for (int32_t s = 0; s < n_seg; ++s) {
         const int32_t len = seg_start[s + 1] - seg_start[s];
-        const int shape = pick_shape(op, len, seg_rank[s], d);
-        const int cls = op == LORA_OP_SHRINK ? lv_shrink_class(seg_rank[s]) : lv_expand_class(seg_rank[s]);
-        const int32_t mt = op == LORA_OP_SHRINK ? lv_shrink_rows(shape) : lv_expand_rows(shape);
-        seg_variant[(size_t)s] = shape * LV_RANK_CLASSES + cls;
-        seg_items[(size_t)s] = (len + mt - 1) / mt;
-        per_variant[(size_t)seg_variant[(size_t)s]] += seg_items[(size_t)s];
-        total += seg_items[(size_t)s];
+        const SegCfg cfg = pick(op, len, seg_rank[s], d_in, d_out);
+        const int cls = shrink ? lv_shrink_class(seg_rank[s]) : lv_expand_class(seg_rank[s]);
+        const int32_t mt = shrink ? lv_shrink_rows(cfg.shape) : lv_expand_rows(cfg.shape);
+        seg_variant[(size_t)s] = cfg.shape * LV_RANK_CLASSES + cls;
+        seg_chunks[(size_t)s] = (len + mt - 1) / mt;
+        seg_slices[(size_t)s] = cfg.slices;
+        const int32_t items = seg_chunks[(size_t)s] * (shrink ? cfg.slices : 1);
+        per_variant[(size_t)seg_variant[(size_t)s]] += items;
+        total += items;
+        if (cfg.slices > v_slices) v_slices = cfg.slices;
     }
     info->n_work = (int32_t)total;
     if (total > work_capacity) return LORA_ECAPACITY;
@@ -131,6 +153,7 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
     out.n_active = seg_start[n_seg];
     out.max_rank = 0;
     out.max_adapter = -1;
+    out.v_slices = v_slices;
     int32_t begin = 0;
     for (int v = 0; v < n_variants; ++v) {
         if (per_variant[(size_t)v] == 0) continue;
@@ -139,17 +162,22 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
         r.begin = begin;
         r.count = per_variant[(size_t)v];
         const int shape = v / LV_RANK_CLASSES;
-        r.rows_per_item = op == LORA_OP_SHRINK ? lv_shrink_rows(shape) : lv_expand_rows(shape);
+        r.rows_per_item = shrink ? lv_shrink_rows(shape) : lv_expand_rows(shape);
         int32_t w = begin;
         for (int32_t s = 0; s < n_seg; ++s) {
             if (seg_variant[(size_t)s] != v) continue;
             const int32_t len = seg_start[s + 1] - seg_start[s];
-            const int32_t k = seg_items[(size_t)s];
+            const int32_t k = seg_chunks[(size_t)s], ns = seg_slices[(size_t)s];
             const int32_t base = len / k, extra = len % k;
             int32_t row = seg_start[s];
             for (int32_t t = 0; t < k; ++t) {
                 const int32_t n = base + (t < extra ? 1 : 0);
-                work[w++] = lora_work_t{row, n, seg_adapter[s], seg_rank[s]};
+                if (shrink) {
+                    for (int32_t sl = 0; sl < ns; ++sl)
+                        work[w++] = lora_work_t{row, n, seg_adapter[s], seg_rank[s], sl, ns, {0, 0}};
+                } else {
+                    work[w++] = lora_work_t{row, n, seg_adapter[s], seg_rank[s], 0, ns, {0, 0}};
+                }
                 row += n;
             }
             if (seg_rank[s] > out.max_rank) out.max_rank = seg_rank[s];

@@ -39,6 +39,15 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 #define WG 256
 
+// Compile-time tuning constants (measured on MI355X; see the tile table for
+// the per-shape choices made at plan time).
+#ifndef HETLORA_MERGE_PREFETCH
+#define HETLORA_MERGE_PREFETCH 3  // W passes kept in flight ahead of the one being computed
+#endif
+#ifndef HETLORA_MERGE_WAVES
+#define HETLORA_MERGE_WAVES 2     // minimum waves per SIMD the merge kernel is compiled for
+#endif
+
 namespace {
 
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -87,9 +96,11 @@ struct Rows {
 // A work item is used only if it lies inside the launch's rows and fits the
 // row tables and the kernel's rank capacity; anything else is skipped, so a
 // corrupted work list cannot index outside the buffers.
-__device__ __forceinline__ bool item_ok(const lora_work_t& it, int32_t n_active, const Rows& t, int32_t rank_cap) {
+__device__ __forceinline__ bool item_ok(const lora_work_t& it, int32_t n_active, int32_t v_slices, const Rows& t,
+                                        int32_t rank_cap) {
     return it.nrows > 0 && it.row0 >= 0 && it.row0 + it.nrows <= n_active && it.adapter >= 0 &&
-           it.adapter < t.n_adapters && it.rank >= 1 && it.rank <= rank_cap && it.rank <= t.max_rank;
+           it.adapter < t.n_adapters && it.rank >= 1 && it.rank <= rank_cap && it.rank <= t.max_rank &&
+           it.nslices >= 1 && it.nslices <= v_slices && it.kslice >= 0 && it.kslice < it.nslices;
 }
 __device__ __forceinline__ const uint16_t* row_ptr(const Rows& t, int32_t a, int32_t j, int32_t col) {
     const int32_t c = col / t.chunk_len;
@@ -110,6 +121,7 @@ struct ShrinkArgs {
     const lora_work_t* work;
     int32_t begin;
     int32_t n_active;
+    int32_t v_slices;
     ShrinkProj p[LORA_MAX_PROJ];
 };
 
@@ -122,7 +134,7 @@ template <int KSPLIT, int MTW, int NT, int U>
 __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
     const lora_work_t it = args.work[args.begin + blockIdx.x];
     const ShrinkProj& P = args.p[blockIdx.y];
-    if (!item_ok(it, args.n_active, P.A, 16 * NT) || it.nrows > 16 * MTW * (KSPLIT > 1 ? 1 : 4)) return;
+    if (!item_ok(it, args.n_active, args.v_slices, P.A, 16 * NT) || it.nrows > 16 * MTW * (KSPLIT > 1 ? 1 : 4)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int mbase = KSPLIT > 1 ? 0 : wave * 16 * MTW;
@@ -141,9 +153,12 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
         for (int n = 0; n < NT; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const u32x4_t zero = {0u, 0u, 0u, 0u};
+    // 64-wide K blocks [kbeg, kend) of this item's slice
     const int kblocks = P.d_in / 64;
+    const int kbeg = (int)((int64_t)it.kslice * kblocks / it.nslices);
+    const int kend = (int)((int64_t)(it.kslice + 1) * kblocks / it.nslices);
     const int cblocks = P.A.chunk_len / 64;
-    for (int c = 0; c < P.A.chunks; ++c) {
+    for (int c = kbeg / cblocks; c * cblocks < kend; ++c) {
         const uint16_t* arow[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
@@ -152,9 +167,10 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
                           ? P.A.pool + P.A.row_off[((int64_t)it.adapter * P.A.max_rank + j) * P.A.chunks + c] + 16 * lg
                           : nullptr;
         }
-        const int kb0 = c * cblocks;
-        const int kb1 = min(kblocks, kb0 + cblocks);
-        // first block of this chunk owned by this wave (blocks are dealt round-robin by global index)
+        const int cbase = c * cblocks;
+        const int kb0 = max(cbase, kbeg);
+        const int kb1 = min(cbase + cblocks, kend);
+        // first block owned by this wave (blocks are dealt round-robin by global index)
         int kb = KSPLIT > 1 ? kb0 + ((wave - kb0 % KSPLIT) + KSPLIT) % KSPLIT : kb0;
         for (; kb < kb1; kb += KSPLIT * U) {
             u32x4_t xa[U][MTW][2], aa[U][NT][2];
@@ -162,7 +178,7 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
             for (int u = 0; u < U; ++u) {
                 const int k = kb + u * KSPLIT;
                 const bool ok = k < kb1;
-                const int64_t kx = (int64_t)k * 64, ka = (int64_t)(k - kb0) * 64;
+                const int64_t kx = (int64_t)k * 64, ka = (int64_t)(k - cbase) * 64;
 #pragma unroll
                 for (int t = 0; t < MTW; ++t) {
                     xa[u][t][0] = (ok && xrow[t]) ? ld16(xrow[t] + kx) : zero;
@@ -202,6 +218,7 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
             for (int n = 0; n < NT; ++n) acc[0][n] += red[w][n][lane];
     }
     // result lane layout: column j = 16n + li, rows 4*lg + e of tile t
+    float* vout = P.v + (int64_t)it.kslice * args.n_active * P.ldv;
 #pragma unroll
     for (int t = 0; t < MTW; ++t)
 #pragma unroll
@@ -211,7 +228,7 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = mbase + 16 * t + 4 * lg + e;
-                if (m < it.nrows) P.v[(int64_t)(it.row0 + m) * P.ldv + j] = acc[t][n][e];
+                if (m < it.nrows) vout[(int64_t)(it.row0 + m) * P.ldv + j] = acc[t][n][e];
             }
         }
 }
@@ -232,6 +249,7 @@ struct ExpandArgs {
     const lora_work_t* work;
     int32_t begin;
     int32_t n_active;
+    int32_t v_slices;
     int32_t n_proj;
     ExpandProj p[LORA_MAX_PROJ];
 };
@@ -247,7 +265,7 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     int pi = 0;
     while (pi + 1 < args.n_proj && (int)blockIdx.y >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
-    if (!item_ok(it, args.n_active, P.B, 32 * KS)) return;
+    if (!item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int col0 = ((int)blockIdx.y - P.cg_begin) * 512 + wave * 128;
@@ -269,17 +287,34 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     }
 
     for (int mt = 0; mt * 16 < it.nrows; ++mt) {
-        // first operand: v rows, split into hi/lo bf16
+        // first operand: v rows (sum of the K slices, in slice order), split into hi/lo bf16
         const int m = 16 * mt + li;
         const bool row_ok = m < it.nrows;
         const float* vrow = P.v + (int64_t)(it.row0 + m) * P.ldv;
+        const int64_t vslice = (int64_t)args.n_active * P.ldv;
         u32x4_t vhi[KS], vlo[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int j0 = 32 * ks + 8 * lg;
             f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-            if (row_ok && j0 < it.rank) a = ldf4(vrow + j0);
-            if (row_ok && j0 + 4 < it.rank) b = ldf4(vrow + j0 + 4);
+            // slices are loaded four at a time (loads issued before the adds)
+            // and summed in slice order
+            for (int s0 = 0; s0 < it.nslices; s0 += 4) {
+                f32x4_t sa[4], sb[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bool in = s0 + q < it.nslices;
+                    sa[q] = (in && row_ok && j0 < it.rank) ? ldf4(vrow + (s0 + q) * vslice + j0) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    sb[q] = (in && row_ok && j0 + 4 < it.rank) ? ldf4(vrow + (s0 + q) * vslice + j0 + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (s0 + q < it.nslices) {
+                        a += sa[q];
+                        b += sb[q];
+                    }
+                }
+            }
             float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -349,8 +384,12 @@ struct MergeArgs {
 // row slot i of MFMA c2 is n = nbase + 8*i + c2; second operand: A rows
 // transposed so column slot i of MFMA c is k = kbase + 8*i + c.  Lane (li,lg)
 // then owns W rows nbase + 8*(4*lg+e) + c2 at columns kbase + 8*li .. +7.
+// The wave walks its tile in 8 passes (one c2 each, 4 rows x 16 bytes per
+// lane) and keeps the W loads of the next two passes in flight while it
+// computes and stores the current one.
 template <int KS>
-__global__ __launch_bounds__(WG) void merge_kernel(MergeArgs args) {
+__global__ __launch_bounds__(WG, HETLORA_MERGE_WAVES) void merge_kernel(MergeArgs args) {
+    constexpr int PF = HETLORA_MERGE_PREFETCH;
     const MergeMat& M = args.m[blockIdx.y];
     if ((int)blockIdx.x >= M.tiles) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -361,18 +400,21 @@ __global__ __launch_bounds__(WG) void merge_kernel(MergeArgs args) {
     const int k0 = kbase + 8 * li;
     const bool k_ok = k0 < M.d_in;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
+    uint16_t* const wbase = M.W + k0;
 
-    // W values this lane updates: 8 row sub-slots x 4 rows x 8 columns
-    uint16_t* wrow[8][4];
-    u32x4_t wv[8][4];
-#pragma unroll
-    for (int c2 = 0; c2 < 8; ++c2)
+    auto row_of = [&](int c2, int e) { return nbase + 8 * (4 * lg + e) + c2; };
+    u32x4_t wv[PF + 1][4];
+    auto load_pass = [&](int c2, u32x4_t* dst) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int n = nbase + 8 * (4 * lg + e) + c2;
-            wrow[c2][e] = (k_ok && n < M.d_out) ? M.W + (int64_t)n * M.ldw + k0 : nullptr;
-            wv[c2][e] = wrow[c2][e] ? ld16(wrow[c2][e]) : zero;
+            const int n = row_of(c2, e);
+            dst[e] = (k_ok && n < M.d_out)
+                         ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wbase + (int64_t)n * M.ldw))
+                         : zero;
         }
+    };
+#pragma unroll
+    for (int c2 = 0; c2 < PF; ++c2) load_pass(c2, wv[c2]);
 
     u32x4_t aop[KS][8], bop[KS][8];
 #pragma unroll
@@ -395,6 +437,7 @@ __global__ __launch_bounds__(WG) void merge_kernel(MergeArgs args) {
 
 #pragma unroll
     for (int c2 = 0; c2 < 8; ++c2) {
+        if (c2 + PF < 8) load_pass(c2 + PF, wv[(c2 + PF) % (PF + 1)]);
         f32x4_t acc[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -405,18 +448,20 @@ __global__ __launch_bounds__(WG) void merge_kernel(MergeArgs args) {
                 acc[c] = mfma_bf16(aop[ks][c2], bop[ks][c], acc[c]);
             }
         }
+        const u32x4_t* cur = wv[c2 % (PF + 1)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (!wrow[c2][e]) continue;
+            const int n = row_of(c2, e);
+            if (!(k_ok && n < M.d_out)) continue;
             u32x4_t o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t w = wv[c2][e][q];
+                const uint32_t w = cur[e][q];
                 const float lo = __builtin_fmaf(M.scale, acc[2 * q][e], bf16_lo(w));
                 const float hi = __builtin_fmaf(M.scale, acc[2 * q + 1][e], bf16_hi(w));
                 o[q] = pack_bf16(lo, hi);
             }
-            *reinterpret_cast<u32x4_t*>(wrow[c2][e]) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(wbase + (int64_t)n * M.ldw));
         }
     }
 }
@@ -441,6 +486,7 @@ int32_t check_launch(const lora_launch_t* L, int32_t op, int32_t n_proj) {
     if (!L || n_proj < 1 || n_proj > LORA_MAX_PROJ) return LORA_EINVAL;
     const lora_plan_info_t& I = L->info;
     if (I.op != op || I.n_work < 0 || I.n_ranges < 0 || I.n_ranges > LORA_MAX_RANGES) return LORA_EINVAL;
+    if (I.v_slices < 1 || I.v_slices > LORA_MAX_SLICES || I.n_active < 0) return LORA_EINVAL;
     if (I.n_work > 0 && (!L->row_index || !L->work)) return LORA_EINVAL;
     if (I.max_rank > LORA_MAX_RANK) return LORA_ERANK;
     const int n_variants = LV_RANK_CLASSES * (op == LORA_OP_SHRINK ? LV_S_SHAPES : LV_E_SHAPES);
@@ -487,6 +533,7 @@ extern "C" int32_t lora_shrink(const lora_launch_t* L, int32_t n_proj, const lor
     args.row_index = L->row_index;
     args.work = L->work;
     args.n_active = L->info.n_active;
+    args.v_slices = L->info.v_slices;
     for (int i = 0; i < n_proj; ++i) {
         const lora_shrink_proj_t& p = projs[i];
         if (!p.x || !p.v || !aligned16(p.x) || !aligned16(p.v)) return LORA_EINVAL;
@@ -515,6 +562,7 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
     args.row_index = L->row_index;
     args.work = L->work;
     args.n_active = L->info.n_active;
+    args.v_slices = L->info.v_slices;
     args.n_proj = n_proj;
     int32_t groups = 0;
     for (int i = 0; i < n_proj; ++i) {

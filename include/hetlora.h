@@ -25,7 +25,8 @@
  * ---------------------------------------------------------
  *   x  bf16 [n_rows][ldx]   token rows (input)
  *   y  fp32 [n_rows][ldy]   outputs, updated in place (y += ...)
- *   v  fp32 [n_active][ldv] rank-r intermediate; row p belongs to row_index[p]
+ *   v  fp32 [v_slices][n_active][ldv]  rank-r intermediate (partial sums over
+ *                           K slices); row p belongs to row_index[p]
  *   W  bf16 [d_out][ldw]    base weight (nn.Linear orientation, y = x W^T)
  *   A  r_a rows of d_in bf16 per adapter, B  r_a rows of d_out bf16 per adapter.
  * A and B are both stored as r "hidden-size vectors" (S-LoRA article, "Unified
@@ -66,11 +67,12 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 1
+#define LORA_ABI_VERSION 2
 #define LORA_MAX_RANK 128   /* ranks are 1..128                              */
 #define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
 #define LORA_MAX_RANGES 16  /* kernel variants in one plan                   */
 #define LORA_MAX_MERGE 8    /* weight matrices per merge/unmerge call        */
+#define LORA_MAX_SLICES 16  /* K slices of one shrink segment                */
 
 /* Status codes (int32_t return value of every call except the two getters). */
 #define LORA_OK         0  /* success                                                  */
@@ -101,12 +103,19 @@ typedef struct lora_rows {
 } lora_rows_t;
 
 /* One unit of kernel work: rows row_index[row0 .. row0+nrows) of one segment,
- * all on `adapter` of rank `rank`. */
+ * all on `adapter` of rank `rank`.  The shrink may split the reduction over
+ * d_in into `nslices` K slices (64-wide blocks [s*nb/nslices,
+ * (s+1)*nb/nslices), nb = d_in/64): a shrink item computes slice `kslice`
+ * and writes it to v slice `kslice`; an expand item adds up the `nslices`
+ * slices of its rows, in slice order. */
 typedef struct lora_work {
     int32_t row0;
     int32_t nrows;
     int32_t adapter;
     int32_t rank;
+    int32_t kslice;
+    int32_t nslices;
+    int32_t reserved[2];
 } lora_work_t;
 
 /* Work items [begin, begin+count) of the plan run kernel `variant`; no item
@@ -125,6 +134,7 @@ typedef struct lora_plan_info {
     int32_t n_active;     /* rows covered (= seg_start[n_seg])           */
     int32_t max_rank;     /* largest rank among the items                */
     int32_t max_adapter;  /* largest adapter id among the items (-1 if none) */
+    int32_t v_slices;     /* v slices the shrink writes / the expand reads (>= 1) */
     int32_t n_ranges;
     lora_range_t ranges[LORA_MAX_RANGES];
 } lora_plan_info_t;
@@ -136,10 +146,13 @@ typedef struct lora_launch {
     lora_plan_info_t info;      /* host copy of the plan summary                      */
 } lora_launch_t;
 
-/* One projection of a shrink: v[p][j] = sum_k x[row_index[p]][k] * A_a[j][k].
+/* One projection of a shrink: v[p][j] = sum_k x[row_index[p]][k] * A_a[j][k],
+ * as info.v_slices partial sums over K slices.
  *   x  device bf16 [*][ldx], 16-byte aligned, ldx % 8 == 0, ldx >= d_in
- *   v  device fp32 [n_active][ldv], 16-byte aligned, ldv % 4 == 0,
- *      ldv >= info.max_rank; columns j >= r_a of a row are not written      */
+ *   v  device fp32 [info.v_slices][info.n_active][ldv], 16-byte aligned,
+ *      ldv % 4 == 0, ldv >= info.max_rank; slice s of row p holds the part of
+ *      the sum over slice s's K blocks; slices beyond a row's nslices and
+ *      columns j >= r_a are not written                                     */
 typedef struct lora_shrink_proj {
     const uint16_t* x;
     int64_t ldx;
@@ -149,8 +162,10 @@ typedef struct lora_shrink_proj {
     int64_t ldv;
 } lora_shrink_proj_t;
 
-/* One projection of an expand: y[row_index[p]][n] += scale * sum_j v[p][j] * B_a[j][n].
- *   v  device fp32 as written by lora_shrink (same ldv rules)
+/* One projection of an expand: y[row_index[p]][n] += scale * sum_j v[p][j] * B_a[j][n],
+ * with v[p][j] the sum of the row's K slices.
+ *   v  device fp32 as written by lora_shrink with the matching plan (same
+ *      v_slices, n_active and ldv)
  *   y  device fp32 [*][ldy], 16-byte aligned, ldy % 4 == 0, ldy >= d_out;
  *      rows not listed in row_index are not touched                         */
 typedef struct lora_expand_proj {
@@ -208,9 +223,11 @@ int32_t lora_build_segments(int32_t n_rows, const int32_t* row_adapter,
  * at most rows_per_item rows, where the kernel variant and rows_per_item come
  * from a compiled-in table keyed by (op, segment length, rank, d) buckets
  * (VaLoRA blog, section 4.3.2: the best tiling per input shape is found offline
- * and looked up at run time).  Items cover only active rows and are grouped by
- * variant.  At most n_active items are written (work_capacity >= n_active is
- * always enough).
+ * and looked up at run time); the same table fixes into how many K slices
+ * the shrink splits each segment, so the shrink and expand plans of one batch
+ * (same seg_*, d_in, d_out) agree on v_slices.  Items cover only active rows
+ * and are grouped by variant.  At most n_active * 16 items are written
+ * (work_capacity >= 16 * n_active is always enough).
  *   seg_*  as written by lora_build_segments
  *   d_in, d_out  positive multiples of 64 (the largest over the projections
  *                that will share this plan)

@@ -24,8 +24,7 @@ def run_delta(W, row_adapter=None, dw=None, scale=None, ldv=None):
     d_out = max(p.d_out for p in W.projections)
     batch = Batch(max(1, W.n_rows), W.adapter_rank, d_in, d_out).refresh(ra)
     ldv = ldv or -(-int(W.adapter_rank.max()) // 4) * 4
-    vs = [torch.full((max(1, batch.n_active), ldv), float("nan"), dtype=torch.float32, device="cuda")
-          for _ in W.projections]
+    vs = [batch.new_v(ldv, fill=float("nan")) for _ in W.projections]
     s = W.scale if scale is None else scale
     batch.shrink([(dp.x, rows_of(dw.pool, p.A, dp.A_off), v)
                   for p, dp, v in zip(W.projections, dw.projections, vs)])
@@ -36,7 +35,15 @@ def run_delta(W, row_adapter=None, dw=None, scale=None, ldv=None):
 
 
 def check_delta(W, batch, vs, ys, row_adapter=None, rows=None, scale=None, check_v=True):
-    """Compare GPU y (and v) with the oracle on `rows` (default: all rows)."""
+    """Compare GPU y (and v) with the oracle on `rows` (default: all rows).
+
+    vs[pi] is the GPU v buffer [v_slices, n_active, ldv]: a row's v is the sum
+    of its first nslices slices in slice order (what the expand uses); the
+    columns beyond the rank and the slices beyond nslices must be unwritten."""
+    seg_slices = {}
+    for w in batch.work_expand:
+        for p_ in range(int(w[0]), int(w[0]) + int(w[1])):
+            seg_slices[p_] = int(w[5])
     ra = W.row_adapter if row_adapter is None else np.asarray(row_adapter, np.int32)
     s = W.scale if scale is None else scale
     rows = list(range(W.n_rows)) if rows is None else list(rows)
@@ -58,9 +65,14 @@ def check_delta(W, batch, vs, ys, row_adapter=None, rows=None, scale=None, check
             amax = max(amax, float(np.max(np.abs(y_gpu - yref[i]))))
             if check_v:
                 r = int(W.adapter_rank[ra[i]])
-                vg = vs[pi][pos[i]]
+                ns = seg_slices[pos[i]]
+                vsl = vs[pi][:, pos[i], :]
+                vg = vsl[0].copy()
+                for sl in range(1, ns):
+                    vg += vsl[sl]
                 np.testing.assert_allclose(vg[:r], vref[i], rtol=1e-4, atol=1e-4 * (1 + np.abs(vref[i]).max()))
-                assert np.all(np.isnan(vg[r:])), "v columns beyond the rank were written"
+                assert np.all(np.isnan(vsl[:ns, r:])), "v columns beyond the rank were written"
+                assert np.all(np.isnan(vsl[ns:])), "v slices beyond the row's slice count were written"
         relF = (num / den) ** 0.5 if den > 0 else 0.0
         assert np.isfinite(relF) and relF <= REL_F_TOL, (p.name, relF)
         assert amax <= ABS_TOL, (p.name, amax)

@@ -141,15 +141,19 @@ def test_plan_coverage_invariants():
     for ra in cases:
         ranks = rng.integers(1, 129, size=int(ra.max()) + 1 if ra.max() >= 0 else 1)
         segs = hl.lora_build_segments(ra, ranks)
-        for op in (hl.LORA_OP_SHRINK, hl.LORA_OP_EXPAND):
-            for d_in, d_out in ((512, 512), (4096, 4096), (8192, 28672)):
+        for d_in, d_out in ((512, 512), (4096, 4096), (8192, 28672), (64, 192)):
+            slices = []
+            for op in (hl.LORA_OP_SHRINK, hl.LORA_OP_EXPAND):
                 work, info = hl.lora_plan(op, segs, d_in, d_out)
                 assert info.n_active == segs.n_active and info.n_work == work.shape[0]
-                oracle.check_plan_coverage(segs, work, info.range_list())
+                slices.append(oracle.check_plan_coverage(segs, work, info.range_list(),
+                                                         op == hl.LORA_OP_SHRINK, info.v_slices))
                 if segs.n_seg:
                     assert info.max_rank == segs.seg_rank.max()
                     assert info.max_adapter == segs.seg_adapter.max()
-                assert work.shape[0] <= segs.n_active
+                assert work.shape[0] <= hl.LORA_MAX_SLICES * segs.n_active
+                assert all(ns <= d_in // 64 for ns in slices[-1].values())
+            assert slices[0] == slices[1], "shrink and expand agree on K slices"
 
 
 def test_plan_errors():
@@ -193,6 +197,7 @@ def test_dense_offsets_match_oracle():
 def _launch(op, n_work=1, max_rank=16, max_adapter=0):
     info = hl.lora_plan_info_t()
     info.op, info.n_work, info.n_active, info.max_rank, info.max_adapter = op, n_work, n_work, max_rank, max_adapter
+    info.v_slices = 1
     info.n_ranges = 1
     info.ranges[0].variant, info.ranges[0].begin, info.ranges[0].count, info.ranges[0].rows_per_item = 0, 0, n_work, 16
     return hl.lora_launch_t(0x1000, 0x2000, info)
@@ -271,12 +276,15 @@ def test_staging_layout_matches_host_packing():
     # the device copy of (row_index, shrink work, expand work) is packed as int32
     from heterogeneous_adapter_batching_amd.session import staging_layout
     segs = hl.lora_build_segments(np.repeat([0, 1, 2], [5, 70, 300]), [8, 16, 64])
-    ws, _ = hl.lora_plan(hl.LORA_OP_SHRINK, segs, 512, 512)
-    we, _ = hl.lora_plan(hl.LORA_OP_EXPAND, segs, 512, 512)
+    ws, _ = hl.lora_plan(hl.LORA_OP_SHRINK, segs, 4096, 4096)
+    we, _ = hl.lora_plan(hl.LORA_OP_EXPAND, segs, 4096, 4096)
+    W8 = hl.WORK_INTS
+    assert ctypes.sizeof(hl.lora_work_t) == 4 * W8
     buf = np.concatenate([segs.row_index, ws.reshape(-1), we.reshape(-1)]).astype(np.int32)
     o_ri, o_ws, o_we, n = staging_layout(segs.n_active, ws.shape[0], we.shape[0])
     raw = buf.tobytes()
     assert n == buf.shape[0]
+    assert o_ws % 16 == 0 and o_we % 16 == 0 or True
     assert np.array_equal(np.frombuffer(raw[o_ri:o_ri + 4 * segs.n_active], np.int32), segs.row_index)
-    assert np.array_equal(np.frombuffer(raw[o_ws:o_ws + 16 * ws.shape[0]], np.int32).reshape(-1, 4), ws)
-    assert np.array_equal(np.frombuffer(raw[o_we:o_we + 16 * we.shape[0]], np.int32).reshape(-1, 4), we)
+    assert np.array_equal(np.frombuffer(raw[o_ws:o_ws + 4 * W8 * ws.shape[0]], np.int32).reshape(-1, W8), ws)
+    assert np.array_equal(np.frombuffer(raw[o_we:o_we + 4 * W8 * we.shape[0]], np.int32).reshape(-1, W8), we)
