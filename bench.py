@@ -3,7 +3,7 @@
 
 Workload (the decode configuration): a Llama-7B-shaped layer, 64 one-token
 rows, d = 4096, q/k/v/o projections, rank-16 adapters.  One step is one pass
-of the whole path over that batch:
+of the whole path over that batch, on one layer:
 
   1. fully heterogeneous batch (row i -> adapter i, 64 adapters):
      segment build + plan (host, C) -> metadata upload -> shrink -> expand
@@ -11,6 +11,10 @@ of the whole path over that batch:
   3. mode switch of the layer: merge adapter 0 into the four W[4096x4096],
      then unmerge it (one launch each, four matrices per launch)
 
+Step k works on layer copy k mod L (default L = 8: each copy has its own
+adapters, x, y and W, about 200 MB), so the working set exceeds the 256 MB
+Infinity Cache and the kernels stream from HBM as they would over a model's
+layers; layer copy 0 is the seeded decode instance the parity tests check.
 Inputs are resident in HBM before the timed region.  `value` is the step's
 algorithmic bytes (what the method must move: x rows, each distinct adapter's
 A and B once, v written and read, y read and written in fp32, W read and
@@ -20,7 +24,7 @@ timed steps; `roofline` describes the kernel with the largest share of the
 step time.  `cpu_baseline` times the CPU oracle on a bounded sample of the
 same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -121,6 +125,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=8, help="layer copies the steps rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -136,31 +141,41 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W = workloads.gen_config(1)
-    dw = to_device(W)
+    layers = []
+    for l in range(max(1, args.layers)):
+        Wl = workloads.gen_config(1, seed=1 + 1000 * l)   # layer 0 = the seeded decode instance
+        dwl = to_device(Wl)
+        rows = lambda desc, off: Rows(dwl.pool, off, desc.n_adapters, desc.max_rank, desc.row_len, desc.chunk_len)
+        A = [rows(p.A, d.A_off) for p, d in zip(Wl.projections, dwl.projections)]
+        B = [rows(p.B, d.B_off) for p, d in zip(Wl.projections, dwl.projections)]
+        mh = [Wl.merge.weight(0, i) for i in Wl.merge.projs]
+        Wt = [bits_to_device(w) for w in mh]
+        layers.append(dict(W=Wl, dw=dwl, A=A, B=B, Wt=Wt, merge_host=mh))
+    W = layers[0]["W"]
     het, homo = W.batches["hetero"], W.batches["homo"]
-    rows = lambda desc, off: Rows(dw.pool, off, desc.n_adapters, desc.max_rank, desc.row_len, desc.chunk_len)
-    A = [rows(p.A, d.A_off) for p, d in zip(W.projections, dw.projections)]
-    B = [rows(p.B, d.B_off) for p, d in zip(W.projections, dw.projections)]
-    merge_host = [W.merge.weight(0, i) for i in W.merge.projs]
-    Wt = [bits_to_device(w) for w in merge_host]
     r_m = int(W.adapter_rank[W.merge.adapter])
-    mats = [(Wt[i], A[i], B[i], W.merge.adapter, r_m, W.scale) for i in range(len(Wt))]
     ldv = 16
     bh = Batch(64, W.adapter_rank, 4096, 4096).refresh(het)
     bo = Batch(64, W.adapter_rank, 4096, 4096).refresh(homo)
+    vs = {id(b): [b.new_v(ldv) for _ in W.projections] for b in (bh, bo)}
     stream = torch.cuda.current_stream()
-    calls = []
-    for b in (bh, bo):
-        v = [b.new_v(ldv) for _ in W.projections]
-        calls.append((b.prepare_shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)]),
-                      b.prepare_expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])))
-    do_merge, do_unmerge = prepare_merge(mats), prepare_merge(mats, unmerge=True)
+    for L in layers:
+        L["calls"] = []
+        for b in (bh, bo):
+            v = vs[id(b)]
+            L["calls"].append((b.prepare_shrink([(d.x, L["A"][i], v[i]) for i, d in enumerate(L["dw"].projections)]),
+                               b.prepare_expand([(v[i], L["B"][i], d.y, W.scale)
+                                                 for i, d in enumerate(L["dw"].projections)])))
+        mats = [(L["Wt"][i], L["A"][i], L["B"][i], W.merge.adapter, r_m, W.scale) for i in range(len(L["Wt"]))]
+        L["merge"], L["unmerge"] = prepare_merge(mats), prepare_merge(mats, unmerge=True)
+    merge_host = layers[0]["merge_host"]
+    n_mats = len(layers[0]["Wt"])
 
     groups = ["hetero_shrink", "hetero_expand", "homo_shrink", "homo_expand", "merge", "unmerge"]
 
-    def step(ev):
-        for (b, ra, g), (do_shrink, do_expand) in zip(((bh, het, 0), (bo, homo, 2)), calls):
+    def step(ev, k):
+        L = layers[k % len(layers)]
+        for (b, ra, g), (do_shrink, do_expand) in zip(((bh, het, 0), (bo, homo, 2)), L["calls"]):
             b.refresh(ra)
             ev[g][0].record(stream)
             do_shrink()
@@ -169,23 +184,23 @@ def main():
             do_expand()
             ev[g + 1][1].record(stream)
         ev[4][0].record(stream)
-        do_merge()
+        L["merge"]()
         ev[4][1].record(stream)
         ev[5][0].record(stream)
-        do_unmerge()
+        L["unmerge"]()
         ev[5][1].record(stream)
 
     def new_events():
         return [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in groups]
 
-    for _ in range(args.warmup):
-        step(new_events())
+    for k in range(args.warmup):
+        step(new_events(), k)
     torch.cuda.synchronize()
     evs = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(evs[k])
+        step(evs[k], args.warmup + k)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
@@ -196,7 +211,7 @@ def main():
     med = {g: float(np.median(us[g])) for g in groups}
 
     ch, co = delta_cost(W, het), delta_cost(W, homo)
-    mc = merge_cost(4096, 4096, r_m, len(Wt))
+    mc = merge_cost(4096, 4096, r_m, n_mats)
     alg = {"hetero_shrink": (ch["shrink_bytes"], ch["flops"] * 0.5),
            "hetero_expand": (ch["expand_bytes"], ch["flops"] * 0.5),
            "homo_shrink": (co["shrink_bytes"], co["flops"] * 0.5),
@@ -231,8 +246,10 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode BGMV, Llama-7B-shaped layer: 64 one-token rows, d 4096, q/k/v/o, "
                                "rank 16; hetero (64 adapters) + homo (1 adapter) batches, then merge+unmerge "
-                               "of one adapter into the layer's 4 W[4096x4096]",
-                   "rows": 64, "d": 4096, "rank": 16, "adapters": 64, "projections": 4},
+                               "of one adapter into the layer's 4 W[4096x4096]; steps rotate over %d layer copies"
+                               % len(layers),
+                   "rows": 64, "d": 4096, "rank": 16, "adapters": 64, "projections": 4,
+                   "layer_copies": len(layers)},
         "roofline": {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "us_per_launch": round(d_us, 3), "alg_bytes_per_launch": int(d_bytes)},

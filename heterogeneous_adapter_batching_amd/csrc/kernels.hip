@@ -25,6 +25,14 @@
 // registers; output column slot i of MFMA c then stands for memory column
 // base + 8*i + c, so each lane still ends up owning 8 consecutive outputs.
 //
+// Row-offset loads are issued unconditionally, in one batch, at clamped valid
+// indices; the data loads that depend on them follow in a second batch, each
+// masked to the lanes whose row, rank slot and column are inside the work
+// (masked-off lanes read nothing and use zero), except the merge's adapter
+// rows, which are read at the clamped addresses and zeroed (L2 hits, cheaper
+// than masking).  So the in-order memory counter never makes a load wait for
+// another it does not depend on.  Stores are masked.
+//
 // No float atomics and a fixed reduction order everywhere: results do not
 // depend on a row's position in a work item or on the launch order.
 #include <hip/hip_runtime.h>
@@ -39,13 +47,16 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 #define WG 256
 
-// Compile-time tuning constants (measured on MI355X; see the tile table for
-// the per-shape choices made at plan time).
+// Compile-time tuning constants (measured on MI355X; the per-shape choices
+// are made at plan time from the tile table).
 #ifndef HETLORA_MERGE_PREFETCH
-#define HETLORA_MERGE_PREFETCH 3  // W passes kept in flight ahead of the one being computed
+#define HETLORA_MERGE_PREFETCH 2  // W passes kept in flight ahead of the one being computed
 #endif
 #ifndef HETLORA_MERGE_WAVES
 #define HETLORA_MERGE_WAVES 2     // minimum waves per SIMD the merge kernel is compiled for
+#endif
+#ifndef HETLORA_HW_CVT
+#define HETLORA_HW_CVT 1          // fp32 -> bf16 with the hardware convert (round to nearest even)
 #endif
 
 namespace {
@@ -56,20 +67,47 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
 }
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+// masked 16-byte load: lanes with ok == false read nothing and get zero
+__device__ __forceinline__ u32x4_t ld16_if(bool ok, const void* p) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (ok) v = *reinterpret_cast<const u32x4_t*>(p);
+    return v;
+}
+__device__ __forceinline__ f32x4_t ldf4_if(bool ok, const float* p) {
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (ok) v = *reinterpret_cast<const f32x4_t*>(p);
+    return v;
+}
 __device__ __forceinline__ f32x4_t ldf4(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
 __device__ __forceinline__ void stf4(float* p, f32x4_t v) { *reinterpret_cast<f32x4_t*>(p) = v; }
+__device__ __forceinline__ u32x4_t sel(bool ok, u32x4_t v) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    return ok ? v : z;
+}
+
+// Compiler-only fence: keeps a batch of loads issued before the code that
+// follows (stops the compiler from sinking a load into the branch that uses
+// it, which would make that branch wait on the whole batch).  No instruction
+// is emitted.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+// Two fp32 -> packed bf16 bits, round to nearest, ties to even.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+#if HETLORA_HW_CVT
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+#else
+    auto rne = [](float f) -> uint32_t {
+        const uint32_t u = __float_as_uint(f);
+        if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+        return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    };
+    return rne(lo) | (rne(hi) << 16);
+#endif
 }
 
 // 8 rows (r[e] = 8 consecutive bf16 columns of row e) -> 8 columns
@@ -86,7 +124,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4_t r[8], u32x4_t out[8])
     }
 }
 
-// Address of element `col` of row j of adapter a in a row table.
+// Row table of one matrix kind (A or B of one projection).
 struct Rows {
     const uint16_t* pool;
     const int64_t* row_off;
@@ -102,9 +140,9 @@ __device__ __forceinline__ bool item_ok(const lora_work_t& it, int32_t n_active,
            it.adapter < t.n_adapters && it.rank >= 1 && it.rank <= rank_cap && it.rank <= t.max_rank &&
            it.nslices >= 1 && it.nslices <= v_slices && it.kslice >= 0 && it.kslice < it.nslices;
 }
-__device__ __forceinline__ const uint16_t* row_ptr(const Rows& t, int32_t a, int32_t j, int32_t col) {
-    const int32_t c = col / t.chunk_len;
-    return t.pool + t.row_off[((int64_t)a * t.max_rank + j) * t.chunks + c] + (col - c * t.chunk_len);
+// Index into row_off of chunk `c` of row j of adapter a.
+__device__ __forceinline__ int64_t off_index(const Rows& t, int32_t a, int32_t j, int32_t c) {
+    return ((int64_t)a * t.max_rank + j) * t.chunks + c;
 }
 
 // ------------------------------------------------------------------ shrink
@@ -125,7 +163,7 @@ struct ShrinkArgs {
     ShrinkProj p[LORA_MAX_PROJ];
 };
 
-// One workgroup = one work item of one projection.
+// One workgroup = one work item (rows x one K slice) of one projection.
 //   KSPLIT = 4: the four waves share the item's 16 rows and take every 4th
 //               64-wide K block; partial sums are added in LDS in wave order.
 //   KSPLIT = 1: wave w owns rows [16*MTW*w, 16*MTW*(w+1)) of the item.
@@ -140,33 +178,38 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
     const int mbase = KSPLIT > 1 ? 0 : wave * 16 * MTW;
     if (KSPLIT == 1 && mbase >= it.nrows) return;  // no barrier in this configuration
 
+    // x rows of this lane (rows past the item read its last row, zeroed below)
     const uint16_t* xrow[MTW];
+    bool xok[MTW];
 #pragma unroll
     for (int t = 0; t < MTW; ++t) {
         const int m = mbase + 16 * t + li;
-        xrow[t] = m < it.nrows ? P.x + (int64_t)args.row_index[it.row0 + m] * P.ldx + 16 * lg : nullptr;
+        xok[t] = m < it.nrows;
+        xrow[t] = P.x + (int64_t)args.row_index[it.row0 + min(m, it.nrows - 1)] * P.ldx + 16 * lg;
     }
+    issue_fence();
     f32x4_t acc[MTW][NT];
 #pragma unroll
     for (int t = 0; t < MTW; ++t)
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
     // 64-wide K blocks [kbeg, kend) of this item's slice
     const int kblocks = P.d_in / 64;
     const int kbeg = (int)((int64_t)it.kslice * kblocks / it.nslices);
     const int kend = (int)((int64_t)(it.kslice + 1) * kblocks / it.nslices);
     const int cblocks = P.A.chunk_len / 64;
     for (int c = kbeg / cblocks; c * cblocks < kend; ++c) {
+        // A rows of this lane's rank slots (slots past the rank read row rank-1, zeroed below)
         const uint16_t* arow[NT];
+        bool aok[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const int j = 16 * n + li;
-            arow[n] = j < it.rank
-                          ? P.A.pool + P.A.row_off[((int64_t)it.adapter * P.A.max_rank + j) * P.A.chunks + c] + 16 * lg
-                          : nullptr;
+            aok[n] = j < it.rank;
+            arow[n] = P.A.pool + P.A.row_off[off_index(P.A, it.adapter, min(j, it.rank - 1), c)] + 16 * lg;
         }
+        issue_fence();
         const int cbase = c * cblocks;
         const int kb0 = max(cbase, kbeg);
         const int kb1 = min(cbase + cblocks, kend);
@@ -177,17 +220,17 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = kb + u * KSPLIT;
-                const bool ok = k < kb1;
+                const bool kin = k < kb1;  // wave-uniform
                 const int64_t kx = (int64_t)k * 64, ka = (int64_t)(k - cbase) * 64;
 #pragma unroll
                 for (int t = 0; t < MTW; ++t) {
-                    xa[u][t][0] = (ok && xrow[t]) ? ld16(xrow[t] + kx) : zero;
-                    xa[u][t][1] = (ok && xrow[t]) ? ld16(xrow[t] + kx + 8) : zero;
+                    xa[u][t][0] = ld16_if(kin && xok[t], xrow[t] + kx);
+                    xa[u][t][1] = ld16_if(kin && xok[t], xrow[t] + kx + 8);
                 }
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    aa[u][n][0] = (ok && arow[n]) ? ld16(arow[n] + ka) : zero;
-                    aa[u][n][1] = (ok && arow[n]) ? ld16(arow[n] + ka + 8) : zero;
+                    aa[u][n][0] = ld16_if(kin && aok[n], arow[n] + ka);
+                    aa[u][n][1] = ld16_if(kin && aok[n], arow[n] + ka + 8);
                 }
             }
 #pragma unroll
@@ -257,8 +300,9 @@ struct ExpandArgs {
 // One workgroup = one work item x one 512-column group of one projection;
 // wave w owns columns [128w, 128w+128) of the group.  The wave loads and
 // transposes its B strip once (KS steps of 32 ranks), then walks the item's
-// rows 16 at a time.  v is split as hi + lo bf16 (two MFMAs) so the product
-// keeps ~16 mantissa bits of v; y is read, updated and written in fp32.
+// rows 16 at a time.  v (the sum of the row's K slices, in slice order) is
+// split as hi + lo bf16 (two MFMAs) so the product keeps ~16 mantissa bits of
+// v; y is read, updated and written in fp32.
 template <int KS>
 __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     const lora_work_t it = args.work[args.begin + blockIdx.x];
@@ -272,48 +316,71 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     if (col0 >= P.d_out) return;  // no barrier in this kernel
     const int n0 = col0 + 8 * li;
     const bool col_ok = n0 < P.d_out;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const int nc = col_ok ? n0 : col0;  // in-bounds column for lanes past d_out
+    const int cchunk = nc / P.B.chunk_len, cin = nc - cchunk * P.B.chunk_len;
 
+    // B strip: all row offsets, then all rows (masked to real ranks and
+    // columns), then the register transpose
+    int64_t boff[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            boff[ks][e] = P.B.row_off[off_index(P.B, it.adapter, min(32 * ks + 8 * lg + e, it.rank - 1), cchunk)];
+    issue_fence();
     u32x4_t bop[KS][8];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         u32x4_t rows[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = 32 * ks + 8 * lg + e;
-            rows[e] = (col_ok && j < it.rank) ? ld16(row_ptr(P.B, it.adapter, j, n0)) : zero;
-        }
+        for (int e = 0; e < 8; ++e) rows[e] = ld16_if(col_ok && 32 * ks + 8 * lg + e < it.rank, P.B.pool + boff[ks][e] + cin);
         transpose8x8(rows, bop[ks]);
     }
 
+    const int64_t vslice = (int64_t)args.n_active * P.ldv;
     for (int mt = 0; mt * 16 < it.nrows; ++mt) {
-        // first operand: v rows (sum of the K slices, in slice order), split into hi/lo bf16
+        // y rows owned by this lane: 4*lg + e of this tile (rows past the item are masked)
+        float* yrow[4];
+        bool yok[4];
+        f32x4_t y0[4], y1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int mm = 16 * mt + 4 * lg + e;
+            yok[e] = col_ok && mm < it.nrows;
+            yrow[e] = P.y + (int64_t)args.row_index[it.row0 + min(mm, it.nrows - 1)] * P.ldy + nc;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            y0[e] = ldf4_if(yok[e], yrow[e]);
+            y1[e] = ldf4_if(yok[e], yrow[e] + 4);
+        }
+        // first operand: v row 16*mt + li
         const int m = 16 * mt + li;
         const bool row_ok = m < it.nrows;
-        const float* vrow = P.v + (int64_t)(it.row0 + m) * P.ldv;
-        const int64_t vslice = (int64_t)args.n_active * P.ldv;
+        const float* vrow = P.v + (int64_t)(it.row0 + min(m, it.nrows - 1)) * P.ldv;
         u32x4_t vhi[KS], vlo[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int j0 = 32 * ks + 8 * lg;
+            const bool ok_a = row_ok && j0 < it.rank, ok_b = row_ok && j0 + 4 < it.rank;
+            const int ja = ok_a ? j0 : 0, jb = ok_b ? j0 + 4 : 0;  // in-bounds columns
             f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-            // slices are loaded four at a time (loads issued before the adds)
-            // and summed in slice order
+            // slices four at a time, loads before adds, summed in slice order
             for (int s0 = 0; s0 < it.nslices; s0 += 4) {
                 f32x4_t sa[4], sb[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const bool in = s0 + q < it.nslices;
-                    sa[q] = (in && row_ok && j0 < it.rank) ? ldf4(vrow + (s0 + q) * vslice + j0) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    sb[q] = (in && row_ok && j0 + 4 < it.rank) ? ldf4(vrow + (s0 + q) * vslice + j0 + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    const int64_t so = (int64_t)min(s0 + q, it.nslices - 1) * vslice;
+                    sa[q] = ldf4_if(in && ok_a, vrow + so + ja);
+                    sb[q] = ldf4_if(in && ok_b, vrow + so + jb);
                 }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < 4; ++q)
                     if (s0 + q < it.nslices) {
                         a += sa[q];
                         b += sb[q];
                     }
-                }
             }
             float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
@@ -324,18 +391,6 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
                 const uint32_t h = pack_bf16(f[2 * q], f[2 * q + 1]);
                 vhi[ks][q] = h;
                 vlo[ks][q] = pack_bf16(f[2 * q] - bf16_lo(h), f[2 * q + 1] - bf16_hi(h));
-            }
-        }
-        // output rows owned by this lane: 4*lg + e of this tile
-        float* yrow[4];
-        f32x4_t y0[4], y1[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int mm = 16 * mt + 4 * lg + e;
-            yrow[e] = (col_ok && mm < it.nrows) ? P.y + (int64_t)args.row_index[it.row0 + mm] * P.ldy + n0 : nullptr;
-            if (yrow[e]) {
-                y0[e] = ldf4(yrow[e]);
-                y1[e] = ldf4(yrow[e] + 4);
             }
         }
         f32x4_t acc[8];
@@ -351,7 +406,7 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (!yrow[e]) continue;
+            if (!yok[e]) continue;
             f32x4_t o0, o1;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -385,8 +440,9 @@ struct MergeArgs {
 // transposed so column slot i of MFMA c is k = kbase + 8*i + c.  Lane (li,lg)
 // then owns W rows nbase + 8*(4*lg+e) + c2 at columns kbase + 8*li .. +7.
 // The wave walks its tile in 8 passes (one c2 each, 4 rows x 16 bytes per
-// lane) and keeps the W loads of the next two passes in flight while it
-// computes and stores the current one.
+// lane); the adapter rows are loaded first, then the W loads of the first
+// passes, and every pass issues the loads of a later pass before it computes
+// and stores its own.
 template <int KS>
 __global__ __launch_bounds__(WG, HETLORA_MERGE_WAVES) void merge_kernel(MergeArgs args) {
     constexpr int PF = HETLORA_MERGE_PREFETCH;
@@ -399,45 +455,65 @@ __global__ __launch_bounds__(WG, HETLORA_MERGE_WAVES) void merge_kernel(MergeArg
     if (kbase >= M.d_in) return;  // no barrier in this kernel
     const int k0 = kbase + 8 * li;
     const bool k_ok = k0 < M.d_in;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    uint16_t* const wbase = M.W + k0;
+    const int kc = k_ok ? k0 : kbase;                   // in-bounds column
+    const int nn = nbase + 8 * li;
+    const bool n_ok = nn < M.d_out;
+    const int ncol = n_ok ? nn : nbase;                 // in-bounds column of B
 
-    auto row_of = [&](int c2, int e) { return nbase + 8 * (4 * lg + e) + c2; };
-    u32x4_t wv[PF + 1][4];
-    auto load_pass = [&](int c2, u32x4_t* dst) {
+    // adapter rows: all row offsets, then all rows
+    int64_t ob[KS][8], oa[KS][8];
+    const int cb = ncol / M.B.chunk_len, ca = kc / M.A.chunk_len;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int n = row_of(c2, e);
-            dst[e] = (k_ok && n < M.d_out)
-                         ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wbase + (int64_t)n * M.ldw))
-                         : zero;
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int jj = min(32 * ks + 8 * lg + e, M.rank - 1);
+            ob[ks][e] = M.B.row_off[off_index(M.B, M.adapter, jj, cb)];
+            oa[ks][e] = M.A.row_off[off_index(M.A, M.adapter, jj, ca)];
         }
-    };
+    issue_fence();
+    u32x4_t rb[KS][8], ra[KS][8];
 #pragma unroll
-    for (int c2 = 0; c2 < PF; ++c2) load_pass(c2, wv[c2]);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            rb[ks][e] = ld16(M.B.pool + ob[ks][e] + (ncol - cb * M.B.chunk_len));
+            ra[ks][e] = ld16(M.A.pool + oa[ks][e] + (kc - ca * M.A.chunk_len));
+        }
+
+    // W: pass c2 covers rows nbase + 8*(4*lg+e) + c2 (rows past d_out read row 0 of the tile)
+    uint16_t* const wcol = M.W + kc;
+    auto wrow = [&](int c2, int e) {
+        const int n = nbase + 8 * (4 * lg + e) + c2;
+        return wcol + (int64_t)(n < M.d_out ? n : nbase) * M.ldw;
+    };
+    u32x4_t wv[PF + 1][4];
+#pragma unroll
+    for (int c2 = 0; c2 < PF; ++c2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[c2][e] = ld16(wrow(c2, e));
 
     u32x4_t aop[KS][8], bop[KS][8];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t rows[8];
-        const int nn = nbase + 8 * li;
+        // rank slots past the rank and columns past the matrix were read at
+        // clamped addresses (no masked loads here: the adapter rows come from
+        // L2 and a masked load would serialise the batch); zero them
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int j = 32 * ks + 8 * lg + e;
-            rows[e] = (nn < M.d_out && j < M.rank) ? ld16(row_ptr(M.B, M.adapter, j, nn)) : zero;
+            const bool jok = 32 * ks + 8 * lg + e < M.rank;
+            rb[ks][e] = sel(jok && n_ok, rb[ks][e]);
+            ra[ks][e] = sel(jok && k_ok, ra[ks][e]);
         }
-        transpose8x8(rows, aop[ks]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = 32 * ks + 8 * lg + e;
-            rows[e] = (k_ok && j < M.rank) ? ld16(row_ptr(M.A, M.adapter, j, k0)) : zero;
-        }
-        transpose8x8(rows, bop[ks]);
+        transpose8x8(rb[ks], aop[ks]);
+        transpose8x8(ra[ks], bop[ks]);
     }
 
 #pragma unroll
     for (int c2 = 0; c2 < 8; ++c2) {
-        if (c2 + PF < 8) load_pass(c2 + PF, wv[(c2 + PF) % (PF + 1)]);
+        if (c2 + PF < 8)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[(c2 + PF) % (PF + 1)][e] = ld16(wrow(c2 + PF, e));
         f32x4_t acc[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -451,7 +527,7 @@ __global__ __launch_bounds__(WG, HETLORA_MERGE_WAVES) void merge_kernel(MergeArg
         const u32x4_t* cur = wv[c2 % (PF + 1)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int n = row_of(c2, e);
+            const int n = nbase + 8 * (4 * lg + e) + c2;
             if (!(k_ok && n < M.d_out)) continue;
             u32x4_t o;
 #pragma unroll
@@ -461,7 +537,7 @@ __global__ __launch_bounds__(WG, HETLORA_MERGE_WAVES) void merge_kernel(MergeArg
                 const float hi = __builtin_fmaf(M.scale, acc[2 * q + 1][e], bf16_hi(w));
                 o[q] = pack_bf16(lo, hi);
             }
-            __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(wbase + (int64_t)n * M.ldw));
+            *reinterpret_cast<u32x4_t*>(wrow(c2, e)) = o;
         }
     }
 }
