@@ -15,10 +15,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
-LORA_ABI_VERSION = 2
+LORA_ABI_VERSION = 3
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
-LORA_MAX_RANGES = 16
+LORA_MAX_RANGES = 32
 LORA_MAX_MERGE = 8
 LORA_MAX_SLICES = 16
 WORK_INTS = 8  # int32 fields of lora_work_t

@@ -132,7 +132,8 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
     for (int32_t s = 0; s < n_seg; ++s) {
         const int32_t len = seg_start[s + 1] - seg_start[s];
         const SegCfg cfg = pick(op, len, seg_rank[s], d_in, d_out);
-        const int cls = shrink ? lv_shrink_class(seg_rank[s]) : lv_expand_class(seg_rank[s]);
+        const int cls = shrink ? lv_shrink_class(seg_rank[s])
+                        : cfg.shape == LV_E_BGMV ? 0 : lv_expand_class(seg_rank[s]);
         const int32_t mt = shrink ? lv_shrink_rows(cfg.shape) : lv_expand_rows(cfg.shape);
         seg_variant[(size_t)s] = cfg.shape * LV_RANK_CLASSES + cls;
         seg_chunks[(size_t)s] = (len + mt - 1) / mt;

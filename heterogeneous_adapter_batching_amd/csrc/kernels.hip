@@ -419,6 +419,114 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     }
 }
 
+// One workgroup = one work item of at most BGMV_ROWS rows x one 2048-column
+// group of one projection (decode rows: BGMV).  Lane t owns columns
+// 8t .. 8t+7 of the group and forms y[row][n] += s * sum_j v[row][j] * B[j][n]
+// with fp32 FMAs in rank order.  v[row][j] is loaded by lane j % 64 of every
+// wave (its K slices summed in slice order) and broadcast with readlane; B is
+// read 16 rank rows at a time (row offsets first, then the rows).
+#define BGMV_ROWS 2
+__global__ __launch_bounds__(WG) void bgmv_expand_kernel(ExpandArgs args) {
+    const lora_work_t it = args.work[args.begin + blockIdx.x];
+    int pi = 0;
+    while (pi + 1 < args.n_proj && (int)blockIdx.y >= args.p[pi + 1].cg_begin) ++pi;
+    const ExpandProj& P = args.p[pi];
+    if (!item_ok(it, args.n_active, args.v_slices, P.B, LORA_MAX_RANK) || it.nrows > BGMV_ROWS) return;
+    const int lane = threadIdx.x & 63;
+    const int n0 = ((int)blockIdx.y - P.cg_begin) * 2048 + 8 * (int)threadIdx.x;
+    const bool col_ok = n0 < P.d_out;  // lanes past d_out stay: they hold v values for readlane
+    const int nc = col_ok ? n0 : 0;
+    const int cchunk = nc / P.B.chunk_len, cin = nc - cchunk * P.B.chunk_len;
+    const int64_t vslice = (int64_t)args.n_active * P.ldv;
+
+    // first batch: y row indices, v (lane j holds ranks j and j + 64), first B row offsets
+    int32_t yidx[BGMV_ROWS];
+#pragma unroll
+    for (int p = 0; p < BGMV_ROWS; ++p) yidx[p] = args.row_index[it.row0 + min(p, it.nrows - 1)];
+    float vsum[BGMV_ROWS][2];
+#pragma unroll
+    for (int p = 0; p < BGMV_ROWS; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int j = lane + 64 * h;
+            const bool ok = p < it.nrows && j < it.rank;
+            const float* vp = P.v + (int64_t)(it.row0 + min(p, it.nrows - 1)) * P.ldv + (ok ? j : 0);
+            float t = 0.f;
+            for (int s0 = 0; s0 < it.nslices; s0 += 4) {
+                float sv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    sv[q] = 0.f;
+                    if (ok && s0 + q < it.nslices) sv[q] = vp[(s0 + q) * vslice];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (s0 + q < it.nslices) t += sv[q];
+            }
+            vsum[p][h] = t;
+        }
+    int64_t boff[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) boff[e] = P.B.row_off[off_index(P.B, it.adapter, min(e, it.rank - 1), cchunk)];
+    issue_fence();
+    // second batch: y rows
+    float* yrow[BGMV_ROWS];
+    f32x4_t y0[BGMV_ROWS], y1[BGMV_ROWS];
+#pragma unroll
+    for (int p = 0; p < BGMV_ROWS; ++p) {
+        yrow[p] = P.y + (int64_t)yidx[p] * P.ldy + nc;
+        const bool ok = col_ok && p < it.nrows;
+        y0[p] = ldf4_if(ok, yrow[p]);
+        y1[p] = ldf4_if(ok, yrow[p] + 4);
+    }
+    f32x4_t acc0[BGMV_ROWS], acc1[BGMV_ROWS];
+#pragma unroll
+    for (int p = 0; p < BGMV_ROWS; ++p) acc0[p] = acc1[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int j0 = 0; j0 < it.rank; j0 += 16) {
+        if (j0 > 0) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                boff[e] = P.B.row_off[off_index(P.B, it.adapter, min(j0 + e, it.rank - 1), cchunk)];
+            issue_fence();
+        }
+        u32x4_t rows[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) rows[e] = ld16_if(col_ok && j0 + e < it.rank, P.B.pool + boff[e] + cin);
+#pragma unroll
+        for (int p = 0; p < BGMV_ROWS; ++p) {
+            if (p >= it.nrows) break;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int j = j0 + e;  // wave-uniform
+                const float vj = __builtin_amdgcn_readlane(__float_as_int(j < 64 ? vsum[p][0] : vsum[p][1]), j & 63);
+                const float w = j < it.rank ? __int_as_float(vj) : 0.f;
+                const u32x4_t r = rows[e];
+                acc0[p][0] = __builtin_fmaf(w, bf16_lo(r[0]), acc0[p][0]);
+                acc0[p][1] = __builtin_fmaf(w, bf16_hi(r[0]), acc0[p][1]);
+                acc0[p][2] = __builtin_fmaf(w, bf16_lo(r[1]), acc0[p][2]);
+                acc0[p][3] = __builtin_fmaf(w, bf16_hi(r[1]), acc0[p][3]);
+                acc1[p][0] = __builtin_fmaf(w, bf16_lo(r[2]), acc1[p][0]);
+                acc1[p][1] = __builtin_fmaf(w, bf16_hi(r[2]), acc1[p][1]);
+                acc1[p][2] = __builtin_fmaf(w, bf16_lo(r[3]), acc1[p][2]);
+                acc1[p][3] = __builtin_fmaf(w, bf16_hi(r[3]), acc1[p][3]);
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < BGMV_ROWS; ++p) {
+        if (p >= it.nrows || !col_ok) continue;
+        f32x4_t o0, o1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            o0[c] = __builtin_fmaf(P.scale, acc0[p][c], y0[p][c]);
+            o1[c] = __builtin_fmaf(P.scale, acc1[p][c], y1[p][c]);
+        }
+        stf4(yrow[p], o0);
+        stf4(yrow[p] + 4, o1);
+    }
+}
+
 // ------------------------------------------------------------------ merge
 struct MergeMat {
     uint16_t* W;
@@ -640,24 +748,32 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
     args.n_active = L->info.n_active;
     args.v_slices = L->info.v_slices;
     args.n_proj = n_proj;
-    int32_t groups = 0;
     for (int i = 0; i < n_proj; ++i) {
         const lora_expand_proj_t& p = projs[i];
         if (!p.v || !p.y || !aligned16(p.v) || !aligned16(p.y)) return LORA_EINVAL;
         if (p.d_out <= 0 || p.d_out % 64 != 0) return LORA_ESHAPE;
         if (p.ldy < p.d_out || p.ldy % 4 != 0 || p.ldv % 4 != 0 || p.ldv < L->info.max_rank) return LORA_EINVAL;
         if ((st = check_rows(p.B, p.d_out, L->info.max_rank, L->info.max_adapter)) != LORA_OK) return st;
-        args.p[i] = ExpandProj{p.v, p.ldv, to_rows(p.B), p.d_out, p.y, p.ldy, p.scale, groups};
-        groups += (p.d_out + 511) / 512;
+        args.p[i] = ExpandProj{p.v, p.ldv, to_rows(p.B), p.d_out, p.y, p.ldy, p.scale, 0};
     }
     if (L->info.n_work == 0) return LORA_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     for (int r = 0; r < L->info.n_ranges; ++r) {
         const lora_range_t& R = L->info.ranges[r];
         if (R.count == 0) continue;
+        const int shape = R.variant / LV_RANK_CLASSES;
+        const int32_t width = lv_expand_cols(shape);
+        int32_t groups = 0;  // column groups of every projection, back to back on grid.y
+        for (int i = 0; i < n_proj; ++i) {
+            args.p[i].cg_begin = groups;
+            groups += (args.p[i].d_out + width - 1) / width;
+        }
         args.begin = R.begin;
-        hipLaunchKernelGGL(expand_table(R.variant % LV_RANK_CLASSES), dim3((unsigned)R.count, (unsigned)groups),
-                           dim3(WG), 0, s, args);
+        if (shape == LV_E_BGMV)
+            hipLaunchKernelGGL(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG), 0, s, args);
+        else
+            hipLaunchKernelGGL(expand_table(R.variant % LV_RANK_CLASSES), dim3((unsigned)R.count, (unsigned)groups),
+                               dim3(WG), 0, s, args);
     }
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
 }

@@ -17,20 +17,26 @@
 #define LV_S_ROWS128 2
 #define LV_S_SHAPES 3
 
-// Expand shapes: the same kernel, work items of 16 / 64 / 128 / 256 rows
-// (more rows reuse each B column strip more, fewer rows give more workgroups).
+// Expand shapes: the MFMA kernel with work items of 16 / 64 / 128 / 256 rows
+// (more rows reuse each B column strip more, fewer rows give more
+// workgroups), and the VALU kernel for decode items of at most 2 rows (BGMV),
+// which has a single rank class.
 #define LV_E_ROWS16 0
 #define LV_E_ROWS64 1
 #define LV_E_ROWS128 2
 #define LV_E_ROWS256 3
-#define LV_E_SHAPES 4
+#define LV_E_BGMV 4
+#define LV_E_SHAPES 5
 
 static inline int32_t lv_shrink_rows(int shape) {
     return shape == LV_S_SPLITK16 ? 16 : shape == LV_S_ROWS64 ? 64 : 128;
 }
 static inline int32_t lv_expand_rows(int shape) {
-    return shape == LV_E_ROWS16 ? 16 : shape == LV_E_ROWS64 ? 64 : shape == LV_E_ROWS128 ? 128 : 256;
+    return shape == LV_E_ROWS16 ? 16 : shape == LV_E_ROWS64 ? 64 : shape == LV_E_ROWS128 ? 128
+         : shape == LV_E_ROWS256 ? 256 : 2;
 }
+// Columns one expand workgroup covers.
+static inline int32_t lv_expand_cols(int shape) { return shape == LV_E_BGMV ? 2048 : 512; }
 
 // Shrink rank classes: N tiles of 16 ranks -> 1, 2, 4, 8 (rank <= 16, 32, 64, 128).
 static inline int lv_shrink_class(int32_t rank) {

@@ -67,10 +67,10 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 2
+#define LORA_ABI_VERSION 3
 #define LORA_MAX_RANK 128   /* ranks are 1..128                              */
 #define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
-#define LORA_MAX_RANGES 16  /* kernel variants in one plan                   */
+#define LORA_MAX_RANGES 32  /* kernel variants in one plan                   */
 #define LORA_MAX_MERGE 8    /* weight matrices per merge/unmerge call        */
 #define LORA_MAX_SLICES 16  /* K slices of one shrink segment                */
 
