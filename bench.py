@@ -126,6 +126,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="layer copies the steps rotate over")
+    ap.add_argument("--workload", default="decode", choices=["decode", "tiny", "prefill", "vision", "mix70b"],
+                    help="decode (default) is the benchmark line; the others time shrink+expand (and the "
+                         "vision mode switch) of that workload for the kernel tables")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -133,6 +136,8 @@ def main():
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload != "decode":
+        return other_workload(args)
     import torch
     import workloads
     from heterogeneous_adapter_batching_amd.session import Batch, Rows, prepare_merge
@@ -261,6 +266,83 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, {"hetero": het, "homo": homo}, merge_host)
+    print(json.dumps(out), flush=True)
+
+
+def other_workload(args):
+    """Kernel timing of the tiny, prefill, vision or 70B workload: shrink and
+    expand over all projections per step (HIP events on the launch stream,
+    median over the timed steps), plus for the vision workload the mode switch
+    (merge then unmerge of adapter 0 into 32 layers x 4 W[4096x4096])."""
+    import torch
+    import workloads
+    from heterogeneous_adapter_batching_amd.session import Batch, Rows, prepare_merge
+    from workloads.device import bits_to_device, to_device
+
+    k = {"tiny": 0, "prefill": 2, "vision": 3, "mix70b": 4}[args.workload]
+    W = workloads.gen_config(k, n_layers=32) if k == 3 else workloads.gen_config(k)
+    dw = to_device(W)
+    rows = lambda desc, off: Rows(dw.pool, off, desc.n_adapters, desc.max_rank, desc.row_len, desc.chunk_len)
+    A = [rows(p.A, d.A_off) for p, d in zip(W.projections, dw.projections)]
+    B = [rows(p.B, d.B_off) for p, d in zip(W.projections, dw.projections)]
+    d_in = max(p.d_in for p in W.projections)
+    d_out = max(p.d_out for p in W.projections)
+    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out).refresh(W.row_adapter)
+    ldv = -(-int(W.adapter_rank.max()) // 4) * 4
+    v = [b.new_v(ldv) for _ in W.projections]
+    do_s = b.prepare_shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)])
+    do_e = b.prepare_expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")   # Infinity Cache flush between steps
+    res = {"shrink": [], "expand": []}
+    for it in range(args.warmup + args.steps):
+        flush.fill_(it & 0xFF)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(); do_s(); e[1].record(); do_e(); e[2].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            res["shrink"].append(e[0].elapsed_time(e[1]) * 1e3)
+            res["expand"].append(e[1].elapsed_time(e[2]) * 1e3)
+    c = delta_cost(W, W.row_adapter)
+    out = {"workload": args.workload, "rows": W.n_rows, "active": int((W.row_adapter >= 0).sum()),
+           "segments": b.segs.n_seg, "layout": W.layout, "kernels": {}}
+    for g, nb, fl in (("shrink", c["shrink_bytes"], c["flops"] * 0.5), ("expand", c["expand_bytes"], c["flops"] * 0.5)):
+        us = float(np.median(res[g]))
+        out["kernels"][g] = {"us_median": round(us, 2), "alg_bytes": int(nb), "GB_s": round(nb / us / 1e3, 1),
+                             "hbm_frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+                             "TFLOP_s": round(fl / us / 1e6, 2)}
+    tot = sum(np.median(res[g]) for g in res)
+    nb = c["shrink_bytes"] + c["expand_bytes"]
+    out["shrink_expand_us"] = round(float(tot), 2)
+    out["shrink_expand_hbm_frac"] = round(nb / tot / 1e3 / HBM_PEAK_GBS, 4)
+    if k == 3:
+        spec = W.merge
+        r = int(W.adapter_rank[spec.adapter])
+        mats = {}
+        for l in range(spec.n_layers):
+            for pi in spec.projs:
+                mats[(l, pi)] = (torch.randn(4096, 4096, device="cuda") / 64).to(torch.bfloat16).view(torch.int16)
+        calls = [(prepare_merge([(mats[(l, pi)], A[pi], B[pi], spec.adapter, r, W.scale) for pi in spec.projs]),
+                  prepare_merge([(mats[(l, pi)], A[pi], B[pi], spec.adapter, r, W.scale) for pi in spec.projs],
+                                unmerge=True)) for l in range(spec.n_layers)]
+        ts = []
+        for rep in range(3):
+            torch.cuda.synchronize()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            for m, _ in calls:
+                m()
+            e[1].record()
+            for _, u in calls:
+                u()
+            e[2].record()
+            torch.cuda.synchronize()
+            ts.append((e[0].elapsed_time(e[1]) * 1e3, e[1].elapsed_time(e[2]) * 1e3))
+        mb = merge_cost(4096, 4096, r, 4 * spec.n_layers)["bytes"]
+        mus, uus = float(np.median([t[0] for t in ts])), float(np.median([t[1] for t in ts]))
+        out["switch"] = {"merge_us": round(mus, 1), "unmerge_us": round(uus, 1),
+                         "merge_us_per_layer": round(mus / spec.n_layers, 2), "alg_bytes_per_phase": int(mb),
+                         "merge_hbm_frac": round(mb / mus / 1e3 / HBM_PEAK_GBS, 4),
+                         "unmerge_hbm_frac": round(mb / uus / 1e3 / HBM_PEAK_GBS, 4)}
     print(json.dumps(out), flush=True)
 
 
