@@ -6,8 +6,10 @@ rows, d = 4096, q/k/v/o projections, rank-16 adapters.  One step is one pass
 of the whole path over that batch, on one layer:
 
   1. fully heterogeneous batch (row i -> adapter i, 64 adapters):
-     segment build + plan (host, C) -> metadata upload -> shrink -> expand
-  2. homogeneous batch (all rows -> adapter 0): the same
+     segment build + plans (host, C) -> metadata upload -> lora_apply (every
+     segment is one row, so shrink and expand run fused in one kernel)
+  2. homogeneous batch (all rows -> adapter 0): the same (one 64-row segment:
+     lora_apply runs the shrink and the expand kernels)
   3. mode switch of the layer: merge adapter 0 into the four W[4096x4096],
      then unmerge it (one launch each, four matrices per launch)
 
@@ -24,7 +26,10 @@ timed steps; `roofline` describes the kernel with the largest share of the
 step time.  `cpu_baseline` times the CPU oracle on a bounded sample of the
 same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu-baseline]
+With --path split the step calls lora_shrink and lora_expand instead.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--path apply|split]
+                       [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -129,6 +134,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "tiny", "prefill", "vision", "mix70b"],
                     help="decode (default) is the benchmark line; the others time shrink+expand (and the "
                          "vision mode switch) of that workload for the kernel tables")
+    ap.add_argument("--path", default="apply", choices=["apply", "split"],
+                    help="apply (default): lora_apply, one-row segments fused; split: lora_shrink then lora_expand")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -164,36 +171,44 @@ def main():
     bo = Batch(64, W.adapter_rank, 4096, 4096).refresh(homo)
     vs = {id(b): [b.new_v(ldv) for _ in W.projections] for b in (bh, bo)}
     stream = torch.cuda.current_stream()
+    split = args.path == "split"
     for L in layers:
         L["calls"] = []
         for b in (bh, bo):
             v = vs[id(b)]
-            L["calls"].append((b.prepare_shrink([(d.x, L["A"][i], v[i]) for i, d in enumerate(L["dw"].projections)]),
-                               b.prepare_expand([(v[i], L["B"][i], d.y, W.scale)
-                                                 for i, d in enumerate(L["dw"].projections)])))
+            pr = L["dw"].projections
+            if split:
+                L["calls"].append((b.prepare_shrink([(d.x, L["A"][i], v[i]) for i, d in enumerate(pr)]),
+                                   b.prepare_expand([(v[i], L["B"][i], d.y, W.scale) for i, d in enumerate(pr)])))
+            else:
+                L["calls"].append((b.prepare_apply([(d.x, L["A"][i], v[i], L["B"][i], d.y, W.scale)
+                                                    for i, d in enumerate(pr)]),))
         mats = [(L["Wt"][i], L["A"][i], L["B"][i], W.merge.adapter, r_m, W.scale) for i in range(len(L["Wt"]))]
         L["merge"], L["unmerge"] = prepare_merge(mats), prepare_merge(mats, unmerge=True)
     merge_host = layers[0]["merge_host"]
     n_mats = len(layers[0]["Wt"])
 
-    groups = ["hetero_shrink", "hetero_expand", "homo_shrink", "homo_expand", "merge", "unmerge"]
+    if split:
+        groups = ["hetero_shrink", "hetero_expand", "homo_shrink", "homo_expand", "merge", "unmerge"]
+    else:
+        groups = ["hetero_apply", "homo_apply", "merge", "unmerge"]
 
     def step(ev, k):
         L = layers[k % len(layers)]
-        for (b, ra, g), (do_shrink, do_expand) in zip(((bh, het, 0), (bo, homo, 2)), L["calls"]):
+        g = 0
+        for (b, ra), fns in zip(((bh, het), (bo, homo)), L["calls"]):
             b.refresh(ra)
-            ev[g][0].record(stream)
-            do_shrink()
-            ev[g][1].record(stream)
-            ev[g + 1][0].record(stream)
-            do_expand()
-            ev[g + 1][1].record(stream)
-        ev[4][0].record(stream)
+            for fn in fns:
+                ev[g][0].record(stream)
+                fn()
+                ev[g][1].record(stream)
+                g += 1
+        ev[g][0].record(stream)
         L["merge"]()
-        ev[4][1].record(stream)
-        ev[5][0].record(stream)
+        ev[g][1].record(stream)
+        ev[g + 1][0].record(stream)
         L["unmerge"]()
-        ev[5][1].record(stream)
+        ev[g + 1][1].record(stream)
 
     def new_events():
         return [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in groups]
@@ -221,7 +236,10 @@ def main():
            "hetero_expand": (ch["expand_bytes"], ch["flops"] * 0.5),
            "homo_shrink": (co["shrink_bytes"], co["flops"] * 0.5),
            "homo_expand": (co["expand_bytes"], co["flops"] * 0.5),
+           "hetero_apply": (ch["shrink_bytes"] + ch["expand_bytes"], ch["flops"]),
+           "homo_apply": (co["shrink_bytes"] + co["expand_bytes"], co["flops"]),
            "merge": (mc["bytes"], mc["flops"]), "unmerge": (mc["bytes"], mc["flops"])}
+    alg = {g: alg[g] for g in groups}
     step_bytes = sum(b for b, _ in alg.values())
     kernels = {}
     for g in groups:
@@ -233,8 +251,8 @@ def main():
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     # dominant kernel: largest share of GPU time; merge and unmerge are the same kernel
     mavg = (med["merge"] + med["unmerge"]) / 2
-    share = {"merge": med["merge"] + med["unmerge"], "hetero_expand": med["hetero_expand"],
-             "hetero_shrink": med["hetero_shrink"]}
+    share = {g: med[g] for g in groups if g not in ("merge", "unmerge")}
+    share["merge"] = med["merge"] + med["unmerge"]
     dom = max(share, key=share.get)
     if dom == "merge":
         d_us, d_bytes, name = mavg, mc["bytes"], "merge_kernel (merge/unmerge, 4 x W[4096x4096], rank 16)"
@@ -250,17 +268,18 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode BGMV, Llama-7B-shaped layer: 64 one-token rows, d 4096, q/k/v/o, "
-                               "rank 16; hetero (64 adapters) + homo (1 adapter) batches, then merge+unmerge "
+                               "rank 16; hetero (64 adapters) + homo (1 adapter) batches via lora_%s, then merge+unmerge "
                                "of one adapter into the layer's 4 W[4096x4096]; steps rotate over %d layer copies"
-                               % len(layers),
+                               % ("apply" if not split else "shrink/lora_expand", len(layers)),
                    "rows": 64, "d": 4096, "rank": 16, "adapters": 64, "projections": 4,
                    "layer_copies": len(layers)},
         "roofline": {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "us_per_launch": round(d_us, 3), "alg_bytes_per_launch": int(d_bytes)},
         "kernels": kernels,
-        "hetero_over_homo": round((med["hetero_shrink"] + med["hetero_expand"]) /
-                                  (med["homo_shrink"] + med["homo_expand"]), 3),
+        "hetero_over_homo": round(sum(med[g] for g in groups if g.startswith("hetero")) /
+                                  sum(med[g] for g in groups if g.startswith("homo")), 3),
+        "path": args.path,
         "merge_us_per_layer": round(mavg, 3),
         "step_alg_bytes": int(step_bytes),
     }

@@ -15,15 +15,15 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
-LORA_ABI_VERSION = 3
+LORA_ABI_VERSION = 4
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
-LORA_MAX_RANGES = 32
+LORA_MAX_RANGES = 48
 LORA_MAX_MERGE = 8
 LORA_MAX_SLICES = 16
 WORK_INTS = 8  # int32 fields of lora_work_t
 LORA_OK, LORA_EINVAL, LORA_EADAPTER, LORA_ERANK, LORA_ESHAPE, LORA_ECAPACITY, LORA_EHIP = 0, -1, -2, -3, -4, -5, -6
-LORA_OP_SHRINK, LORA_OP_EXPAND = 0, 1
+LORA_OP_SHRINK, LORA_OP_EXPAND, LORA_OP_APPLY = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python __graft_entry__.py` (build()) first")
@@ -69,6 +69,11 @@ class lora_expand_proj_t(ctypes.Structure):
                 ("ldy", _i64), ("scale", _f32)]
 
 
+class lora_apply_proj_t(ctypes.Structure):
+    _fields_ = [("x", _vp), ("ldx", _i64), ("d_in", _i32), ("A", lora_rows_t), ("v", _vp), ("ldv", _i64),
+                ("B", lora_rows_t), ("d_out", _i32), ("y", _vp), ("ldy", _i64), ("scale", _f32)]
+
+
 class lora_merge_mat_t(ctypes.Structure):
     _fields_ = [("W", _vp), ("ldw", _i64), ("d_out", _i32), ("d_in", _i32), ("A", lora_rows_t),
                 ("B", lora_rows_t), ("adapter", _i32), ("rank", _i32), ("scale", _f32)]
@@ -81,6 +86,7 @@ _sig = {
     "lora_plan": (_i32, [_i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _P(lora_plan_info_t)]),
     "lora_shrink": (_i32, [_P(lora_launch_t), _i32, _P(lora_shrink_proj_t), _vp]),
     "lora_expand": (_i32, [_P(lora_launch_t), _i32, _P(lora_expand_proj_t), _vp]),
+    "lora_apply": (_i32, [_P(lora_launch_t), _i32, _P(lora_apply_proj_t), _vp]),
     "lora_merge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
     "lora_unmerge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
     "lora_rows_dense_offsets": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _P(_i64)]),
@@ -167,7 +173,7 @@ def lora_plan(op, segs, d_in, d_out, work_capacity=None, work_out=None, info_out
         work = work_out
         cap = work.shape[0] if work_capacity is None else int(work_capacity)
     else:
-        cap = LORA_MAX_SLICES * segs.n_active if work_capacity is None else int(work_capacity)
+        cap = (LORA_MAX_SLICES + 1) * segs.n_active if work_capacity is None else int(work_capacity)
         work = np.zeros((max(cap, 1), WORK_INTS), np.int32)
     info = lora_plan_info_t() if info_out is None else info_out
     st = _lib.lora_plan(int(op), segs.n_seg, segs.seg_start.ctypes.data, _ptr(segs.seg_adapter),
@@ -195,6 +201,10 @@ def call_expand(launch, arr, n, stream):
     _check(_lib.lora_expand(ctypes.byref(launch), n, arr, stream), "lora_expand")
 
 
+def call_apply(launch, arr, n, stream):
+    _check(_lib.lora_apply(ctypes.byref(launch), n, arr, stream), "lora_apply")
+
+
 def call_merge(arr, n, stream, unmerge=False):
     fn = _lib.lora_unmerge if unmerge else _lib.lora_merge
     _check(fn(n, arr, stream), "lora_unmerge" if unmerge else "lora_merge")
@@ -208,6 +218,11 @@ def lora_shrink(launch, projs, stream):
 def lora_expand(launch, projs, stream):
     arr = (lora_expand_proj_t * len(projs))(*projs)
     _check(_lib.lora_expand(ctypes.byref(launch), len(projs), arr, stream), "lora_expand")
+
+
+def lora_apply(launch, projs, stream):
+    arr = (lora_apply_proj_t * len(projs))(*projs)
+    _check(_lib.lora_apply(ctypes.byref(launch), len(projs), arr, stream), "lora_apply")
 
 
 def lora_merge(mats, stream):

@@ -101,17 +101,50 @@ SegCfg pick(int32_t op, int32_t len, int32_t rank, int32_t d_in, int32_t d_out) 
 
 }  // namespace
 
+namespace {
+
+// One segment's share of a plan.
+struct SegPlan {
+    int variant;      // op-local variant id
+    int32_t chunks;   // row chunks
+    int32_t slices;   // K slices of the shrink (1 for expand-only / fused)
+    int32_t mt;       // rows per item
+    bool shrink;      // items carry K slices (one item per chunk x slice)
+};
+
+// Shrink and expand parts of a segment (the expand variant is op-local to an
+// expand plan; an apply plan shifts it by LV_APPLY_EXPAND0).
+SegPlan shrink_part(int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
+    const SegCfg c = pick(LORA_OP_SHRINK, len, rank, d_in, d_out);
+    const int32_t mt = lv_shrink_rows(c.shape);
+    return SegPlan{c.shape * LV_RANK_CLASSES + lv_shrink_class(rank), (len + mt - 1) / mt, c.slices, mt, true};
+}
+SegPlan expand_part(int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
+    const SegCfg c = pick(LORA_OP_EXPAND, len, rank, d_in, d_out);
+    const int32_t mt = lv_expand_rows(c.shape);
+    const int cls = c.shape == LV_E_BGMV ? 0 : lv_expand_class(rank);
+    return SegPlan{c.shape * LV_RANK_CLASSES + cls, (len + mt - 1) / mt, c.slices, mt, false};
+}
+// One-row segments whose whole reduction fits one workgroup are fused (the
+// shrink result never leaves the chip) in an apply plan.
+bool fused(int32_t len, int32_t d_in, int32_t d_out) {
+    return len == 1 && d_in <= LV_FUSED_MAX_D && d_out <= LV_FUSED_MAX_D;
+}
+
+}  // namespace
+
 // Launch plan: every segment is cut into ceil(len / rows_per_item) row chunks
 // whose sizes differ by at most one row; a shrink item is one row chunk x one
-// K slice, an expand item one row chunk.  Items are grouped by variant (in
-// ascending variant id, segments in order inside a variant) so that each
-// variant is one launch over a contiguous range.
+// K slice, an expand item one row chunk.  An apply plan holds, per segment,
+// either one fused item or the segment's shrink and expand items.  Items are
+// grouped by variant (in ascending variant id, segments in order inside a
+// variant) so that each variant is one launch over a contiguous range.
 extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
                              const int32_t* seg_adapter, const int32_t* seg_rank,
                              int32_t d_in, int32_t d_out, int32_t work_capacity,
                              lora_work_t* work, lora_plan_info_t* info) {
-    if ((op != LORA_OP_SHRINK && op != LORA_OP_EXPAND) || n_seg < 0 || work_capacity < 0 ||
-        info == nullptr || seg_start == nullptr)
+    if ((op != LORA_OP_SHRINK && op != LORA_OP_EXPAND && op != LORA_OP_APPLY) || n_seg < 0 ||
+        work_capacity < 0 || info == nullptr || seg_start == nullptr)
         return LORA_EINVAL;
     if (n_seg > 0 && (seg_adapter == nullptr || seg_rank == nullptr)) return LORA_EINVAL;
     if (d_in <= 0 || d_out <= 0 || d_in % 64 != 0 || d_out % 64 != 0) return LORA_ESHAPE;
@@ -121,27 +154,38 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
         if (seg_adapter[s] < 0) return LORA_EADAPTER;
         if (seg_rank[s] < 1 || seg_rank[s] > LORA_MAX_RANK) return LORA_ERANK;
     }
-    const bool shrink = op == LORA_OP_SHRINK;
-    const int n_variants = LV_RANK_CLASSES * (shrink ? LV_S_SHAPES : LV_E_SHAPES);
+    const int n_variants = op == LORA_OP_SHRINK ? LV_S_SHAPES * LV_RANK_CLASSES
+                         : op == LORA_OP_EXPAND ? LV_E_SHAPES * LV_RANK_CLASSES
+                                                : LV_APPLY_VARIANTS;
 
-    std::vector<int> seg_variant((size_t)n_seg);
-    std::vector<int32_t> seg_chunks((size_t)n_seg), seg_slices((size_t)n_seg),
-        per_variant((size_t)n_variants, 0);
+    // each segment contributes up to two parts (shrink + expand of an apply plan)
+    std::vector<SegPlan> parts((size_t)n_seg * 2);
+    std::vector<int32_t> per_variant((size_t)n_variants, 0);
     int64_t total = 0;
     int32_t v_slices = 1;
     for (int32_t s = 0; s < n_seg; ++s) {
-        const int32_t len = seg_start[s + 1] - seg_start[s];
-        const SegCfg cfg = pick(op, len, seg_rank[s], d_in, d_out);
-        const int cls = shrink ? lv_shrink_class(seg_rank[s])
-                        : cfg.shape == LV_E_BGMV ? 0 : lv_expand_class(seg_rank[s]);
-        const int32_t mt = shrink ? lv_shrink_rows(cfg.shape) : lv_expand_rows(cfg.shape);
-        seg_variant[(size_t)s] = cfg.shape * LV_RANK_CLASSES + cls;
-        seg_chunks[(size_t)s] = (len + mt - 1) / mt;
-        seg_slices[(size_t)s] = cfg.slices;
-        const int32_t items = seg_chunks[(size_t)s] * (shrink ? cfg.slices : 1);
-        per_variant[(size_t)seg_variant[(size_t)s]] += items;
-        total += items;
-        if (cfg.slices > v_slices) v_slices = cfg.slices;
+        const int32_t len = seg_start[s + 1] - seg_start[s], r = seg_rank[s];
+        SegPlan a{-1, 0, 1, 1, false}, b{-1, 0, 1, 1, false};
+        if (op == LORA_OP_SHRINK) {
+            a = shrink_part(len, r, d_in, d_out);
+        } else if (op == LORA_OP_EXPAND) {
+            a = expand_part(len, r, d_in, d_out);
+        } else if (fused(len, d_in, d_out)) {
+            a = SegPlan{LV_APPLY_FUSED, 1, 1, 1, false};
+        } else {
+            a = shrink_part(len, r, d_in, d_out);
+            b = expand_part(len, r, d_in, d_out);
+            b.variant += LV_APPLY_EXPAND0;
+        }
+        for (SegPlan* q : {&a, &b}) {
+            if (q->variant < 0) continue;
+            const int32_t items = q->chunks * (q->shrink ? q->slices : 1);
+            per_variant[(size_t)q->variant] += items;
+            total += items;
+            if (q->slices > v_slices) v_slices = q->slices;
+        }
+        parts[2 * (size_t)s] = a;
+        parts[2 * (size_t)s + 1] = b;
     }
     info->n_work = (int32_t)total;
     if (total > work_capacity) return LORA_ECAPACITY;
@@ -158,31 +202,34 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
     int32_t begin = 0;
     for (int v = 0; v < n_variants; ++v) {
         if (per_variant[(size_t)v] == 0) continue;
-        lora_range_t& r = out.ranges[out.n_ranges++];
-        r.variant = v;
-        r.begin = begin;
-        r.count = per_variant[(size_t)v];
-        const int shape = v / LV_RANK_CLASSES;
-        r.rows_per_item = shrink ? lv_shrink_rows(shape) : lv_expand_rows(shape);
+        lora_range_t& rg = out.ranges[out.n_ranges++];
+        rg.variant = v;
+        rg.begin = begin;
+        rg.count = per_variant[(size_t)v];
         int32_t w = begin;
         for (int32_t s = 0; s < n_seg; ++s) {
-            if (seg_variant[(size_t)s] != v) continue;
-            const int32_t len = seg_start[s + 1] - seg_start[s];
-            const int32_t k = seg_chunks[(size_t)s], ns = seg_slices[(size_t)s];
-            const int32_t base = len / k, extra = len % k;
-            int32_t row = seg_start[s];
-            for (int32_t t = 0; t < k; ++t) {
-                const int32_t n = base + (t < extra ? 1 : 0);
-                if (shrink) {
-                    for (int32_t sl = 0; sl < ns; ++sl)
-                        work[w++] = lora_work_t{row, n, seg_adapter[s], seg_rank[s], sl, ns, {0, 0}};
-                } else {
-                    work[w++] = lora_work_t{row, n, seg_adapter[s], seg_rank[s], 0, ns, {0, 0}};
+            for (int h = 0; h < 2; ++h) {
+                const SegPlan& q = parts[2 * (size_t)s + h];
+                if (q.variant != v) continue;
+                rg.rows_per_item = q.mt;
+                const int32_t len = seg_start[s + 1] - seg_start[s];
+                const int32_t base = len / q.chunks, extra = len % q.chunks;
+                const int32_t ns = parts[2 * (size_t)s].slices;  // the segment's K slices
+                int32_t row = seg_start[s];
+                for (int32_t t = 0; t < q.chunks; ++t) {
+                    const int32_t n = base + (t < extra ? 1 : 0);
+                    if (q.shrink) {
+                        for (int32_t sl = 0; sl < q.slices; ++sl)
+                            work[w++] = lora_work_t{row, n, seg_adapter[s], seg_rank[s], sl, q.slices, {0, 0}};
+                    } else {
+                        work[w++] = lora_work_t{row, n, seg_adapter[s], seg_rank[s], 0,
+                                                v == LV_APPLY_FUSED && op == LORA_OP_APPLY ? 1 : ns, {0, 0}};
+                    }
+                    row += n;
                 }
-                row += n;
+                if (seg_rank[s] > out.max_rank) out.max_rank = seg_rank[s];
+                if (seg_adapter[s] > out.max_adapter) out.max_adapter = seg_adapter[s];
             }
-            if (seg_rank[s] > out.max_rank) out.max_rank = seg_rank[s];
-            if (seg_adapter[s] > out.max_adapter) out.max_adapter = seg_adapter[s];
         }
         begin = w;
     }

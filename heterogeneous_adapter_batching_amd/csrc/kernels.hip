@@ -136,9 +136,11 @@ struct Rows {
 // corrupted work list cannot index outside the buffers.
 __device__ __forceinline__ bool item_ok(const lora_work_t& it, int32_t n_active, int32_t v_slices, const Rows& t,
                                         int32_t rank_cap) {
-    return it.nrows > 0 && it.row0 >= 0 && it.row0 + it.nrows <= n_active && it.adapter >= 0 &&
-           it.adapter < t.n_adapters && it.rank >= 1 && it.rank <= rank_cap && it.rank <= t.max_rank &&
-           it.nslices >= 1 && it.nslices <= v_slices && it.kslice >= 0 && it.kslice < it.nslices;
+    // bitwise, not short-circuit: every field is already loaded, and one
+    // combined test lets the loads it needs issue together
+    return (it.nrows > 0) & (it.row0 >= 0) & (it.row0 + it.nrows <= n_active) & (it.adapter >= 0) &
+           (it.adapter < t.n_adapters) & (it.rank >= 1) & (it.rank <= rank_cap) & (it.rank <= t.max_rank) &
+           (it.nslices >= 1) & (it.nslices <= v_slices) & (it.kslice >= 0) & (it.kslice < it.nslices);
 }
 // Index into row_off of chunk `c` of row j of adapter a.
 __device__ __forceinline__ int64_t off_index(const Rows& t, int32_t a, int32_t j, int32_t c) {
@@ -527,6 +529,205 @@ __global__ __launch_bounds__(WG) void bgmv_expand_kernel(ExpandArgs args) {
     }
 }
 
+// ------------------------------------------------------------------ fused (apply)
+struct ApplyProj {
+    const uint16_t* x;
+    int64_t ldx;
+    int32_t d_in;
+    Rows A;
+    Rows B;
+    int32_t d_out;
+    float* y;
+    int64_t ldy;
+    float scale;
+};
+struct FusedArgs {
+    const int32_t* row_index;
+    const lora_work_t* work;
+    int32_t begin;
+    int32_t n_active;
+    ApplyProj p[LORA_MAX_PROJ];
+};
+
+// Wave-uniform read through the scalar data cache (row tables are read-only
+// for the whole launch).  `i` must be the same in every lane of the wave.
+__device__ __forceinline__ int64_t ld_uniform(const int64_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int64_t*)p)[i];
+}
+
+// Sums of 8 values over the 64 lanes of a wave by reduce-scatter: at the
+// steps 32, 16, 8 a lane keeps half of its remaining values and adds its
+// partner's copy of them, then 4, 2, 1 are a plain butterfly on the one value
+// left.  On return lane l holds the wave's sum of value 4*b5 + 2*b4 + b3
+// (b_i = bit i of l); 10 cross-lane moves instead of 48.
+__device__ __forceinline__ float wave_sum8(const float (&in)[8], int lane) {
+    float a4[4], a2[2], a1;
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float keep = b5 ? in[4 + i] : in[i], give = b5 ? in[i] : in[4 + i];
+        a4[i] = keep + __shfl_xor(give, 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float keep = b4 ? a4[2 + i] : a4[i], give = b4 ? a4[i] : a4[2 + i];
+        a2[i] = keep + __shfl_xor(give, 16);
+    }
+    {
+        const float keep = b3 ? a2[1] : a2[0], give = b3 ? a2[0] : a2[1];
+        a1 = keep + __shfl_xor(give, 8);
+    }
+    a1 += __shfl_xor(a1, 4);
+    a1 += __shfl_xor(a1, 2);
+    a1 += __shfl_xor(a1, 1);
+    return a1;
+}
+
+// One workgroup of FWG threads = one one-row work item of one projection:
+// shrink, reduction and expand without v leaving the chip.  Thread t works on
+// input elements and output columns 8c .. 8c+7 (c = t mod FWG/2; d_in, d_out
+// <= 4*FWG) for ranks 8h .. 8h+7 of each group of 16 ranks (h = t / (FWG/2)).
+// Per rank group: every thread forms its 8-element partial dot for each of its
+// ranks, the partials are summed inside each wave (wave_sum8) and over the
+// half's waves in wave order through LDS, and every thread then adds
+// v[j] * B[j][n] for its ranks and columns; at the end the second half's
+// column sums are added to the first half's through LDS (first half + second
+// half, a fixed order) and the first half updates y.  Each thread loads its
+// group's row offsets, then its 8 A rows and 8 B rows, so a decode row costs
+// one round trip for metadata and one for data.  With UNI (every chunk_len a
+// multiple of 512, so that a wave's 512 elements lie in one chunk) the row
+// offsets are wave-uniform and come through the scalar cache.
+#define FWG 1024
+#define FHALF (FWG / 2)
+template <bool UNI>
+__global__ __launch_bounds__(FWG) void fused_kernel(FusedArgs args) {
+    __shared__ float s_part[FWG / 64][8];
+    __shared__ float s_v[16];
+    __shared__ f32x4_t s_acc[FHALF][2];
+    const lora_work_t it = args.work[args.begin + blockIdx.x];
+    const ApplyProj& P = args.p[blockIdx.y];
+    // uniform over the workgroup, so returning here skips no barrier
+    if (!(item_ok(it, args.n_active, 1, P.A, LORA_MAX_RANK) & (it.nrows == 1) & (it.adapter < P.B.n_adapters) &
+          (it.rank <= P.B.max_rank) & (P.d_in <= 8 * FHALF) & (P.d_out <= 8 * FHALF)))
+        return;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int c = t & (FHALF - 1);
+    const int h = __builtin_amdgcn_readfirstlane(t / FHALF);  // a wave lies in one half
+    const int k0 = 8 * c, n0 = 8 * c;
+    const bool k_ok = k0 < P.d_in, n_ok = n0 < P.d_out;
+    const int kc = k_ok ? k0 : 0, nc = n_ok ? n0 : 0;  // in-bounds positions for idle threads
+    // chunk of each lane's elements; with UNI the wave's first element decides
+    const int kw = UNI ? __builtin_amdgcn_readfirstlane(kc) : kc;
+    const int nw = UNI ? __builtin_amdgcn_readfirstlane(nc) : nc;
+    const int ca = kw / P.A.chunk_len, cina = kc - ca * P.A.chunk_len;
+    const int cb = nw / P.B.chunk_len, cinb = nc - cb * P.B.chunk_len;
+
+    int32_t row = 0;
+    int64_t aoff[8], boff[8];
+    u32x4_t ar[8], br[8];
+    // row offsets of this thread's 8 ranks of group g0 (and, for the first
+    // group, the row index beside them), then (after a fence) their A and B
+    // rows; rank slots past the rank read row rank-1 (zeroed)
+    auto load_group = [&](int g0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = min(g0 + 8 * h + e, it.rank - 1);
+            if (UNI) {
+                aoff[e] = ld_uniform(P.A.row_off, off_index(P.A, it.adapter, j, ca));
+                boff[e] = ld_uniform(P.B.row_off, off_index(P.B, it.adapter, j, cb));
+            } else {
+                aoff[e] = P.A.row_off[off_index(P.A, it.adapter, j, ca)];
+                boff[e] = P.B.row_off[off_index(P.B, it.adapter, j, cb)];
+            }
+        }
+        if (g0 == 0) row = args.row_index[it.row0];
+        issue_fence();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ar[e] = ld16(P.A.pool + aoff[e] + cina);
+            br[e] = ld16(P.B.pool + boff[e] + cinb);
+        }
+    };
+    load_group(0);
+    // y and x after the first group's rows (unconditional loads at clamped,
+    // in-bounds positions; idle threads' values are zeroed or never stored),
+    // so that waiting for x does not hold back the A and B loads
+    float* const yp = P.y + (int64_t)row * P.ldy + nc;
+    const f32x4_t y0 = ldf4(yp), y1 = ldf4(yp + 4);
+    issue_fence();
+    const u32x4_t xv = sel(k_ok, ld16(P.x + (int64_t)row * P.ldx + kc));
+    float xf[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        xf[2 * q] = bf16_lo(xv[q]);
+        xf[2 * q + 1] = bf16_hi(xv[q]);
+    }
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+
+    for (int g0 = 0; g0 < it.rank; g0 += 16) {
+        if (g0 > 0) load_group(g0);
+        const int jb = g0 + 8 * h;  // first rank of this thread's half
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ar[e] = sel(k_ok && jb + e < it.rank, ar[e]);
+            br[e] = sel(n_ok && jb + e < it.rank, br[e]);
+        }
+        float part[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float d = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                d = __builtin_fmaf(xf[2 * q], bf16_lo(ar[e][q]), d);
+                d = __builtin_fmaf(xf[2 * q + 1], bf16_hi(ar[e][q]), d);
+            }
+            part[e] = d;
+        }
+        const float ws = wave_sum8(part, lane);
+        if ((lane & 7) == 0) s_part[wave][((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1)] = ws;
+        __syncthreads();
+        if (t < 16) {  // rank g0 + t: half t / 8, its waves in order
+            const int hh = t >> 3, e = t & 7;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < FHALF / 64; ++w) v += s_part[hh * (FHALF / 64) + w][e];
+            s_v[t] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float vj = jb + e < it.rank ? s_v[8 * h + e] : 0.f;
+            const u32x4_t r = br[e];
+            acc0[0] = __builtin_fmaf(vj, bf16_lo(r[0]), acc0[0]);
+            acc0[1] = __builtin_fmaf(vj, bf16_hi(r[0]), acc0[1]);
+            acc0[2] = __builtin_fmaf(vj, bf16_lo(r[1]), acc0[2]);
+            acc0[3] = __builtin_fmaf(vj, bf16_hi(r[1]), acc0[3]);
+            acc1[0] = __builtin_fmaf(vj, bf16_lo(r[2]), acc1[0]);
+            acc1[1] = __builtin_fmaf(vj, bf16_hi(r[2]), acc1[1]);
+            acc1[2] = __builtin_fmaf(vj, bf16_lo(r[3]), acc1[2]);
+            acc1[3] = __builtin_fmaf(vj, bf16_hi(r[3]), acc1[3]);
+        }
+        __syncthreads();  // s_part / s_v are reused by the next group
+    }
+    if (h == 1) {
+        s_acc[c][0] = acc0;
+        s_acc[c][1] = acc1;
+    }
+    __syncthreads();
+    if (h == 0 && n_ok) {
+        acc0 += s_acc[c][0];
+        acc1 += s_acc[c][1];
+        f32x4_t o0, o1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            o0[q] = __builtin_fmaf(P.scale, acc0[q], y0[q]);
+            o1[q] = __builtin_fmaf(P.scale, acc1[q], y1[q]);
+        }
+        stf4(yp, o0);
+        stf4(yp + 4, o1);
+    }
+}
+
 // ------------------------------------------------------------------ merge
 struct MergeMat {
     uint16_t* W;
@@ -673,7 +874,9 @@ int32_t check_launch(const lora_launch_t* L, int32_t op, int32_t n_proj) {
     if (I.v_slices < 1 || I.v_slices > LORA_MAX_SLICES || I.n_active < 0) return LORA_EINVAL;
     if (I.n_work > 0 && (!L->row_index || !L->work)) return LORA_EINVAL;
     if (I.max_rank > LORA_MAX_RANK) return LORA_ERANK;
-    const int n_variants = LV_RANK_CLASSES * (op == LORA_OP_SHRINK ? LV_S_SHAPES : LV_E_SHAPES);
+    const int n_variants = op == LORA_OP_SHRINK ? LV_S_SHAPES * LV_RANK_CLASSES
+                         : op == LORA_OP_EXPAND ? LV_E_SHAPES * LV_RANK_CLASSES
+                                                : LV_APPLY_VARIANTS;
     for (int r = 0; r < I.n_ranges; ++r) {
         const lora_range_t& R = I.ranges[r];
         if (R.variant < 0 || R.variant >= n_variants || R.begin < 0 || R.count < 0 || R.begin + R.count > I.n_work)
@@ -774,6 +977,75 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
         else
             hipLaunchKernelGGL(expand_table(R.variant % LV_RANK_CLASSES), dim3((unsigned)R.count, (unsigned)groups),
                                dim3(WG), 0, s, args);
+    }
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
+extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora_apply_proj_t* projs,
+                              void* hip_stream) {
+    int32_t st = check_launch(L, LORA_OP_APPLY, n_proj);
+    if (st != LORA_OK) return st;
+    if (!projs) return LORA_EINVAL;
+    bool need_v = false;  // any shrink or expand range (segments that are not fused)
+    for (int r = 0; r < L->info.n_ranges; ++r)
+        if (L->info.ranges[r].variant != LV_APPLY_FUSED && L->info.ranges[r].count > 0) need_v = true;
+    ShrinkArgs sa;
+    ExpandArgs ea;
+    FusedArgs fa;
+    sa.row_index = ea.row_index = fa.row_index = L->row_index;
+    sa.work = ea.work = fa.work = L->work;
+    sa.n_active = ea.n_active = fa.n_active = L->info.n_active;
+    sa.v_slices = ea.v_slices = L->info.v_slices;
+    ea.n_proj = n_proj;
+    const int32_t mr = L->info.max_rank, ma = L->info.max_adapter;
+    for (int i = 0; i < n_proj; ++i) {
+        const lora_apply_proj_t& p = projs[i];
+        if (!p.x || !p.y || !aligned16(p.x) || !aligned16(p.y)) return LORA_EINVAL;
+        if (need_v && (!p.v || !aligned16(p.v) || p.ldv % 4 != 0 || p.ldv < mr)) return LORA_EINVAL;
+        if (p.d_in <= 0 || p.d_in % 64 != 0 || p.d_out <= 0 || p.d_out % 64 != 0) return LORA_ESHAPE;
+        if (p.ldx < p.d_in || p.ldx % 8 != 0 || p.ldy < p.d_out || p.ldy % 4 != 0) return LORA_EINVAL;
+        if ((st = check_rows(p.A, p.d_in, mr, ma)) != LORA_OK) return st;
+        if ((st = check_rows(p.B, p.d_out, mr, ma)) != LORA_OK) return st;
+        sa.p[i] = ShrinkProj{p.x, p.ldx, to_rows(p.A), p.d_in, p.v, p.ldv};
+        ea.p[i] = ExpandProj{p.v, p.ldv, to_rows(p.B), p.d_out, p.y, p.ldy, p.scale, 0};
+        fa.p[i] = ApplyProj{p.x, p.ldx, p.d_in, to_rows(p.A), to_rows(p.B), p.d_out, p.y, p.ldy, p.scale};
+    }
+    if (L->info.n_work == 0) return LORA_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    // ranges come in variant order: shrink, expand, fused; the expand ranges
+    // follow every shrink range on the stream
+    for (int r = 0; r < L->info.n_ranges; ++r) {
+        const lora_range_t& R = L->info.ranges[r];
+        if (R.count == 0) continue;
+        if (R.variant < LV_APPLY_EXPAND0) {
+            sa.begin = R.begin;
+            hipLaunchKernelGGL(shrink_table(R.variant), dim3((unsigned)R.count, (unsigned)n_proj), dim3(WG), 0, s, sa);
+        } else if (R.variant < LV_APPLY_FUSED) {
+            const int ev = R.variant - LV_APPLY_EXPAND0;
+            const int shape = ev / LV_RANK_CLASSES;
+            const int32_t width = lv_expand_cols(shape);
+            int32_t groups = 0;
+            for (int i = 0; i < n_proj; ++i) {
+                ea.p[i].cg_begin = groups;
+                groups += (ea.p[i].d_out + width - 1) / width;
+            }
+            ea.begin = R.begin;
+            if (shape == LV_E_BGMV)
+                hipLaunchKernelGGL(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG), 0, s, ea);
+            else
+                hipLaunchKernelGGL(expand_table(ev % LV_RANK_CLASSES), dim3((unsigned)R.count, (unsigned)groups),
+                                   dim3(WG), 0, s, ea);
+        } else {
+            fa.begin = R.begin;
+            bool uni = true;  // every wave's row offsets are uniform
+            for (int i = 0; i < n_proj; ++i)
+                uni = uni && fa.p[i].A.chunk_len % 512 == 0 && fa.p[i].B.chunk_len % 512 == 0;
+            if (uni)
+                hipLaunchKernelGGL(fused_kernel<true>, dim3((unsigned)R.count, (unsigned)n_proj), dim3(FWG), 0, s, fa);
+            else
+                hipLaunchKernelGGL(fused_kernel<false>, dim3((unsigned)R.count, (unsigned)n_proj), dim3(FWG), 0, s,
+                                   fa);
+        }
     }
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
 }

@@ -35,6 +35,14 @@ static inline int32_t lv_expand_rows(int shape) {
     return shape == LV_E_ROWS16 ? 16 : shape == LV_E_ROWS64 ? 64 : shape == LV_E_ROWS128 ? 128
          : shape == LV_E_ROWS256 ? 256 : 2;
 }
+// Variant ids of an apply plan: the shrink variants, then the expand
+// variants shifted by LV_APPLY_EXPAND0, then the fused one-row kernel.
+#define LV_APPLY_EXPAND0 (LV_S_SHAPES * LV_RANK_CLASSES)
+#define LV_APPLY_FUSED (LV_APPLY_EXPAND0 + LV_E_SHAPES * LV_RANK_CLASSES)
+#define LV_APPLY_VARIANTS (LV_APPLY_FUSED + 1)
+// The fused kernel covers d_in and d_out up to 8 x half its 1024 threads.
+#define LV_FUSED_MAX_D 4096
+
 // Columns one expand workgroup covers.
 static inline int32_t lv_expand_cols(int shape) { return shape == LV_E_BGMV ? 2048 : 512; }
 

@@ -10,19 +10,23 @@ PyTorch only provides memory and streams here.
 import numpy as np
 import torch
 
-from . import (LORA_MAX_SLICES, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, call_expand, call_merge,
-               call_shrink, lora_build_segments, lora_expand_proj_t, lora_launch_t, lora_merge_mat_t,
-               lora_plan, lora_plan_info_t, lora_shrink_proj_t, make_rows)
+from . import (LORA_MAX_SLICES, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, call_apply,
+               call_expand, call_merge, call_shrink, lora_apply_proj_t, lora_build_segments, lora_expand_proj_t,
+               lora_launch_t, lora_merge_mat_t, lora_plan, lora_plan_info_t, lora_shrink_proj_t, make_rows)
 
 
-def staging_layout(n_active, n_work_shrink, n_work_expand):
-    """Byte offsets of (row_index, shrink work, expand work) in the staging
-    buffer, and its size in int32 elements: row_index is int32 [n_active],
-    each work item WORK_INTS int32."""
+def staging_layout(n_active, n_work_shrink, n_work_expand, n_work_apply=0):
+    """Byte offsets of (row_index, shrink work, expand work, apply work) in the
+    staging buffer, and its size in int32 elements: row_index is int32
+    [n_active], each work item WORK_INTS int32.  (The first four results are
+    kept in this order for callers that use only the shrink/expand lists.)"""
     ri = 0
     ws = 4 * n_active
     we = ws + 4 * WORK_INTS * n_work_shrink
-    n = max(1, n_active + WORK_INTS * (n_work_shrink + n_work_expand))
+    wa = we + 4 * WORK_INTS * n_work_expand
+    n = max(1, n_active + WORK_INTS * (n_work_shrink + n_work_expand + n_work_apply))
+    if n_work_apply:
+        return ri, ws, we, n, wa
     return ri, ws, we, n
 
 
@@ -62,11 +66,14 @@ class Batch:
                          np.empty(nseg, np.int32))
         self._ws = np.empty((LORA_MAX_SLICES * n, WORK_INTS), np.int32)
         self._we = np.empty((n, WORK_INTS), np.int32)
+        self._wa = np.empty(((LORA_MAX_SLICES + 1) * n, WORK_INTS), np.int32)
         self.info_shrink, self.info_expand = lora_plan_info_t(), lora_plan_info_t()
+        self.info_apply = lora_plan_info_t()
         self.shrink_launch, self.expand_launch = lora_launch_t(), lora_launch_t()
+        self.apply_launch = lora_launch_t()
         self._copied = None          # event of the last staging copy
         self._host = self._dev = None
-        self._alloc(staging_layout(n, 4 * n, n)[3])
+        self._alloc(staging_layout(n, 4 * n, n, 5 * n)[3])
         self.segs = None
 
     def _alloc(self, cap):
@@ -83,8 +90,10 @@ class Batch:
                                info_out=self.info_shrink)
         we, info_e = lora_plan(LORA_OP_EXPAND, segs, self.d_in, self.d_out, work_out=self._we,
                                info_out=self.info_expand)
-        na, ns, ne = segs.n_active, ws.shape[0], we.shape[0]
-        o_ri, o_ws, o_we, n = staging_layout(na, ns, ne)
+        wa, info_a = lora_plan(LORA_OP_APPLY, segs, self.d_in, self.d_out, work_out=self._wa,
+                               info_out=self.info_apply)
+        na, ns, ne, nap = segs.n_active, ws.shape[0], we.shape[0], wa.shape[0]
+        o_ri, o_ws, o_we, n, o_wa = staging_layout(na, ns, ne, max(1, nap))
         if n > self._host.shape[0]:
             self._alloc(n)
         if self._copied is not None:
@@ -93,14 +102,16 @@ class Batch:
         h[:na] = segs.row_index
         h[na:na + WORK_INTS * ns] = ws.reshape(-1)
         h[na + WORK_INTS * ns:na + WORK_INTS * (ns + ne)] = we.reshape(-1)
+        h[na + WORK_INTS * (ns + ne):na + WORK_INTS * (ns + ne + nap)] = wa.reshape(-1)
         s = torch.cuda.current_stream() if stream is None else stream
         with torch.cuda.stream(s):
             self._dev[:n].copy_(self._host[:n], non_blocking=True)
             self._copied = torch.cuda.Event()
             self._copied.record(s)
         base = self._dev.data_ptr()
-        self.segs, self.work_shrink, self.work_expand = segs, ws, we
-        for L, info, off in ((self.shrink_launch, info_s, o_ws), (self.expand_launch, info_e, o_we)):
+        self.segs, self.work_shrink, self.work_expand, self.work_apply = segs, ws, we, wa
+        for L, info, off in ((self.shrink_launch, info_s, o_ws), (self.expand_launch, info_e, o_we),
+                             (self.apply_launch, info_a, o_wa)):
             L.row_index = base + o_ri
             L.work = base + off
             L.info = info
@@ -156,6 +167,27 @@ class Batch:
             call_expand(self.expand_launch, arr, len(vs), h)
         run.keep = (projs, arr)
         return run
+
+    def prepare_apply(self, projs, stream=None):
+        """projs: list of (x, Rows A, v, Rows B, y, scale) as for the shrink and the
+        expand; v (fp32 [v_slices, n_active, ldv]) serves the segments that are
+        not fused.  Returns fn() that runs lora_apply for the current plan."""
+        arr = (lora_apply_proj_t * len(projs))(*[
+            lora_apply_proj_t(x.data_ptr(), x.stride(0), x.shape[1], A.c(), v.data_ptr(), v.stride(1), B.c(),
+                              y.shape[1], y.data_ptr(), y.stride(0), float(s))
+            for x, A, v, B, y, s in projs])
+        vs = [p[2] for p in projs]
+        h = stream_handle(stream)
+
+        def run():
+            for v in vs:
+                self._check_v(v)
+            call_apply(self.apply_launch, arr, len(vs), h)
+        run.keep = (projs, arr)
+        return run
+
+    def apply(self, projs, stream=None):
+        self.prepare_apply(projs, stream)()
 
     def shrink(self, projs, stream=None):
         self.prepare_shrink(projs, stream)()

@@ -67,10 +67,10 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 3
+#define LORA_ABI_VERSION 4
 #define LORA_MAX_RANK 128   /* ranks are 1..128                              */
 #define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
-#define LORA_MAX_RANGES 32  /* kernel variants in one plan                   */
+#define LORA_MAX_RANGES 48  /* kernel variants in one plan                   */
 #define LORA_MAX_MERGE 8    /* weight matrices per merge/unmerge call        */
 #define LORA_MAX_SLICES 16  /* K slices of one shrink segment                */
 
@@ -85,6 +85,7 @@ extern "C" {
 
 #define LORA_OP_SHRINK 0
 #define LORA_OP_EXPAND 1
+#define LORA_OP_APPLY 2   /* shrink + expand in one call, fused where chosen */
 
 /* Adapter rows of one matrix kind (A or B of one projection).
  *   pool      device, bf16 elements; 16-byte aligned
@@ -129,7 +130,7 @@ typedef struct lora_range {
 
 /* Host-side summary of a plan, written by lora_plan. */
 typedef struct lora_plan_info {
-    int32_t op;           /* LORA_OP_SHRINK or LORA_OP_EXPAND            */
+    int32_t op;           /* LORA_OP_SHRINK, LORA_OP_EXPAND or LORA_OP_APPLY */
     int32_t n_work;       /* work items written                          */
     int32_t n_active;     /* rows covered (= seg_start[n_seg])           */
     int32_t max_rank;     /* largest rank among the items                */
@@ -194,6 +195,28 @@ typedef struct lora_merge_mat {
     float scale;
 } lora_merge_mat_t;
 
+/* One projection of lora_apply: the shrink's and the expand's arguments.
+ *   x, ldx, d_in, A      as in lora_shrink_proj_t
+ *   v, ldv               scratch for the segments that are not fused: device
+ *                        fp32 [info.v_slices][info.n_active][ldv] as in
+ *                        lora_shrink_proj_t; may be NULL when the plan has no
+ *                        shrink or expand range (every segment fused); its
+ *                        contents after the call are unspecified
+ *   B, d_out, y, ldy, scale  as in lora_expand_proj_t                    */
+typedef struct lora_apply_proj {
+    const uint16_t* x;
+    int64_t ldx;
+    int32_t d_in;
+    lora_rows_t A;
+    float* v;
+    int64_t ldv;
+    lora_rows_t B;
+    int32_t d_out;
+    float* y;
+    int64_t ldy;
+    float scale;
+} lora_apply_proj_t;
+
 /* ABI version (LORA_ABI_VERSION of the built library). */
 int32_t lora_abi_version(void);
 
@@ -227,7 +250,9 @@ int32_t lora_build_segments(int32_t n_rows, const int32_t* row_adapter,
  * the shrink splits each segment, so the shrink and expand plans of one batch
  * (same seg_*, d_in, d_out) agree on v_slices.  Items cover only active rows
  * and are grouped by variant.  At most n_active * 16 items are written
- * (work_capacity >= 16 * n_active is always enough).
+ * (work_capacity >= 16 * n_active is always enough; 17 * n_active for
+ * LORA_OP_APPLY, whose plan holds the shrink items, the expand items and the
+ * fused items of its segments in one list).
  *   seg_*  as written by lora_build_segments
  *   d_in, d_out  positive multiples of 64 (the largest over the projections
  *                that will share this plan)
@@ -249,6 +274,16 @@ int32_t lora_shrink(const lora_launch_t* launch, int32_t n_proj,
  * (launch->info.op == LORA_OP_EXPAND).  Same errors as lora_shrink. */
 int32_t lora_expand(const lora_launch_t* launch, int32_t n_proj,
                     const lora_expand_proj_t* projs, void* hip_stream);
+
+/* Shrink and expand in one call, for a plan made with op = LORA_OP_APPLY:
+ * y[row_index[p]] += scale * (x[row_index[p]] . A_a^T) . B_a for every active
+ * row.  The plan fuses one-row segments (decode rows) of small enough d_in and
+ * d_out into a single kernel that keeps v on chip; the other segments run the
+ * shrink and expand kernels of lora_shrink / lora_expand through v.  The
+ * result is the same delta within rounding (the fused kernel reduces over
+ * d_in in another order).  Errors: as lora_shrink and lora_expand. */
+int32_t lora_apply(const lora_launch_t* launch, int32_t n_proj,
+                   const lora_apply_proj_t* projs, void* hip_stream);
 
 /* Merge n_mats (1..LORA_MAX_MERGE) adapters into their weights in place, one
  * launch: W <- RNE_bf16(W + scale * B_a^T A_a), with Delta W accumulated in

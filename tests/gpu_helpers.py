@@ -34,6 +34,23 @@ def run_delta(W, row_adapter=None, dw=None, scale=None, ldv=None):
     return batch, [v.cpu().numpy() for v in vs], [dp.y.cpu().numpy() for dp in dw.projections]
 
 
+def run_apply(W, row_adapter=None, dw=None, scale=None, ldv=None):
+    """lora_apply (fused where the plan says so) for every projection of W;
+    returns (batch, y list) on the host."""
+    dw = dw if dw is not None else to_device(W)
+    ra = W.row_adapter if row_adapter is None else np.asarray(row_adapter, np.int32)
+    d_in = max(p.d_in for p in W.projections)
+    d_out = max(p.d_out for p in W.projections)
+    batch = Batch(max(1, W.n_rows), W.adapter_rank, d_in, d_out).refresh(ra)
+    ldv = ldv or -(-int(W.adapter_rank.max()) // 4) * 4
+    s = W.scale if scale is None else scale
+    vs = [batch.new_v(ldv, fill=float("nan")) for _ in W.projections]
+    batch.apply([(dp.x, rows_of(dw.pool, p.A, dp.A_off), v, rows_of(dw.pool, p.B, dp.B_off), dp.y, s)
+                 for p, dp, v in zip(W.projections, dw.projections, vs)])
+    torch.cuda.synchronize()
+    return batch, [dp.y.cpu().numpy() for dp in dw.projections]
+
+
 def check_delta(W, batch, vs, ys, row_adapter=None, rows=None, scale=None, check_v=True):
     """Compare GPU y (and v) with the oracle on `rows` (default: all rows).
 
@@ -41,7 +58,7 @@ def check_delta(W, batch, vs, ys, row_adapter=None, rows=None, scale=None, check
     of its first nslices slices in slice order (what the expand uses); the
     columns beyond the rank and the slices beyond nslices must be unwritten."""
     seg_slices = {}
-    for w in batch.work_expand:
+    for w in (batch.work_expand if check_v else []):
         for p_ in range(int(w[0]), int(w[0]) + int(w[1])):
             seg_slices[p_] = int(w[5])
     ra = W.row_adapter if row_adapter is None else np.asarray(row_adapter, np.int32)
@@ -63,7 +80,7 @@ def check_delta(W, batch, vs, ys, row_adapter=None, rows=None, scale=None, check
             num += float(np.sum((d_gpu - d_ref) ** 2))
             den += float(np.sum(d_ref ** 2))
             amax = max(amax, float(np.max(np.abs(y_gpu - yref[i]))))
-            if check_v:
+            if check_v and vs is not None:
                 r = int(W.adapter_rank[ra[i]])
                 ns = seg_slices[pos[i]]
                 vsl = vs[pi][:, pos[i], :]

@@ -205,3 +205,46 @@ def test_merge_shapes_parity(d_out, d_in, r):
     check_merge_bits(restored[0], merged[0], Aa, Ba, -2.0, min_equal=0.999)
     w0, w2 = oracle.bf16_to_f64(Wb), oracle.bf16_to_f64(restored[0])
     assert np.linalg.norm(w2 - w0) / np.linalg.norm(w0) <= 4e-3
+
+
+# ------------------------------------------------------------------ lora_apply (fused decode rows)
+def _apply_check(W, ra=None):
+    from gpu_helpers import run_apply
+    batch, ys = run_apply(W, ra)
+    n_fused = sum(c for v, b, c, m in batch.info_apply.range_list() if v == 32)
+    rep = check_delta(W, batch, None, ys, row_adapter=ra, check_v=False)
+    _say("apply: fused items", n_fused, rep)
+    return n_fused
+
+
+@pytest.mark.parametrize("which", ["hetero", "homo"])
+def test_apply_decode_parity(which):
+    W = workloads.gen_config(1)
+    n_fused = _apply_check(W, W.batches[which])
+    assert n_fused == (64 if which == "hetero" else 0)
+
+
+def test_apply_tiny_and_mixed_lengths():
+    _apply_check(workloads.gen_config(0))
+    # one-row segments of several ranks (1..128: several rank groups of 16) next to longer ones
+    ra = np.repeat([0, 1, 2, 3, 4, 5, 6], [1, 1, 1, 1, 40, 1, 300])
+    W = workloads.gen_custom(31, ra, [1, 16, 17, 33, 64, 128, 8], 4096, 3072, n_proj=2)
+    assert _apply_check(W) == 5    # 5 one-row segments (the projections share each item)
+
+
+@pytest.mark.parametrize("page", [64, 448])
+def test_apply_paged_and_small_d(page):
+    ra = np.repeat([2, 0, 1, 3], [1, 1, 77, 1])
+    W = workloads.gen_custom(32, ra, [24, 5, 64, 96], 448, 1984, layout="paged", page_elems=page)
+    _apply_check(W)
+
+
+def test_apply_matches_shrink_expand_when_nothing_fuses():
+    # d_out beyond the fused limit: apply runs the shrink and expand kernels, bit-identical to them
+    ra = np.repeat([0, 1, 2], [1, 5, 130])
+    W = workloads.gen_custom(33, ra, [16, 32, 64], 1024, 4160)
+    from gpu_helpers import run_apply
+    batch, ya = run_apply(W)
+    assert all(v != 32 for v, b, c, m in batch.info_apply.range_list())
+    _, _, yd = run_delta(W)
+    assert np.array_equal(ya[0], yd[0])

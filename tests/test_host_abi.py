@@ -288,3 +288,50 @@ def test_staging_layout_matches_host_packing():
     assert np.array_equal(np.frombuffer(raw[o_ri:o_ri + 4 * segs.n_active], np.int32), segs.row_index)
     assert np.array_equal(np.frombuffer(raw[o_ws:o_ws + 4 * W8 * ws.shape[0]], np.int32).reshape(-1, W8), ws)
     assert np.array_equal(np.frombuffer(raw[o_we:o_we + 4 * W8 * we.shape[0]], np.int32).reshape(-1, W8), we)
+
+
+def test_apply_plan_partitions_segments():
+    """An apply plan fuses exactly the one-row segments with d_in, d_out <= 4096;
+    every other segment is covered by its shrink items (each row x K slice
+    once) and its expand items (each row once); fused items cover one row."""
+    N_SHRINK = 3 * 4            # shrink variants
+    FUSED = N_SHRINK + 5 * 4    # the fused variant follows the expand variants
+    rng = np.random.default_rng(12)
+    cases = [np.arange(64), np.zeros(64, int), np.repeat(rng.integers(-1, 30, size=40), rng.integers(1, 5, size=40)),
+             np.repeat(rng.integers(0, 8, size=20), rng.integers(1, 300, size=20)), np.array([3])]
+    for ra in cases:
+        ranks = rng.integers(1, 129, size=int(ra.max()) + 1)
+        segs = hl.lora_build_segments(ra, ranks)
+        for d_in, d_out in ((512, 512), (4096, 4096), (4096, 8192), (8192, 4096), (64, 4096)):
+            work, info = hl.lora_plan(hl.LORA_OP_APPLY, segs, d_in, d_out)
+            _, info_s = hl.lora_plan(hl.LORA_OP_SHRINK, segs, d_in, d_out)
+            assert info.op == hl.LORA_OP_APPLY and info.n_work == work.shape[0]
+            assert work.shape[0] <= (hl.LORA_MAX_SLICES + 1) * segs.n_active
+            cov_s = np.zeros((segs.n_active, hl.LORA_MAX_SLICES), int)
+            cov_e = np.zeros(segs.n_active, int)
+            fused_rows = set()
+            prev_v = -1
+            for v, begin, count, mt in info.range_list():
+                assert v > prev_v
+                prev_v = v
+                for w in work[begin:begin + count]:
+                    row0, nrows, ad, rk, ks, ns = (int(t) for t in w[:6])
+                    assert 1 <= nrows <= mt
+                    if v < N_SHRINK:
+                        cov_s[row0:row0 + nrows, ks] += 1
+                    else:
+                        cov_e[row0:row0 + nrows] += 1
+                        if v == FUSED:
+                            assert nrows == 1 and ns == 1
+                            fused_rows.add(row0)
+            assert np.all(cov_e == 1)
+            assert info.v_slices <= max(1, info_s.v_slices)
+            for s in range(segs.n_seg):
+                lo, hi = int(segs.seg_start[s]), int(segs.seg_start[s + 1])
+                fused = hi - lo == 1 and d_in <= 4096 and d_out <= 4096
+                assert (lo in fused_rows) == fused
+                if fused:
+                    assert np.all(cov_s[lo] == 0)
+                else:
+                    ns = int(work[[i for i in range(work.shape[0]) if work[i, 0] == lo][0], 5])
+                    assert np.all(cov_s[lo:hi, :ns] == 1) and np.all(cov_s[lo:hi, ns:] == 0)
