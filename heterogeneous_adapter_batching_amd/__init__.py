@@ -27,6 +27,15 @@ LORA_OP_SHRINK, LORA_OP_EXPAND, LORA_OP_APPLY = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python __graft_entry__.py` (build()) first")
+# The library must use the same HIP runtime as the caller's streams and
+# memory.  PyTorch-ROCm ships its own libamdhip64 under the same soname as the
+# system one: loaded after torch, the library binds to torch's copy; loaded
+# before it, the process ends up with two runtimes and launches on torch's
+# streams fail.  So torch, when installed, is loaded first.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
 _lib = ctypes.CDLL(LIB_PATH)
 
 _i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p

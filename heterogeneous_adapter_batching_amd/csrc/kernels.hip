@@ -91,6 +91,12 @@ __device__ __forceinline__ u32x4_t sel(bool ok, u32x4_t v) {
 // is emitted.
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value.  Branches on it are then scalar branches: an MFMA inside a branch the
+// compiler takes for divergent runs under EXEC = 0 when no lane takes the
+// branch, and MFMA does not honour EXEC, so it would still accumulate.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -165,28 +171,28 @@ struct ShrinkArgs {
     ShrinkProj p[LORA_MAX_PROJ];
 };
 
-// One workgroup = one work item (rows x one K slice) of one projection.
-//   KSPLIT = 4: the four waves share the item's 16 rows and take every 4th
-//               64-wide K block; partial sums are added in LDS in wave order.
-//   KSPLIT = 1: wave w owns rows [16*MTW*w, 16*MTW*(w+1)) of the item.
+// One workgroup = one short-segment work item (at most 16 rows x one K
+// slice) of one projection.  With KSPLIT = 4 (the configuration in use) the
+// four waves share the item's 16 rows and take every 4th 64-wide K block;
+// partial sums are added in LDS in wave order.  (KSPLIT = 1 would give wave w
+// rows [16*MTW*w, 16*MTW*(w+1)); long segments use shrink_rows_kernel.)
 // NT = number of 16-wide rank tiles; U = K blocks loaded ahead per step.
 template <int KSPLIT, int MTW, int NT, int U>
 __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
     const lora_work_t it = args.work[args.begin + blockIdx.x];
     const ShrinkProj& P = args.p[blockIdx.y];
     if (!item_ok(it, args.n_active, args.v_slices, P.A, 16 * NT) || it.nrows > 16 * MTW * (KSPLIT > 1 ? 1 : 4)) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int li = lane & 15, lg = lane >> 4;
     const int mbase = KSPLIT > 1 ? 0 : wave * 16 * MTW;
     if (KSPLIT == 1 && mbase >= it.nrows) return;  // no barrier in this configuration
 
-    // x rows of this lane (rows past the item read its last row, zeroed below)
+    // x rows of this lane (rows past the item read its last row; their
+    // results are not stored)
     const uint16_t* xrow[MTW];
-    bool xok[MTW];
 #pragma unroll
     for (int t = 0; t < MTW; ++t) {
         const int m = mbase + 16 * t + li;
-        xok[t] = m < it.nrows;
         xrow[t] = P.x + (int64_t)args.row_index[it.row0 + min(m, it.nrows - 1)] * P.ldx + 16 * lg;
     }
     issue_fence();
@@ -202,13 +208,12 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
     const int kend = (int)((int64_t)(it.kslice + 1) * kblocks / it.nslices);
     const int cblocks = P.A.chunk_len / 64;
     for (int c = kbeg / cblocks; c * cblocks < kend; ++c) {
-        // A rows of this lane's rank slots (slots past the rank read row rank-1, zeroed below)
+        // A rows of this lane's rank slots (slots past the rank read row
+        // rank-1; their results are not stored)
         const uint16_t* arow[NT];
-        bool aok[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const int j = 16 * n + li;
-            aok[n] = j < it.rank;
             arow[n] = P.A.pool + P.A.row_off[off_index(P.A, it.adapter, min(j, it.rank - 1), c)] + 16 * lg;
         }
         issue_fence();
@@ -216,37 +221,81 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
         const int kb0 = max(cbase, kbeg);
         const int kb1 = min(cbase + cblocks, kend);
         // first block owned by this wave (blocks are dealt round-robin by global index)
-        int kb = KSPLIT > 1 ? kb0 + ((wave - kb0 % KSPLIT) + KSPLIT) % KSPLIT : kb0;
-        for (; kb < kb1; kb += KSPLIT * U) {
-            u32x4_t xa[U][MTW][2], aa[U][NT][2];
+        const int first = KSPLIT > 1 ? kb0 + ((wave - kb0 % KSPLIT) + KSPLIT) % KSPLIT : kb0;
+        if (first >= kb1) continue;  // wave-uniform
+        // Two register stages of U blocks each: the loads of the next stage are
+        // issued before the MFMAs of the current one, so a wave always has a
+        // stage in flight.  Blocks past the slice are loaded at the last
+        // block's address (in bounds; their MFMAs are skipped).  Rows past the
+        // item and rank slots past the rank read clamped, real rows; their
+        // outputs are never stored, so no load is masked.
+        const int last = first + (kb1 - 1 - first) / KSPLIT * KSPLIT;
+        u32x4_t xs[2][U][MTW][2], as[2][U][NT][2];
+        auto load_stage = [&](int st, int k0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int k = kb + u * KSPLIT;
-                const bool kin = k < kb1;  // wave-uniform
+                const int k = min(k0 + u * KSPLIT, last);
                 const int64_t kx = (int64_t)k * 64, ka = (int64_t)(k - cbase) * 64;
 #pragma unroll
                 for (int t = 0; t < MTW; ++t) {
-                    xa[u][t][0] = ld16_if(kin && xok[t], xrow[t] + kx);
-                    xa[u][t][1] = ld16_if(kin && xok[t], xrow[t] + kx + 8);
+                    xs[st][u][t][0] = ld16(xrow[t] + kx);
+                    xs[st][u][t][1] = ld16(xrow[t] + kx + 8);
                 }
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    aa[u][n][0] = ld16_if(kin && aok[n], arow[n] + ka);
-                    aa[u][n][1] = ld16_if(kin && aok[n], arow[n] + ka + 8);
+                    as[st][u][n][0] = ld16(arow[n] + ka);
+                    as[st][u][n][1] = ld16(arow[n] + ka + 8);
                 }
             }
+        };
+        auto mma_stage = [&](int st, int k0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (kb + u * KSPLIT >= kb1) break;
+                if (u > 0 && k0 + u * KSPLIT > last) break;  // wave-uniform; k0 <= last
+                // every rank tile, used or not: straight-line MFMAs (a tile
+                // past the rank only adds to results that are not stored)
 #pragma unroll
                 for (int t = 0; t < MTW; ++t)
 #pragma unroll
                     for (int n = 0; n < NT; ++n) {
-                        if (16 * n >= it.rank) continue;
-                        acc[t][n] = mfma_bf16(xa[u][t][0], aa[u][n][0], acc[t][n]);
-                        acc[t][n] = mfma_bf16(xa[u][t][1], aa[u][n][1], acc[t][n]);
+                        acc[t][n] = mfma_bf16(xs[st][u][t][0], as[st][u][n][0], acc[t][n]);
+                        acc[t][n] = mfma_bf16(xs[st][u][t][1], as[st][u][n][1], acc[t][n]);
                     }
             }
+        };
+        // Empty asm that takes a stage's registers as in/out operands: placed
+        // after the next stage's loads, it keeps those loads issued before
+        // this stage's MFMAs (which consume its outputs), so the compiler can
+        // neither sink the loads nor merge the two stages' registers.
+        auto pin_stage = [&](int st) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int t = 0; t < MTW; ++t) {
+                    asm volatile("" : "+v"(xs[st][u][t][0]));
+                    asm volatile("" : "+v"(xs[st][u][t][1]));
+                }
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    asm volatile("" : "+v"(as[st][u][n][0]));
+                    asm volatile("" : "+v"(as[st][u][n][1]));
+                }
+            }
+        };
+        constexpr int STEP = KSPLIT * U;
+        int kb = first;
+        load_stage(0, kb);
+        for (;;) {
+            load_stage(1, kb + STEP);
+            pin_stage(0);
+            mma_stage(0, kb);
+            kb += STEP;
+            if (kb > last) break;
+            load_stage(0, kb + STEP);
+            pin_stage(1);
+            mma_stage(1, kb);
+            kb += STEP;
+            if (kb > last) break;
         }
     }
 
@@ -278,6 +327,159 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
         }
 }
 
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its global loads (a __syncthreads() fence would also drain the global loads
+// that are in flight for the next K block).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Long segments (items of 64*MTW rows; wave w computes rows 16*MTW*w ..).
+// Both operands of a 64-wide K step pass through LDS: the workgroup loads
+// the x tile (64*MTW rows x 128 B) and the A tile (16*NT rank rows x 128 B)
+// in row-contiguous 16 B pieces, 8 pieces = one full 128 B line per row, so
+// every load instruction covers 8 whole lines.  Loading MFMA fragments
+// straight from memory would touch 16 rows per instruction and use half of
+// each line, and A would be loaded by every wave: the L1 request rate, not
+// HBM, then bounds the kernel.  Pieces are stored XOR-swizzled by (row mod
+// 8), so the 8 lanes of a fragment read that share a piece index hit 8
+// different bank groups.
+// K order inside a step: lane group lg takes pieces lg and lg+4 (elements
+// 8*lg .. +7 and 32 + 8*lg .. +7) for its two MFMAs; x and A use the same
+// order.  Pipeline: the next step's pieces are loaded into registers while
+// the current step's MFMAs run from LDS; after a barrier they replace the
+// tiles, and a second barrier publishes them.  One LDS buffer (24 KiB at 128
+// rows and rank 64) rather than two lets four workgroups share a CU, so the
+// grids of the large workloads are resident in one round; the other
+// workgroups on the CU cover the barriers.
+template <int MTW, int NT>
+__device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& args, const lora_work_t& it, const ShrinkProj& P,
+                                                 u32x4_t* sX, u32x4_t* sA) {
+    constexpr int ROWS = 64 * MTW;        // rows of the item tile
+    constexpr int XP = ROWS * 8 / WG;     // x pieces per thread
+    constexpr int AP = NT >= 2 ? NT / 2 : 1;  // A pieces per thread (one rank tile: 128 pieces,
+                                              // threads t and t+128 load and store the same one)
+    const int t = threadIdx.x, lane = t & 63, wave = wave_id();
+    const int li = lane & 15, lg = lane >> 4;
+    const int mbase = wave * 16 * MTW;
+
+    const uint16_t* xpiece[XP];
+    int xslot[XP];
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+        const int id = t + WG * p, row = id >> 3, pc = id & 7;
+        // rows past the item read its last row (results not stored)
+        xpiece[p] = P.x + (int64_t)args.row_index[it.row0 + min(row, it.nrows - 1)] * P.ldx + 8 * pc;
+        xslot[p] = row * 8 + (pc ^ (row & 7));
+    }
+    f32x4_t acc[MTW][NT];
+#pragma unroll
+    for (int q = 0; q < MTW; ++q)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[q][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int kblocks = P.d_in / 64;
+    const int kbeg = (int)((int64_t)it.kslice * kblocks / it.nslices);
+    const int kend = (int)((int64_t)(it.kslice + 1) * kblocks / it.nslices);
+    const int cblocks = P.A.chunk_len / 64;
+    for (int c = kbeg / cblocks; c * cblocks < kend; ++c) {
+        const int cbase = c * cblocks;
+        const int b0 = max(cbase, kbeg), b1 = min(cbase + cblocks, kend);
+        const uint16_t* apiece[AP];
+        int aslot[AP];
+#pragma unroll
+        for (int p = 0; p < AP; ++p) {
+            const int id = (NT >= 2 ? t : (t & 127)) + WG * p, row = id >> 3, pc = id & 7;
+            apiece[p] = P.A.pool + P.A.row_off[off_index(P.A, it.adapter, min(row, it.rank - 1), c)] +
+                        (b0 - cbase) * 64 + 8 * pc;
+            aslot[p] = row * 8 + (pc ^ (row & 7));
+        }
+        issue_fence();
+        u32x4_t xr[XP], ar[AP];
+        auto load = [&](int k) {  // step k of this chunk (relative to b0): A first, then x
+#pragma unroll
+            for (int p = 0; p < AP; ++p) ar[p] = ld16(apiece[p] + (int64_t)k * 64);
+#pragma unroll
+            for (int p = 0; p < XP; ++p) xr[p] = ld16(xpiece[p] + (int64_t)(b0 + k) * 64);
+        };
+        auto store = [&]() {
+#pragma unroll
+            for (int p = 0; p < AP; ++p) sA[aslot[p]] = ar[p];
+#pragma unroll
+            for (int p = 0; p < XP; ++p) sX[xslot[p]] = xr[p];
+        };
+        auto mma = [&]() {
+            u32x4_t xf[MTW][2];
+#pragma unroll
+            for (int q = 0; q < MTW; ++q) {
+                const int row = mbase + 16 * q + li;
+                xf[q][0] = sX[row * 8 + (lg ^ (li & 7))];
+                xf[q][1] = sX[row * 8 + ((lg + 4) ^ (li & 7))];
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const int row = 16 * n + li;
+                const u32x4_t a0 = sA[row * 8 + (lg ^ (li & 7))];
+                const u32x4_t a1 = sA[row * 8 + ((lg + 4) ^ (li & 7))];
+#pragma unroll
+                for (int q = 0; q < MTW; ++q) {
+                    acc[q][n] = mfma_bf16(xf[q][0], a0, acc[q][n]);
+                    acc[q][n] = mfma_bf16(xf[q][1], a1, acc[q][n]);
+                }
+            }
+        };
+        const int nb = b1 - b0;
+        load(0);
+        store();
+        lds_barrier();
+        for (int i = 0;;) {
+            // step i is in LDS; fetch step i+1 (the last step again at the
+            // end: in bounds, never used)
+            load(min(i + 1, nb - 1));
+            issue_fence();
+            mma();
+            lds_barrier();  // every wave is done with step i's tiles
+            if (++i >= nb) break;
+            store();
+            lds_barrier();
+        }
+    }
+    if (mbase >= it.nrows) return;
+    float* vout = P.v + (int64_t)it.kslice * args.n_active * P.ldv;
+#pragma unroll
+    for (int q = 0; q < MTW; ++q)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int j = 16 * n + li;
+            if (j >= it.rank) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = mbase + 16 * q + 4 * lg + e;
+                if (m < it.nrows) vout[(int64_t)(it.row0 + m) * P.ldv + j] = acc[q][n][e];
+            }
+        }
+}
+
+// One workgroup = one long-segment work item of one projection; the item's
+// rank picks the number of rank tiles (1, 2 or 4 up to NTMAX = 4; NTMAX = 8 is
+// its own kernel for ranks above 64, whose registers would lower the
+// occupancy of the others).
+template <int MTW, int NTMAX>
+__global__ __launch_bounds__(WG) void shrink_rows_kernel(ShrinkArgs args) {
+    __shared__ u32x4_t sX[64 * MTW * 8];    // 64*MTW rows x 8 pieces of 16 B
+    __shared__ u32x4_t sA[16 * NTMAX * 8];  // 16*NT rank rows x 8 pieces
+    const lora_work_t it = args.work[args.begin + blockIdx.x];
+    const ShrinkProj& P = args.p[blockIdx.y];
+    // uniform over the workgroup, so returning here skips no barrier
+    if (!(item_ok(it, args.n_active, args.v_slices, P.A, 16 * NTMAX) & (it.nrows <= 64 * MTW))) return;
+    if (NTMAX == 8)
+        shrink_rows_body<MTW, 8>(args, it, P, sX, sA);
+    else if (it.rank > 32)
+        shrink_rows_body<MTW, 4>(args, it, P, sX, sA);
+    else if (it.rank > 16)
+        shrink_rows_body<MTW, 2>(args, it, P, sX, sA);
+    else
+        shrink_rows_body<MTW, 1>(args, it, P, sX, sA);
+}
+
 // ------------------------------------------------------------------ expand
 struct ExpandProj {
     const float* v;
@@ -307,22 +509,25 @@ struct ExpandArgs {
 // v; y is read, updated and written in fp32.
 template <int KS>
 __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
+    __shared__ int32_t s_rows[256];  // the item's y row indices (items hold at most 256 rows)
     const lora_work_t it = args.work[args.begin + blockIdx.x];
     int pi = 0;
     while (pi + 1 < args.n_proj && (int)blockIdx.y >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
-    if (!item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS)) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // uniform over the workgroup, so returning here skips no barrier
+    if (!(item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS) & (it.nrows <= 256))) return;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int li = lane & 15, lg = lane >> 4;
     const int col0 = ((int)blockIdx.y - P.cg_begin) * 512 + wave * 128;
-    if (col0 >= P.d_out) return;  // no barrier in this kernel
+    const bool wave_ok = col0 < P.d_out;  // wave-uniform; waves past d_out only help with s_rows
     const int n0 = col0 + 8 * li;
     const bool col_ok = n0 < P.d_out;
-    const int nc = col_ok ? n0 : col0;  // in-bounds column for lanes past d_out
+    const int nc = col_ok ? n0 : (wave_ok ? col0 : 0);  // in-bounds column for lanes past d_out
     const int cchunk = nc / P.B.chunk_len, cin = nc - cchunk * P.B.chunk_len;
 
     // B strip: all row offsets, then all rows (masked to real ranks and
-    // columns), then the register transpose
+    // columns), then the register transpose; the row indices go to LDS
+    // meanwhile, so no y address waits on a row index load later
     int64_t boff[KS][8];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -338,25 +543,47 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
         for (int e = 0; e < 8; ++e) rows[e] = ld16_if(col_ok && 32 * ks + 8 * lg + e < it.rank, P.B.pool + boff[ks][e] + cin);
         transpose8x8(rows, bop[ks]);
     }
+    if ((int)threadIdx.x < it.nrows) s_rows[threadIdx.x] = args.row_index[it.row0 + threadIdx.x];
+    lds_barrier();
+    if (!wave_ok) return;  // no barrier follows
 
+    // One 16-row tile = y rows 4*lg + e (this lane's outputs) and v row li
+    // (this lane's MFMA operand).  The loads of tile mt+1 are issued before
+    // tile mt is computed and stored.
     const int64_t vslice = (int64_t)args.n_active * P.ldv;
-    for (int mt = 0; mt * 16 < it.nrows; ++mt) {
-        // y rows owned by this lane: 4*lg + e of this tile (rows past the item are masked)
-        float* yrow[4];
-        bool yok[4];
-        f32x4_t y0[4], y1[4];
+    const int ntiles = (it.nrows + 15) / 16;
+    // the first VQ v slices are prefetched with the tile; items with more
+    // slices (short segments with wide d_in) load the rest while computing
+    constexpr int VQ = 2;
+    f32x4_t ys[2][4][2], va[2][KS][VQ][2];
+    // v columns j .. j+3 when they start below the rank, else column 0: every
+    // read stays inside the row (ldv is a multiple of 4 and at least the
+    // rank), and values past the rank are zeroed before use
+    auto v_col = [&](int j) { return j < it.rank ? j : 0; };
+    auto yrow_of = [&](int mt, int e) {
+        const int mm = min(16 * mt + 4 * lg + e, it.nrows - 1);
+        return P.y + (int64_t)s_rows[mm] * P.ldy + nc;
+    };
+    auto load_tile = [&](int st, int mt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int mm = 16 * mt + 4 * lg + e;
-            yok[e] = col_ok && mm < it.nrows;
-            yrow[e] = P.y + (int64_t)args.row_index[it.row0 + min(mm, it.nrows - 1)] * P.ldy + nc;
+            const float* yr = yrow_of(mt, e);
+            ys[st][e][0] = ldf4(yr);
+            ys[st][e][1] = ldf4(yr + 4);
         }
+        const float* vrow = P.v + (int64_t)(it.row0 + min(16 * mt + li, it.nrows - 1)) * P.ldv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            y0[e] = ldf4_if(yok[e], yrow[e]);
-            y1[e] = ldf4_if(yok[e], yrow[e] + 4);
+        for (int ks = 0; ks < KS; ++ks) {
+            const int ja = v_col(32 * ks + 8 * lg), jb = v_col(32 * ks + 8 * lg + 4);
+#pragma unroll
+            for (int q = 0; q < VQ; ++q) {
+                const int64_t so = (int64_t)min(q, it.nslices - 1) * vslice;
+                va[st][ks][q][0] = ldf4(vrow + so + ja);
+                va[st][ks][q][1] = ldf4(vrow + so + jb);
+            }
         }
-        // first operand: v row 16*mt + li
+    };
+    auto compute_tile = [&](int st, int mt) {
         const int m = 16 * mt + li;
         const bool row_ok = m < it.nrows;
         const float* vrow = P.v + (int64_t)(it.row0 + min(m, it.nrows - 1)) * P.ldv;
@@ -364,30 +591,23 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int j0 = 32 * ks + 8 * lg;
-            const bool ok_a = row_ok && j0 < it.rank, ok_b = row_ok && j0 + 4 < it.rank;
-            const int ja = ok_a ? j0 : 0, jb = ok_b ? j0 + 4 : 0;  // in-bounds columns
-            f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-            // slices four at a time, loads before adds, summed in slice order
-            for (int s0 = 0; s0 < it.nslices; s0 += 4) {
-                f32x4_t sa[4], sb[4];
+            const int ja = v_col(j0), jb = v_col(j0 + 4);
+            // slices in slice order: the first VQ from the prefetch, the rest loaded here
+            f32x4_t a = va[st][ks][0][0], b = va[st][ks][0][1];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const bool in = s0 + q < it.nslices;
-                    const int64_t so = (int64_t)min(s0 + q, it.nslices - 1) * vslice;
-                    sa[q] = ldf4_if(in && ok_a, vrow + so + ja);
-                    sb[q] = ldf4_if(in && ok_b, vrow + so + jb);
+            for (int q = 1; q < VQ; ++q)
+                if (q < it.nslices) {
+                    a += va[st][ks][q][0];
+                    b += va[st][ks][q][1];
                 }
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (s0 + q < it.nslices) {
-                        a += sa[q];
-                        b += sb[q];
-                    }
+            for (int sl = VQ; sl < it.nslices; ++sl) {
+                a += ldf4(vrow + sl * vslice + ja);
+                b += ldf4(vrow + sl * vslice + jb);
             }
             float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (j0 + e >= it.rank) f[e] = 0.f;
+                if (!row_ok || j0 + e >= it.rank) f[e] = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t h = pack_bf16(f[2 * q], f[2 * q + 1]);
@@ -401,23 +621,52 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
             acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                if (32 * ks >= it.rank) continue;
                 acc[c] = mfma_bf16(vhi[ks], bop[ks][c], acc[c]);
                 acc[c] = mfma_bf16(vlo[ks], bop[ks][c], acc[c]);
             }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (!yok[e]) continue;
+            if (!col_ok || 16 * mt + 4 * lg + e >= it.nrows) continue;
+            float* yr = yrow_of(mt, e);
             f32x4_t o0, o1;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                o0[c] = __builtin_fmaf(P.scale, acc[c][e], y0[e][c]);
-                o1[c] = __builtin_fmaf(P.scale, acc[c + 4][e], y1[e][c]);
+                o0[c] = __builtin_fmaf(P.scale, acc[c][e], ys[st][e][0][c]);
+                o1[c] = __builtin_fmaf(P.scale, acc[c + 4][e], ys[st][e][1][c]);
             }
-            stf4(yrow[e], o0);
-            stf4(yrow[e] + 4, o1);
+            stf4(yr, o0);
+            stf4(yr + 4, o1);
         }
+    };
+    auto pin = [&](int st) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            asm volatile("" : "+v"(ys[st][e][0]));
+            asm volatile("" : "+v"(ys[st][e][1]));
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int q = 0; q < VQ; ++q) {
+                asm volatile("" : "+v"(va[st][ks][q][0]));
+                asm volatile("" : "+v"(va[st][ks][q][1]));
+            }
+    };
+    load_tile(0, 0);
+    for (int mt = 0;;) {
+        // tile mt is in stage 0; fetch tile mt+1 (the last tile again at the
+        // end: in bounds, never used)
+        load_tile(1, min(mt + 1, ntiles - 1));
+        issue_fence();
+        pin(0);
+        compute_tile(0, mt);
+        if (++mt >= ntiles) break;
+        load_tile(0, min(mt + 1, ntiles - 1));
+        issue_fence();
+        pin(1);
+        compute_tile(1, mt);
+        if (++mt >= ntiles) break;
     }
 }
 
@@ -757,7 +1006,7 @@ __global__ __launch_bounds__(WG, HETLORA_MERGE_WAVES) void merge_kernel(MergeArg
     constexpr int PF = HETLORA_MERGE_PREFETCH;
     const MergeMat& M = args.m[blockIdx.y];
     if ((int)blockIdx.x >= M.tiles) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int li = lane & 15, lg = lane >> 4;
     const int tn = blockIdx.x / M.tiles_k, tk = blockIdx.x % M.tiles_k;
     const int nbase = tn * 128, kbase = tk * 512 + wave * 128;
@@ -888,25 +1137,74 @@ int32_t check_launch(const lora_launch_t* L, int32_t op, int32_t n_proj) {
 typedef void (*shrink_fn)(ShrinkArgs);
 template <int KSPLIT, int MTW, int NT>
 constexpr int unroll_for() {
-    return KSPLIT > 1 ? (NT == 1 ? 8 : NT == 2 ? 4 : NT == 4 ? 2 : 1) : ((MTW + NT) <= 2 ? 4 : (MTW + NT) <= 4 ? 2 : 1);
+    return KSPLIT > 1 ? (NT == 1 ? 4 : NT == 2 ? 2 : 1) : ((MTW + NT) <= 2 ? 2 : 1);
 }
 template <int KSPLIT, int MTW, int NT>
 shrink_fn shrink_inst() {
     return shrink_kernel<KSPLIT, MTW, NT, unroll_for<KSPLIT, MTW, NT>()>;
 }
+// Short-segment (SPLITK16) shrink kernels by rank class.
 shrink_fn shrink_table(int variant) {
-    static const shrink_fn t[LV_S_SHAPES * LV_RANK_CLASSES] = {
-        shrink_inst<4, 1, 1>(), shrink_inst<4, 1, 2>(), shrink_inst<4, 1, 4>(), shrink_inst<4, 1, 8>(),
-        shrink_inst<1, 1, 1>(), shrink_inst<1, 1, 2>(), shrink_inst<1, 1, 4>(), shrink_inst<1, 1, 8>(),
-        shrink_inst<1, 2, 1>(), shrink_inst<1, 2, 2>(), shrink_inst<1, 2, 4>(), shrink_inst<1, 2, 8>(),
-    };
-    return t[variant];
+    static const shrink_fn t[LV_RANK_CLASSES] = {shrink_inst<4, 1, 1>(), shrink_inst<4, 1, 2>(),
+                                                 shrink_inst<4, 1, 4>(), shrink_inst<4, 1, 8>()};
+    return t[variant % LV_RANK_CLASSES];
 }
 
 typedef void (*expand_fn)(ExpandArgs);
 expand_fn expand_table(int rank_class) {
     static const expand_fn t[3] = {expand_kernel<1>, expand_kernel<2>, expand_kernel<4>};
     return t[rank_class];
+}
+
+// Launches `fn` and returns the status of this launch alone
+// (hipLaunchKernel's own result: an error left behind by an earlier,
+// unrelated runtime call is neither reported here nor cleared).
+template <typename A>
+hipError_t launch(void (*fn)(A), dim3 grid, dim3 block, hipStream_t s, A& args) {
+    void* p[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, p, 0, s);
+}
+// The first failure of a sequence of launches.
+inline hipError_t first_error(hipError_t acc, hipError_t e) { return acc != hipSuccess ? acc : e; }
+
+// Shrink launches for the plan's ranges [r0, r1) (shrink variants only).
+// Short-segment ranges get one launch each; the long-segment ranges of one
+// shape with ranks up to 64 are consecutive in the work list and share one
+// launch (the kernel picks the rank tiles per item), ranks above 64 get their
+// own.
+hipError_t launch_shrink_ranges(const lora_plan_info_t& info, int r0, int r1, int32_t n_proj, hipStream_t s,
+                                ShrinkArgs& args) {
+    hipError_t err = hipSuccess;
+    for (int r = r0; r < r1;) {
+        const lora_range_t& R = info.ranges[r];
+        const int shape = R.variant / LV_RANK_CLASSES, cls = R.variant % LV_RANK_CLASSES;
+        if (shape == LV_S_SPLITK16 || cls == LV_RANK_CLASSES - 1) {
+            if (R.count > 0) {
+                args.begin = R.begin;
+                shrink_fn fn = shape == LV_S_SPLITK16 ? shrink_table(R.variant)
+                             : shape == LV_S_ROWS64   ? shrink_rows_kernel<1, 8>
+                                                      : shrink_rows_kernel<2, 8>;
+                err = first_error(err, launch(fn, dim3((unsigned)R.count, (unsigned)n_proj), dim3(WG), s, args));
+            }
+            ++r;
+            continue;
+        }
+        // ranges r .. e-1: same shape, rank classes below the last one
+        int e = r, count = 0;
+        while (e < r1 && info.ranges[e].variant / LV_RANK_CLASSES == shape &&
+               info.ranges[e].variant % LV_RANK_CLASSES < LV_RANK_CLASSES - 1 &&
+               info.ranges[e].begin == R.begin + count) {
+            count += info.ranges[e].count;
+            ++e;
+        }
+        if (count > 0) {
+            args.begin = R.begin;
+            shrink_fn fn = shape == LV_S_ROWS64 ? shrink_rows_kernel<1, 4> : shrink_rows_kernel<2, 4>;
+            err = first_error(err, launch(fn, dim3((unsigned)count, (unsigned)n_proj), dim3(WG), s, args));
+        }
+        r = e;
+    }
+    return err;
 }
 
 }  // namespace
@@ -931,13 +1229,9 @@ extern "C" int32_t lora_shrink(const lora_launch_t* L, int32_t n_proj, const lor
     }
     if (L->info.n_work == 0) return LORA_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-    for (int r = 0; r < L->info.n_ranges; ++r) {
-        const lora_range_t& R = L->info.ranges[r];
-        if (R.count == 0) continue;
-        args.begin = R.begin;
-        hipLaunchKernelGGL(shrink_table(R.variant), dim3((unsigned)R.count, (unsigned)n_proj), dim3(WG), 0, s, args);
-    }
-    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
+    hipError_t err = hipSuccess;
+    err = launch_shrink_ranges(L->info, 0, L->info.n_ranges, n_proj, s, args);
+    return err == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
 extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lora_expand_proj_t* projs,
@@ -961,6 +1255,7 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
     }
     if (L->info.n_work == 0) return LORA_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    hipError_t err = hipSuccess;
     for (int r = 0; r < L->info.n_ranges; ++r) {
         const lora_range_t& R = L->info.ranges[r];
         if (R.count == 0) continue;
@@ -972,13 +1267,12 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
             groups += (args.p[i].d_out + width - 1) / width;
         }
         args.begin = R.begin;
-        if (shape == LV_E_BGMV)
-            hipLaunchKernelGGL(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG), 0, s, args);
-        else
-            hipLaunchKernelGGL(expand_table(R.variant % LV_RANK_CLASSES), dim3((unsigned)R.count, (unsigned)groups),
-                               dim3(WG), 0, s, args);
+        const dim3 grid((unsigned)R.count, (unsigned)groups);
+        err = first_error(err, shape == LV_E_BGMV ? launch(bgmv_expand_kernel, grid, dim3(WG), s, args)
+                                                  : launch(expand_table(R.variant % LV_RANK_CLASSES), grid, dim3(WG),
+                                                           s, args));
     }
-    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
+    return err == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
 extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora_apply_proj_t* projs,
@@ -1012,15 +1306,16 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
     }
     if (L->info.n_work == 0) return LORA_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    hipError_t err = hipSuccess;
     // ranges come in variant order: shrink, expand, fused; the expand ranges
     // follow every shrink range on the stream
-    for (int r = 0; r < L->info.n_ranges; ++r) {
+    int r_shrink = 0;
+    while (r_shrink < L->info.n_ranges && L->info.ranges[r_shrink].variant < LV_APPLY_EXPAND0) ++r_shrink;
+    err = launch_shrink_ranges(L->info, 0, r_shrink, n_proj, s, sa);
+    for (int r = r_shrink; r < L->info.n_ranges; ++r) {
         const lora_range_t& R = L->info.ranges[r];
         if (R.count == 0) continue;
-        if (R.variant < LV_APPLY_EXPAND0) {
-            sa.begin = R.begin;
-            hipLaunchKernelGGL(shrink_table(R.variant), dim3((unsigned)R.count, (unsigned)n_proj), dim3(WG), 0, s, sa);
-        } else if (R.variant < LV_APPLY_FUSED) {
+        if (R.variant < LV_APPLY_FUSED) {
             const int ev = R.variant - LV_APPLY_EXPAND0;
             const int shape = ev / LV_RANK_CLASSES;
             const int32_t width = lv_expand_cols(shape);
@@ -1030,24 +1325,20 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
                 groups += (ea.p[i].d_out + width - 1) / width;
             }
             ea.begin = R.begin;
-            if (shape == LV_E_BGMV)
-                hipLaunchKernelGGL(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG), 0, s, ea);
-            else
-                hipLaunchKernelGGL(expand_table(ev % LV_RANK_CLASSES), dim3((unsigned)R.count, (unsigned)groups),
-                                   dim3(WG), 0, s, ea);
+            const dim3 grid((unsigned)R.count, (unsigned)groups);
+            err = first_error(err, shape == LV_E_BGMV
+                                       ? launch(bgmv_expand_kernel, grid, dim3(WG), s, ea)
+                                       : launch(expand_table(ev % LV_RANK_CLASSES), grid, dim3(WG), s, ea));
         } else {
             fa.begin = R.begin;
             bool uni = true;  // every wave's row offsets are uniform
             for (int i = 0; i < n_proj; ++i)
                 uni = uni && fa.p[i].A.chunk_len % 512 == 0 && fa.p[i].B.chunk_len % 512 == 0;
-            if (uni)
-                hipLaunchKernelGGL(fused_kernel<true>, dim3((unsigned)R.count, (unsigned)n_proj), dim3(FWG), 0, s, fa);
-            else
-                hipLaunchKernelGGL(fused_kernel<false>, dim3((unsigned)R.count, (unsigned)n_proj), dim3(FWG), 0, s,
-                                   fa);
+            err = first_error(err, launch(uni ? fused_kernel<true> : fused_kernel<false>,
+                                          dim3((unsigned)R.count, (unsigned)n_proj), dim3(FWG), s, fa));
         }
     }
-    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
+    return err == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
 namespace {
@@ -1072,14 +1363,11 @@ int32_t merge_impl(int32_t n_mats, const lora_merge_mat_t* mats, float sign, voi
         if (m.rank > max_rank) max_rank = m.rank;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    hipError_t err = hipSuccess;
     const dim3 grid((unsigned)max_tiles, (unsigned)n_mats);
-    if (max_rank <= 32)
-        hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(WG), 0, s, args);
-    else if (max_rank <= 64)
-        hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(WG), 0, s, args);
-    else
-        hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(WG), 0, s, args);
-    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_EHIP;
+    err = launch(max_rank <= 32 ? merge_kernel<1> : max_rank <= 64 ? merge_kernel<2> : merge_kernel<4>, grid, dim3(WG),
+                 s, args);
+    return err == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 }  // namespace
 

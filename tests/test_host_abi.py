@@ -335,3 +335,22 @@ def test_apply_plan_partitions_segments():
                 else:
                     ns = int(work[[i for i in range(work.shape[0]) if work[i, 0] == lo][0], 5])
                     assert np.all(cov_s[lo:hi, :ns] == 1) and np.all(cov_s[lo:hi, ns:] == 0)
+
+
+def test_one_hip_runtime_in_process():
+    """Importing the binding first must not bring a second HIP runtime into the
+    process: torch ships its own libamdhip64 under the system one's soname, so
+    the binding loads torch before the library (fresh interpreter, no GPU needed)."""
+    import subprocess
+    import sys
+    code = ("import heterogeneous_adapter_batching_amd, torch\n"
+            "paths = set()\n"
+            "for line in open('/proc/self/maps'):\n"
+            "    f = line.split()[-1]\n"
+            "    if 'libamdhip64' in f: paths.add(__import__('os').path.realpath(f))\n"
+            "print(len(paths), sorted(paths))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr
+    n = int(out.stdout.split()[0])
+    assert n == 1, out.stdout
