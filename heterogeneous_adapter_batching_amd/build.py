@@ -17,7 +17,7 @@ ARCH = os.environ.get("HETLORA_ARCH", "gfx950")
 # packed fp32 ops are disabled on purpose: plain fp32 VALU code only.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}"]
+             "-Wall", "-Wno-unused-function", "-Wno-inline-asm", f"-I{INCLUDE}"]
 
 
 def _hipcc():

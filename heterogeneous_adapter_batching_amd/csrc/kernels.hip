@@ -38,12 +38,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/hetlora.h"
 #include "variants.h"
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 #define WG 256
 
@@ -71,6 +74,11 @@ __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cas
 __device__ __forceinline__ u32x4_t ld16_if(bool ok, const void* p) {
     u32x4_t v = {0u, 0u, 0u, 0u};
     if (ok) v = *reinterpret_cast<const u32x4_t*>(p);
+    return v;
+}
+__device__ __forceinline__ u32x2_t ld8_if(bool ok, const void* p) {
+    u32x2_t v = {0u, 0u};
+    if (ok) v = *reinterpret_cast<const u32x2_t*>(p);
     return v;
 }
 __device__ __forceinline__ f32x4_t ldf4_if(bool ok, const float* p) {
@@ -168,6 +176,8 @@ struct ShrinkArgs {
     int32_t begin;
     int32_t n_active;
     int32_t v_slices;
+    int32_t count;   // work items of the launch (persistent kernel: tasks = count x n_proj)
+    int32_t n_proj;
     ShrinkProj p[LORA_MAX_PROJ];
 };
 
@@ -333,42 +343,91 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Long segments (items of 64*MTW rows; wave w computes rows 16*MTW*w ..).
-// Both operands of a 64-wide K step pass through LDS: the workgroup loads
-// the x tile (64*MTW rows x 128 B) and the A tile (16*NT rank rows x 128 B)
-// in row-contiguous 16 B pieces, 8 pieces = one full 128 B line per row, so
-// every load instruction covers 8 whole lines.  Loading MFMA fragments
-// straight from memory would touch 16 rows per instruction and use half of
-// each line, and A would be loaded by every wave: the L1 request rate, not
-// HBM, then bounds the kernel.  Pieces are stored XOR-swizzled by (row mod
-// 8), so the 8 lanes of a fragment read that share a piece index hit 8
-// different bank groups.
+// Both operands of a 64-wide K step pass through LDS: the x tile (64*MTW rows
+// x 128 B) and the A tile (16*NT rank rows x 128 B) are fetched with direct
+// global-to-LDS loads (global_load_lds_dwordx4: lane l of a wave's load
+// lands in LDS slot base + 16*l), eight lanes per row, so every load covers
+// eight whole 128 B lines and A is read once per workgroup.  Fetching MFMA
+// fragments straight from memory would touch 16 rows per load and use half
+// of each line, and every wave would fetch A: the L1 request rate, not HBM,
+// would bound the kernel.  A row's eight 16 B pieces are stored XOR-swizzled
+// by (row mod 8), so the eight lanes of a fragment read that share a piece
+// index hit eight different bank groups; with direct loads the swizzle is
+// applied to the source address (lane l of a row fetches piece
+// (l mod 8) ^ (row mod 8)).
 // K order inside a step: lane group lg takes pieces lg and lg+4 (elements
 // 8*lg .. +7 and 32 + 8*lg .. +7) for its two MFMAs; x and A use the same
-// order.  Pipeline: the next step's pieces are loaded into registers while
-// the current step's MFMAs run from LDS; after a barrier they replace the
-// tiles, and a second barrier publishes them.  One LDS buffer (24 KiB at 128
-// rows and rank 64) rather than two lets four workgroups share a CU, so the
-// grids of the large workloads are resident in one round; the other
-// workgroups on the CU cover the barriers.
-template <int MTW, int NT>
-__device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& args, const lora_work_t& it, const ShrinkProj& P,
-                                                 u32x4_t* sX, u32x4_t* sA) {
-    constexpr int ROWS = 64 * MTW;        // rows of the item tile
-    constexpr int XP = ROWS * 8 / WG;     // x pieces per thread
-    constexpr int AP = NT >= 2 ? NT / 2 : 1;  // A pieces per thread (one rank tile: 128 pieces,
-                                              // threads t and t+128 load and store the same one)
+// order.
+// Pipeline: NBUF LDS buffers; the loads of step i+NBUF-1 are issued before
+// the MFMAs of step i, and one barrier per step (after this wave's loads of
+// step i+1 have landed) hands the buffers over.  Every wave issues the same
+// number of loads per step (with one rank tile, waves 2 and 3 repeat the A
+// loads of waves 0 and 1: the same bytes to the same LDS slots), and these
+// are the only vector-memory loads during the steps, so the wait counts are
+// exact.
+// One direct global-to-LDS load of 16 B per lane: lane l's bytes land in
+// LDS at dst + 16*l (dst is the same for the whole wave).  Issued as inline
+// asm: the compiler's own wait insertion, which knows the builtin writes LDS,
+// would wait for every load in flight before each LDS read, including the
+// next step's prefetch.  The caller waits for these loads itself (vmcnt(0)
+// before the step barrier); compiler-issued loads stay correct because the
+// counter is in order (its waits can only over-wait for these).
+__device__ __forceinline__ void dma16(const void* src, u32x4_t* dst) {
+    const unsigned lds = (unsigned)(uintptr_t)((__attribute__((address_space(3))) u32x4_t*)dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+// Barrier once this wave has at most N vector-memory operations in flight
+// and no LDS operation.
+template <int N>
+__device__ __forceinline__ void step_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int MTW, int NT, bool WHOLE_ROWS, int NBUF>
+__device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const lora_work_t& it, const ShrinkProj& P,
+                                                 int proj, u32x4_t* sX, u32x4_t* sA) {
+    constexpr int ROWS = 64 * MTW;           // rows of the item tile
+    constexpr int XBUF = ROWS * 8;           // x pieces per LDS buffer
+    constexpr int ABUF = 16 * NT * 8;        // A pieces per LDS buffer
+    constexpr int XW = XBUF / WG;            // x loads per lane (wave-loads per wave)
+    constexpr int AWT = ABUF / 64;           // A wave-loads of the workgroup
+    constexpr int AW = AWT >= 4 ? AWT / 4 : 1;  // A wave-loads per wave
+    constexpr int DPW = XW + AW;             // loads per wave per step
     const int t = threadIdx.x, lane = t & 63, wave = wave_id();
     const int li = lane & 15, lg = lane >> 4;
     const int mbase = wave * 16 * MTW;
 
-    const uint16_t* xpiece[XP];
-    int xslot[XP];
+    // x sources: wave-load j of this wave fills slots (XW*wave + j)*64 + lane
+    const uint16_t* xsrc[XW];
 #pragma unroll
-    for (int p = 0; p < XP; ++p) {
-        const int id = t + WG * p, row = id >> 3, pc = id & 7;
+    for (int j = 0; j < XW; ++j) {
+        const int row = (XW * wave + j) * 8 + (lane >> 3);
+        const int pc = (lane & 7) ^ (row & 7);
         // rows past the item read its last row (results not stored)
-        xpiece[p] = P.x + (int64_t)args.row_index[it.row0 + min(row, it.nrows - 1)] * P.ldx + 8 * pc;
-        xslot[p] = row * 8 + (pc ^ (row & 7));
+        xsrc[j] = P.x + (int64_t)args.row_index[it.row0 + min(row, it.nrows - 1)] * P.ldx + 8 * pc;
+    }
+    const int kblocks = P.d_in / 64;
+    const int kbeg = (int)((int64_t)it.kslice * kblocks / it.nslices);
+    const int kend = (int)((int64_t)(it.kslice + 1) * kblocks / it.nslices);
+    const int cblocks = P.A.chunk_len / 64;
+    // A sources: wave-load j of this wave fills slots aw*64 + lane, aw =
+    // (AW*wave + j) mod AWT (rank row aw*8 + lane/8, clamped to the rank);
+    // with whole A
+    // rows in one chunk the row pointers are fixed, otherwise each step looks
+    // its chunk up
+    const bool one_chunk = WHOLE_ROWS || kbeg / cblocks == (kend - 1) / cblocks;
+    int arow[AW], apc[AW];
+    const uint16_t* asrc[AW];
+#pragma unroll
+    for (int j = 0; j < AW; ++j) {
+        const int row = ((AW * wave + j) % AWT) * 8 + (lane >> 3);
+        arow[j] = min(row, it.rank - 1);
+        apc[j] = (lane & 7) ^ (row & 7);
+        const int c0 = kbeg / cblocks;
+        // element offset of global K step 0 in this chunk's addressing (the
+        // loads add k*64 for k inside the chunk, so every address is in it)
+        asrc[j] = P.A.pool + (P.A.row_off[off_index(P.A, it.adapter, arow[j], c0)] -
+                              (int64_t)c0 * cblocks * 64 + 8 * apc[j]);
     }
     f32x4_t acc[MTW][NT];
 #pragma unroll
@@ -376,71 +435,72 @@ __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& args, const l
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[q][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int kblocks = P.d_in / 64;
-    const int kbeg = (int)((int64_t)it.kslice * kblocks / it.nslices);
-    const int kend = (int)((int64_t)(it.kslice + 1) * kblocks / it.nslices);
-    const int cblocks = P.A.chunk_len / 64;
-    for (int c = kbeg / cblocks; c * cblocks < kend; ++c) {
-        const int cbase = c * cblocks;
-        const int b0 = max(cbase, kbeg), b1 = min(cbase + cblocks, kend);
-        const uint16_t* apiece[AP];
-        int aslot[AP];
+    auto fetch = [&](int k, int buf) {  // global K step k -> LDS buffer buf
 #pragma unroll
-        for (int p = 0; p < AP; ++p) {
-            const int id = (NT >= 2 ? t : (t & 127)) + WG * p, row = id >> 3, pc = id & 7;
-            apiece[p] = P.A.pool + P.A.row_off[off_index(P.A, it.adapter, min(row, it.rank - 1), c)] +
-                        (b0 - cbase) * 64 + 8 * pc;
-            aslot[p] = row * 8 + (pc ^ (row & 7));
+        for (int j = 0; j < AW; ++j) {
+            const uint16_t* src;
+            if (one_chunk) {
+                src = asrc[j] + (int64_t)k * 64;
+            } else {
+                const int c = k / cblocks;
+                src = P.A.pool + P.A.row_off[off_index(P.A, it.adapter, arow[j], c)] + (int64_t)(k - c * cblocks) * 64 +
+                      8 * apc[j];
+            }
+            dma16(src, sA + buf * ABUF + ((AW * wave + j) % AWT) * 64);
         }
-        issue_fence();
-        u32x4_t xr[XP], ar[AP];
-        auto load = [&](int k) {  // step k of this chunk (relative to b0): A first, then x
 #pragma unroll
-            for (int p = 0; p < AP; ++p) ar[p] = ld16(apiece[p] + (int64_t)k * 64);
+        for (int j = 0; j < XW; ++j)
+            dma16(xsrc[j] + (int64_t)k * 64, sX + buf * XBUF + (XW * wave + j) * 64);
+    };
+    auto mma = [&](int buf) {
+        const u32x4_t* X = sX + buf * XBUF;
+        const u32x4_t* A = sA + buf * ABUF;
+        u32x4_t xf[MTW][2];
 #pragma unroll
-            for (int p = 0; p < XP; ++p) xr[p] = ld16(xpiece[p] + (int64_t)(b0 + k) * 64);
-        };
-        auto store = [&]() {
+        for (int q = 0; q < MTW; ++q) {
+            const int row = mbase + 16 * q + li;
+            xf[q][0] = X[row * 8 + (lg ^ (li & 7))];
+            xf[q][1] = X[row * 8 + ((lg + 4) ^ (li & 7))];
+        }
 #pragma unroll
-            for (int p = 0; p < AP; ++p) sA[aslot[p]] = ar[p];
-#pragma unroll
-            for (int p = 0; p < XP; ++p) sX[xslot[p]] = xr[p];
-        };
-        auto mma = [&]() {
-            u32x4_t xf[MTW][2];
+        for (int n = 0; n < NT; ++n) {
+            const int row = 16 * n + li;
+            const u32x4_t a0 = A[row * 8 + (lg ^ (li & 7))];
+            const u32x4_t a1 = A[row * 8 + ((lg + 4) ^ (li & 7))];
 #pragma unroll
             for (int q = 0; q < MTW; ++q) {
-                const int row = mbase + 16 * q + li;
-                xf[q][0] = sX[row * 8 + (lg ^ (li & 7))];
-                xf[q][1] = sX[row * 8 + ((lg + 4) ^ (li & 7))];
+                acc[q][n] = mfma_bf16(xf[q][0], a0, acc[q][n]);
+                acc[q][n] = mfma_bf16(xf[q][1], a1, acc[q][n]);
             }
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const int row = 16 * n + li;
-                const u32x4_t a0 = sA[row * 8 + (lg ^ (li & 7))];
-                const u32x4_t a1 = sA[row * 8 + ((lg + 4) ^ (li & 7))];
-#pragma unroll
-                for (int q = 0; q < MTW; ++q) {
-                    acc[q][n] = mfma_bf16(xf[q][0], a0, acc[q][n]);
-                    acc[q][n] = mfma_bf16(xf[q][1], a1, acc[q][n]);
-                }
-            }
-        };
-        const int nb = b1 - b0;
-        load(0);
-        store();
-        lds_barrier();
-        for (int i = 0;;) {
-            // step i is in LDS; fetch step i+1 (the last step again at the
-            // end: in bounds, never used)
-            load(min(i + 1, nb - 1));
-            issue_fence();
-            mma();
-            lds_barrier();  // every wave is done with step i's tiles
-            if (++i >= nb) break;
-            store();
-            lds_barrier();
         }
+    };
+    // Steps start at a point that depends on (adapter, projection, K
+    // slice).  x rows and A rows lie a power-of-two distance apart, so
+    // workgroups that read the same step in lock-step all hit the same
+    // address bits; spreading the starting steps spreads the traffic.  The
+    // start is the same for every item of a segment and for every storage
+    // layout, so a row's sum order (and hence its result, to the bit)
+    // depends on neither which item holds it nor how A is paged.
+    const int nb = kend - kbeg;
+    const unsigned h = (unsigned)it.adapter * 2654435761u ^ ((unsigned)proj * 40503u + (unsigned)it.kslice * 977u);
+    const int rot = (int)((h >> 7) % (unsigned)nb);
+    auto step = [&](int i) { return kbeg + (i + rot < nb ? i + rot : i + rot - nb); };
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b)
+        if (b < nb) fetch(step(b), b);
+    if (nb >= NBUF - 1)
+        step_barrier<(NBUF - 2) * DPW>();  // step 0 has landed
+    else
+        step_barrier<0>();
+    for (int i = 0; i < nb; ++i) {
+        const int ahead = i + NBUF - 1;
+        if (ahead < nb) fetch(step(ahead), ahead % NBUF);
+        mma(i % NBUF);
+        // step i+1 has landed and every wave is done with step i's buffer
+        if (ahead < nb)
+            step_barrier<(NBUF - 2) * DPW>();
+        else
+            step_barrier<0>();
     }
     if (mbase >= it.nrows) return;
     float* vout = P.v + (int64_t)it.kslice * args.n_active * P.ldv;
@@ -458,26 +518,33 @@ __device__ __forceinline__ void shrink_rows_body(const ShrinkArgs& args, const l
         }
 }
 
-// One workgroup = one long-segment work item of one projection; the item's
-// rank picks the number of rank tiles (1, 2 or 4 up to NTMAX = 4; NTMAX = 8 is
-// its own kernel for ranks above 64, whose registers would lower the
-// occupancy of the others).
-template <int MTW, int NTMAX>
+// Persistent: workgroup g takes tasks g, g + G, ... of the launch's
+// count x n_proj (item, projection) tasks; the launcher sizes the grid so
+// that every workgroup gets the same number of tasks and all are resident.
+// The item's rank picks the number of rank tiles (1, 2 or 4 up to NTMAX = 4;
+// NTMAX = 8 is its own kernel for ranks above 64, whose registers and LDS
+// would lower the occupancy of the others).
+template <int MTW, int NTMAX, bool WHOLE_ROWS>
 __global__ __launch_bounds__(WG) void shrink_rows_kernel(ShrinkArgs args) {
-    __shared__ u32x4_t sX[64 * MTW * 8];    // 64*MTW rows x 8 pieces of 16 B
-    __shared__ u32x4_t sA[16 * NTMAX * 8];  // 16*NT rank rows x 8 pieces
-    const lora_work_t it = args.work[args.begin + blockIdx.x];
-    const ShrinkProj& P = args.p[blockIdx.y];
-    // uniform over the workgroup, so returning here skips no barrier
-    if (!(item_ok(it, args.n_active, args.v_slices, P.A, 16 * NTMAX) & (it.nrows <= 64 * MTW))) return;
-    if (NTMAX == 8)
-        shrink_rows_body<MTW, 8>(args, it, P, sX, sA);
-    else if (it.rank > 32)
-        shrink_rows_body<MTW, 4>(args, it, P, sX, sA);
-    else if (it.rank > 16)
-        shrink_rows_body<MTW, 2>(args, it, P, sX, sA);
-    else
-        shrink_rows_body<MTW, 1>(args, it, P, sX, sA);
+    constexpr int NBUF = NTMAX == 8 ? 2 : 3;        // LDS stages (two steps in flight below rank 64)
+    __shared__ u32x4_t sX[NBUF * 64 * MTW * 8];    // NBUF buffers x 64*MTW rows x 8 pieces of 16 B
+    __shared__ u32x4_t sA[NBUF * 16 * NTMAX * 8];  // NBUF buffers x 16*NT rank rows x 8 pieces
+    const int ntasks = args.count * args.n_proj;
+    for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
+        const int proj = task / args.count;
+        const lora_work_t it = args.work[args.begin + task - proj * args.count];
+        const ShrinkProj& P = args.p[proj];
+        // uniform over the workgroup: a skipped task skips no barrier
+        if (!(item_ok(it, args.n_active, args.v_slices, P.A, 16 * NTMAX) & (it.nrows <= 64 * MTW))) continue;
+        if (NTMAX == 8)
+            shrink_rows_task<MTW, 8, WHOLE_ROWS, NBUF>(args, it, P, proj, sX, sA);
+        else if (it.rank > 32)
+            shrink_rows_task<MTW, 4, WHOLE_ROWS, NBUF>(args, it, P, proj, sX, sA);
+        else if (it.rank > 16)
+            shrink_rows_task<MTW, 2, WHOLE_ROWS, NBUF>(args, it, P, proj, sX, sA);
+        else
+            shrink_rows_task<MTW, 1, WHOLE_ROWS, NBUF>(args, it, P, proj, sX, sA);
+    }
 }
 
 // ------------------------------------------------------------------ expand
@@ -501,119 +568,138 @@ struct ExpandArgs {
     ExpandProj p[LORA_MAX_PROJ];
 };
 
-// One workgroup = one work item x one 512-column group of one projection;
-// wave w owns columns [128w, 128w+128) of the group.  The wave loads and
-// transposes its B strip once (KS steps of 32 ranks), then walks the item's
-// rows 16 at a time.  v (the sum of the row's K slices, in slice order) is
-// split as hi + lo bf16 (two MFMAs) so the product keeps ~16 mantissa bits of
-// v; y is read, updated and written in fp32.
+// One workgroup = one work item (at most EXPAND_ROWS rows) x one 512-column
+// group of one projection; wave w owns columns [128w, 128w+128) of the
+// group.  v (the sum of the row's K slices, in slice order) is split as hi +
+// lo bf16 (two MFMAs, so the product keeps ~16 mantissa bits of v) once per
+// workgroup into LDS; the wave loads and transposes its B strip once (KS
+// steps of 32 ranks), then walks the item's rows 16 at a time, loading the
+// next tile's y while the current one is computed; y is read, updated and
+// written in fp32.
+#define EXPAND_ROWS 128
 template <int KS>
 __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
-    __shared__ int32_t s_rows[256];  // the item's y row indices (items hold at most 256 rows)
+    constexpr int G = 4 * KS;  // groups of 8 ranks
+    __shared__ int32_t s_rows[EXPAND_ROWS];          // the item's y row indices
+    __shared__ u32x4_t s_v[EXPAND_ROWS * 2 * G];     // per row: (hi, lo) x G groups, XOR-swizzled
     const lora_work_t it = args.work[args.begin + blockIdx.x];
     int pi = 0;
     while (pi + 1 < args.n_proj && (int)blockIdx.y >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
     // uniform over the workgroup, so returning here skips no barrier
-    if (!(item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS) & (it.nrows <= 256))) return;
+    if (!(item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS) & (it.nrows <= EXPAND_ROWS))) return;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int li = lane & 15, lg = lane >> 4;
+    // The wave's 128 columns are two halves of 64 (d_out is a multiple of
+    // 64, so each half is wholly in or out of range, and lies in one chunk
+    // of B).  Lane li owns columns 4*li .. +3 of each half: one 16 B y load
+    // or store of the 16 lanes of a row group then covers 256 contiguous
+    // bytes of the row (two whole lines).  MFMA c (c < 4) produces column
+    // 4*li + c of the first half, MFMA c + 4 the same of the second half.
     const int col0 = ((int)blockIdx.y - P.cg_begin) * 512 + wave * 128;
-    const bool wave_ok = col0 < P.d_out;  // wave-uniform; waves past d_out only help with s_rows
-    const int n0 = col0 + 8 * li;
-    const bool col_ok = n0 < P.d_out;
-    const int nc = col_ok ? n0 : (wave_ok ? col0 : 0);  // in-bounds column for lanes past d_out
-    const int cchunk = nc / P.B.chunk_len, cin = nc - cchunk * P.B.chunk_len;
+    const bool wave_ok = col0 < P.d_out;  // wave-uniform; waves past d_out only help with the LDS tables
+    const bool hi_ok = col0 + 64 < P.d_out;
+    const int nlo = wave_ok ? col0 + 4 * li : 0;         // in-bounds columns for halves past d_out
+    const int nhi = hi_ok ? col0 + 64 + 4 * li : nlo;
+    const int clo = nlo / P.B.chunk_len, chi = nhi / P.B.chunk_len;
+    const int inlo = nlo - clo * P.B.chunk_len, inhi = nhi - chi * P.B.chunk_len;
 
     // B strip: all row offsets, then all rows (masked to real ranks and
-    // columns), then the register transpose; the row indices go to LDS
-    // meanwhile, so no y address waits on a row index load later
-    int64_t boff[KS][8];
+    // columns), then the register transpose
+    int64_t blo[KS][8], bhi[KS][8];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            boff[ks][e] = P.B.row_off[off_index(P.B, it.adapter, min(32 * ks + 8 * lg + e, it.rank - 1), cchunk)];
+        for (int e = 0; e < 8; ++e) {
+            const int j = min(32 * ks + 8 * lg + e, it.rank - 1);
+            blo[ks][e] = P.B.row_off[off_index(P.B, it.adapter, j, clo)];
+            bhi[ks][e] = P.B.row_off[off_index(P.B, it.adapter, j, chi)];
+        }
     issue_fence();
     u32x4_t bop[KS][8];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         u32x4_t rows[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rows[e] = ld16_if(col_ok && 32 * ks + 8 * lg + e < it.rank, P.B.pool + boff[ks][e] + cin);
+        for (int e = 0; e < 8; ++e) {
+            const bool rk = 32 * ks + 8 * lg + e < it.rank;
+            const u32x2_t lo = ld8_if(wave_ok && rk, P.B.pool + blo[ks][e] + inlo);
+            const u32x2_t hi = ld8_if(hi_ok && rk, P.B.pool + bhi[ks][e] + inhi);
+            rows[e] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
         transpose8x8(rows, bop[ks]);
     }
+
+    // LDS tables: row indices, and v summed over its slices (in slice
+    // order), zero past the rank, split into bf16 hi + lo.  Piece (g, h) of
+    // row m (h = 0 hi, 1 lo) sits at slot m*2G + ((2g + h) ^ (m & 7)), so the
+    // eight lanes of a fragment read that share g and h hit eight bank groups.
+    const int64_t vslice = (int64_t)args.n_active * P.ldv;
     if ((int)threadIdx.x < it.nrows) s_rows[threadIdx.x] = args.row_index[it.row0 + threadIdx.x];
+    for (int u = threadIdx.x; u < it.nrows * G; u += WG) {
+        const int m = u / G, g = u - m * G, j0 = 8 * g;
+        // columns j .. j+3 when they start below the rank, else column 0
+        // (in the row: ldv is a multiple of 4 and at least the rank)
+        const int ja = j0 < it.rank ? j0 : 0, jb = j0 + 4 < it.rank ? j0 + 4 : 0;
+        const float* vrow = P.v + (int64_t)(it.row0 + m) * P.ldv;
+        f32x4_t a = ldf4(vrow + ja), b = ldf4(vrow + jb);
+        for (int sl = 1; sl < it.nslices; ++sl) {
+            a += ldf4(vrow + sl * vslice + ja);
+            b += ldf4(vrow + sl * vslice + jb);
+        }
+        float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        u32x4_t vh, vl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (j0 + e >= it.rank) f[e] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t h = pack_bf16(f[2 * q], f[2 * q + 1]);
+            vh[q] = h;
+            vl[q] = pack_bf16(f[2 * q] - bf16_lo(h), f[2 * q + 1] - bf16_hi(h));
+        }
+        s_v[m * 2 * G + ((2 * g) ^ (m & 7))] = vh;
+        s_v[m * 2 * G + ((2 * g + 1) ^ (m & 7))] = vl;
+    }
+
+    // One 16-row tile = y rows 4*lg + e (this lane's outputs) and v row li
+    // (this lane's MFMA operand).  Tile 0's y is loaded before the tables
+    // are complete; the loads of tile mt+1 are issued before tile mt is
+    // computed and stored.
+    const int ntiles = (it.nrows + 15) / 16;
+    f32x4_t ys[2][4][2];
+    auto yrow_of = [&](int mt, int e) {
+        const int mm = min(16 * mt + 4 * lg + e, it.nrows - 1);
+        return P.y + (int64_t)args.row_index[it.row0 + mm] * P.ldy;
+    };
+    auto yrow_lds = [&](int mt, int e) {
+        const int mm = min(16 * mt + 4 * lg + e, it.nrows - 1);
+        return P.y + (int64_t)s_rows[mm] * P.ldy;
+    };
+    auto load_tile = [&](int st, const float* const (&yr)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ys[st][e][0] = ldf4(yr[e] + nlo);
+            ys[st][e][1] = ldf4(yr[e] + nhi);
+        }
+    };
+    {
+        const float* yr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yr[e] = yrow_of(0, e);
+        if (wave_ok) load_tile(0, yr);
+    }
     lds_barrier();
     if (!wave_ok) return;  // no barrier follows
 
-    // One 16-row tile = y rows 4*lg + e (this lane's outputs) and v row li
-    // (this lane's MFMA operand).  The loads of tile mt+1 are issued before
-    // tile mt is computed and stored.
-    const int64_t vslice = (int64_t)args.n_active * P.ldv;
-    const int ntiles = (it.nrows + 15) / 16;
-    // the first VQ v slices are prefetched with the tile; items with more
-    // slices (short segments with wide d_in) load the rest while computing
-    constexpr int VQ = 2;
-    f32x4_t ys[2][4][2], va[2][KS][VQ][2];
-    // v columns j .. j+3 when they start below the rank, else column 0: every
-    // read stays inside the row (ldv is a multiple of 4 and at least the
-    // rank), and values past the rank are zeroed before use
-    auto v_col = [&](int j) { return j < it.rank ? j : 0; };
-    auto yrow_of = [&](int mt, int e) {
-        const int mm = min(16 * mt + 4 * lg + e, it.nrows - 1);
-        return P.y + (int64_t)s_rows[mm] * P.ldy + nc;
-    };
-    auto load_tile = [&](int st, int mt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float* yr = yrow_of(mt, e);
-            ys[st][e][0] = ldf4(yr);
-            ys[st][e][1] = ldf4(yr + 4);
-        }
-        const float* vrow = P.v + (int64_t)(it.row0 + min(16 * mt + li, it.nrows - 1)) * P.ldv;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int ja = v_col(32 * ks + 8 * lg), jb = v_col(32 * ks + 8 * lg + 4);
-#pragma unroll
-            for (int q = 0; q < VQ; ++q) {
-                const int64_t so = (int64_t)min(q, it.nslices - 1) * vslice;
-                va[st][ks][q][0] = ldf4(vrow + so + ja);
-                va[st][ks][q][1] = ldf4(vrow + so + jb);
-            }
-        }
-    };
     auto compute_tile = [&](int st, int mt) {
-        const int m = 16 * mt + li;
-        const bool row_ok = m < it.nrows;
-        const float* vrow = P.v + (int64_t)(it.row0 + min(m, it.nrows - 1)) * P.ldv;
+        const int m = min(16 * mt + li, it.nrows - 1);  // rows past the item: results not stored
         u32x4_t vhi[KS], vlo[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int j0 = 32 * ks + 8 * lg;
-            const int ja = v_col(j0), jb = v_col(j0 + 4);
-            // slices in slice order: the first VQ from the prefetch, the rest loaded here
-            f32x4_t a = va[st][ks][0][0], b = va[st][ks][0][1];
-#pragma unroll
-            for (int q = 1; q < VQ; ++q)
-                if (q < it.nslices) {
-                    a += va[st][ks][q][0];
-                    b += va[st][ks][q][1];
-                }
-            for (int sl = VQ; sl < it.nslices; ++sl) {
-                a += ldf4(vrow + sl * vslice + ja);
-                b += ldf4(vrow + sl * vslice + jb);
-            }
-            float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (!row_ok || j0 + e >= it.rank) f[e] = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t h = pack_bf16(f[2 * q], f[2 * q + 1]);
-                vhi[ks][q] = h;
-                vlo[ks][q] = pack_bf16(f[2 * q] - bf16_lo(h), f[2 * q + 1] - bf16_hi(h));
-            }
+            const int g = 4 * ks + lg;
+            vhi[ks] = s_v[m * 2 * G + ((2 * g) ^ (m & 7))];
+            vlo[ks] = s_v[m * 2 * G + ((2 * g + 1) ^ (m & 7))];
         }
         f32x4_t acc[8];
 #pragma unroll
@@ -627,16 +713,16 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (!col_ok || 16 * mt + 4 * lg + e >= it.nrows) continue;
-            float* yr = yrow_of(mt, e);
+            if (16 * mt + 4 * lg + e >= it.nrows) continue;
+            float* yr = yrow_lds(mt, e);
             f32x4_t o0, o1;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 o0[c] = __builtin_fmaf(P.scale, acc[c][e], ys[st][e][0][c]);
                 o1[c] = __builtin_fmaf(P.scale, acc[c + 4][e], ys[st][e][1][c]);
             }
-            stf4(yr, o0);
-            stf4(yr + 4, o1);
+            stf4(yr + nlo, o0);  // the wave's first half is in range (wave_ok)
+            if (hi_ok) stf4(yr + nhi, o1);
         }
     };
     auto pin = [&](int st) {
@@ -645,24 +731,22 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
             asm volatile("" : "+v"(ys[st][e][0]));
             asm volatile("" : "+v"(ys[st][e][1]));
         }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int q = 0; q < VQ; ++q) {
-                asm volatile("" : "+v"(va[st][ks][q][0]));
-                asm volatile("" : "+v"(va[st][ks][q][1]));
-            }
     };
-    load_tile(0, 0);
+    auto fetch = [&](int st, int mt) {
+        const float* yr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yr[e] = yrow_lds(mt, e);
+        load_tile(st, yr);
+    };
     for (int mt = 0;;) {
         // tile mt is in stage 0; fetch tile mt+1 (the last tile again at the
         // end: in bounds, never used)
-        load_tile(1, min(mt + 1, ntiles - 1));
+        fetch(1, min(mt + 1, ntiles - 1));
         issue_fence();
         pin(0);
         compute_tile(0, mt);
         if (++mt >= ntiles) break;
-        load_tile(0, min(mt + 1, ntiles - 1));
+        fetch(0, min(mt + 1, ntiles - 1));
         issue_fence();
         pin(1);
         compute_tile(1, mt);
@@ -1172,19 +1256,58 @@ inline hipError_t first_error(hipError_t acc, hipError_t e) { return acc != hipS
 // shape with ranks up to 64 are consecutive in the work list and share one
 // launch (the kernel picks the rank tiles per item), ranks above 64 get their
 // own.
+// Workgroups of `fn` (WG threads) that the current device holds at once:
+// CUs x resident workgroups per CU, cached per (device, kernel).
+int resident_slots(const void* fn) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    static std::mutex mu;
+    static struct Entry { int dev; const void* fn; int slots; } cache[64];
+    static int n_cache = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cache; ++i)
+        if (cache[i].dev == dev && cache[i].fn == fn) return cache[i].slots;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, WG, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    const int slots = cus * per_cu;
+    if (n_cache < 64) cache[n_cache++] = Entry{dev, fn, slots};
+    return slots;
+}
+
+// Grid of a persistent launch over `tasks` equal tasks: as few rounds as
+// the resident slots allow, and the tasks spread evenly over the workgroups
+// (every workgroup gets the same number, give or take one, and no partly
+// filled last round).
+unsigned persistent_grid(const void* fn, int64_t tasks) {
+    const int64_t slots = resident_slots(fn);
+    const int64_t rounds = (tasks + slots - 1) / slots;
+    return (unsigned)((tasks + rounds - 1) / rounds);
+}
+
 hipError_t launch_shrink_ranges(const lora_plan_info_t& info, int r0, int r1, int32_t n_proj, hipStream_t s,
                                 ShrinkArgs& args) {
     hipError_t err = hipSuccess;
+    args.n_proj = n_proj;
+    bool whole = true;  // every projection keeps each A row in one chunk
+    for (int i = 0; i < n_proj; ++i) whole = whole && args.p[i].A.chunk_len >= args.p[i].d_in;
     for (int r = r0; r < r1;) {
         const lora_range_t& R = info.ranges[r];
         const int shape = R.variant / LV_RANK_CLASSES, cls = R.variant % LV_RANK_CLASSES;
         if (shape == LV_S_SPLITK16 || cls == LV_RANK_CLASSES - 1) {
             if (R.count > 0) {
                 args.begin = R.begin;
-                shrink_fn fn = shape == LV_S_SPLITK16 ? shrink_table(R.variant)
-                             : shape == LV_S_ROWS64   ? shrink_rows_kernel<1, 8>
-                                                      : shrink_rows_kernel<2, 8>;
-                err = first_error(err, launch(fn, dim3((unsigned)R.count, (unsigned)n_proj), dim3(WG), s, args));
+                args.count = R.count;
+                if (shape == LV_S_SPLITK16) {
+                    err = first_error(err, launch(shrink_table(R.variant), dim3((unsigned)R.count, (unsigned)n_proj),
+                                                  dim3(WG), s, args));
+                } else {
+                    shrink_fn fn = shape == LV_S_ROWS64
+                                       ? (whole ? shrink_rows_kernel<1, 8, true> : shrink_rows_kernel<1, 8, false>)
+                                       : (whole ? shrink_rows_kernel<2, 8, true> : shrink_rows_kernel<2, 8, false>);
+                    const unsigned g = persistent_grid(reinterpret_cast<const void*>(fn), (int64_t)R.count * n_proj);
+                    err = first_error(err, launch(fn, dim3(g), dim3(WG), s, args));
+                }
             }
             ++r;
             continue;
@@ -1199,8 +1322,12 @@ hipError_t launch_shrink_ranges(const lora_plan_info_t& info, int r0, int r1, in
         }
         if (count > 0) {
             args.begin = R.begin;
-            shrink_fn fn = shape == LV_S_ROWS64 ? shrink_rows_kernel<1, 4> : shrink_rows_kernel<2, 4>;
-            err = first_error(err, launch(fn, dim3((unsigned)count, (unsigned)n_proj), dim3(WG), s, args));
+            args.count = count;
+            shrink_fn fn = shape == LV_S_ROWS64
+                               ? (whole ? shrink_rows_kernel<1, 4, true> : shrink_rows_kernel<1, 4, false>)
+                               : (whole ? shrink_rows_kernel<2, 4, true> : shrink_rows_kernel<2, 4, false>);
+            const unsigned g = persistent_grid(reinterpret_cast<const void*>(fn), (int64_t)count * n_proj);
+            err = first_error(err, launch(fn, dim3(g), dim3(WG), s, args));
         }
         r = e;
     }

@@ -17,14 +17,15 @@
 #define LV_S_ROWS128 2
 #define LV_S_SHAPES 3
 
-// Expand shapes: the MFMA kernel with work items of 16 / 64 / 128 / 256 rows
+// Expand shapes: the MFMA kernel with work items of 16 / 64 / 128 rows
 // (more rows reuse each B column strip more, fewer rows give more
 // workgroups), and the VALU kernel for decode items of at most 2 rows (BGMV),
-// which has a single rank class.
+// which has a single rank class.  Shape 3 is a spare MFMA shape (items of
+// 128 rows, the kernel's maximum); the table does not use it.
 #define LV_E_ROWS16 0
 #define LV_E_ROWS64 1
 #define LV_E_ROWS128 2
-#define LV_E_ROWS256 3
+#define LV_E_SPARE 3
 #define LV_E_BGMV 4
 #define LV_E_SHAPES 5
 
@@ -32,8 +33,7 @@ static inline int32_t lv_shrink_rows(int shape) {
     return shape == LV_S_SPLITK16 ? 16 : shape == LV_S_ROWS64 ? 64 : 128;
 }
 static inline int32_t lv_expand_rows(int shape) {
-    return shape == LV_E_ROWS16 ? 16 : shape == LV_E_ROWS64 ? 64 : shape == LV_E_ROWS128 ? 128
-         : shape == LV_E_ROWS256 ? 256 : 2;
+    return shape == LV_E_ROWS16 ? 16 : shape == LV_E_ROWS64 ? 64 : shape == LV_E_BGMV ? 2 : 128;
 }
 // Variant ids of an apply plan: the shrink variants, then the expand
 // variants shifted by LV_APPLY_EXPAND0, then the fused one-row kernel.
