@@ -235,16 +235,17 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
         if (first >= kb1) continue;  // wave-uniform
         // Two register stages of U blocks each: the loads of the next stage are
         // issued before the MFMAs of the current one, so a wave always has a
-        // stage in flight.  Blocks past the slice are loaded at the last
-        // block's address (in bounds; their MFMAs are skipped).  Rows past the
-        // item and rank slots past the rank read clamped, real rows; their
-        // outputs are never stored, so no load is masked.
+        // stage in flight.  Blocks past the slice are not loaded (a
+        // wave-uniform branch; their MFMAs are skipped).  Rows past the item
+        // and rank slots past the rank read clamped, real rows; their outputs
+        // are never stored, so no load is masked.
         const int last = first + (kb1 - 1 - first) / KSPLIT * KSPLIT;
         u32x4_t xs[2][U][MTW][2], as[2][U][NT][2];
         auto load_stage = [&](int st, int k0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int k = min(k0 + u * KSPLIT, last);
+                const int k = k0 + u * KSPLIT;
+                if (k > last) break;  // wave-uniform
                 const int64_t kx = (int64_t)k * 64, ka = (int64_t)(k - cbase) * 64;
 #pragma unroll
                 for (int t = 0; t < MTW; ++t) {
