@@ -32,6 +32,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--path 
                        [--no-cpu-baseline]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -45,6 +46,51 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 METRIC = "hetero-LoRA shrink+expand µs, GB/s & TFLOP/s vs roofline; merge µs/layer"
+
+
+KERNELS_SRC = os.path.join(ROOT, "heterogeneous_adapter_batching_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "merge_kernel_traffic.json")
+SECTION = "// " + "-" * 66 + " "
+
+
+def merge_source_digest():
+    """sha256 of the merge kernel's device code (its section of kernels.hip)."""
+    src = open(KERNELS_SRC).read()
+    a = src.index(SECTION + "merge\n")
+    b = src.index(SECTION + "host side\n")
+    return hashlib.sha256(src[a:b].encode()).hexdigest()
+
+
+def merge_traffic():
+    """HBM bytes per merge launch from the committed rocprofv3 counters:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one pass each) of the merge
+    kernel, each scaled by copy_bytes / (the same counter's KiB for one plain
+    copy of copy_bytes).  None when the record is missing or was taken on a
+    different version of the merge kernel's source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("merge_source_sha256") != merge_source_digest():
+        return None
+    c = rec["copy"]
+    f_fetch = c["bytes"] / (c["fetch_kib"] * 1024.0)
+    f_write = c["bytes"] / (c["write_kib"] * 1024.0)
+    return round(rec["merge"]["fetch_kib"] * 1024.0 * f_fetch + rec["merge"]["write_kib"] * 1024.0 * f_write)
+
+
+def copy_calibration():
+    """One plain device-to-device copy of 1 GiB (after a warm-up copy), for
+    calibrating the FETCH_SIZE / WRITE_SIZE counters under rocprofv3 --pmc."""
+    import torch
+    n = 1 << 30
+    src = torch.full((n,), 1, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n}), flush=True)
 
 
 def delta_cost(W, row_adapter):
@@ -137,7 +183,11 @@ def main():
     ap.add_argument("--path", default="apply", choices=["apply", "split"],
                     help="apply (default): lora_apply, one-row segments fused; split: lora_shrink then lora_expand")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy (counter calibration under rocprofv3 --pmc) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path is single-GPU by design (no sharding, no collectives); "
               "run it with --gpus 1", file=sys.stderr)
@@ -188,10 +238,13 @@ def main():
     merge_host = layers[0]["merge_host"]
     n_mats = len(layers[0]["Wt"])
 
+    # merge and unmerge run back to back between one pair of events (the same
+    # kernel twice: the per-launch figure is half the pair, and an event pair
+    # per launch would add its dispatch gap to each)
     if split:
-        groups = ["hetero_shrink", "hetero_expand", "homo_shrink", "homo_expand", "merge", "unmerge"]
+        groups = ["hetero_shrink", "hetero_expand", "homo_shrink", "homo_expand", "merge_unmerge"]
     else:
-        groups = ["hetero_apply", "homo_apply", "merge", "unmerge"]
+        groups = ["hetero_apply", "homo_apply", "merge_unmerge"]
 
     def step(ev, k):
         L = layers[k % len(layers)]
@@ -205,10 +258,8 @@ def main():
                 g += 1
         ev[g][0].record(stream)
         L["merge"]()
-        ev[g][1].record(stream)
-        ev[g + 1][0].record(stream)
         L["unmerge"]()
-        ev[g + 1][1].record(stream)
+        ev[g][1].record(stream)
 
     def new_events():
         return [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in groups]
@@ -238,7 +289,7 @@ def main():
            "homo_expand": (co["expand_bytes"], co["flops"] * 0.5),
            "hetero_apply": (ch["shrink_bytes"] + ch["expand_bytes"], ch["flops"]),
            "homo_apply": (co["shrink_bytes"] + co["expand_bytes"], co["flops"]),
-           "merge": (mc["bytes"], mc["flops"]), "unmerge": (mc["bytes"], mc["flops"])}
+           "merge_unmerge": (2 * mc["bytes"], 2 * mc["flops"])}
     alg = {g: alg[g] for g in groups}
     step_bytes = sum(b for b, _ in alg.values())
     kernels = {}
@@ -250,12 +301,12 @@ def main():
                       "GB_s": round(gbs, 1), "TFLOP_s": round(f / (med[g] * 1e-6) / 1e12, 3),
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     # dominant kernel: largest share of GPU time; merge and unmerge are the same kernel
-    mavg = (med["merge"] + med["unmerge"]) / 2
-    share = {g: med[g] for g in groups if g not in ("merge", "unmerge")}
-    share["merge"] = med["merge"] + med["unmerge"]
-    dom = max(share, key=share.get)
-    if dom == "merge":
+    mavg = med["merge_unmerge"] / 2
+    dom = max(groups, key=lambda g: med[g])
+    traffic = None
+    if dom == "merge_unmerge":
         d_us, d_bytes, name = mavg, mc["bytes"], "merge_kernel (merge/unmerge, 4 x W[4096x4096], rank 16)"
+        traffic = merge_traffic()
     else:
         d_us, d_bytes, name = med[dom], alg[dom][0], dom
     achieved = d_bytes / (d_us * 1e-6) / 1e9
@@ -274,7 +325,7 @@ def main():
                    "rows": 64, "d": 4096, "rank": 16, "adapters": 64, "projections": 4,
                    "layer_copies": len(layers)},
         "roofline": {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "us_per_launch": round(d_us, 3), "alg_bytes_per_launch": int(d_bytes)},
         "kernels": kernels,
         "hetero_over_homo": round(sum(med[g] for g in groups if g.startswith("hetero")) /
