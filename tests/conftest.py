@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # gpu tests are skipped (not failed) where no GPU is visible, so a plain
-    # `pytest tests/` on a CPU host stays green; `-m gpu` on the GPU machine runs them.
+    # `pytest tests/` on a CPU host stays green; `-m gpu` on a GPU host runs them.
     try:
         import torch
         have_gpu = torch.cuda.is_available()

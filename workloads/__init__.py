@@ -54,7 +54,7 @@ from typing import Callable, Dict, List, Optional
 import numpy as np
 
 __all__ = [
-    "RowsDesc", "Projection", "MergeSpec", "Workload", "CONFIGS", "gen_config",
+    "RowsDesc", "Projection", "MergeSpec", "Workload", "GENERATORS", "gen_config",
     "to_bf16_bits", "normal_f32", "build_pool", "NAN_BF16",
 ]
 
@@ -327,12 +327,12 @@ def gen_mix70b(seed=4, layout="paged"):
     return _make("mix70b", seed, row_adapter, ranks, projs, layout, 8192, rng)
 
 
-CONFIGS = {0: gen_tiny, 1: gen_decode, 2: gen_prefill, 3: gen_vision, 4: gen_mix70b}
+GENERATORS = {0: gen_tiny, 1: gen_decode, 2: gen_prefill, 3: gen_vision, 4: gen_mix70b}
 
 
 def gen_config(k: int, seed: Optional[int] = None, **kw) -> Workload:
-    """Workload k (0..4); the official instance uses seed = k."""
-    return CONFIGS[k](k if seed is None else seed, **kw)
+    """Workload k (0 tiny, 1 decode, 2 prefill, 3 vision, 4 70B mix); the seeded instance uses seed = k."""
+    return GENERATORS[k](k if seed is None else seed, **kw)
 
 
 def gen_custom(seed, row_adapter, ranks, d_in, d_out, n_proj=1, layout="dense",
