@@ -20,6 +20,9 @@ What it follows (page titles as printed; sections named on the page):
   Delta W = B x A computed at run time and added to / subtracted from W once.
 * LoRazor news article, "mechanism" section: LoRA work is launched over the
   rows whose adapter is still held; released rows get no LoRA work.
+* VaLoRA blog, section 4.4.2 "Mixture Inference Mode" (deLoRA): with adapter
+  m merged, a request on adapter x uses W_merge - Delta W_m + Delta W_x
+  (``mixture``).
 
 Readings where the pages are silent (kept identical in the HIP path's docs):
 A is stored [r][d_in] and B [r][d_out] (both as r hidden-size vectors), W as
@@ -35,9 +38,10 @@ from .bf16 import bf16_to_f64, f64_to_bf16_rne
 from .segments import build_segments_ref, SegmentsRef, dense_offsets_ref, SegmentError
 from .lora import gather_rows_ref, apply_ref, merge_ref, unmerge_ref, merge_dense_ref
 from .plan_check import check_plan_coverage
+from .mixture import mixture_ref
 
 __all__ = [
     "bf16_to_f64", "f64_to_bf16_rne", "build_segments_ref", "SegmentsRef",
     "dense_offsets_ref", "SegmentError", "gather_rows_ref", "apply_ref",
-    "merge_ref", "unmerge_ref", "merge_dense_ref", "check_plan_coverage",
+    "merge_ref", "unmerge_ref", "merge_dense_ref", "check_plan_coverage", "mixture_ref",
 ]

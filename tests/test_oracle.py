@@ -286,3 +286,51 @@ def test_workload_shapes_and_determinism():
     assert len(np.unique(np.diff(np.nonzero(np.diff(np.r_[-2, a.row_adapter]))[0]))) >= 1
     s = build_segments_ref(a.row_adapter, a.adapter_rank)
     assert s.n_active == 64 and 1 <= s.n_seg <= 4
+
+
+# ----------------------------------------------------------------------------- deLoRA mixture
+def test_mixture_rank1_closed_form_bit_exact():
+    """Adapter 0 (rank 1) merged; a row on adapter 1 gets s*(v_1 B_1 - v_0 B_0):
+    x = [3, 0, 5, 0, ...], A_0 = e_0, A_1 = e_2 -> v_0 = 3, v_1 = 5."""
+    x = np.zeros((3, 8)); x[:, 0] = 3.0; x[:, 2] = 5.0
+    a0 = np.zeros((1, 8)); a0[0, 0] = 1.0
+    a1 = np.zeros((1, 8)); a1[0, 2] = 1.0
+    b0 = np.array([[1.0, 1.0, 1.0, 1.0]])
+    b1 = np.array([[1.0, 0.5, -2.0, 4.0]])
+    p = _tiny_problem(x, [a0, a1], [b0, b1], [1, 0, -1], np.zeros((3, 4)))
+    y = oracle.mixture_ref(p["row_adapter"], p["adapter_rank"], 0, p["x_bits"], p["y0"], p["pool"],
+                           p["A"], p["B"], 2.0)
+    assert y[0].tolist() == [4.0, -1.0, -26.0, 34.0]     # 2*(5*b1 - 3*b0)
+    assert y[1].tolist() == [0.0] * 4                     # on the merged adapter: W_merge serves it
+    assert y[2].tolist() == [0.0] * 4                     # released
+
+
+@pytest.mark.parametrize("layout", ["dense", "paged"])
+def test_mixture_equals_unmerged_inference(layout):
+    """VaLoRA's identity: x (W_merge - dW_m + dW_x)^T with W_merge = W + dW_m equals the
+    unmerged output x W^T + s x A_x^T B_x, for rows on any adapter; rows on m get
+    x W_merge^T; released rows keep y0.  Exact real arithmetic, so fp64 agrees to rounding."""
+    rng = np.random.default_rng(11)
+    d_in, d_out, s, m = 96, 64, 2.0, 1
+    ranks = [4, 8, 3]
+    A = [rng.standard_normal((r, d_in)) / 8 for r in ranks]
+    B = [rng.standard_normal((r, d_out)) / 3 for r in ranks]
+    ra = np.array([0, 1, 2, -1, 2, 1, 0, 0], np.int32)
+    x = rng.standard_normal((len(ra), d_in))
+    p = _tiny_problem(x, A, B, ra, np.zeros((len(ra), d_out)), layout=layout)
+    Ae, Be, xe = [bf16_to_f64(_bits(a)) for a in A], [bf16_to_f64(_bits(b)) for b in B], bf16_to_f64(p["x_bits"])
+    Wb = rng.standard_normal((d_out, d_in)) / 10
+    Wm = Wb + s * Be[m].T @ Ae[m]                          # merged weights (unrounded)
+    y0 = xe @ Wm.T                                         # shared merged GEMM
+    y = oracle.mixture_ref(ra, p["adapter_rank"], m, p["x_bits"], y0, p["pool"], p["A"], p["B"], s)
+    for i, a in enumerate(ra):
+        if a < 0:
+            want = y0[i]
+        elif a == m:
+            want = xe[i] @ Wm.T
+        else:
+            want = xe[i] @ Wb.T + s * (xe[i] @ Ae[a].T) @ Be[a]    # unmerged, adapter a
+        np.testing.assert_allclose(y[i], want, rtol=1e-11, atol=1e-11)
+    # adding the merged adapter instead of subtracting it would be far off
+    bad = xe[0] @ Wm.T + s * (xe[0] @ Ae[0].T) @ Be[0]
+    assert np.max(np.abs(bad - (xe[0] @ Wb.T + s * (xe[0] @ Ae[0].T) @ Be[0]))) > 1e-2
