@@ -15,7 +15,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
-LORA_ABI_VERSION = 4
+LORA_ABI_VERSION = 5
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
 LORA_MAX_RANGES = 48
@@ -44,7 +44,7 @@ _P = ctypes.POINTER
 
 class lora_rows_t(ctypes.Structure):
     _fields_ = [("pool", _vp), ("row_off", _vp), ("n_adapters", _i32), ("max_rank", _i32),
-                ("row_len", _i32), ("chunk_len", _i32)]
+                ("row_len", _i32), ("chunk_len", _i32), ("neg_from", _vp)]
 
 
 class lora_work_t(ctypes.Structure):
@@ -99,6 +99,8 @@ _sig = {
     "lora_merge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
     "lora_unmerge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
     "lora_rows_dense_offsets": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _P(_i64)]),
+    "lora_mixture_row_adapter": (_i32, [_i32, _vp, _i32, _vp]),
+    "lora_mixture_rows": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -193,8 +195,9 @@ def lora_plan(op, segs, d_in, d_out, work_capacity=None, work_out=None, info_out
     return work[:info.n_work].copy(), info
 
 
-def make_rows(pool_ptr, row_off_ptr, n_adapters, max_rank, row_len, chunk_len):
-    return lora_rows_t(pool_ptr, row_off_ptr, int(n_adapters), int(max_rank), int(row_len), int(chunk_len))
+def make_rows(pool_ptr, row_off_ptr, n_adapters, max_rank, row_len, chunk_len, neg_from_ptr=None):
+    return lora_rows_t(pool_ptr, row_off_ptr, int(n_adapters), int(max_rank), int(row_len), int(chunk_len),
+                       neg_from_ptr)
 
 
 def make_launch(row_index_ptr, work_ptr, info):
@@ -253,3 +256,33 @@ def lora_rows_dense_offsets(rank, max_rank, row_len, chunk_len):
     _check(_lib.lora_rows_dense_offsets(rk.shape[0], int(max_rank), _ptr(rk), int(row_len), int(chunk_len),
                                         off.ctypes.data, ctypes.byref(pe)), "lora_rows_dense_offsets")
     return off[:rk.shape[0] * int(max_rank) * chunks].copy(), pe.value
+
+
+def lora_mixture_row_adapter(row_adapter, merged, raw=False):
+    """deLoRA mixture batch (host): rows on the merged adapter -> -1.  With
+    raw=True returns (status, out) instead of raising."""
+    ra = np.ascontiguousarray(row_adapter, dtype=np.int32)
+    out = np.empty(max(1, ra.shape[0]), np.int32)
+    st = _lib.lora_mixture_row_adapter(ra.shape[0], _ptr(ra), int(merged), out.ctypes.data)
+    if raw:
+        return st, out[:ra.shape[0]]
+    _check(st, "lora_mixture_row_adapter")
+    return out[:ra.shape[0]].copy()
+
+
+def lora_mixture_rows(rank, merged, chunks, row_off, max_rank, out_max_rank, raw=False):
+    """deLoRA composite row table (host): returns (out_row_off int64, out_rank
+    int32, out_neg_from int32).  With raw=True returns (status, ...)."""
+    rk = np.ascontiguousarray(rank, dtype=np.int32)
+    ro = np.ascontiguousarray(row_off, dtype=np.int64)
+    n = rk.shape[0]
+    out_off = np.zeros(max(1, n * int(out_max_rank) * int(chunks)), np.int64)
+    out_rank = np.zeros(max(1, n), np.int32)
+    out_neg = np.zeros(max(1, n), np.int32)
+    st = _lib.lora_mixture_rows(n, int(max_rank), _ptr(rk), int(merged), int(chunks), _ptr(ro), int(out_max_rank),
+                                out_off.ctypes.data, out_rank.ctypes.data, out_neg.ctypes.data)
+    res = (out_off[:n * int(out_max_rank) * int(chunks)], out_rank[:n], out_neg[:n])
+    if raw:
+        return (st,) + res
+    _check(st, "lora_mixture_rows")
+    return res

@@ -261,3 +261,48 @@ extern "C" int32_t lora_rows_dense_offsets(int32_t n_adapters, int32_t max_rank,
     *pool_elems = row * stride;
     return LORA_OK;
 }
+
+// deLoRA mixture (VaLoRA blog, section 4.4.2): rows on the merged adapter
+// get no delta; every other row keeps its adapter, which the composite
+// tables below turn into "adapter a, minus the merged one".
+extern "C" int32_t lora_mixture_row_adapter(int32_t n_rows, const int32_t* row_adapter, int32_t merged,
+                                            int32_t* out_row_adapter) {
+    if (n_rows < 0 || merged < 0 || (n_rows > 0 && (row_adapter == nullptr || out_row_adapter == nullptr)))
+        return LORA_EINVAL;
+    for (int32_t i = 0; i < n_rows; ++i) out_row_adapter[i] = row_adapter[i] == merged ? -1 : row_adapter[i];
+    return LORA_OK;
+}
+
+// Composite row table: adapter a's rows, then the merged adapter's rows;
+// the merged adapter's part is marked negative through neg_from.
+extern "C" int32_t lora_mixture_rows(int32_t n_adapters, int32_t max_rank, const int32_t* rank, int32_t merged,
+                                     int32_t chunks, const int64_t* row_off, int32_t out_max_rank,
+                                     int64_t* out_row_off, int32_t* out_rank, int32_t* out_neg_from) {
+    if (n_adapters < 1 || chunks < 1 || rank == nullptr || row_off == nullptr || out_row_off == nullptr ||
+        out_rank == nullptr || out_neg_from == nullptr || merged < 0 || merged >= n_adapters)
+        return LORA_EINVAL;
+    if (max_rank < 1 || max_rank > LORA_MAX_RANK || out_max_rank < 1 || out_max_rank > LORA_MAX_RANK) return LORA_ERANK;
+    const int32_t rm = rank[merged];
+    for (int32_t a = 0; a < n_adapters; ++a) {
+        if (rank[a] < 1 || rank[a] > max_rank) return LORA_ERANK;
+        const int32_t r = a == merged ? rm : rank[a] + rm;
+        if (r > out_max_rank || r > LORA_MAX_RANK) return LORA_ERANK;
+    }
+    for (int32_t a = 0; a < n_adapters; ++a) {
+        const int32_t ra = rank[a];
+        const int32_t r = a == merged ? rm : ra + rm;
+        for (int32_t j = 0; j < out_max_rank; ++j) {
+            int32_t src_a = a, src_j = j;
+            if (a != merged && j >= ra) {
+                src_a = merged;
+                src_j = j - ra;
+            }
+            for (int32_t c = 0; c < chunks; ++c)
+                out_row_off[((int64_t)a * out_max_rank + j) * chunks + c] =
+                    j < r ? row_off[((int64_t)src_a * max_rank + src_j) * chunks + c] : 0;
+        }
+        out_rank[a] = r;
+        out_neg_from[a] = a == merged ? rm : ra;
+    }
+    return LORA_OK;
+}

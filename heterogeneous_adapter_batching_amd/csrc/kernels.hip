@@ -143,7 +143,13 @@ struct Rows {
     const uint16_t* pool;
     const int64_t* row_off;
     int32_t n_adapters, max_rank, chunk_len, chunks;
+    const int32_t* neg_from;  // A side: v_j negated for j >= neg_from[adapter] (NULL: none)
 };
+// First rank row of `adapter` whose v enters negated (a deLoRA composite
+// adapter's merged part); `rank` when the table marks none.
+__device__ __forceinline__ int32_t neg_start(const Rows& t, int32_t adapter, int32_t rank) {
+    return t.neg_from ? t.neg_from[adapter] : rank;
+}
 
 // A work item is used only if it lies inside the launch's rows and fits the
 // row tables and the kernel's rank capacity; anything else is skipped, so a
@@ -322,8 +328,10 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
 #pragma unroll
             for (int n = 0; n < NT; ++n) acc[0][n] += red[w][n][lane];
     }
-    // result lane layout: column j = 16n + li, rows 4*lg + e of tile t
+    // result lane layout: column j = 16n + li, rows 4*lg + e of tile t;
+    // rank rows from neg_start on enter negated (deLoRA composite adapters)
     float* vout = P.v + (int64_t)it.kslice * args.n_active * P.ldv;
+    const int jneg = neg_start(P.A, it.adapter, it.rank);
 #pragma unroll
     for (int t = 0; t < MTW; ++t)
 #pragma unroll
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = mbase + 16 * t + 4 * lg + e;
-                if (m < it.nrows) vout[(int64_t)(it.row0 + m) * P.ldv + j] = acc[t][n][e];
+                if (m < it.nrows) vout[(int64_t)(it.row0 + m) * P.ldv + j] = j >= jneg ? -acc[t][n][e] : acc[t][n][e];
             }
         }
 }
@@ -505,6 +513,7 @@ __device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const l
     }
     if (mbase >= it.nrows) return;
     float* vout = P.v + (int64_t)it.kslice * args.n_active * P.ldv;
+    const int jneg = neg_start(P.A, it.adapter, it.rank);  // deLoRA: negated rank rows
 #pragma unroll
     for (int q = 0; q < MTW; ++q)
 #pragma unroll
@@ -514,7 +523,7 @@ __device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const l
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = mbase + 16 * q + 4 * lg + e;
-                if (m < it.nrows) vout[(int64_t)(it.row0 + m) * P.ldv + j] = acc[q][n][e];
+                if (m < it.nrows) vout[(int64_t)(it.row0 + m) * P.ldv + j] = j >= jneg ? -acc[q][n][e] : acc[q][n][e];
             }
         }
 }
@@ -997,6 +1006,7 @@ __global__ __launch_bounds__(FWG) void fused_kernel(FusedArgs args) {
         xf[2 * q + 1] = bf16_hi(xv[q]);
     }
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const int jneg = neg_start(P.A, it.adapter, it.rank);
 
     for (int g0 = 0; g0 < it.rank; g0 += 16) {
         if (g0 > 0) load_group(g0);
@@ -1025,7 +1035,7 @@ __global__ __launch_bounds__(FWG) void fused_kernel(FusedArgs args) {
             float v = 0.f;
 #pragma unroll
             for (int w = 0; w < FHALF / 64; ++w) v += s_part[hh * (FHALF / 64) + w][e];
-            s_v[t] = v;
+            s_v[t] = g0 + t >= jneg ? -v : v;  // deLoRA: negated rank rows
         }
         __syncthreads();
 #pragma unroll
@@ -1198,7 +1208,8 @@ int32_t check_rows(const lora_rows_t& r, int32_t d, int32_t max_rank, int32_t ma
 }
 
 Rows to_rows(const lora_rows_t& r) {
-    return Rows{r.pool, r.row_off, r.n_adapters, r.max_rank, r.chunk_len, (r.row_len + r.chunk_len - 1) / r.chunk_len};
+    return Rows{r.pool, r.row_off, r.n_adapters, r.max_rank, r.chunk_len, (r.row_len + r.chunk_len - 1) / r.chunk_len,
+                r.neg_from};
 }
 
 int32_t check_launch(const lora_launch_t* L, int32_t op, int32_t n_proj) {
@@ -1484,6 +1495,7 @@ int32_t merge_impl(int32_t n_mats, const lora_merge_mat_t* mats, float sign, voi
         int32_t st;
         if ((st = check_rows(m.A, m.d_in, m.rank, m.adapter)) != LORA_OK) return st;
         if ((st = check_rows(m.B, m.d_out, m.rank, m.adapter)) != LORA_OK) return st;
+        if (m.A.neg_from || m.B.neg_from) return LORA_EINVAL;  // the merge takes plain adapters
         const int32_t tk = (m.d_in + 511) / 512, tn = (m.d_out + 127) / 128;
         args.m[i] = MergeMat{m.W, m.ldw, m.d_out, m.d_in, to_rows(m.A), to_rows(m.B), m.adapter, m.rank,
                              sign * m.scale, tk, tk * tn};

@@ -12,7 +12,8 @@ import torch
 
 from . import (LORA_MAX_SLICES, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, call_apply,
                call_expand, call_merge, call_shrink, lora_apply_proj_t, lora_build_segments, lora_expand_proj_t,
-               lora_launch_t, lora_merge_mat_t, lora_plan, lora_plan_info_t, lora_shrink_proj_t, make_rows)
+               lora_launch_t, lora_merge_mat_t, lora_mixture_rows, lora_plan, lora_plan_info_t, lora_shrink_proj_t,
+               make_rows)
 
 
 def staging_layout(n_active, n_work_shrink, n_work_expand, n_work_apply=0):
@@ -36,16 +37,20 @@ def stream_handle(stream=None):
 
 
 class Rows:
-    """A row table on the device: pool (bf16 bits) + row_off (int64)."""
+    """A row table on the device: pool (bf16 bits) + row_off (int64), and
+    optionally neg_from (int32 per adapter: rank rows from there on enter
+    negated, the A side of a deLoRA composite table)."""
 
-    def __init__(self, pool, row_off, n_adapters, max_rank, row_len, chunk_len):
+    def __init__(self, pool, row_off, n_adapters, max_rank, row_len, chunk_len, neg_from=None):
         assert pool.is_cuda and row_off.is_cuda and row_off.dtype == torch.int64
-        self.pool, self.row_off = pool, row_off
+        assert neg_from is None or (neg_from.is_cuda and neg_from.dtype == torch.int32)
+        self.pool, self.row_off, self.neg_from = pool, row_off, neg_from
         self.n_adapters, self.max_rank, self.row_len, self.chunk_len = n_adapters, max_rank, row_len, chunk_len
 
     def c(self):
         return make_rows(self.pool.data_ptr(), self.row_off.data_ptr(), self.n_adapters, self.max_rank,
-                         self.row_len, self.chunk_len)
+                         self.row_len, self.chunk_len,
+                         None if self.neg_from is None else self.neg_from.data_ptr())
 
 
 class Batch:
@@ -220,3 +225,17 @@ def merge(mats, stream=None):
 
 def unmerge(mats, stream=None):
     prepare_merge(mats, stream, unmerge=True)()
+
+
+def mixture_tables(rows_host, rank, merged, out_max_rank, device="cuda"):
+    """deLoRA (VaLoRA section 4.4.2) tables for one projection while adapter
+    `merged` is merged: rows_host = (A_row_off, B_row_off, max_rank, A_chunks,
+    B_chunks) of the real adapters (host int64 arrays).  Returns
+    (A_row_off, B_row_off, neg_from) on the device and the composite ranks
+    (host), for Rows(..., max_rank=out_max_rank, neg_from=neg_from) on the A
+    side and Rows(..., max_rank=out_max_rank) on the B side."""
+    a_off, b_off, max_rank, a_chunks, b_chunks = rows_host
+    ca, crank, neg = lora_mixture_rows(rank, merged, a_chunks, a_off, max_rank, out_max_rank)
+    cb, _, _ = lora_mixture_rows(rank, merged, b_chunks, b_off, max_rank, out_max_rank)
+    dev = torch.device(device)
+    return (torch.from_numpy(ca).to(dev), torch.from_numpy(cb).to(dev), torch.from_numpy(neg).to(dev), crank)

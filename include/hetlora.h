@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 4
+#define LORA_ABI_VERSION 5
 #define LORA_MAX_RANK 128   /* ranks are 1..128                              */
 #define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
 #define LORA_MAX_RANGES 48  /* kernel variants in one plan                   */
@@ -93,7 +93,13 @@ extern "C" {
  *             multiple of 8 (16 bytes); entries for j >= r_a are never read
  *   max_rank  row-slot stride of the table (>= every rank used with it)
  *   row_len   elements per row (d_in for A, d_out for B)
- *   chunk_len elements per chunk, a positive multiple of 64              */
+ *   chunk_len elements per chunk, a positive multiple of 64
+ *   neg_from  device, int32 [n_adapters], or NULL.  Read on the A side only
+ *             (by the calls that compute v): for adapter a, the rank rows
+ *             j >= neg_from[a] enter with a minus sign, v_j = -(x . A_a[j]).
+ *             This is how a deLoRA composite adapter (lora_mixture_rows)
+ *             subtracts the merged adapter.  NULL: no row is negated.  The
+ *             merge calls require NULL on both sides.                      */
 typedef struct lora_rows {
     const uint16_t* pool;
     const int64_t* row_off;
@@ -101,6 +107,7 @@ typedef struct lora_rows {
     int32_t max_rank;
     int32_t row_len;
     int32_t chunk_len;
+    const int32_t* neg_from;
 } lora_rows_t;
 
 /* One unit of kernel work: rows row_index[row0 .. row0+nrows) of one segment,
@@ -306,6 +313,46 @@ int32_t lora_rows_dense_offsets(int32_t n_adapters, int32_t max_rank,
                                 const int32_t* rank, int32_t row_len,
                                 int32_t chunk_len, int64_t* row_off,
                                 int64_t* pool_elems);
+
+/* deLoRA mixture inference (VaLoRA blog, section 4.4.2 "Mixture Inference
+ * Mode"): while adapter `merged` (m) is merged into the weights, a request
+ * on adapter x != m is served with W_merge - Delta W_m + Delta W_x, i.e. on
+ * the delta path y += s (x A_x^T) B_x - s (x A_m^T) B_m, and a request on m
+ * needs no delta at all.  The two calls below express this as an ordinary
+ * heterogeneous batch over "composite" adapters, so every call above
+ * (lora_apply, lora_shrink + lora_expand) serves it in one pass:
+ *
+ * lora_mixture_row_adapter: host.  out_row_adapter[i] = -1 where
+ *   row_adapter[i] == merged, else row_adapter[i] (rows on the merged
+ *   adapter get no work; released rows stay released).
+ *   row_adapter, out_row_adapter: host int32 [n_rows] (may be the same
+ *   array).  Errors: LORA_EINVAL (null pointer, n_rows < 0, merged < 0).
+ *
+ * lora_mixture_rows: host.  Builds the composite row-offset table of one
+ *   matrix kind (call it once for A and once for B) from the table of the
+ *   real adapters: composite adapter a (a != m) has rank r_a + r_m, rows
+ *   j < r_a are adapter a's rows and rows r_a + i are the merged adapter's
+ *   row i; composite adapter m keeps m's own rows.
+ *   rank        host int32 [n_adapters], ranks of the real adapters
+ *   row_off     host int64 [n_adapters * max_rank * chunks], the real table
+ *   out_row_off host int64 [n_adapters * out_max_rank * chunks]; slots past
+ *               a composite rank are set to 0 (never read)
+ *   out_rank    host int32 [n_adapters] (composite ranks; the adapter_rank
+ *               argument of lora_build_segments for the mixture batch)
+ *   out_neg_from host int32 [n_adapters]: r_a for a != m (the merged
+ *               adapter's rows enter negated), r_m for m; upload it and pass
+ *               it as the A side's neg_from
+ *   Outputs are written only on LORA_OK.  Errors: LORA_EINVAL (null
+ *   pointer, n_adapters < 1, chunks < 1, merged outside [0, n_adapters)),
+ *   LORA_ERANK (a rank outside [1, max_rank], or r_a + r_m > out_max_rank
+ *   or > LORA_MAX_RANK).                                                    */
+int32_t lora_mixture_row_adapter(int32_t n_rows, const int32_t* row_adapter,
+                                 int32_t merged, int32_t* out_row_adapter);
+int32_t lora_mixture_rows(int32_t n_adapters, int32_t max_rank,
+                          const int32_t* rank, int32_t merged, int32_t chunks,
+                          const int64_t* row_off, int32_t out_max_rank,
+                          int64_t* out_row_off, int32_t* out_rank,
+                          int32_t* out_neg_from);
 
 #ifdef __cplusplus
 }

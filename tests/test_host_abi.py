@@ -354,3 +354,48 @@ def test_one_hip_runtime_in_process():
     assert out.returncode == 0, out.stderr
     n = int(out.stdout.split()[0])
     assert n == 1, out.stdout
+
+
+def test_mixture_row_adapter():
+    ra = np.array([0, 2, -1, 2, 1, 0, 2], np.int32)
+    out = hl.lora_mixture_row_adapter(ra, 2)
+    assert out.tolist() == [0, -1, -1, -1, 1, 0, -1]
+    st, _ = hl.lora_mixture_row_adapter(ra, -1, raw=True)
+    assert st == hl.LORA_EINVAL
+
+
+@pytest.mark.parametrize("chunks", [1, 3])
+def test_mixture_rows_composite_table(chunks):
+    """Composite adapter a != m: rows j < r_a are a's, rows r_a + i are m's row i;
+    m keeps its own rows; neg_from = r_a (m: r_m)."""
+    rng = np.random.default_rng(chunks)
+    rank = np.array([3, 8, 5, 1], np.int32)
+    max_rank, m, out_max = 8, 2, 16
+    row_off = rng.integers(0, 1 << 40, size=len(rank) * max_rank * chunks).astype(np.int64) * 8
+    off, crank, neg = hl.lora_mixture_rows(rank, m, chunks, row_off, max_rank, out_max)
+    R = lambda t, a, j, c, mr: t[(a * mr + j) * chunks + c]
+    for a in range(len(rank)):
+        r = rank[m] if a == m else rank[a] + rank[m]
+        assert crank[a] == r and neg[a] == (rank[m] if a == m else rank[a])
+        for j in range(out_max):
+            for c in range(chunks):
+                if j >= r:
+                    want = 0
+                elif a == m or j < rank[a]:
+                    want = R(row_off, a, j, c, max_rank)
+                else:
+                    want = R(row_off, m, j - rank[a], c, max_rank)
+                assert R(off, a, j, c, out_max) == want, (a, j, c)
+
+
+def test_mixture_rows_errors():
+    rank = np.array([64, 70, 8], np.int32)
+    row_off = np.zeros(3 * 80, np.int64)
+    st, *_ = hl.lora_mixture_rows(rank, 1, 1, row_off, 80, 128, raw=True)
+    assert st == hl.LORA_ERANK                       # 64 + 70 > 128
+    st, *_ = hl.lora_mixture_rows(rank, 3, 1, row_off, 80, 128, raw=True)
+    assert st == hl.LORA_EINVAL                      # merged adapter out of range
+    st, *_ = hl.lora_mixture_rows(rank, 2, 1, row_off, 80, 64, raw=True)
+    assert st == hl.LORA_ERANK                       # 70 + 8 > out_max_rank
+    st, off, crank, neg = hl.lora_mixture_rows(rank, 2, 1, row_off, 80, 128, raw=True)
+    assert st == hl.LORA_OK and crank.tolist() == [72, 78, 8] and neg.tolist() == [64, 70, 8]
