@@ -177,7 +177,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="layer copies the steps rotate over")
-    ap.add_argument("--workload", default="decode", choices=["decode", "tiny", "prefill", "vision", "mix70b"],
+    ap.add_argument("--workload", default="decode", choices=["decode", "tiny", "prefill", "vision", "mix70b",
+                                                             "mixture"],
                     help="decode (default) is the benchmark line; the others time shrink+expand (and the "
                          "vision mode switch) of that workload for the kernel tables")
     ap.add_argument("--path", default="apply", choices=["apply", "split"],
@@ -193,6 +194,8 @@ def main():
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "mixture":
+        return mixture_workload(args)
     if args.workload != "decode":
         return other_workload(args)
     import torch
@@ -413,6 +416,67 @@ def other_workload(args):
                          "merge_us_per_layer": round(mus / spec.n_layers, 2), "alg_bytes_per_phase": int(mb),
                          "merge_hbm_frac": round(mb / mus / 1e3 / HBM_PEAK_GBS, 4),
                          "unmerge_hbm_frac": round(mb / uus / 1e3 / HBM_PEAK_GBS, 4)}
+    print(json.dumps(out), flush=True)
+
+
+def mixture_workload(args):
+    """deLoRA mixture inference (VaLoRA blog, section 4.4.2) on the decode
+    layer: adapter 0 merged, the other 63 one-token rows get
+    +s x A_x^T B_x - s x A_0^T B_0 through composite adapters in one
+    lora_apply (the fused kernel), timed next to the plain heterogeneous
+    lora_apply of the same rows (no adapter merged); HIP events, medians,
+    a 512 MB fill between steps to evict the Infinity Cache."""
+    import torch
+    import workloads
+    from heterogeneous_adapter_batching_amd import lora_mixture_row_adapter
+    from heterogeneous_adapter_batching_amd.session import Batch, Rows, mixture_tables
+    from workloads.device import to_device
+
+    W = workloads.gen_config(1)
+    dw = to_device(W)
+    m = W.merge.adapter
+    ra = W.batches["hetero"]
+    ra_mix = lora_mixture_row_adapter(ra, m)
+    r_max = int(W.adapter_rank.max())
+    out_max = 2 * r_max
+    mix, plain, crank = [], [], None
+    for p, d in zip(W.projections, dw.projections):
+        ca, cb, neg, crank = mixture_tables((p.A.row_off, p.B.row_off, p.A.max_rank, p.A.chunks, p.B.chunks),
+                                            W.adapter_rank, m, out_max)
+        mix.append((d, Rows(dw.pool, ca, p.A.n_adapters, out_max, p.A.row_len, p.A.chunk_len, neg_from=neg),
+                    Rows(dw.pool, cb, p.B.n_adapters, out_max, p.B.row_len, p.B.chunk_len), (ca, cb, neg)))
+        plain.append((d, Rows(dw.pool, d.A_off, p.A.n_adapters, p.A.max_rank, p.A.row_len, p.A.chunk_len),
+                      Rows(dw.pool, d.B_off, p.B.n_adapters, p.B.max_rank, p.B.row_len, p.B.chunk_len)))
+    bm = Batch(W.n_rows, crank, 4096, 4096).refresh(ra_mix)
+    bp = Batch(W.n_rows, W.adapter_rank, 4096, 4096).refresh(np.where(ra == m, -1, ra).astype(np.int32))
+    vm = [bm.new_v(out_max) for _ in mix]
+    vp = [bp.new_v(r_max) for _ in plain]
+    run_mix = bm.prepare_apply([(d.x, A, v, B, d.y, W.scale) for (d, A, B, _), v in zip(mix, vm)])
+    run_plain = bp.prepare_apply([(d.x, A, v, B, d.y, W.scale) for (d, A, B), v in zip(plain, vp)])
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    res = {"mixture_apply": [], "unmerged_apply": []}
+    for it in range(args.warmup + args.steps):
+        for name, fn in (("mixture_apply", run_mix), ("unmerged_apply", run_plain)):
+            flush.fill_(it & 0xFF)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(); fn(); e[1].record()
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                res[name].append(e[0].elapsed_time(e[1]) * 1e3)
+    act = ra_mix >= 0
+    n, d_in, d_out, r = int(act.sum()), 4096, 4096, int(W.adapter_rank[1])
+    rm = int(W.adapter_rank[m])
+    n_proj = len(W.projections)
+    # algorithmic bytes: x, y read+write, each distinct adapter's A and B once, the merged adapter's once, v
+    plain_b = n_proj * (n * d_in * 2 + n * d_out * 8 + n * r * (d_in + d_out) * 2 + n * r * 8)
+    mix_b = plain_b + n_proj * (rm * (d_in + d_out) * 2 + n * rm * 8)
+    out = {"workload": "mixture", "rows": n, "merged_adapter": int(m), "kernels": {}}
+    for name, nb in (("mixture_apply", mix_b), ("unmerged_apply", plain_b)):
+        us = float(np.median(res[name]))
+        out["kernels"][name] = {"us_median": round(us, 2), "alg_bytes": int(nb), "GB_s": round(nb / us / 1e3, 1),
+                                "hbm_frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    out["mixture_over_unmerged"] = round(out["kernels"]["mixture_apply"]["us_median"] /
+                                         out["kernels"]["unmerged_apply"]["us_median"], 3)
     print(json.dumps(out), flush=True)
 
 
