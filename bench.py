@@ -30,6 +30,8 @@ With --path split the step calls lora_shrink and lora_expand instead.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--path apply|split]
                        [--no-cpu-baseline]
+       python bench.py --workload tiny|prefill|vision|mix70b|mixture   (kernel timing of the other workloads)
+       python bench.py --copy-calibration                             (counter calibration under rocprofv3)
 """
 import argparse
 import hashlib
