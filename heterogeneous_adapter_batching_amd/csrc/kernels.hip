@@ -575,8 +575,19 @@ struct ExpandArgs {
     int32_t n_active;
     int32_t v_slices;
     int32_t n_proj;
+    int32_t count;   // work items of the launch (MFMA expand: 1-D grid of count x groups)
+    int32_t groups;  // column groups of all projections
     ExpandProj p[LORA_MAX_PROJ];
 };
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  The MFMA expand's 1-D grid (a multiple of 8) is remapped so that XCD x
+// takes the contiguous block x*G/8 .. (x+1)*G/8 - 1 of logical ids, ordered
+// item-major: all column groups of an item (which share its v rows) and the
+// neighbouring items of a segment (which share its B strips) then meet in
+// one L2 instead of being fetched again by every XCD.
+#define N_XCD 8
+__device__ __forceinline__ int xcd_block(int wg, int n_wg) { return (wg % N_XCD) * (n_wg / N_XCD) + wg / N_XCD; }
 
 // One workgroup = one work item (at most EXPAND_ROWS rows) x one 512-column
 // group of one projection; wave w owns columns [128w, 128w+128) of the
@@ -592,9 +603,12 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     constexpr int G = 4 * KS;  // groups of 8 ranks
     __shared__ int32_t s_rows[EXPAND_ROWS];          // the item's y row indices
     __shared__ u32x4_t s_v[EXPAND_ROWS * 2 * G];     // per row: (hi, lo) x G groups, XOR-swizzled
-    const lora_work_t it = args.work[args.begin + blockIdx.x];
+    const int lid = xcd_block((int)blockIdx.x, (int)gridDim.x);
+    if (lid >= args.count * args.groups) return;      // padding of the grid to a multiple of 8
+    const int item = lid / args.groups, cg = lid - item * args.groups;
+    const lora_work_t it = args.work[args.begin + item];
     int pi = 0;
-    while (pi + 1 < args.n_proj && (int)blockIdx.y >= args.p[pi + 1].cg_begin) ++pi;
+    while (pi + 1 < args.n_proj && cg >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
     // uniform over the workgroup, so returning here skips no barrier
     if (!(item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS) & (it.nrows <= EXPAND_ROWS))) return;
@@ -606,7 +620,7 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     // or store of the 16 lanes of a row group then covers 256 contiguous
     // bytes of the row (two whole lines).  MFMA c (c < 4) produces column
     // 4*li + c of the first half, MFMA c + 4 the same of the second half.
-    const int col0 = ((int)blockIdx.y - P.cg_begin) * 512 + wave * 128;
+    const int col0 = (cg - P.cg_begin) * 512 + wave * 128;
     const bool wave_ok = col0 < P.d_out;  // wave-uniform; waves past d_out only help with the LDS tables
     const bool hi_ok = col0 + 64 < P.d_out;
     const int nlo = wave_ok ? col0 + 4 * li : 0;         // in-bounds columns for halves past d_out
@@ -1406,10 +1420,13 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
             groups += (args.p[i].d_out + width - 1) / width;
         }
         args.begin = R.begin;
-        const dim3 grid((unsigned)R.count, (unsigned)groups);
-        err = first_error(err, shape == LV_E_BGMV ? launch(bgmv_expand_kernel, grid, dim3(WG), s, args)
-                                                  : launch(expand_table(R.variant % LV_RANK_CLASSES), grid, dim3(WG),
-                                                           s, args));
+        args.count = R.count;
+        args.groups = groups;
+        const unsigned n1 = (unsigned)((R.count * groups + N_XCD - 1) / N_XCD * N_XCD);
+        err = first_error(err, shape == LV_E_BGMV
+                                   ? launch(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG), s,
+                                            args)
+                                   : launch(expand_table(R.variant % LV_RANK_CLASSES), dim3(n1), dim3(WG), s, args));
     }
     return err == hipSuccess ? LORA_OK : LORA_EHIP;
 }
@@ -1464,10 +1481,13 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
                 groups += (ea.p[i].d_out + width - 1) / width;
             }
             ea.begin = R.begin;
-            const dim3 grid((unsigned)R.count, (unsigned)groups);
+            ea.count = R.count;
+            ea.groups = groups;
+            const unsigned n1 = (unsigned)((R.count * groups + N_XCD - 1) / N_XCD * N_XCD);
             err = first_error(err, shape == LV_E_BGMV
-                                       ? launch(bgmv_expand_kernel, grid, dim3(WG), s, ea)
-                                       : launch(expand_table(ev % LV_RANK_CLASSES), grid, dim3(WG), s, ea));
+                                       ? launch(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG),
+                                                s, ea)
+                                       : launch(expand_table(ev % LV_RANK_CLASSES), dim3(n1), dim3(WG), s, ea));
         } else {
             fa.begin = R.begin;
             bool uni = true;  // every wave's row offsets are uniform
