@@ -536,7 +536,10 @@ __device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const l
 // would lower the occupancy of the others).
 template <int MTW, int NTMAX, bool WHOLE_ROWS>
 __global__ __launch_bounds__(WG) void shrink_rows_kernel(ShrinkArgs args) {
-    constexpr int NBUF = NTMAX == 8 ? 2 : 3;        // LDS stages (two steps in flight below rank 64)
+    // LDS stages: three steps in flight below rank 64 (96 KiB: one workgroup
+    // per CU; measured against two and three stages: prefill -11%, vision
+    // -1%, 70B mix +1%), one above
+    constexpr int NBUF = NTMAX == 8 ? 2 : 4;
     __shared__ u32x4_t sX[NBUF * 64 * MTW * 8];    // NBUF buffers x 64*MTW rows x 8 pieces of 16 B
     __shared__ u32x4_t sA[NBUF * 16 * NTMAX * 8];  // NBUF buffers x 16*NT rank rows x 8 pieces
     const int ntasks = args.count * args.n_proj;
