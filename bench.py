@@ -32,6 +32,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--path 
                        [--no-cpu-baseline]
        python bench.py --workload tiny|prefill|vision|mix70b|mixture   (kernel timing of the other workloads)
        python bench.py --copy-calibration                             (counter calibration under rocprofv3)
+       python bench.py --rmw-ceiling                                  (in-place streaming rate of this HBM)
 """
 import argparse
 import hashlib
@@ -93,6 +94,30 @@ def copy_calibration():
     dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n}), flush=True)
+
+
+def rmw_ceiling(reps=24):
+    """The rate at which this device streams an in-place read-modify-write of
+    the merge's size (4 x W[4096x4096] bf16 = 128 MiB read and written), with
+    a plain library kernel (torch's elementwise add) and the Infinity Cache
+    cold: launches rotate over 4 such buffers (512 MiB).  The merge cannot
+    beat this stream by much: it moves the same bytes in the same pattern."""
+    import torch
+    n = 4 * 4096 * 4096
+    bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    for k in range(8):
+        bufs[k % 4].add_(1.0)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for k in range(reps):
+        ev[k].record()
+        bufs[k % 4].add_(1.0)
+    ev[reps].record()
+    torch.cuda.synchronize()
+    us = float(np.median([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(reps)]))
+    nbytes = 2 * n * 2
+    print(json.dumps({"rmw_bytes": nbytes, "us_median": round(us, 2), "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
 
 
 def delta_cost(W, row_adapter):
@@ -188,9 +213,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy (counter calibration under rocprofv3 --pmc) and exit")
+    ap.add_argument("--rmw-ceiling", action="store_true",
+                    help="time a plain in-place read-modify-write stream of the merge's size (cold) and exit")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration()
+    if args.rmw_ceiling:
+        return rmw_ceiling()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path is single-GPU by design (no sharding, no collectives); "
               "run it with --gpus 1", file=sys.stderr)

@@ -52,12 +52,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Compile-time tuning constants (measured on MI355X; the per-shape choices
 // are made at plan time from the tile table).
-#ifndef HETLORA_MERGE_PREFETCH
-#define HETLORA_MERGE_PREFETCH 2  // W passes kept in flight ahead of the one being computed
-#endif
-#ifndef HETLORA_MERGE_WAVES
-#define HETLORA_MERGE_WAVES 2     // minimum waves per SIMD the merge kernel is compiled for
-#endif
 #ifndef HETLORA_HW_CVT
 #define HETLORA_HW_CVT 1          // fp32 -> bf16 with the hardware convert (round to nearest even)
 #endif
@@ -1104,101 +1098,127 @@ struct MergeArgs {
     MergeMat m[LORA_MAX_MERGE];
 };
 
+// W passes the merge keeps in flight ahead of the one being computed.  The
+// kernel runs two waves per SIMD at every rank: its A operands take 32 VGPRs
+// per 32 ranks, 238 VGPRs in all at rank 128.
+constexpr int MERGE_PREFETCH = 2;
+
 // One workgroup = a 128 (rows n of W) x 512 (columns k) tile; wave w owns
-// columns [128w, 128w+128).  First operand: B rows (rank x n) transposed so
-// row slot i of MFMA c2 is n = nbase + 8*i + c2; second operand: A rows
+// columns [128w, 128w+128).  First MFMA operand: B rows (rank x n) transposed
+// so row slot i of MFMA c2 is n = nbase + 8*i + c2; second operand: A rows
 // transposed so column slot i of MFMA c is k = kbase + 8*i + c.  Lane (li,lg)
 // then owns W rows nbase + 8*(4*lg+e) + c2 at columns kbase + 8*li .. +7.
-// The wave walks its tile in 8 passes (one c2 each, 4 rows x 16 bytes per
-// lane); the adapter rows are loaded first, then the W loads of the first
-// passes, and every pass issues the loads of a later pass before it computes
-// and stores its own.
+//
+// Order of work: every wave first issues the W loads of its first passes (they
+// need no adapter data), then the adapter row offsets and rows.  The B strip is
+// the same for the four waves: wave w < KS loads and transposes rank group w
+// of it into LDS (one 1-KiB operand block per (group, c2)); each wave keeps
+// its own A operands in registers.  After the one barrier the wave walks its
+// tile in 8 passes (one c2 each, 4 rows x 16 bytes per lane), issuing the W
+// loads of a later pass before it computes and stores the current one.
+//
+// Rows past d_out: d_out - nbase is a multiple of 64, so row 8*(4*lg+e) + c2
+// of the tile is inside the matrix exactly when 8*(4*lg+e) is; such rows read
+// row c2 of the tile instead and are never stored.
 template <int KS>
-__global__ __launch_bounds__(WG, HETLORA_MERGE_WAVES) void merge_kernel(MergeArgs args) {
-    constexpr int PF = HETLORA_MERGE_PREFETCH;
+__global__ __launch_bounds__(WG, 2) void merge_kernel(MergeArgs args) {
+    constexpr int PF = MERGE_PREFETCH;
+    __shared__ u32x4_t s_bstrip[KS][8][64];
     const MergeMat& M = args.m[blockIdx.y];
     if ((int)blockIdx.x >= M.tiles) return;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int li = lane & 15, lg = lane >> 4;
     const int tn = blockIdx.x / M.tiles_k, tk = blockIdx.x % M.tiles_k;
     const int nbase = tn * 128, kbase = tk * 512 + wave * 128;
-    if (kbase >= M.d_in) return;  // no barrier in this kernel
+    const bool live = kbase < M.d_in;                  // wave-uniform
     const int k0 = kbase + 8 * li;
     const bool k_ok = k0 < M.d_in;
-    const int kc = k_ok ? k0 : kbase;                   // in-bounds column
+    const int kc = k_ok ? k0 : 0;                       // in-bounds column
     const int nn = nbase + 8 * li;
     const bool n_ok = nn < M.d_out;
     const int ncol = n_ok ? nn : nbase;                 // in-bounds column of B
 
-    // adapter rows: all row offsets, then all rows
-    int64_t ob[KS][8], oa[KS][8];
-    const int cb = ncol / M.B.chunk_len, ca = kc / M.A.chunk_len;
+    // W rows of this lane: pass c2 reads wrow[e] + c2 * ldw
+    bool row_ok[4];
+    uint16_t* wrow[4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int jj = min(32 * ks + 8 * lg + e, M.rank - 1);
-            ob[ks][e] = M.B.row_off[off_index(M.B, M.adapter, jj, cb)];
-            oa[ks][e] = M.A.row_off[off_index(M.A, M.adapter, jj, ca)];
-        }
-    issue_fence();
-    u32x4_t rb[KS][8], ra[KS][8];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            rb[ks][e] = ld16(M.B.pool + ob[ks][e] + (ncol - cb * M.B.chunk_len));
-            ra[ks][e] = ld16(M.A.pool + oa[ks][e] + (kc - ca * M.A.chunk_len));
-        }
-
-    // W: pass c2 covers rows nbase + 8*(4*lg+e) + c2 (rows past d_out read row 0 of the tile)
-    uint16_t* const wcol = M.W + kc;
-    auto wrow = [&](int c2, int e) {
-        const int n = nbase + 8 * (4 * lg + e) + c2;
-        return wcol + (int64_t)(n < M.d_out ? n : nbase) * M.ldw;
-    };
-    u32x4_t wv[PF + 1][4];
-#pragma unroll
-    for (int c2 = 0; c2 < PF; ++c2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wv[c2][e] = ld16(wrow(c2, e));
-
-    u32x4_t aop[KS][8], bop[KS][8];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        // rank slots past the rank and columns past the matrix were read at
-        // clamped addresses (no masked loads here: the adapter rows come from
-        // L2 and a masked load would serialise the batch); zero them
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const bool jok = 32 * ks + 8 * lg + e < M.rank;
-            rb[ks][e] = sel(jok && n_ok, rb[ks][e]);
-            ra[ks][e] = sel(jok && k_ok, ra[ks][e]);
-        }
-        transpose8x8(rb[ks], aop[ks]);
-        transpose8x8(ra[ks], bop[ks]);
+    for (int e = 0; e < 4; ++e) {
+        const int n = nbase + 8 * (4 * lg + e);
+        row_ok[e] = n < M.d_out;
+        wrow[e] = M.W + kc + (int64_t)(row_ok[e] ? n : nbase) * M.ldw;
     }
+    u32x4_t wv[PF + 1][4];
+    if (live) {
+#pragma unroll
+        for (int c2 = 0; c2 < PF; ++c2)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[c2][e] = ld16(wrow[e] + (int64_t)c2 * M.ldw);
+    }
+    issue_fence();
+
+    // adapter rows (no masked loads: rank slots past the rank and columns past
+    // the matrix read clamped addresses and are zeroed after the transpose)
+    const bool b_wave = wave < KS && 32 * wave < M.rank;   // wave-uniform
+    u32x4_t astrip[KS][8];
+    if (b_wave) {
+        const int cb = ncol / M.B.chunk_len;
+        int64_t ob[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            ob[e] = M.B.row_off[off_index(M.B, M.adapter, min(32 * wave + 8 * lg + e, M.rank - 1), cb)];
+        issue_fence();
+        u32x4_t rb[8], tb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rb[e] = ld16(M.B.pool + ob[e] + (ncol - cb * M.B.chunk_len));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rb[e] = sel(32 * wave + 8 * lg + e < M.rank && n_ok, rb[e]);
+        transpose8x8(rb, tb);
+#pragma unroll
+        for (int c2 = 0; c2 < 8; ++c2) s_bstrip[wave][c2][lane] = tb[c2];
+    }
+    if (live) {
+        const int ca = kc / M.A.chunk_len;
+        int64_t oa[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                oa[ks][e] = M.A.row_off[off_index(M.A, M.adapter, min(32 * ks + 8 * lg + e, M.rank - 1), ca)];
+        issue_fence();
+        u32x4_t ra[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ra[ks][e] = ld16(M.A.pool + oa[ks][e] + (kc - ca * M.A.chunk_len));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ra[ks][e] = sel(32 * ks + 8 * lg + e < M.rank && k_ok, ra[ks][e]);
+            transpose8x8(ra[ks], astrip[ks]);
+        }
+    }
+    __syncthreads();
+    if (!live) return;
 
 #pragma unroll
     for (int c2 = 0; c2 < 8; ++c2) {
         if (c2 + PF < 8)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[(c2 + PF) % (PF + 1)][e] = ld16(wrow(c2 + PF, e));
+            for (int e = 0; e < 4; ++e) wv[(c2 + PF) % (PF + 1)][e] = ld16(wrow[e] + (int64_t)(c2 + PF) * M.ldw);
         f32x4_t acc[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (32 * ks >= M.rank) continue;
-                acc[c] = mfma_bf16(aop[ks][c2], bop[ks][c], acc[c]);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            if (32 * ks >= M.rank) break;
+            const u32x4_t b = s_bstrip[ks][c2][lane];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = mfma_bf16(b, astrip[ks][c], acc[c]);
         }
         const u32x4_t* cur = wv[c2 % (PF + 1)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int n = nbase + 8 * (4 * lg + e) + c2;
-            if (!(k_ok && n < M.d_out)) continue;
+            if (!(k_ok && row_ok[e])) continue;
             u32x4_t o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1207,7 +1227,7 @@ __global__ __launch_bounds__(WG, HETLORA_MERGE_WAVES) void merge_kernel(MergeArg
                 const float hi = __builtin_fmaf(M.scale, acc[2 * q + 1][e], bf16_hi(w));
                 o[q] = pack_bf16(lo, hi);
             }
-            *reinterpret_cast<u32x4_t*>(wrow(c2, e)) = o;
+            *reinterpret_cast<u32x4_t*>(wrow[e] + (int64_t)c2 * M.ldw) = o;
         }
     }
 }
