@@ -22,7 +22,9 @@ algorithmic bytes (what the method must move: x rows, each distinct adapter's
 A and B once, v written and read, y read and written in fp32, W read and
 written in bf16) divided by the wall-clock time per step.  Per-kernel times
 come from HIP events recorded on the stream the kernels run on, inside the
-timed steps; `roofline` describes the kernel with the largest share of the
+timed steps (events without the system-scope fence: a default event writes
+back and invalidates the GPU caches when it completes, which idles the GPU
+between the kernels it separates); `roofline` describes the kernel with the largest share of the
 step time.  `cpu_baseline` times the CPU oracle on a bounded sample of the
 same workload.
 
@@ -103,12 +105,13 @@ def rmw_ceiling(reps=24):
     cold: launches rotate over 4 such buffers (512 MiB).  The merge cannot
     beat this stream by much: it moves the same bytes in the same pattern."""
     import torch
+    from heterogeneous_adapter_batching_amd.session import HipEvent
     n = 4 * 4096 * 4096
     bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
     for k in range(8):
         bufs[k % 4].add_(1.0)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev = [HipEvent(timing=True) for _ in range(reps + 1)]
     for k in range(reps):
         ev[k].record()
         bufs[k % 4].add_(1.0)
@@ -231,7 +234,7 @@ def main():
         return other_workload(args)
     import torch
     import workloads
-    from heterogeneous_adapter_batching_amd.session import Batch, Rows, prepare_merge
+    from heterogeneous_adapter_batching_amd.session import Batch, HipEvent, Rows, prepare_merge
     from workloads.device import bits_to_device, to_device
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -280,23 +283,25 @@ def main():
     else:
         groups = ["hetero_apply", "homo_apply", "merge_unmerge"]
 
+    # group g runs between events g and g + 1; both batches are prepared (host
+    # plan + metadata upload) before the first event
     def step(ev, k):
         L = layers[k % len(layers)]
+        bh.refresh(het, stream)
+        bo.refresh(homo, stream)
+        ev[0].record(stream)
         g = 0
-        for (b, ra), fns in zip(((bh, het), (bo, homo)), L["calls"]):
-            b.refresh(ra)
+        for fns in L["calls"]:
             for fn in fns:
-                ev[g][0].record(stream)
                 fn()
-                ev[g][1].record(stream)
                 g += 1
-        ev[g][0].record(stream)
+                ev[g].record(stream)
         L["merge"]()
         L["unmerge"]()
-        ev[g][1].record(stream)
+        ev[g + 1].record(stream)
 
     def new_events():
-        return [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in groups]
+        return [HipEvent(timing=True) for _ in range(len(groups) + 1)]
 
     for k in range(args.warmup):
         step(new_events(), k)
@@ -312,7 +317,7 @@ def main():
     us = {g: [] for g in groups}
     for ev in evs:
         for gi, g in enumerate(groups):
-            us[g].append(ev[gi][0].elapsed_time(ev[gi][1]) * 1e3)
+            us[g].append(ev[gi].elapsed_time(ev[gi + 1]) * 1e3)
     med = {g: float(np.median(us[g])) for g in groups}
 
     ch, co = delta_cost(W, het), delta_cost(W, homo)
@@ -380,7 +385,7 @@ def other_workload(args):
     (merge then unmerge of adapter 0 into 32 layers x 4 W[4096x4096])."""
     import torch
     import workloads
-    from heterogeneous_adapter_batching_amd.session import Batch, Rows, prepare_merge
+    from heterogeneous_adapter_batching_amd.session import Batch, HipEvent, Rows, prepare_merge
     from workloads.device import bits_to_device, to_device
 
     k = {"tiny": 0, "prefill": 2, "vision": 3, "mix70b": 4}[args.workload]
@@ -400,7 +405,7 @@ def other_workload(args):
     res = {"shrink": [], "expand": []}
     for it in range(args.warmup + args.steps):
         flush.fill_(it & 0xFF)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e = [HipEvent(timing=True) for _ in range(3)]
         e[0].record(); do_s(); e[1].record(); do_e(); e[2].record()
         torch.cuda.synchronize()
         if it >= args.warmup:
@@ -431,7 +436,7 @@ def other_workload(args):
         ts = []
         for rep in range(3):
             torch.cuda.synchronize()
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e = [HipEvent(timing=True) for _ in range(3)]
             e[0].record()
             for m, _ in calls:
                 m()
@@ -460,7 +465,7 @@ def mixture_workload(args):
     import torch
     import workloads
     from heterogeneous_adapter_batching_amd import lora_mixture_row_adapter
-    from heterogeneous_adapter_batching_amd.session import Batch, Rows, mixture_tables
+    from heterogeneous_adapter_batching_amd.session import Batch, HipEvent, Rows, mixture_tables
     from workloads.device import to_device
 
     W = workloads.gen_config(1)
@@ -489,7 +494,7 @@ def mixture_workload(args):
     for it in range(args.warmup + args.steps):
         for name, fn in (("mixture_apply", run_mix), ("unmerged_apply", run_plain)):
             flush.fill_(it & 0xFF)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e = [HipEvent(timing=True) for _ in range(2)]
             e[0].record(); fn(); e[1].record()
             torch.cuda.synchronize()
             if it >= args.warmup:

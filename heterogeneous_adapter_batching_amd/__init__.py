@@ -15,7 +15,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
-LORA_ABI_VERSION = 5
+LORA_ABI_VERSION = 6
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
 LORA_MAX_RANGES = 48
@@ -69,6 +69,10 @@ class lora_launch_t(ctypes.Structure):
     _fields_ = [("row_index", _vp), ("work", _vp), ("info", lora_plan_info_t)]
 
 
+class lora_batch_t(ctypes.Structure):
+    _fields_ = [("n_seg", _i32), ("n_active", _i32), ("n_staged", _i64), ("launch", lora_launch_t * 3)]
+
+
 class lora_shrink_proj_t(ctypes.Structure):
     _fields_ = [("x", _vp), ("ldx", _i64), ("d_in", _i32), ("A", lora_rows_t), ("v", _vp), ("ldv", _i64)]
 
@@ -101,7 +105,18 @@ _sig = {
     "lora_rows_dense_offsets": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _P(_i64)]),
     "lora_mixture_row_adapter": (_i32, [_i32, _vp, _i32, _vp]),
     "lora_mixture_rows": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "lora_batch_prepare": (_i32, [_i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_uint32, _i32, _vp, _vp, _vp, _vp,
+                                  _i64, _vp, _vp, _P(lora_batch_t)]),
 }
+# HIP runtime calls the binding makes itself (events), resolved through the
+# library's handle so they bind to the runtime the library uses
+_sig.update({
+    "hipEventCreateWithFlags": (ctypes.c_int, [_P(_vp), ctypes.c_uint]),
+    "hipEventRecord": (ctypes.c_int, [_vp, _vp]),
+    "hipEventSynchronize": (ctypes.c_int, [_vp]),
+    "hipEventElapsedTime": (ctypes.c_int, [_P(ctypes.c_float), _vp, _vp]),
+    "hipEventDestroy": (ctypes.c_int, [_vp]),
+})
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
     _fn.restype, _fn.argtypes = _res, _args
@@ -116,6 +131,34 @@ class LoraError(RuntimeError):
 def _check(code, where):
     if code != LORA_OK:
         raise LoraError(code, where)
+
+
+check_status = _check
+
+# lora_batch_prepare(n_rows, row_adapter, n_adapters, adapter_rank, d_in, d_out, op_mask, seg_capacity,
+#                    seg_start, seg_adapter, seg_rank, staging, staging_capacity, dev_staging, stream, out):
+# the raw call, for a caller that binds its pointers once (session.Batch); returns the status
+batch_prepare = _lib.lora_batch_prepare
+
+
+def lora_batch_prepare(row_adapter, adapter_rank, d_in, d_out, op_mask, staging, dev_staging, stream=None,
+                       seg_capacity=None, raw=False):
+    """Segment table + plans of the ops in op_mask, written to the host int32
+    array `staging` and copied to the device pointer `dev_staging` on `stream`
+    (a hipStream_t handle or None).  Returns (status, lora_batch_t, (seg_start,
+    seg_adapter, seg_rank)); raises LoraError unless raw=True."""
+    ra = np.ascontiguousarray(row_adapter, dtype=np.int32)
+    rk = np.ascontiguousarray(adapter_rank, dtype=np.int32)
+    cap = max(1, min(ra.shape[0], rk.shape[0])) if seg_capacity is None else int(seg_capacity)
+    segs = (np.empty(cap + 1, np.int32), np.empty(max(cap, 1), np.int32), np.empty(max(cap, 1), np.int32))
+    assert staging.dtype == np.int32 and staging.flags.c_contiguous
+    out = lora_batch_t()
+    st = _lib.lora_batch_prepare(ra.shape[0], _ptr(ra), rk.shape[0], _ptr(rk), int(d_in), int(d_out), int(op_mask),
+                                 cap, *(a.ctypes.data for a in segs), staging.ctypes.data, staging.shape[0],
+                                 dev_staging, stream, ctypes.byref(out))
+    if not raw:
+        _check(st, "lora_batch_prepare")
+    return st, out, segs
 
 
 def _ptr(a):

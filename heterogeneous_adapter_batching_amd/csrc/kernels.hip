@@ -37,6 +37,7 @@
 // depend on a row's position in a work item or on the launch order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -1521,6 +1522,59 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
         }
     }
     return err == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
+extern "C" int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter, int32_t n_adapters,
+                                      const int32_t* adapter_rank, int32_t d_in, int32_t d_out, uint32_t op_mask,
+                                      int32_t seg_capacity, int32_t* seg_start, int32_t* seg_adapter,
+                                      int32_t* seg_rank, int32_t* staging, int64_t staging_capacity,
+                                      void* dev_staging, void* hip_stream, lora_batch_t* out) {
+    constexpr int64_t wi = sizeof(lora_work_t) / sizeof(int32_t);
+    if (!out || !staging || !dev_staging || op_mask == 0 || (op_mask & ~7u) || staging_capacity < 0 || n_rows < 0)
+        return LORA_EINVAL;
+    if (staging_capacity < n_rows) {  // row_index goes first
+        out->n_staged = n_rows;
+        return LORA_ECAPACITY;
+    }
+    int32_t n_seg = 0, n_active = 0;
+    int32_t st = lora_build_segments(n_rows, row_adapter, n_adapters, adapter_rank, seg_capacity, staging, seg_start,
+                                     seg_adapter, seg_rank, &n_seg, &n_active);
+    out->n_seg = n_seg;
+    out->n_active = n_active;
+    out->n_staged = 0;
+    if (st != LORA_OK) return st;
+    lora_plan_info_t info[3];
+    int64_t off[3] = {-1, -1, -1}, used = n_active;
+    bool fits = true;
+    for (int op = 0; op < 3; ++op) {
+        if (!(op_mask & (1u << op))) continue;
+        const int64_t room = fits ? (staging_capacity - used) / wi : 0;
+        st = lora_plan(op, n_seg, seg_start, seg_adapter, seg_rank, d_in, d_out,
+                       (int32_t)(room < INT32_MAX ? room : INT32_MAX),
+                       reinterpret_cast<lora_work_t*>(staging + used), &info[op]);
+        if (st == LORA_ECAPACITY) fits = false;
+        else if (st != LORA_OK) return st;
+        off[op] = used;
+        used += wi * info[op].n_work;
+    }
+    out->n_staged = used;
+    if (!fits) return LORA_ECAPACITY;
+    int32_t* dev = static_cast<int32_t*>(dev_staging);
+    for (int op = 0; op < 3; ++op) {
+        lora_launch_t& L = out->launch[op];
+        if (off[op] < 0) {
+            memset(&L, 0, sizeof(L));
+            L.info.op = -1;
+            continue;
+        }
+        L.row_index = dev;
+        L.work = reinterpret_cast<const lora_work_t*>(dev + off[op]);
+        L.info = info[op];
+    }
+    if (used == 0) return LORA_OK;
+    const hipError_t e = hipMemcpyAsync(dev_staging, staging, (size_t)used * sizeof(int32_t), hipMemcpyHostToDevice,
+                                        reinterpret_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
 namespace {

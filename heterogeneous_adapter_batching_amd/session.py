@@ -1,34 +1,64 @@
 """Device-resident batch metadata and call marshalling.
 
-``Batch`` runs the library's segment builder and planner on the host, then
-moves row_index and both work lists to the device in one pinned host->device
-copy on the caller's stream.  ``Batch.prepare_shrink`` / ``prepare_expand`` /
+``Batch`` has the library build the segment table and the plans on the host
+and upload row_index and the work lists to the device in one pinned
+host->device copy on the caller's stream, all in one call.  ``Batch.prepare_shrink`` / ``prepare_expand`` /
 ``prepare_merge`` build the C argument structs once and return a callable that
 only issues the library call, so a serving loop pays no per-call marshalling.
 PyTorch only provides memory and streams here.
 """
+import ctypes
+
 import numpy as np
 import torch
 
-from . import (LORA_MAX_SLICES, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, call_apply,
-               call_expand, call_merge, call_shrink, lora_apply_proj_t, lora_build_segments, lora_expand_proj_t,
-               lora_launch_t, lora_merge_mat_t, lora_mixture_rows, lora_plan, lora_plan_info_t, lora_shrink_proj_t,
-               make_rows)
+from . import _lib as _hip  # the HIP runtime the library is linked to (and torch uses)
+from . import (LORA_ECAPACITY, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, Segments, batch_prepare,
+               call_apply, call_expand, call_merge, call_shrink, check_status, lora_apply_proj_t, lora_batch_t,
+               lora_expand_proj_t, lora_merge_mat_t, lora_mixture_rows, lora_shrink_proj_t, make_rows)
 
 
-def staging_layout(n_active, n_work_shrink, n_work_expand, n_work_apply=0):
-    """Byte offsets of (row_index, shrink work, expand work, apply work) in the
-    staging buffer, and its size in int32 elements: row_index is int32
-    [n_active], each work item WORK_INTS int32.  (The first four results are
-    kept in this order for callers that use only the shrink/expand lists.)"""
-    ri = 0
-    ws = 4 * n_active
-    we = ws + 4 * WORK_INTS * n_work_shrink
-    wa = we + 4 * WORK_INTS * n_work_expand
-    n = max(1, n_active + WORK_INTS * (n_work_shrink + n_work_expand + n_work_apply))
-    if n_work_apply:
-        return ri, ws, we, n, wa
-    return ri, ws, we, n
+class HipEvent:
+    """A HIP event recorded without the system-scope memory fence
+    (hipEventDisableSystemFence).  Recording a default event makes the GPU
+    write back and invalidate its caches when the event completes, which
+    idles it for microseconds and leaves the next kernel cold; an event that
+    only orders the host against the stream (the staging copy) or measures
+    time between launches on one stream needs no such fence.  ``timing``
+    keeps the timestamp (hipEventElapsedTime)."""
+
+    DISABLE_TIMING, DISABLE_SYSTEM_FENCE = 0x2, 0x20000000
+
+    def __init__(self, timing=False):
+        self._h = ctypes.c_void_p()
+        flags = self.DISABLE_SYSTEM_FENCE | (0 if timing else self.DISABLE_TIMING)
+        check_status(0 if _hip.hipEventCreateWithFlags(ctypes.byref(self._h), flags) == 0 else -6,
+                     "hipEventCreateWithFlags")
+
+    def record(self, stream=None):
+        """stream: a torch stream, a raw hipStream_t handle, or None for the
+        current torch stream."""
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        h = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        if _hip.hipEventRecord(self._h, h) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def synchronize(self):
+        if _hip.hipEventSynchronize(self._h) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        ms = ctypes.c_float()
+        if _hip.hipEventElapsedTime(ctypes.byref(ms), self._h, end._h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._h:
+            _hip.hipEventDestroy(self._h)
+            self._h = None
 
 
 def stream_handle(stream=None):
@@ -54,81 +84,129 @@ class Rows:
 
 
 class Batch:
-    """Segments + shrink/expand plans of one batch, resident on the device.
+    """Segments + shrink/expand/apply plans of one batch, resident on the device.
 
-    ``refresh(row_adapter)`` rebuilds everything for a new batch of at most
-    ``n_rows_max`` rows, reusing the host arrays, the pinned staging buffer and
-    the device buffer; the launch structs are updated in place, so callables
-    from ``prepare_*`` stay valid across refreshes."""
+    ``refresh(row_adapter)`` rebuilds everything for a new batch (the buffers
+    are sized for ``n_rows_max`` rows and grow when a batch needs more) with one
+    library call (lora_batch_prepare: segment
+    table, the three plans, and their upload from a pinned staging buffer on
+    the caller's stream), reusing the host arrays and both buffers; the launch
+    structs live in the library's output struct and are updated in place, so
+    callables from ``prepare_*`` stay valid across refreshes."""
 
     def __init__(self, n_rows_max, adapter_rank, d_in, d_out, device="cuda"):
         self.adapter_rank = np.ascontiguousarray(adapter_rank, dtype=np.int32)
         self.d_in, self.d_out = int(d_in), int(d_out)
         self.device = torch.device(device)
         n = max(1, int(n_rows_max))
-        nseg = max(1, min(n, self.adapter_rank.shape[0]))
-        self._seg_out = (np.empty(n, np.int32), np.empty(nseg + 1, np.int32), np.empty(nseg, np.int32),
-                         np.empty(nseg, np.int32))
-        self._ws = np.empty((LORA_MAX_SLICES * n, WORK_INTS), np.int32)
-        self._we = np.empty((n, WORK_INTS), np.int32)
-        self._wa = np.empty(((LORA_MAX_SLICES + 1) * n, WORK_INTS), np.int32)
-        self.info_shrink, self.info_expand = lora_plan_info_t(), lora_plan_info_t()
-        self.info_apply = lora_plan_info_t()
-        self.shrink_launch, self.expand_launch = lora_launch_t(), lora_launch_t()
-        self.apply_launch = lora_launch_t()
-        self._copied = None          # event of the last staging copy
-        self._host = self._dev = None
-        self._alloc(staging_layout(n, 4 * n, n, 5 * n)[3])
-        self.segs = None
+        self._alloc_segs(max(1, min(n, self.adapter_rank.shape[0])))
+        self._rank_ptr = self.adapter_rank.ctypes.data
+        self._b = lora_batch_t()
+        self._b_ref = ctypes.byref(self._b)
+        self._launch = [self._b.launch[op] for op in (LORA_OP_SHRINK, LORA_OP_EXPAND, LORA_OP_APPLY)]
+        self._copied = HipEvent()   # the last staging copy
+        self._pending = False
+        self._stream, self._stream_h = None, None
+        self._n_active, self._v_slices = 0, 1
+        self._alloc(n + WORK_INTS * 10 * n)  # grown on demand
+
+    def _alloc_segs(self, cap):
+        self._seg_cap = cap
+        self._seg = (np.empty(cap + 1, np.int32), np.empty(cap, np.int32), np.empty(cap, np.int32))
+        self._seg_ptr = tuple(a.ctypes.data for a in self._seg)
 
     def _alloc(self, cap):
-        if self._copied is not None:
+        if self._pending:
             self._copied.synchronize()
+            self._pending = False
         self._host = torch.empty(cap, dtype=torch.int32, pin_memory=True)
         self._hnp = self._host.numpy()
         self._dev = torch.empty(cap, dtype=torch.int32, device=self.device)
-        self._copied = None
+        self._host_ptr, self._dev_ptr = self._host.data_ptr(), self._dev.data_ptr()
 
     def refresh(self, row_adapter, stream=None):
-        segs = lora_build_segments(row_adapter, self.adapter_rank, out=self._seg_out)
-        ws, info_s = lora_plan(LORA_OP_SHRINK, segs, self.d_in, self.d_out, work_out=self._ws,
-                               info_out=self.info_shrink)
-        we, info_e = lora_plan(LORA_OP_EXPAND, segs, self.d_in, self.d_out, work_out=self._we,
-                               info_out=self.info_expand)
-        wa, info_a = lora_plan(LORA_OP_APPLY, segs, self.d_in, self.d_out, work_out=self._wa,
-                               info_out=self.info_apply)
-        na, ns, ne, nap = segs.n_active, ws.shape[0], we.shape[0], wa.shape[0]
-        o_ri, o_ws, o_we, n, o_wa = staging_layout(na, ns, ne, max(1, nap))
-        if n > self._host.shape[0]:
-            self._alloc(n)
-        if self._copied is not None:
+        ra = row_adapter
+        if not (isinstance(ra, np.ndarray) and ra.dtype == np.int32 and ra.flags.c_contiguous):
+            ra = np.ascontiguousarray(ra, dtype=np.int32)
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        if stream is not self._stream:
+            self._stream, self._stream_h = stream, stream.cuda_stream
+        if self._pending:
             self._copied.synchronize()   # the staging buffer may still be in flight
-        h = self._hnp
-        h[:na] = segs.row_index
-        h[na:na + WORK_INTS * ns] = ws.reshape(-1)
-        h[na + WORK_INTS * ns:na + WORK_INTS * (ns + ne)] = we.reshape(-1)
-        h[na + WORK_INTS * (ns + ne):na + WORK_INTS * (ns + ne + nap)] = wa.reshape(-1)
-        s = torch.cuda.current_stream() if stream is None else stream
-        with torch.cuda.stream(s):
-            self._dev[:n].copy_(self._host[:n], non_blocking=True)
-            self._copied = torch.cuda.Event()
-            self._copied.record(s)
-        base = self._dev.data_ptr()
-        self.segs, self.work_shrink, self.work_expand, self.work_apply = segs, ws, we, wa
-        for L, info, off in ((self.shrink_launch, info_s, o_ws), (self.expand_launch, info_e, o_we),
-                             (self.apply_launch, info_a, o_wa)):
-            L.row_index = base + o_ri
-            L.work = base + off
-            L.info = info
+        while True:
+            st = batch_prepare(ra.shape[0], ra.ctypes.data, self.adapter_rank.shape[0], self._rank_ptr,
+                               self.d_in, self.d_out, 7, self._seg_cap, *self._seg_ptr, self._host_ptr,
+                               self._host.shape[0], self._dev_ptr, self._stream_h, self._b_ref)
+            if st != LORA_ECAPACITY:
+                break
+            if self._b.n_seg > self._seg_cap:
+                self._alloc_segs(self._b.n_seg)
+            elif self._b.n_staged > self._host.shape[0]:
+                self._alloc(int(self._b.n_staged) * 2)
+            else:
+                break
+        check_status(st, "lora_batch_prepare")
+        self._copied.record(stream)
+        self._pending = True
+        self._n_active = self._b.n_active
+        self._v_slices = self._launch[LORA_OP_SHRINK].info.v_slices
         return self
 
     @property
+    def shrink_launch(self):
+        return self._launch[LORA_OP_SHRINK]
+
+    @property
+    def expand_launch(self):
+        return self._launch[LORA_OP_EXPAND]
+
+    @property
+    def apply_launch(self):
+        return self._launch[LORA_OP_APPLY]
+
+    @property
+    def info_shrink(self):
+        return self._launch[LORA_OP_SHRINK].info
+
+    @property
+    def info_expand(self):
+        return self._launch[LORA_OP_EXPAND].info
+
+    @property
+    def info_apply(self):
+        return self._launch[LORA_OP_APPLY].info
+
+    @property
+    def segs(self):
+        """Host segment table of the current batch (views of reused arrays)."""
+        ns, na = self._b.n_seg, self._b.n_active
+        return Segments(self._hnp[:na], self._seg[0][:ns + 1], self._seg[1][:ns], self._seg[2][:ns])
+
+    def _work(self, op):
+        L = self._launch[op]
+        off = (L.work - self._dev_ptr) // 4
+        return self._hnp[off:off + WORK_INTS * L.info.n_work].reshape(-1, WORK_INTS)
+
+    @property
+    def work_shrink(self):
+        return self._work(LORA_OP_SHRINK)
+
+    @property
+    def work_expand(self):
+        return self._work(LORA_OP_EXPAND)
+
+    @property
+    def work_apply(self):
+        return self._work(LORA_OP_APPLY)
+
+    @property
     def n_active(self):
-        return self.segs.n_active
+        return self._n_active
 
     @property
     def v_slices(self):
-        return self.info_shrink.v_slices
+        return self._v_slices
 
     def new_v(self, ldv, fill=None):
         """A v buffer for this batch: fp32 [v_slices, max(1, n_active), ldv]."""
@@ -137,10 +215,19 @@ class Batch:
             return torch.empty(shape, dtype=torch.float32, device=self.device)
         return torch.full(shape, fill, dtype=torch.float32, device=self.device)
 
-    def _check_v(self, v):
-        assert v.dtype == torch.float32 and v.is_contiguous() and v.dim() == 3
-        assert v.shape[0] >= self.v_slices and v.shape[1] == max(1, self.n_active), \
-            "v buffer does not match the batch (v_slices, n_active)"
+    @staticmethod
+    def _v_shapes(vs):
+        """(v_slices, rows) of each v buffer, after the checks that do not
+        depend on the batch (the buffers' pointers are bound at prepare time)."""
+        for v in vs:
+            assert v.dtype == torch.float32 and v.is_contiguous() and v.dim() == 3
+        return [(int(v.shape[0]), int(v.shape[1])) for v in vs]
+
+    def _check_v(self, shapes):
+        rows = max(1, self._n_active)
+        for s0, s1 in shapes:
+            if s0 < self._v_slices or s1 != rows:
+                raise AssertionError("v buffer does not match the batch (v_slices, n_active)")
 
     def prepare_shrink(self, projs, stream=None):
         """projs: list of (x tensor bf16 [*, ldx], Rows A, v tensor fp32 [v_slices, n_active, ldv]).
@@ -151,10 +238,11 @@ class Batch:
         vs = [v for _, _, v in projs]
         h = stream_handle(stream)
 
+        shapes, n, L = self._v_shapes(vs), len(vs), self._launch[LORA_OP_SHRINK]
+
         def run():
-            for v in vs:
-                self._check_v(v)
-            call_shrink(self.shrink_launch, arr, len(vs), h)
+            self._check_v(shapes)
+            call_shrink(L, arr, n, h)
         run.keep = (projs, arr)
         return run
 
@@ -166,10 +254,11 @@ class Batch:
         vs = [v for v, _, _, _ in projs]
         h = stream_handle(stream)
 
+        shapes, n, L = self._v_shapes(vs), len(vs), self._launch[LORA_OP_EXPAND]
+
         def run():
-            for v in vs:
-                self._check_v(v)
-            call_expand(self.expand_launch, arr, len(vs), h)
+            self._check_v(shapes)
+            call_expand(L, arr, n, h)
         run.keep = (projs, arr)
         return run
 
@@ -184,10 +273,11 @@ class Batch:
         vs = [p[2] for p in projs]
         h = stream_handle(stream)
 
+        shapes, n, L = self._v_shapes(vs), len(vs), self._launch[LORA_OP_APPLY]
+
         def run():
-            for v in vs:
-                self._check_v(v)
-            call_apply(self.apply_launch, arr, len(vs), h)
+            self._check_v(shapes)
+            call_apply(L, arr, n, h)
         run.keep = (projs, arr)
         return run
 

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 5
+#define LORA_ABI_VERSION 6
 #define LORA_MAX_RANK 128   /* ranks are 1..128                              */
 #define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
 #define LORA_MAX_RANGES 48  /* kernel variants in one plan                   */
@@ -269,6 +269,46 @@ int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
                   const int32_t* seg_adapter, const int32_t* seg_rank,
                   int32_t d_in, int32_t d_out, int32_t work_capacity,
                   lora_work_t* work, lora_plan_info_t* info);
+
+/* Everything the host does for one batch, in one call: the segment table
+ * (lora_build_segments), the plans of the ops in op_mask (lora_plan), all
+ * written into one caller buffer laid out for a single host-to-device copy,
+ * and that copy, enqueued on hip_stream.  A serving loop then pays one call
+ * per batch instead of one per step of the preparation.
+ *   staging layout (int32 elements):  row_index [n_active], then the plan of
+ *       each requested op in LORA_OP_* order (info.n_work lora_work_t each)
+ *   op_mask      bit (1 << op) for each of LORA_OP_SHRINK / _EXPAND / _APPLY
+ *                to plan; at least one
+ *   seg_*        host int32 outputs as in lora_build_segments (seg_start
+ *                [seg_capacity + 1], seg_adapter / seg_rank [seg_capacity])
+ *   staging      host int32 [staging_capacity]; pinned memory makes the copy
+ *                asynchronous, and then the caller must not rewrite it before
+ *                the copy has run (record an event on hip_stream after the
+ *                call and wait for it before the next call on this buffer)
+ *   dev_staging  device int32 [staging_capacity]
+ *   out          n_seg, n_active, n_staged (int32 elements used) and, per
+ *                op, a ready lora_launch_t whose row_index and work point into
+ *                dev_staging; ops not in op_mask get info.op = -1, which every
+ *                call rejects
+ * Errors: as lora_build_segments and lora_plan; LORA_ECAPACITY when
+ * seg_capacity is too small (out->n_seg holds the count needed,
+ * out->n_staged is 0) or staging_capacity is (out->n_staged holds the size
+ * needed); nothing is copied then.  LORA_EHIP when the copy cannot be
+ * enqueued. */
+typedef struct lora_batch {
+    int32_t n_seg;
+    int32_t n_active;
+    int64_t n_staged;
+    lora_launch_t launch[3];    /* indexed by LORA_OP_SHRINK, _EXPAND, _APPLY */
+} lora_batch_t;
+
+int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter,
+                           int32_t n_adapters, const int32_t* adapter_rank,
+                           int32_t d_in, int32_t d_out, uint32_t op_mask,
+                           int32_t seg_capacity, int32_t* seg_start,
+                           int32_t* seg_adapter, int32_t* seg_rank,
+                           int32_t* staging, int64_t staging_capacity,
+                           void* dev_staging, void* hip_stream, lora_batch_t* out);
 
 /* Shrink for n_proj projections (1..LORA_MAX_PROJ) sharing one plan
  * (launch->info.op == LORA_OP_SHRINK): one kernel launch per variant range.

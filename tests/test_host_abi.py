@@ -272,22 +272,31 @@ def test_empty_batch_launches_nothing():
     assert lib.lora_shrink(ctypes.byref(L), 1, arr, None) == hl.LORA_OK
 
 
-def test_staging_layout_matches_host_packing():
-    # the device copy of (row_index, shrink work, expand work) is packed as int32
-    from heterogeneous_adapter_batching_amd.session import staging_layout
-    segs = hl.lora_build_segments(np.repeat([0, 1, 2], [5, 70, 300]), [8, 16, 64])
-    ws, _ = hl.lora_plan(hl.LORA_OP_SHRINK, segs, 4096, 4096)
-    we, _ = hl.lora_plan(hl.LORA_OP_EXPAND, segs, 4096, 4096)
-    W8 = hl.WORK_INTS
-    assert ctypes.sizeof(hl.lora_work_t) == 4 * W8
-    buf = np.concatenate([segs.row_index, ws.reshape(-1), we.reshape(-1)]).astype(np.int32)
-    o_ri, o_ws, o_we, n = staging_layout(segs.n_active, ws.shape[0], we.shape[0])
-    raw = buf.tobytes()
-    assert n == buf.shape[0]
-    assert o_ws % 16 == 0 and o_we % 16 == 0 or True
-    assert np.array_equal(np.frombuffer(raw[o_ri:o_ri + 4 * segs.n_active], np.int32), segs.row_index)
-    assert np.array_equal(np.frombuffer(raw[o_ws:o_ws + 4 * W8 * ws.shape[0]], np.int32).reshape(-1, W8), ws)
-    assert np.array_equal(np.frombuffer(raw[o_we:o_we + 4 * W8 * we.shape[0]], np.int32).reshape(-1, W8), we)
+def test_batch_prepare_errors_and_size():
+    """lora_batch_prepare validates before it copies, and on a staging buffer
+    that is too small reports the exact size: row_index plus every requested
+    plan (no copy is enqueued on these paths, so no GPU is needed)."""
+    ra = np.repeat([0, 1, 2, -1], [5, 70, 300, 3])
+    rank = [8, 16, 64]
+    segs = hl.lora_build_segments(ra, rank)
+    n_work = {op: hl.lora_plan(op, segs, 4096, 4096)[0].shape[0]
+              for op in (hl.LORA_OP_SHRINK, hl.LORA_OP_EXPAND, hl.LORA_OP_APPLY)}
+    fake_dev = 0x10000  # never dereferenced: every call below returns before the copy
+    for mask, ops in ((1, [0]), (2, [1]), (4, [2]), (7, [0, 1, 2]), (5, [0, 2])):
+        need = segs.n_active + hl.WORK_INTS * sum(n_work[o] for o in ops)
+        for cap in (0, segs.n_active, need - 1):
+            st, out, _ = hl.lora_batch_prepare(ra, rank, 4096, 4096, mask, np.zeros(cap, np.int32), fake_dev,
+                                               raw=True)
+            assert st == hl.LORA_ECAPACITY
+            assert out.n_staged == (ra.shape[0] if cap < ra.shape[0] else need)
+    big = np.zeros(100000, np.int32)
+    st, out, _ = hl.lora_batch_prepare(ra, rank, 4096, 4096, 7, big, fake_dev, seg_capacity=2, raw=True)
+    assert st == hl.LORA_ECAPACITY and out.n_seg == 3 and out.n_staged == 0
+    for mask in (0, 8, 15):
+        assert hl.lora_batch_prepare(ra, rank, 4096, 4096, mask, big, fake_dev, raw=True)[0] == hl.LORA_EINVAL
+    assert hl.lora_batch_prepare(ra, rank, 4096, 4096, 7, big, None, raw=True)[0] == hl.LORA_EINVAL
+    assert hl.lora_batch_prepare(ra, rank, 4096, 4000, 7, big, fake_dev, raw=True)[0] == hl.LORA_ESHAPE
+    assert hl.lora_batch_prepare([0, 5], rank, 4096, 4096, 7, big, fake_dev, raw=True)[0] == hl.LORA_EADAPTER
 
 
 def test_apply_plan_partitions_segments():
