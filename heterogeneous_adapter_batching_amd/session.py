@@ -56,9 +56,10 @@ class HipEvent:
         return ms.value
 
     def __del__(self):
-        if self._h:
+        # at interpreter exit the module globals may already be gone
+        if self._h and _hip is not None:
             _hip.hipEventDestroy(self._h)
-            self._h = None
+        self._h = None
 
 
 def stream_handle(stream=None):
