@@ -207,6 +207,39 @@ def test_merge_shapes_parity(d_out, d_in, r):
     assert np.linalg.norm(w2 - w0) / np.linalg.norm(w0) <= 4e-3
 
 
+def test_merge_mixed_launch():
+    """One launch merges matrices of different shapes and ranks: the launch
+    compiles for its largest rank (128, four 32-rank groups), each matrix stops
+    at its own rank, and the tiles past d_in (waves with no columns still load
+    their share of the B strip) and past d_out are partial."""
+    from heterogeneous_adapter_batching_amd.session import merge, unmerge
+    from workloads.device import bits_to_device
+    rng = np.random.default_rng(77)
+    specs = [(192, 704, 128, "dense"), (576, 320, 40, "paged"), (1024, 1536, 5, "dense"), (64, 192, 97, "paged")]
+    mats, refs, keep = [], [], []
+    for i, (d_out, d_in, r, layout) in enumerate(specs):
+        W = workloads.gen_custom(300 + i, [0], np.array([r], np.int32), d_in, d_out, layout=layout, page_elems=128)
+        dw = to_device(W)
+        p, dp = W.projections[0], dw.projections[0]
+        Wb = to_bf16_bits(rng.standard_normal((d_out, d_in)).astype(np.float32) / np.sqrt(d_in))
+        Wt = bits_to_device(Wb)
+        mats.append((Wt, rows_of(dw.pool, p.A, dp.A_off), rows_of(dw.pool, p.B, dp.B_off), 0, r, 1.5))
+        Aa = oracle.gather_rows_ref(W.pool, p.A.row_off, p.A.max_rank, p.A.row_len, p.A.chunk_len, 0, r)
+        Ba = oracle.gather_rows_ref(W.pool, p.B.row_off, p.B.max_rank, p.B.row_len, p.B.chunk_len, 0, r)
+        refs.append((Wb, Aa, Ba))
+        keep.append(dw)
+    merge(mats)
+    torch.cuda.synchronize()
+    merged = [m[0].cpu().numpy().view(np.uint16).copy() for m in mats]
+    for (d_out, d_in, r, _), got, (Wb, Aa, Ba) in zip(specs, merged, refs):
+        _say("mixed merge", d_out, d_in, r, check_merge_bits(got, Wb, Aa, Ba, 1.5))
+    unmerge(mats)
+    torch.cuda.synchronize()
+    for m, got, (Wb, Aa, Ba) in zip(mats, merged, refs):
+        back = m[0].cpu().numpy().view(np.uint16)
+        check_merge_bits(back, got, Aa, Ba, -1.5, min_equal=0.999)
+
+
 # ------------------------------------------------------------------ lora_apply (fused decode rows)
 def _apply_check(W, ra=None):
     from gpu_helpers import run_apply
