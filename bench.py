@@ -33,6 +33,7 @@ With --path split the step calls lora_shrink and lora_expand instead.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--path apply|split]
                        [--no-cpu-baseline]
        python bench.py --workload tiny|prefill|vision|mix70b|mixture   (kernel timing of the other workloads)
+       python bench.py --workload prefill|vision --shared-x           (the same with q/k/v reading one x)
        python bench.py --copy-calibration                             (counter calibration under rocprofv3)
        python bench.py --rmw-ceiling                                  (in-place streaming rate of this HBM)
 """
@@ -131,8 +132,11 @@ def delta_cost(W, row_adapter):
     r_act = W.adapter_rank[act].astype(np.int64)
     r_dis = W.adapter_rank[distinct].astype(np.int64)
     cost = {"shrink_bytes": 0, "expand_bytes": 0, "flops": 0}
+    seen_x = set()  # projections that share one x read it once
     for p in W.projections:
-        cost["shrink_bytes"] += act.size * p.d_in * 2 + int(r_dis.sum()) * p.d_in * 2 + int(r_act.sum()) * 4
+        x_bytes = 0 if id(p.x) in seen_x else act.size * p.d_in * 2
+        seen_x.add(id(p.x))
+        cost["shrink_bytes"] += x_bytes + int(r_dis.sum()) * p.d_in * 2 + int(r_act.sum()) * 4
         cost["expand_bytes"] += int(r_act.sum()) * 4 + int(r_dis.sum()) * p.d_out * 2 + act.size * p.d_out * 8
         cost["flops"] += int(2 * r_act.sum() * (p.d_in + p.d_out))
     return cost
@@ -214,6 +218,8 @@ def main():
     ap.add_argument("--path", default="apply", choices=["apply", "split"],
                     help="apply (default): lora_apply, one-row segments fused; split: lora_shrink then lora_expand")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared-x", action="store_true",
+                    help="with --workload prefill|vision: q, k and v take one x (the layer input), o its own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy (counter calibration under rocprofv3 --pmc) and exit")
     ap.add_argument("--rmw-ceiling", action="store_true",
@@ -389,7 +395,11 @@ def other_workload(args):
     from workloads.device import bits_to_device, to_device
 
     k = {"tiny": 0, "prefill": 2, "vision": 3, "mix70b": 4}[args.workload]
-    W = workloads.gen_config(k, n_layers=32) if k == 3 else workloads.gen_config(k)
+    kw = {"n_layers": 32} if k == 3 else {}
+    if getattr(args, "shared_x", False):
+        assert k in (2, 3), "--shared-x applies to the prefill and vision workloads (q/k/v share x)"
+        kw["shared_qkv"] = True
+    W = workloads.gen_config(k, **kw)
     dw = to_device(W)
     rows = lambda desc, off: Rows(dw.pool, off, desc.n_adapters, desc.max_rank, desc.row_len, desc.chunk_len)
     A = [rows(p.A, d.A_off) for p, d in zip(W.projections, dw.projections)]
@@ -412,7 +422,8 @@ def other_workload(args):
             res["shrink"].append(e[0].elapsed_time(e[1]) * 1e3)
             res["expand"].append(e[1].elapsed_time(e[2]) * 1e3)
     c = delta_cost(W, W.row_adapter)
-    out = {"workload": args.workload, "rows": W.n_rows, "active": int((W.row_adapter >= 0).sum()),
+    out = {"workload": args.workload + ("+shared-x" if getattr(args, "shared_x", False) else ""),
+           "rows": W.n_rows, "active": int((W.row_adapter >= 0).sum()),
            "segments": b.segs.n_seg, "layout": W.layout, "kernels": {}}
     for g, nb, fl in (("shrink", c["shrink_bytes"], c["flops"] * 0.5), ("expand", c["expand_bytes"], c["flops"] * 0.5)):
         us = float(np.median(res[g]))

@@ -179,6 +179,11 @@ struct ShrinkArgs {
     int32_t v_slices;
     int32_t count;   // work items of the launch (persistent kernel: tasks = count x n_proj)
     int32_t n_proj;
+    // projections that share x, for the grouped long-segment kernel: group g
+    // is gproj[gbeg[g]] .. gproj[gbeg[g+1] - 1]
+    int32_t n_groups;
+    int8_t gbeg[LORA_MAX_PROJ + 1];
+    int8_t gproj[LORA_MAX_PROJ];
     ShrinkProj p[LORA_MAX_PROJ];
 };
 
@@ -387,19 +392,25 @@ __device__ __forceinline__ void step_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int MTW, int NT, bool WHOLE_ROWS, int NBUF>
-__device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const lora_work_t& it, const ShrinkProj& P,
-                                                 int proj, u32x4_t* sX, u32x4_t* sA) {
+// One task: item `it` for the G projections pj[0..G) that share x (the same
+// x, ldx and d_in): each x tile is loaded once and multiplied by the G A
+// tiles (a q/k/v group reads x once instead of three times).  G = 1 is the
+// plain per-projection task.  The LDS holds GS A buffers per stage.
+template <int MTW, int NT, int G, int GS, bool WHOLE_ROWS, int NBUF>
+__device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const lora_work_t& it, const int (&pj)[4],
+                                                 u32x4_t* sX, u32x4_t* sA) {
     constexpr int ROWS = 64 * MTW;           // rows of the item tile
     constexpr int XBUF = ROWS * 8;           // x pieces per LDS buffer
-    constexpr int ABUF = 16 * NT * 8;        // A pieces per LDS buffer
+    constexpr int ABUF = 16 * NT * 8;        // A pieces per LDS buffer and projection (NT rank tiles)
+    constexpr int ASTRIDE = GS * ABUF;       // A pieces per LDS stage
     constexpr int XW = XBUF / WG;            // x loads per lane (wave-loads per wave)
-    constexpr int AWT = ABUF / 64;           // A wave-loads of the workgroup
-    constexpr int AW = AWT >= 4 ? AWT / 4 : 1;  // A wave-loads per wave
-    constexpr int DPW = XW + AW;             // loads per wave per step
+    constexpr int AWT = ABUF / 64;           // A wave-loads of the workgroup, per projection
+    constexpr int AW = AWT >= 4 ? AWT / 4 : 1;  // A wave-loads per wave, per projection
+    constexpr int DPW = XW + G * AW;         // loads per wave per step
     const int t = threadIdx.x, lane = t & 63, wave = wave_id();
     const int li = lane & 15, lg = lane >> 4;
     const int mbase = wave * 16 * MTW;
+    const ShrinkProj& P0 = args.p[pj[0]];
 
     // x sources: wave-load j of this wave fills slots (XW*wave + j)*64 + lane
     const uint16_t* xsrc[XW];
@@ -408,57 +419,69 @@ __device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const l
         const int row = (XW * wave + j) * 8 + (lane >> 3);
         const int pc = (lane & 7) ^ (row & 7);
         // rows past the item read its last row (results not stored)
-        xsrc[j] = P.x + (int64_t)args.row_index[it.row0 + min(row, it.nrows - 1)] * P.ldx + 8 * pc;
+        xsrc[j] = P0.x + (int64_t)args.row_index[it.row0 + min(row, it.nrows - 1)] * P0.ldx + 8 * pc;
     }
-    const int kblocks = P.d_in / 64;
+    const int kblocks = P0.d_in / 64;
     const int kbeg = (int)((int64_t)it.kslice * kblocks / it.nslices);
     const int kend = (int)((int64_t)(it.kslice + 1) * kblocks / it.nslices);
-    const int cblocks = P.A.chunk_len / 64;
     // A sources: wave-load j of this wave fills slots aw*64 + lane, aw =
     // (AW*wave + j) mod AWT (rank row aw*8 + lane/8, clamped to the rank);
-    // with whole A
-    // rows in one chunk the row pointers are fixed, otherwise each step looks
-    // its chunk up
-    const bool one_chunk = WHOLE_ROWS || kbeg / cblocks == (kend - 1) / cblocks;
-    int arow[AW], apc[AW];
-    const uint16_t* asrc[AW];
+    // with whole A rows in one chunk the row pointers are fixed, otherwise
+    // each step looks its chunk up
+    int arow[AW], apc[AW], cblocks[G];
+    bool one_chunk = true;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        cblocks[g] = args.p[pj[g]].A.chunk_len / 64;
+        one_chunk = one_chunk && (WHOLE_ROWS || kbeg / cblocks[g] == (kend - 1) / cblocks[g]);
+    }
+    const uint16_t* asrc[G][AW];
 #pragma unroll
     for (int j = 0; j < AW; ++j) {
         const int row = ((AW * wave + j) % AWT) * 8 + (lane >> 3);
         arow[j] = min(row, it.rank - 1);
         apc[j] = (lane & 7) ^ (row & 7);
-        const int c0 = kbeg / cblocks;
-        // element offset of global K step 0 in this chunk's addressing (the
-        // loads add k*64 for k inside the chunk, so every address is in it)
-        asrc[j] = P.A.pool + (P.A.row_off[off_index(P.A, it.adapter, arow[j], c0)] -
-                              (int64_t)c0 * cblocks * 64 + 8 * apc[j]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const Rows& A = args.p[pj[g]].A;
+            const int c0 = kbeg / cblocks[g];
+            // element offset of global K step 0 in this chunk's addressing
+            // (the loads add k*64 for k inside the chunk, so every address
+            // is in it)
+            asrc[g][j] = A.pool + (A.row_off[off_index(A, it.adapter, arow[j], c0)] -
+                                   (int64_t)c0 * cblocks[g] * 64 + 8 * apc[j]);
+        }
     }
-    f32x4_t acc[MTW][NT];
+    f32x4_t acc[G][MTW][NT];
 #pragma unroll
-    for (int q = 0; q < MTW; ++q)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[q][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < MTW; ++q)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[g][q][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto fetch = [&](int k, int buf) {  // global K step k -> LDS buffer buf
 #pragma unroll
-        for (int j = 0; j < AW; ++j) {
-            const uint16_t* src;
-            if (one_chunk) {
-                src = asrc[j] + (int64_t)k * 64;
-            } else {
-                const int c = k / cblocks;
-                src = P.A.pool + P.A.row_off[off_index(P.A, it.adapter, arow[j], c)] + (int64_t)(k - c * cblocks) * 64 +
-                      8 * apc[j];
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int j = 0; j < AW; ++j) {
+                const uint16_t* src;
+                if (one_chunk) {
+                    src = asrc[g][j] + (int64_t)k * 64;
+                } else {
+                    const Rows& A = args.p[pj[g]].A;
+                    const int c = k / cblocks[g];
+                    src = A.pool + A.row_off[off_index(A, it.adapter, arow[j], c)] +
+                          (int64_t)(k - c * cblocks[g]) * 64 + 8 * apc[j];
+                }
+                dma16(src, sA + buf * ASTRIDE + g * ABUF + ((AW * wave + j) % AWT) * 64);
             }
-            dma16(src, sA + buf * ABUF + ((AW * wave + j) % AWT) * 64);
-        }
 #pragma unroll
         for (int j = 0; j < XW; ++j)
             dma16(xsrc[j] + (int64_t)k * 64, sX + buf * XBUF + (XW * wave + j) * 64);
     };
     auto mma = [&](int buf) {
         const u32x4_t* X = sX + buf * XBUF;
-        const u32x4_t* A = sA + buf * ABUF;
         u32x4_t xf[MTW][2];
 #pragma unroll
         for (int q = 0; q < MTW; ++q) {
@@ -467,26 +490,30 @@ __device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const l
             xf[q][1] = X[row * 8 + ((lg + 4) ^ (li & 7))];
         }
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const int row = 16 * n + li;
-            const u32x4_t a0 = A[row * 8 + (lg ^ (li & 7))];
-            const u32x4_t a1 = A[row * 8 + ((lg + 4) ^ (li & 7))];
+        for (int g = 0; g < G; ++g) {
+            const u32x4_t* A = sA + buf * ASTRIDE + g * ABUF;
 #pragma unroll
-            for (int q = 0; q < MTW; ++q) {
-                acc[q][n] = mfma_bf16(xf[q][0], a0, acc[q][n]);
-                acc[q][n] = mfma_bf16(xf[q][1], a1, acc[q][n]);
+            for (int n = 0; n < NT; ++n) {
+                const int row = 16 * n + li;
+                const u32x4_t a0 = A[row * 8 + (lg ^ (li & 7))];
+                const u32x4_t a1 = A[row * 8 + ((lg + 4) ^ (li & 7))];
+#pragma unroll
+                for (int q = 0; q < MTW; ++q) {
+                    acc[g][q][n] = mfma_bf16(xf[q][0], a0, acc[g][q][n]);
+                    acc[g][q][n] = mfma_bf16(xf[q][1], a1, acc[g][q][n]);
+                }
             }
         }
     };
-    // Steps start at a point that depends on (adapter, projection, K
-    // slice).  x rows and A rows lie a power-of-two distance apart, so
-    // workgroups that read the same step in lock-step all hit the same
-    // address bits; spreading the starting steps spreads the traffic.  The
-    // start is the same for every item of a segment and for every storage
-    // layout, so a row's sum order (and hence its result, to the bit)
-    // depends on neither which item holds it nor how A is paged.
+    // Steps start at a point that depends on (adapter, first projection of
+    // the group, K slice).  x rows and A rows lie a power-of-two distance
+    // apart, so workgroups that read the same step in lock-step all hit the
+    // same address bits; spreading the starting steps spreads the traffic.
+    // The start is the same for every item of a segment and for every storage
+    // layout, so a row's sum order (and hence its result, to the bit) depends
+    // on neither which item holds it nor how A is paged.
     const int nb = kend - kbeg;
-    const unsigned h = (unsigned)it.adapter * 2654435761u ^ ((unsigned)proj * 40503u + (unsigned)it.kslice * 977u);
+    const unsigned h = (unsigned)it.adapter * 2654435761u ^ ((unsigned)pj[0] * 40503u + (unsigned)it.kslice * 977u);
     const int rot = (int)((h >> 7) % (unsigned)nb);
     auto step = [&](int i) { return kbeg + (i + rot < nb ? i + rot : i + rot - nb); };
 #pragma unroll
@@ -507,51 +534,86 @@ __device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const l
             step_barrier<0>();
     }
     if (mbase >= it.nrows) return;
-    float* vout = P.v + (int64_t)it.kslice * args.n_active * P.ldv;
-    const int jneg = neg_start(P.A, it.adapter, it.rank);  // deLoRA: negated rank rows
 #pragma unroll
-    for (int q = 0; q < MTW; ++q)
+    for (int g = 0; g < G; ++g) {
+        const ShrinkProj& P = args.p[pj[g]];
+        float* vout = P.v + (int64_t)it.kslice * args.n_active * P.ldv;
+        const int jneg = neg_start(P.A, it.adapter, it.rank);  // deLoRA: negated rank rows
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const int j = 16 * n + li;
-            if (j >= it.rank) continue;
+        for (int q = 0; q < MTW; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = mbase + 16 * q + 4 * lg + e;
-                if (m < it.nrows) vout[(int64_t)(it.row0 + m) * P.ldv + j] = j >= jneg ? -acc[q][n][e] : acc[q][n][e];
+            for (int n = 0; n < NT; ++n) {
+                const int j = 16 * n + li;
+                if (j >= it.rank) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = mbase + 16 * q + 4 * lg + e;
+                    if (m < it.nrows)
+                        vout[(int64_t)(it.row0 + m) * P.ldv + j] = j >= jneg ? -acc[g][q][n][e] : acc[g][q][n][e];
+                }
             }
-        }
+    }
 }
 
-// Persistent: workgroup g takes tasks g, g + G, ... of the launch's
-// count x n_proj (item, projection) tasks; the launcher sizes the grid so
-// that every workgroup gets the same number of tasks and all are resident.
-// The item's rank picks the number of rank tiles (1, 2 or 4 up to NTMAX = 4;
+// Persistent: workgroup g takes tasks g, g + G, ... of the launch's tasks;
+// the launcher sizes the grid so that every workgroup gets the same number of
+// tasks and all are resident.  With GS = 1 a task is (item, projection); with
+// GS > 1 it is (item, group of up to GS projections that share x).  The
+// item's rank picks the number of rank tiles (1, 2 or 4 up to NTMAX = 4;
 // NTMAX = 8 is its own kernel for ranks above 64, whose registers and LDS
 // would lower the occupancy of the others).
-template <int MTW, int NTMAX, bool WHOLE_ROWS>
+template <int MTW, int NTMAX, bool WHOLE_ROWS, int GS>
 __global__ __launch_bounds__(WG) void shrink_rows_kernel(ShrinkArgs args) {
-    // LDS stages: three steps in flight below rank 64 (96 KiB: one workgroup
-    // per CU; measured against two and three stages: prefill -11%, vision
-    // -1%, 70B mix +1%), one above
+    // LDS stages: three steps in flight below rank 64 (96 KiB with one
+    // projection per task: one workgroup per CU; measured against two and
+    // three stages: prefill -11%, vision -1%, 70B mix +1%; 160 KiB with
+    // three A tiles per stage), one above
     constexpr int NBUF = NTMAX == 8 ? 2 : 4;
-    __shared__ u32x4_t sX[NBUF * 64 * MTW * 8];    // NBUF buffers x 64*MTW rows x 8 pieces of 16 B
-    __shared__ u32x4_t sA[NBUF * 16 * NTMAX * 8];  // NBUF buffers x 16*NT rank rows x 8 pieces
-    const int ntasks = args.count * args.n_proj;
+    __shared__ u32x4_t sX[NBUF * 64 * MTW * 8];         // NBUF buffers x 64*MTW rows x 8 pieces of 16 B
+    __shared__ u32x4_t sA[NBUF * GS * 16 * NTMAX * 8];  // NBUF x GS buffers x 16*NT rank rows x 8 pieces
+    const int n_units = GS == 1 ? args.n_proj : args.n_groups;
+    const int ntasks = args.count * n_units;
     for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
-        const int proj = task / args.count;
-        const lora_work_t it = args.work[args.begin + task - proj * args.count];
-        const ShrinkProj& P = args.p[proj];
+        const int unit = task / args.count;
+        const lora_work_t it = args.work[args.begin + task - unit * args.count];
+        int pj[4] = {unit, unit, unit, unit};
+        int ng = 1;
+        if (GS > 1) {
+            const int g0 = args.gbeg[unit];
+            ng = args.gbeg[unit + 1] - g0;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) pj[g] = args.gproj[g0 + (g < ng ? g : 0)];
+        }
         // uniform over the workgroup: a skipped task skips no barrier
-        if (!(item_ok(it, args.n_active, args.v_slices, P.A, 16 * NTMAX) & (it.nrows <= 64 * MTW))) continue;
-        if (NTMAX == 8)
-            shrink_rows_task<MTW, 8, WHOLE_ROWS, NBUF>(args, it, P, proj, sX, sA);
-        else if (it.rank > 32)
-            shrink_rows_task<MTW, 4, WHOLE_ROWS, NBUF>(args, it, P, proj, sX, sA);
-        else if (it.rank > 16)
-            shrink_rows_task<MTW, 2, WHOLE_ROWS, NBUF>(args, it, P, proj, sX, sA);
-        else
-            shrink_rows_task<MTW, 1, WHOLE_ROWS, NBUF>(args, it, P, proj, sX, sA);
+        bool ok = (it.nrows <= 64 * MTW) & (ng >= 1) & (ng <= GS);
+#pragma unroll
+        for (int g = 0; g < GS; ++g)
+            if (g < ng) ok = ok & item_ok(it, args.n_active, args.v_slices, args.p[pj[g]].A, 16 * NTMAX);
+        if (!ok) continue;
+        if (NTMAX == 8) {
+            shrink_rows_task<MTW, 8, 1, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+        } else if (ng == 1 || GS == 1) {
+            if (it.rank > 32)
+                shrink_rows_task<MTW, 4, 1, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+            else if (it.rank > 16)
+                shrink_rows_task<MTW, 2, 1, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+            else
+                shrink_rows_task<MTW, 1, 1, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+        } else if (ng == 2) {
+            if (it.rank > 32)
+                shrink_rows_task<MTW, 4, 2 <= GS ? 2 : 1, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+            else if (it.rank > 16)
+                shrink_rows_task<MTW, 2, 2 <= GS ? 2 : 1, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+            else
+                shrink_rows_task<MTW, 1, 2 <= GS ? 2 : 1, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+        } else {
+            if (it.rank > 32)
+                shrink_rows_task<MTW, 4, GS, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+            else if (it.rank > 16)
+                shrink_rows_task<MTW, 2, GS, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+            else
+                shrink_rows_task<MTW, 1, GS, GS, WHOLE_ROWS, NBUF>(args, it, pj, sX, sA);
+        }
     }
 }
 
@@ -1335,12 +1397,41 @@ unsigned persistent_grid(const void* fn, int64_t tasks) {
     return (unsigned)((tasks + rounds - 1) / rounds);
 }
 
+// Groups of up to SHRINK_GROUP projections with the same x (pointer, ldx
+// and d_in), in first-appearance order; returns true when some group has more
+// than one projection.
+constexpr int SHRINK_GROUP = 3;
+bool group_shared_x(ShrinkArgs& args, int32_t n_proj) {
+    bool taken[LORA_MAX_PROJ] = {};
+    int n = 0, ng = 0;
+    bool shared = false;
+    for (int i = 0; i < n_proj; ++i) {
+        if (taken[i]) continue;
+        args.gbeg[ng++] = (int8_t)n;
+        args.gproj[n++] = (int8_t)i;
+        taken[i] = true;
+        int size = 1;
+        for (int j = i + 1; j < n_proj && size < SHRINK_GROUP; ++j) {
+            const ShrinkProj &a = args.p[i], &b = args.p[j];
+            if (taken[j] || a.x != b.x || a.ldx != b.ldx || a.d_in != b.d_in) continue;
+            args.gproj[n++] = (int8_t)j;
+            taken[j] = true;
+            ++size;
+            shared = true;
+        }
+    }
+    args.gbeg[ng] = (int8_t)n;
+    args.n_groups = ng;
+    return shared;
+}
+
 hipError_t launch_shrink_ranges(const lora_plan_info_t& info, int r0, int r1, int32_t n_proj, hipStream_t s,
                                 ShrinkArgs& args) {
     hipError_t err = hipSuccess;
     args.n_proj = n_proj;
     bool whole = true;  // every projection keeps each A row in one chunk
     for (int i = 0; i < n_proj; ++i) whole = whole && args.p[i].A.chunk_len >= args.p[i].d_in;
+    const bool grouped = group_shared_x(args, n_proj);
     for (int r = r0; r < r1;) {
         const lora_range_t& R = info.ranges[r];
         const int shape = R.variant / LV_RANK_CLASSES, cls = R.variant % LV_RANK_CLASSES;
@@ -1353,8 +1444,8 @@ hipError_t launch_shrink_ranges(const lora_plan_info_t& info, int r0, int r1, in
                                                   dim3(WG), s, args));
                 } else {
                     shrink_fn fn = shape == LV_S_ROWS64
-                                       ? (whole ? shrink_rows_kernel<1, 8, true> : shrink_rows_kernel<1, 8, false>)
-                                       : (whole ? shrink_rows_kernel<2, 8, true> : shrink_rows_kernel<2, 8, false>);
+                                       ? (whole ? shrink_rows_kernel<1, 8, true, 1> : shrink_rows_kernel<1, 8, false, 1>)
+                                       : (whole ? shrink_rows_kernel<2, 8, true, 1> : shrink_rows_kernel<2, 8, false, 1>);
                     const unsigned g = persistent_grid(reinterpret_cast<const void*>(fn), (int64_t)R.count * n_proj);
                     err = first_error(err, launch(fn, dim3(g), dim3(WG), s, args));
                 }
@@ -1373,10 +1464,19 @@ hipError_t launch_shrink_ranges(const lora_plan_info_t& info, int r0, int r1, in
         if (count > 0) {
             args.begin = R.begin;
             args.count = count;
-            shrink_fn fn = shape == LV_S_ROWS64
-                               ? (whole ? shrink_rows_kernel<1, 4, true> : shrink_rows_kernel<1, 4, false>)
-                               : (whole ? shrink_rows_kernel<2, 4, true> : shrink_rows_kernel<2, 4, false>);
-            const unsigned g = persistent_grid(reinterpret_cast<const void*>(fn), (int64_t)count * n_proj);
+            shrink_fn fn;
+            if (grouped)  // tasks are (item, group of projections that share x)
+                fn = shape == LV_S_ROWS64
+                         ? (whole ? shrink_rows_kernel<1, 4, true, SHRINK_GROUP>
+                                  : shrink_rows_kernel<1, 4, false, SHRINK_GROUP>)
+                         : (whole ? shrink_rows_kernel<2, 4, true, SHRINK_GROUP>
+                                  : shrink_rows_kernel<2, 4, false, SHRINK_GROUP>);
+            else
+                fn = shape == LV_S_ROWS64
+                         ? (whole ? shrink_rows_kernel<1, 4, true, 1> : shrink_rows_kernel<1, 4, false, 1>)
+                         : (whole ? shrink_rows_kernel<2, 4, true, 1> : shrink_rows_kernel<2, 4, false, 1>);
+            const unsigned g = persistent_grid(reinterpret_cast<const void*>(fn),
+                                               (int64_t)count * (grouped ? args.n_groups : n_proj));
             err = first_error(err, launch(fn, dim3(g), dim3(WG), s, args));
         }
         r = e;

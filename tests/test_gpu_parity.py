@@ -336,3 +336,57 @@ def test_batch_prepare_layout_and_upload():
         torch.cuda.synchronize()
         got = b._dev.cpu().numpy()
         assert np.array_equal(got[:ref.n_active], ref.row_index)
+
+
+# ------------------------------------------------------------------ projections that share x
+def _shared_x_workload(layout, seed=41):
+    """q/k/v (projections 0-2) read one x, o its own.  Long segments (the
+    grouped long-segment shrink), one of rank above 64 (its own kernel, not
+    grouped), one short segment, rows scattered over the batch."""
+    rng = np.random.default_rng(seed)
+    ranks = np.array([8, 16, 32, 64, 100, 40], np.int32)
+    lens = [300, 520, 270, 700, 290, 3]
+    ra = np.repeat(rng.permutation(6), lens).astype(np.int32)
+    ra = ra[rng.permutation(ra.shape[0])]
+    return workloads.gen_custom(seed, ra, ranks, 4096, 1024, n_proj=4, layout=layout, page_elems=512,
+                                shared_x=[(0, 1, 2)])
+
+
+@pytest.mark.parametrize("layout", ["dense", "paged"])
+def test_shared_x_parity(layout):
+    W = _shared_x_workload(layout)
+    assert W.projections[0].x is W.projections[2].x
+    _say("shared x", layout, "rows", W.n_rows)
+    batch, vs, ys = run_delta(W)
+    _say(check_delta(W, batch, vs, ys))
+
+
+def test_shared_x_apply_and_storage():
+    """lora_apply over the same batch (its shrink ranges group q/k/v too)
+    matches the oracle, and dense and paged storage give bit-identical y."""
+    from gpu_helpers import run_apply
+    Wd, Wp = _shared_x_workload("dense"), _shared_x_workload("paged")
+    ys_d = run_delta(Wd)[2]
+    ys_p = run_delta(Wp)[2]
+    for a, b in zip(ys_d, ys_p):
+        assert np.array_equal(a, b)
+    batch, ys = run_apply(Wd)
+    _say("shared x apply", check_delta(Wd, batch, None, ys, check_v=False))
+
+
+def test_shared_x_against_separate_copies():
+    """The same values with a private copy of x per projection (no grouping):
+    the group's first projection sums in the same order (bit-identical y);
+    the others start their K steps elsewhere, so they agree to fp32 rounding."""
+    from workloads import Projection as Proj
+    W = _shared_x_workload("dense")
+    _, _, ys_g = run_delta(W)
+    W.projections = [Proj(p.name, p.d_in, p.d_out, p.x.copy(), p.y0, p.A, p.B) for p in W.projections]
+    _, _, ys_s = run_delta(W)
+    assert np.array_equal(ys_g[0], ys_s[0]) and np.array_equal(ys_g[3], ys_s[3])
+    for pi in (1, 2):
+        d_g = ys_g[pi].astype(np.float64) - W.projections[pi].y0
+        d_s = ys_s[pi].astype(np.float64) - W.projections[pi].y0
+        rel = np.linalg.norm(d_g - d_s) / np.linalg.norm(d_s)
+        _say("shared vs separate x, projection", pi, rel)
+        assert rel <= 1e-5

@@ -334,3 +334,15 @@ def test_mixture_equals_unmerged_inference(layout):
     # adding the merged adapter instead of subtracting it would be far off
     bad = xe[0] @ Wm.T + s * (xe[0] @ Ae[0].T) @ Be[0]
     assert np.max(np.abs(bad - (xe[0] @ Wb.T + s * (xe[0] @ Ae[0].T) @ Be[0]))) > 1e-2
+
+
+def test_shared_x_workload_recipe():
+    """Projections that share x take one array (the group's first projection's
+    draw); everything else is the same instance as without sharing."""
+    W = workloads.gen_config(2, shared_qkv=True)
+    W0 = workloads.gen_config(2)
+    assert W.projections[0].x is W.projections[1].x is W.projections[2].x
+    assert W.projections[3].x is not W.projections[0].x
+    assert np.array_equal(W.projections[0].x, W0.projections[0].x)
+    assert np.array_equal(W.projections[3].x, W0.projections[3].x)
+    assert np.array_equal(W.row_adapter, W0.row_adapter) and np.array_equal(W.pool, W0.pool)

@@ -222,14 +222,22 @@ def _zipf_choice(rng, n_ids, size, s=1.1):
 
 
 def _make(name, seed, row_adapter, ranks, projs, layout, page_elems, rng,
-          batches=None, merge=None, scale=2.0):
+          batches=None, merge=None, scale=2.0, shared_x=()):
+    """shared_x: groups of projection indices that take the same x (one
+    array, drawn for the group's first projection), as q, k and v do in a
+    transformer layer."""
     row_adapter = np.asarray(row_adapter, dtype=np.int32)
     ranks = np.asarray(ranks, dtype=np.int32)
     n_rows, n_ad = row_adapter.shape[0], ranks.shape[0]
     max_rank = int(ranks.max())
+    x_of = {}
+    for grp in shared_x:
+        for pi in grp[1:]:
+            assert projs[pi][1] == projs[grp[0]][1], "projections that share x share d_in"
+            x_of[pi] = grp[0]
     items, tensors = [], []
     for pi, (pname, d_in, d_out) in enumerate(projs):
-        x = bf16_normal(seed, (_TAG_X, pi), (n_rows, d_in))
+        x = tensors[x_of[pi]][3] if pi in x_of else bf16_normal(seed, (_TAG_X, pi), (n_rows, d_in))
         A = [bf16_normal(seed, (_TAG_A, pi, a), (int(ranks[a]), d_in), 1.0 / math.sqrt(d_in))
              for a in range(n_ad)]
         B = [bf16_normal(seed, (_TAG_B, pi, a), (int(ranks[a]), d_out), 1.0 / math.sqrt(int(ranks[a])))
@@ -285,9 +293,10 @@ def gen_decode(seed=1, layout="dense"):
                  batches={"hetero": het, "homo": homo}, merge=merge)
 
 
-def gen_prefill(seed=2, layout="dense"):
+def gen_prefill(seed=2, layout="dense", shared_qkv=False):
     """16 requests, lognormal lengths, 16 adapters with ranks U{8,16,32,64},
-    Zipf(1.1) adapter choice, q/k/v/o at d 4096."""
+    Zipf(1.1) adapter choice, q/k/v/o at d 4096.  shared_qkv: q, k and v
+    take one x (the layer input), o its own."""
     rng = np.random.default_rng([seed, 0])
     z = rng.standard_normal(16)
     lens = np.clip(np.rint(np.exp(math.log(512.0) + 0.6 * z)), 32, 2048).astype(np.int64)
@@ -295,20 +304,22 @@ def gen_prefill(seed=2, layout="dense"):
     req_ad = _zipf_choice(rng, 16, 16)
     row_adapter = np.repeat(req_ad, lens)
     projs = [(p, 4096, 4096) for p in ("q", "k", "v", "o")]
-    return _make("prefill", seed, row_adapter, ranks, projs, layout, 4096, rng)
+    return _make("prefill", seed, row_adapter, ranks, projs, layout, 4096, rng,
+                 shared_x=[(0, 1, 2)] if shared_qkv else ())
 
 
-def gen_vision(seed=3, layout="dense", n_layers=32):
+def gen_vision(seed=3, layout="dense", n_layers=32, shared_qkv=False):
     """24 requests of U{256..1024} visual + 32 text tokens, 32 adapters of rank
     64, Zipf(1.1); q/k/v/o at d 4096; mode switch of adapter 0 over
-    n_layers x 4 W[4096x4096]."""
+    n_layers x 4 W[4096x4096].  shared_qkv: q, k and v take one x."""
     rng = np.random.default_rng([seed, 0])
     lens = rng.integers(256, 1025, size=24) + 32
     req_ad = _zipf_choice(rng, 32, 24)
     row_adapter = np.repeat(req_ad, lens)
     projs = [(p, 4096, 4096) for p in ("q", "k", "v", "o")]
     merge = _merge_spec(seed, 0, n_layers, [(i, 4096, 4096) for i in range(4)])
-    return _make("vision", seed, row_adapter, np.full(32, 64), projs, layout, 4096, rng, merge=merge)
+    return _make("vision", seed, row_adapter, np.full(32, 64), projs, layout, 4096, rng, merge=merge,
+                 shared_x=[(0, 1, 2)] if shared_qkv else ())
 
 
 def gen_mix70b(seed=4, layout="paged"):
@@ -336,9 +347,9 @@ def gen_config(k: int, seed: Optional[int] = None, **kw) -> Workload:
 
 
 def gen_custom(seed, row_adapter, ranks, d_in, d_out, n_proj=1, layout="dense",
-               page_elems=None, scale=2.0):
+               page_elems=None, scale=2.0, shared_x=()):
     """Small ad-hoc workload for tests: given row->adapter map and ranks."""
     rng = np.random.default_rng([seed, 0])
     projs = [(f"p{i}", d_in, d_out) for i in range(n_proj)]
     return _make("custom", seed, row_adapter, ranks, projs, layout,
-                 page_elems or max(d_in, d_out), rng, scale=scale)
+                 page_elems or max(d_in, d_out), rng, scale=scale, shared_x=shared_x)

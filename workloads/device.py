@@ -28,11 +28,14 @@ def bits_to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 def to_device(W, device="cuda") -> DeviceWorkload:
+    """Projections that share one host x array share one device x."""
     pool = bits_to_device(W.pool, device)
-    projs = []
+    projs, xs = [], {}
     for p in W.projections:
+        if id(p.x) not in xs:
+            xs[id(p.x)] = bits_to_device(p.x, device)
         projs.append(DeviceProjection(
-            x=bits_to_device(p.x, device),
+            x=xs[id(p.x)],
             y=torch.from_numpy(p.y0).to(device),
             A_off=torch.from_numpy(p.A.row_off).to(device),
             B_off=torch.from_numpy(p.B.row_off).to(device)))
