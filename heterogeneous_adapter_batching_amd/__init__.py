@@ -15,7 +15,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
-LORA_ABI_VERSION = 6
+LORA_ABI_VERSION = 7
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
 LORA_MAX_RANGES = 48
@@ -107,6 +107,14 @@ _sig = {
     "lora_mixture_rows": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "lora_batch_prepare": (_i32, [_i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_uint32, _i32, _vp, _vp, _vp, _vp,
                                   _i64, _vp, _vp, _P(lora_batch_t)]),
+    "lora_pool_create": (_i32, [_i64, _i32, _i32, _i32, _i32, _vp, _P(_vp)]),
+    "lora_pool_destroy": (_i32, [_vp]),
+    "lora_pool_acquire": (_i32, [_vp, _i32, _vp, _vp, _vp, _P(_i32)]),
+    "lora_pool_release": (_i32, [_vp, _i32, _vp]),
+    "lora_pool_row_off": (_i32, [_vp, _i32, _P(_P(_i64)), _P(_i32)]),
+    "lora_pool_stats": (_i32, [_vp, _P(_i32), _P(_i64), _P(_i32)]),
+    "lora_pool_load_list": (_i32, [_vp, _i32, _vp, _i64, _vp, _vp, _vp, _P(_i64), _P(_i64)]),
+    "lora_pool_scatter": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _vp]),
 }
 # HIP runtime calls the binding makes itself (events), resolved through the
 # library's handle so they bind to the runtime the library uses
@@ -114,6 +122,8 @@ _sig.update({
     "hipEventCreateWithFlags": (ctypes.c_int, [_P(_vp), ctypes.c_uint]),
     "hipEventRecord": (ctypes.c_int, [_vp, _vp]),
     "hipEventSynchronize": (ctypes.c_int, [_vp]),
+    "hipEventQuery": (ctypes.c_int, [_vp]),
+    "hipStreamWaitEvent": (ctypes.c_int, [_vp, _vp, ctypes.c_uint]),
     "hipEventElapsedTime": (ctypes.c_int, [_P(ctypes.c_float), _vp, _vp]),
     "hipEventDestroy": (ctypes.c_int, [_vp]),
 })
@@ -159,6 +169,78 @@ def lora_batch_prepare(row_adapter, adapter_rank, d_in, d_out, op_mask, staging,
     if not raw:
         _check(st, "lora_batch_prepare")
     return st, out, segs
+
+
+class LoraPool:
+    """Host-side pool manager (lora_pool_*): pages of a device pool assigned
+    to adapters on demand.  row_len: the row length of each row table."""
+
+    def __init__(self, n_pages, page_elems, n_adapters, max_rank, row_len):
+        self.row_len = np.ascontiguousarray(row_len, dtype=np.int32)
+        self.n_pages, self.page_elems = int(n_pages), int(page_elems)
+        self.n_adapters, self.max_rank = int(n_adapters), int(max_rank)
+        h = _vp()
+        _check(_lib.lora_pool_create(self.n_pages, self.page_elems, self.n_adapters, self.max_rank,
+                                     self.row_len.shape[0], self.row_len.ctypes.data, ctypes.byref(h)),
+               "lora_pool_create")
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.lora_pool_destroy(self._h)
+            self._h = None
+
+    def acquire(self, adapters, ranks, raw=False):
+        """Returns the adapters whose rows must be copied in (int32 array), or
+        (status, that array) with raw=True."""
+        a = np.ascontiguousarray(adapters, dtype=np.int32)
+        r = np.ascontiguousarray(ranks, dtype=np.int32)
+        load = np.empty(max(1, a.shape[0]), np.int32)
+        nl = _i32(0)
+        st = _lib.lora_pool_acquire(self._h, a.shape[0], _ptr(a), _ptr(r), load.ctypes.data, ctypes.byref(nl))
+        if raw:
+            return st, load[:nl.value].copy()
+        _check(st, "lora_pool_acquire")
+        return load[:nl.value].copy()
+
+    def release(self, adapters, raw=False):
+        a = np.ascontiguousarray(adapters, dtype=np.int32)
+        st = _lib.lora_pool_release(self._h, a.shape[0], _ptr(a))
+        if raw:
+            return st
+        _check(st, "lora_pool_release")
+
+    def row_off(self, table):
+        """(view of the host row-offset table, chunks per row); the view is
+        valid until the next acquire."""
+        p, ch = _P(_i64)(), _i32(0)
+        _check(_lib.lora_pool_row_off(self._h, int(table), ctypes.byref(p), ctypes.byref(ch)), "lora_pool_row_off")
+        n = self.n_adapters * self.max_rank * ch.value
+        return np.ctypeslib.as_array(p, shape=(n,)), ch.value
+
+    def stats(self):
+        """(resident adapters, free pages, pinned adapters)."""
+        r, f, p = _i32(0), _i64(0), _i32(0)
+        _check(_lib.lora_pool_stats(self._h, ctypes.byref(r), ctypes.byref(f), ctypes.byref(p)), "lora_pool_stats")
+        return r.value, f.value, p.value
+
+    def load_list(self, adapters):
+        """(src_off int64, dst_off int64, len int32, packed source elements)."""
+        a = np.ascontiguousarray(adapters, dtype=np.int32)
+        n, src = _i64(0), _i64(0)
+        st = _lib.lora_pool_load_list(self._h, a.shape[0], _ptr(a), 0, None, None, None, ctypes.byref(n),
+                                      ctypes.byref(src))
+        if st not in (LORA_OK, LORA_ECAPACITY):
+            _check(st, "lora_pool_load_list")
+        so, do, ln = np.empty(n.value, np.int64), np.empty(n.value, np.int64), np.empty(n.value, np.int32)
+        _check(_lib.lora_pool_load_list(self._h, a.shape[0], _ptr(a), n.value, _ptr(so), _ptr(do), _ptr(ln),
+                                        ctypes.byref(n), ctypes.byref(src)), "lora_pool_load_list")
+        return so, do, ln, src.value
+
+
+def lora_pool_scatter(src_ptr, pool_ptr, n, src_off_ptr, dst_off_ptr, len_ptr, stream=None):
+    _check(_lib.lora_pool_scatter(src_ptr, pool_ptr, int(n), src_off_ptr, dst_off_ptr, len_ptr, stream),
+           "lora_pool_scatter")
 
 
 def _ptr(a):

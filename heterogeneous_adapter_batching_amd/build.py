@@ -1,7 +1,8 @@
 """Build libhetlora.so in-tree for gfx950.
 
-host.cpp (no HIP) is compiled by g++, kernels.hip by hipcc; hipcc links the
-shared library next to this file.  Every build compiles from scratch.
+host.cpp and pool.cpp (no HIP) are compiled by g++, kernels.hip by hipcc;
+hipcc links the shared library next to this file.  Every build compiles from
+scratch.
 """
 import os
 import shutil
@@ -40,14 +41,15 @@ def build(verbose=False, out=LIB, defines=(), build_dir=None):
     (tuning constants); the default build uses none."""
     out_dir = build_dir or os.path.join(HERE, "_build")
     os.makedirs(out_dir, exist_ok=True)
-    host_o = os.path.join(out_dir, "host.o")
+    host_o = [os.path.join(out_dir, f"{n}.o") for n in ("host", "pool")]
     kern_o = os.path.join(out_dir, "kernels.o")
     dflags = [f"-D{d}" for d in defines]
-    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", *dflags, "-c",
-          os.path.join(CSRC, "host.cpp"), "-o", host_o])
+    for n, o in zip(("host", "pool"), host_o):
+        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", *dflags, "-c",
+              os.path.join(CSRC, f"{n}.cpp"), "-o", o])
     _run([_hipcc(), *HIP_FLAGS, *dflags, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
     tmp = out + ".tmp"
-    _run([_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", host_o, kern_o, "-o", tmp])
+    _run([_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *host_o, kern_o, "-o", tmp])
     os.replace(tmp, out)
     if verbose:
         print("built", out)

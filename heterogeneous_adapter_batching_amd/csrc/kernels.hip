@@ -1624,6 +1624,38 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
     return err == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
+// ------------------------------------------------------------------ pool scatter
+struct ScatterArgs {
+    const uint16_t* src;
+    uint16_t* pool;
+    int64_t n;
+    const int64_t* src_off;
+    const int64_t* dst_off;
+    const int32_t* len;
+};
+// One workgroup per piece (grid-stride over pieces): 16 bytes per lane and
+// step, so a 8192-element page is four steps of the workgroup.
+__global__ __launch_bounds__(WG) void pool_scatter_kernel(ScatterArgs a) {
+    for (int64_t i = blockIdx.x; i < a.n; i += gridDim.x) {
+        const int64_t so = a.src_off[i], d = a.dst_off[i];
+        const int32_t l = a.len[i];
+        if (so < 0 || d < 0 || l <= 0 || l > 65536 || ((so | d | (int64_t)l) & 7)) continue;  // cheap to refuse
+        for (int32_t e = 8 * (int32_t)threadIdx.x; e < l; e += 8 * WG)
+            *reinterpret_cast<u32x4_t*>(a.pool + d + e) = *reinterpret_cast<const u32x4_t*>(a.src + so + e);
+    }
+}
+
+extern "C" int32_t lora_pool_scatter(const uint16_t* src, uint16_t* pool, int64_t n, const int64_t* src_off,
+                                     const int64_t* dst_off, const int32_t* len, void* hip_stream) {
+    if (n < 0) return LORA_EINVAL;
+    if (n == 0) return LORA_OK;
+    if (!src || !pool || !src_off || !dst_off || !len || !aligned16(src) || !aligned16(pool)) return LORA_EINVAL;
+    ScatterArgs a{src, pool, n, src_off, dst_off, len};
+    const unsigned grid = (unsigned)(n < 65536 ? n : 65536);
+    const hipError_t e = launch(pool_scatter_kernel, dim3(grid), dim3(WG), reinterpret_cast<hipStream_t>(hip_stream), a);
+    return e == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
 extern "C" int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter, int32_t n_adapters,
                                       const int32_t* adapter_rank, int32_t d_in, int32_t d_out, uint32_t op_mask,
                                       int32_t seg_capacity, int32_t* seg_start, int32_t* seg_adapter,

@@ -13,9 +13,10 @@ import numpy as np
 import torch
 
 from . import _lib as _hip  # the HIP runtime the library is linked to (and torch uses)
-from . import (LORA_ECAPACITY, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, Segments, batch_prepare,
-               call_apply, call_expand, call_merge, call_shrink, check_status, lora_apply_proj_t, lora_batch_t,
-               lora_expand_proj_t, lora_merge_mat_t, lora_mixture_rows, lora_shrink_proj_t, make_rows)
+from . import (LORA_ECAPACITY, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, LoraPool, Segments,
+               batch_prepare, call_apply, call_expand, call_merge, call_shrink, check_status, lora_apply_proj_t,
+               lora_batch_t, lora_expand_proj_t, lora_merge_mat_t, lora_mixture_rows, lora_pool_scatter,
+               lora_shrink_proj_t, make_rows)
 
 
 class HipEvent:
@@ -47,6 +48,18 @@ class HipEvent:
     def synchronize(self):
         if _hip.hipEventSynchronize(self._h) != 0:
             raise RuntimeError("hipEventSynchronize failed")
+
+    def query(self):
+        """True once the recorded work has completed."""
+        return _hip.hipEventQuery(self._h) == 0
+
+    def wait(self, stream=None):
+        """Make `stream` (torch stream or raw handle; None: current) wait for this event."""
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        h = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        if _hip.hipStreamWaitEvent(h, self._h, 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
 
     def elapsed_time(self, end):
         """Milliseconds from this event to `end` (both recorded and complete)."""
@@ -330,3 +343,132 @@ def mixture_tables(rows_host, rank, merged, out_max_rank, device="cuda"):
     cb, _, _ = lora_mixture_rows(rank, merged, b_chunks, b_off, max_rank, out_max_rank)
     dev = torch.device(device)
     return (torch.from_numpy(ca).to(dev), torch.from_numpy(cb).to(dev), torch.from_numpy(neg).to(dev), crank)
+
+
+class AdapterPool:
+    """Adapters paged into one device pool on demand (S-LoRA article,
+    "Unified Paging").  LoraPool (the library's pool manager) decides which
+    pages hold which adapter and keeps the row-offset tables; this class
+    copies the rows of newly placed adapters in on its own stream (one
+    host-to-device copy of the packed rows, then lora_pool_scatter into their
+    pages) together with their table entries.
+
+    weights(a) returns, per row table t, adapter a's rows as host bf16 bits
+    [rank][row_len[t]].  acquire() pins a batch's adapters and starts the
+    copies; the compute stream waits for them with wait(); release_after()
+    unpins the adapters once the work enqueued so far on a stream has finished
+    (an adapter is only evicted after its last batch has run)."""
+
+    def __init__(self, n_pages, page_elems, n_adapters, max_rank, row_len, weights, device="cuda"):
+        self.mgr = LoraPool(n_pages, page_elems, n_adapters, max_rank, row_len)
+        self.device = torch.device(device)
+        self.row_len = [int(r) for r in row_len]
+        self.page_elems, self.n_adapters, self.max_rank = int(page_elems), int(n_adapters), int(max_rank)
+        self.weights = weights
+        self.pool = torch.zeros(int(n_pages) * self.page_elems, dtype=torch.int16, device=self.device)
+        self.chunks = [-(-r // self.page_elems) for r in self.row_len]
+        self.tables = [torch.zeros(self.n_adapters * self.max_rank * c, dtype=torch.int64, device=self.device)
+                       for c in self.chunks]
+        self.stream = torch.cuda.Stream(device=self.device)
+        self._done = HipEvent()      # the last upload on self.stream
+        self._uploading = False
+        self._pending = []           # (event, adapters): pins to drop once the event completes
+        self._stage = self._meta = None
+        self.loaded = 0              # adapters copied in so far
+
+    def rows(self, table):
+        """lora_rows_t descriptor of row table `table` in the pool."""
+        return Rows(self.pool, self.tables[table], self.n_adapters, self.max_rank, self.row_len[table],
+                    self.page_elems)
+
+    def _collect(self, block):
+        while self._pending and (block or self._pending[0][0].query()):
+            ev, ads = self._pending.pop(0)
+            ev.synchronize()
+            self.mgr.release(ads)
+            block = False
+
+    def acquire(self, adapters, ranks):
+        """Pins the adapters, evicting unpinned ones if needed, and enqueues
+        the copies of those not resident.  Returns the adapters copied in."""
+        self._collect(False)
+        st, load = self.mgr.acquire(adapters, ranks, raw=True)
+        while st == LORA_ECAPACITY and self._pending:
+            self._collect(True)      # wait for the oldest batch in flight and retry
+            st, load = self.mgr.acquire(adapters, ranks, raw=True)
+        check_status(st, "lora_pool_acquire")
+        if len(load):
+            rank_of = {int(a): int(r) for a, r in zip(np.asarray(adapters).reshape(-1), np.asarray(ranks).reshape(-1))}
+            self._upload(load, rank_of)
+        return load
+
+    def _buffers(self, n_src, n_meta):
+        if self._stage is None or self._stage[0].shape[0] < n_src:
+            self._stage = (torch.empty(max(n_src, 1 << 20), dtype=torch.int16, pin_memory=True),
+                           torch.empty(max(n_src, 1 << 20), dtype=torch.int16, device=self.device))
+        if self._meta is None or self._meta[0].shape[0] < n_meta:
+            self._meta = (torch.empty(max(n_meta, 1 << 16), dtype=torch.int64, pin_memory=True),
+                          torch.empty(max(n_meta, 1 << 16), dtype=torch.int64, device=self.device))
+
+    def _upload(self, load, rank_of):
+        if self._uploading:
+            self._done.synchronize()  # the staging buffers may still be in flight
+        so, do, ln, n_src = self.mgr.load_list(load)
+        n = so.shape[0]
+        blocks = [(t, int(a)) for t in range(len(self.row_len)) for a in load]
+        per = [self.max_rank * c for c in self.chunks]
+        n_meta = 3 * n + sum(per[t] for t, _ in blocks)
+        self._buffers(n_src, n_meta)
+        hs, ds = self._stage
+        hm, dm = self._meta
+        h = hs.numpy().view(np.uint16)
+        o = 0
+        for a in load:
+            for t, w in enumerate(self.weights(int(a))):
+                w = np.ascontiguousarray(w, dtype=np.uint16).reshape(-1)
+                assert w.shape[0] == rank_of[int(a)] * self.row_len[t], "weights do not match the rank"
+                h[o:o + w.shape[0]] = w
+                o += w.shape[0]
+        m = hm.numpy()
+        m[:n], m[n:2 * n], m[2 * n:3 * n] = so, do, ln
+        o = 3 * n
+        for t, a in blocks:
+            tab, _ = self.mgr.row_off(t)
+            m[o:o + per[t]] = tab[a * per[t]:(a + 1) * per[t]]
+            o += per[t]
+        with torch.cuda.stream(self.stream):
+            ds[:n_src].copy_(hs[:n_src], non_blocking=True)
+            dm[:n_meta].copy_(hm[:n_meta], non_blocking=True)
+            base = dm.data_ptr()
+            lens = dm[2 * n:3 * n].to(torch.int32) if n else dm[:0].to(torch.int32)
+            lora_pool_scatter(ds.data_ptr(), self.pool.data_ptr(), n, base, base + 8 * n, lens.data_ptr(),
+                              self.stream.cuda_stream)
+            o = 3 * n
+            for t, a in blocks:
+                self.tables[t][a * per[t]:(a + 1) * per[t]].copy_(dm[o:o + per[t]])
+                o += per[t]
+            self._lens = lens    # kept alive until the next upload
+        self._done.record(self.stream)
+        self._uploading = True
+        self.loaded += len(load)
+
+    def mgr_rank(self, a):
+        """Resident rank of adapter a (from its copy list size)."""
+        so, _, ln, n_src = self.mgr.load_list([int(a)])
+        return n_src // sum(self.row_len)
+
+    def wait(self, stream=None):
+        """Make `stream` wait for the copies enqueued so far."""
+        if self._uploading:
+            self._done.wait(stream)
+
+    def release_after(self, adapters, stream=None):
+        """Unpin the adapters once the work enqueued so far on `stream` is done."""
+        ev = HipEvent()
+        ev.record(stream)
+        self._pending.append((ev, np.ascontiguousarray(adapters, dtype=np.int32)))
+
+    def drain(self):
+        """Wait for every batch in flight and drop their pins."""
+        while self._pending:
+            self._collect(True)

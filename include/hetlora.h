@@ -45,10 +45,13 @@
  * --------------------------
  * Every buffer belongs to the caller.  Pointers documented "device" must be
  * device memory of the current HIP device; "host" pointers are ordinary host
- * memory.  The library allocates no memory and keeps no pointer after a call
- * returns.  GPU work is enqueued on the given hipStream_t (passed as void*;
- * NULL = the null stream) and is asynchronous: no call synchronises.  All
- * functions are re-entrant; the only global state is constant tables.
+ * memory.  The library allocates no device memory, and apart from the pool
+ * manager (lora_pool_create .. lora_pool_destroy: host state the caller owns
+ * through its handle) it keeps no state or pointer after a call returns.
+ * GPU work is enqueued on the given hipStream_t (passed as void*; NULL = the
+ * null stream) and is asynchronous: no call synchronises.  All functions are
+ * re-entrant (a pool manager serves one thread at a time); the only global
+ * state is constant tables and a per-device occupancy cache.
  * Arguments are validated before anything is launched; on error nothing is
  * launched and no output is written, except that the counts of
  * lora_build_segments / lora_plan are written on LORA_ECAPACITY so the caller
@@ -67,7 +70,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 6
+#define LORA_ABI_VERSION 7
 #define LORA_MAX_RANK 128   /* ranks are 1..128                              */
 #define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
 #define LORA_MAX_RANGES 48  /* kernel variants in one plan                   */
@@ -393,6 +396,81 @@ int32_t lora_mixture_rows(int32_t n_adapters, int32_t max_rank,
                           const int64_t* row_off, int32_t out_max_rank,
                           int64_t* out_row_off, int32_t* out_rank,
                           int32_t* out_neg_from);
+
+/* ---------------------------------------------------------------------------
+ * Unified adapter pool (S-LoRA article, "Unified Paging": a rank-R adapter
+ * weight occupies R pages of hidden-size vectors in one memory pool; adapters
+ * are brought in on demand).  The pool is one caller-owned device array of
+ * n_pages pages of page_elems bf16 elements.  A pool manager (host state
+ * only, created and destroyed by the caller: the one library object that
+ * outlives a call) assigns pages to adapters and keeps the row-offset tables
+ * (lora_rows_t.row_off, chunk_len = page_elems) of n_tables row tables, e.g.
+ * the A and B tables of every projection; table t has rows of row_len[t]
+ * elements, each row taking ceil(row_len[t] / page_elems) pages.  An adapter
+ * of rank r takes sum_t r * ceil(row_len[t] / page_elems) pages.
+ * Pinned adapters (those of batches in flight) are never evicted; when the
+ * pool is short, unpinned resident adapters are evicted least recently used
+ * first.  Entries of adapters that are not resident are 0 (page 0, never read
+ * by a valid batch).  Not thread-safe: one manager per caller thread.
+ * ------------------------------------------------------------------------ */
+typedef struct lora_pool lora_pool_t;
+
+/* Errors: LORA_EINVAL (null out, non-positive sizes, n_tables outside
+ * [1, 64]), LORA_ESHAPE (page_elems or a row_len not a positive multiple of
+ * 64), LORA_ERANK (max_rank outside [1, LORA_MAX_RANK]). */
+int32_t lora_pool_create(int64_t n_pages, int32_t page_elems, int32_t n_adapters,
+                         int32_t max_rank, int32_t n_tables, const int32_t* row_len,
+                         lora_pool_t** out);
+int32_t lora_pool_destroy(lora_pool_t* pool);
+
+/* Makes the n listed adapters (ranks[i] = rank of adapters[i]) resident and
+ * pins each once (pins count; lora_pool_release drops one).  Adapters already
+ * resident with that rank only get pinned and their use time refreshed; the
+ * others get pages (evicting as above) and their ids are written to
+ * load[0 .. *n_load), in the order given: their rows must be copied in before
+ * a batch reads them (lora_pool_load_list, lora_pool_scatter).  A resident
+ * adapter listed with another rank is reloaded.  Duplicates in the list are
+ * allowed.  On LORA_ECAPACITY (the listed adapters do not fit beside the
+ * pinned ones) nothing changes.  Errors: LORA_EINVAL, LORA_EADAPTER,
+ * LORA_ERANK, LORA_ECAPACITY. */
+int32_t lora_pool_acquire(lora_pool_t* pool, int32_t n, const int32_t* adapters,
+                          const int32_t* ranks, int32_t* load, int32_t* n_load);
+
+/* Drops one pin of each listed adapter (call once the batches that used them
+ * have finished on the GPU).  Errors: LORA_EINVAL (an adapter not pinned). */
+int32_t lora_pool_release(lora_pool_t* pool, int32_t n, const int32_t* adapters);
+
+/* Host row-offset table of table t (n_adapters * max_rank * chunks int64,
+ * element offsets into the pool), valid until the next acquire; *chunks =
+ * ceil(row_len[t] / page_elems).  Adapter a's entries are the contiguous
+ * block [a * max_rank * chunks, (a + 1) * max_rank * chunks). */
+int32_t lora_pool_row_off(const lora_pool_t* pool, int32_t table, const int64_t** row_off,
+                          int32_t* chunks);
+
+/* Resident adapters, free pages and pinned adapters (any may be NULL). */
+int32_t lora_pool_stats(const lora_pool_t* pool, int32_t* n_resident, int64_t* free_pages,
+                        int32_t* n_pinned);
+
+/* Copy list that places the rows of the n listed resident adapters: source
+ * layout = the adapters in the order given, each as table 0's r rows of
+ * row_len[0] elements, then table 1's, ... (packed, no gaps); one piece per
+ * (adapter, table, rank row, chunk): src_off (elements into the packed
+ * source), dst_off (elements into the pool), len (elements, <= page_elems).
+ * Writes min(capacity, needed) pieces and *n_pieces = needed; *src_elems =
+ * packed source size.  Errors: LORA_EINVAL (an adapter not resident),
+ * LORA_ECAPACITY (capacity < needed). */
+int32_t lora_pool_load_list(const lora_pool_t* pool, int32_t n, const int32_t* adapters,
+                            int64_t capacity, int64_t* src_off, int64_t* dst_off, int32_t* len,
+                            int64_t* n_pieces, int64_t* src_elems);
+
+/* GPU: pool[dst_off[i] + e] = src[src_off[i] + e] for e < len[i], i < n
+ * (bf16 bits; src, pool, src_off, dst_off, len device; offsets in elements,
+ * multiples of 8, len a multiple of 8 and <= 65536; pieces must not
+ * overlap in the pool).  One launch on hip_stream.  Errors: LORA_EINVAL,
+ * LORA_EHIP. */
+int32_t lora_pool_scatter(const uint16_t* src, uint16_t* pool, int64_t n,
+                          const int64_t* src_off, const int64_t* dst_off, const int32_t* len,
+                          void* hip_stream);
 
 #ifdef __cplusplus
 }
