@@ -32,7 +32,7 @@ With --path split the step calls lora_shrink and lora_expand instead.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--path apply|split]
                        [--no-cpu-baseline]
-       python bench.py --workload tiny|prefill|vision|mix70b|mixture   (kernel timing of the other workloads)
+       python bench.py --workload tiny|prefill|vision|mix70b|mixture|swap   (the other workloads; swap: adapter pool)
        python bench.py --workload prefill|vision --shared-x           (the same with q/k/v reading one x)
        python bench.py --copy-calibration                             (counter calibration under rocprofv3)
        python bench.py --rmw-ceiling                                  (in-place streaming rate of this HBM)
@@ -212,7 +212,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="layer copies the steps rotate over")
     ap.add_argument("--workload", default="decode", choices=["decode", "tiny", "prefill", "vision", "mix70b",
-                                                             "mixture"],
+                                                             "mixture", "swap"],
                     help="decode (default) is the benchmark line; the others time shrink+expand (and the "
                          "vision mode switch) of that workload for the kernel tables")
     ap.add_argument("--path", default="apply", choices=["apply", "split"],
@@ -236,6 +236,8 @@ def main():
 
     if args.workload == "mixture":
         return mixture_workload(args)
+    if args.workload == "swap":
+        return swap_workload(args)
     if args.workload != "decode":
         return other_workload(args)
     import torch
@@ -524,6 +526,118 @@ def mixture_workload(args):
                                 "hbm_frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
     out["mixture_over_unmerged"] = round(out["kernels"]["mixture_apply"]["us_median"] /
                                          out["kernels"]["unmerged_apply"]["us_median"], 3)
+    print(json.dumps(out), flush=True)
+
+
+def swap_workload(args):
+    """Unified adapter pool (S-LoRA's unified paging): the vision workload's
+    32 rank-64 adapters (q/k/v/o: 8 row tables of 4096) paged on demand into
+    a pool that holds 16 of them.  Reports (1) copy-in of 16 adapters (packed
+    rows host -> device, then the scatter into their pages) on the pool's
+    stream, (2) the scatter kernel alone, against HBM, and (3) the vision
+    shrink + expand on the compute stream alone and with a copy-in of 16
+    other adapters running beside it on the pool's stream."""
+    import torch
+    import workloads
+    from heterogeneous_adapter_batching_amd.session import AdapterPool, Batch, HipEvent, Rows
+    from heterogeneous_adapter_batching_amd import lora_pool_scatter
+    from workloads.device import to_device
+
+    W = workloads.gen_config(3, n_layers=1)
+    dw = to_device(W)
+    n_ad, r = W.n_adapters, int(W.adapter_rank.max())
+    tables = [d for p in W.projections for d in (p.A, p.B)]
+
+    def rows_of_adapter(a):
+        out = []
+        for d in tables:
+            blk = np.empty((int(W.adapter_rank[a]), d.row_len), np.uint16)
+            for j in range(blk.shape[0]):
+                o = int(d.row_off[(a * d.max_rank + j) * d.chunks])
+                blk[j] = W.pool[o:o + d.row_len]
+            out.append(blk)
+        return out
+    host_rows = {a: rows_of_adapter(a) for a in range(n_ad)}
+    page = 4096
+    per_adapter = r * sum(d.row_len for d in tables) * 2          # bytes
+    pool = AdapterPool(16 * r * len(tables), page, n_ad, r, [d.row_len for d in tables], host_rows.__getitem__)
+    res = {"copy_in_16": [], "scatter_16": [], "compute_alone": [], "compute_with_copy_in": []}
+    # the vision batch on the compute stream, from the dense layout
+    rows = lambda desc, off: Rows(dw.pool, off, desc.n_adapters, desc.max_rank, desc.row_len, desc.chunk_len)
+    A = [rows(p.A, d.A_off) for p, d in zip(W.projections, dw.projections)]
+    B = [rows(p.B, d.B_off) for p, d in zip(W.projections, dw.projections)]
+    b = Batch(W.n_rows, W.adapter_rank, 4096, 4096).refresh(W.row_adapter)
+    v = [b.new_v(r) for _ in W.projections]
+    do_s = b.prepare_shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)])
+    do_e = b.prepare_expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
+    compute = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    sets = [np.arange(0, 16), np.arange(16, 32)]
+    cur = 1  # the set resident last (none yet): each acquire below loads the other one
+    for it in range(args.warmup + args.steps):
+        for _ in range(2):
+            cur = 1 - cur
+            S = sets[cur]
+            flush.fill_(it & 0xFF)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            load = pool.acquire(S, W.adapter_rank[S])
+            t1 = time.perf_counter()
+            assert len(load) == 16
+            pool.release_after(S, pool.stream)
+            pool.drain()
+            if it >= args.warmup:
+                res["copy_in_16"].append(pool.last_upload_ms() * 1e3)
+                res.setdefault("host_pack_16", []).append((t1 - t0) * 1e3)  # ms: manager + packing + enqueue
+            # the scatter alone, from the packed rows now on the device
+            so, do, ln, n_src = pool.mgr.load_list(S)
+            d_so, d_do = torch.from_numpy(so).cuda(), torch.from_numpy(do).cuda()
+            d_ln = torch.from_numpy(ln).cuda()
+            torch.cuda.synchronize()
+            e = [HipEvent(timing=True) for _ in range(2)]
+            e[0].record(compute)
+            lora_pool_scatter(pool._stage[1].data_ptr(), pool.pool.data_ptr(), so.shape[0], d_so.data_ptr(),
+                              d_do.data_ptr(), d_ln.data_ptr(), compute.cuda_stream)
+            e[1].record(compute)
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                res["scatter_16"].append(e[0].elapsed_time(e[1]) * 1e3)
+        # compute alone, then with the copy-in of the set not resident
+        for name in ("compute_alone", "compute_with_copy_in"):
+            flush.fill_(it & 0xFF)
+            torch.cuda.synchronize()
+            if name == "compute_with_copy_in":
+                # the copy-in is enqueued (host packing done) before the compute starts
+                cur = 1 - cur
+                S = sets[cur]
+                assert len(pool.acquire(S, W.adapter_rank[S])) == 16
+            e = [HipEvent(timing=True) for _ in range(2)]
+            e[0].record(compute)
+            do_s()
+            do_e()
+            e[1].record(compute)
+            torch.cuda.synchronize()
+            if name == "compute_with_copy_in":
+                pool.release_after(S, pool.stream)
+                pool.drain()
+            if it >= args.warmup:
+                res[name].append(e[0].elapsed_time(e[1]) * 1e3)
+    med = {k: float(np.median(v_)) for k, v_ in res.items()}
+    nbytes = 16 * per_adapter
+    out = {"workload": "swap", "adapters": n_ad, "rank": r, "pool_adapters": 16,
+           "adapter_bytes": per_adapter, "kernels": {
+               "copy_in_16": {"us_median": round(med["copy_in_16"], 1), "bytes": nbytes,
+                              "GB_s": round(nbytes / med["copy_in_16"] / 1e3, 1),
+                              "what": "device time on the pool stream: host->device copy of the packed rows, "
+                                      "scatter into pages, table entries",
+                              "host_acquire_ms": round(med["host_pack_16"], 2)},
+               "scatter_16": {"us_median": round(med["scatter_16"], 2), "alg_bytes": 2 * nbytes,
+                              "GB_s": round(2 * nbytes / med["scatter_16"] / 1e3, 1),
+                              "hbm_frac": round(2 * nbytes / med["scatter_16"] / 1e3 / HBM_PEAK_GBS, 4)},
+               "vision_shrink_expand": {"alone_us": round(med["compute_alone"], 1),
+                                        "with_copy_in_us": round(med["compute_with_copy_in"], 1),
+                                        "what": "one layer's shrink + expand on the compute stream, alone and "
+                                                "while the pool stream copies 16 adapters in"}}}
     print(json.dumps(out), flush=True)
 
 

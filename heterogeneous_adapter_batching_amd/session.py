@@ -375,6 +375,7 @@ class AdapterPool:
         self._pending = []           # (event, adapters): pins to drop once the event completes
         self._stage = self._meta = None
         self.loaded = 0              # adapters copied in so far
+        self._t = (HipEvent(timing=True), HipEvent(timing=True))  # around the last upload's device work
 
     def rows(self, table):
         """lora_rows_t descriptor of row table `table` in the pool."""
@@ -436,6 +437,7 @@ class AdapterPool:
             tab, _ = self.mgr.row_off(t)
             m[o:o + per[t]] = tab[a * per[t]:(a + 1) * per[t]]
             o += per[t]
+        self._t[0].record(self.stream)
         with torch.cuda.stream(self.stream):
             ds[:n_src].copy_(hs[:n_src], non_blocking=True)
             dm[:n_meta].copy_(hm[:n_meta], non_blocking=True)
@@ -448,6 +450,7 @@ class AdapterPool:
                 self.tables[t][a * per[t]:(a + 1) * per[t]].copy_(dm[o:o + per[t]])
                 o += per[t]
             self._lens = lens    # kept alive until the next upload
+        self._t[1].record(self.stream)
         self._done.record(self.stream)
         self._uploading = True
         self.loaded += len(load)
@@ -456,6 +459,12 @@ class AdapterPool:
         """Resident rank of adapter a (from its copy list size)."""
         so, _, ln, n_src = self.mgr.load_list([int(a)])
         return n_src // sum(self.row_len)
+
+    def last_upload_ms(self):
+        """Device time of the last upload (host-to-device copies, scatter and
+        table entries on the pool's stream), once it has completed."""
+        self._t[1].synchronize()
+        return self._t[0].elapsed_time(self._t[1])
 
     def wait(self, stream=None):
         """Make `stream` wait for the copies enqueued so far."""
