@@ -32,7 +32,8 @@ With --path split the step calls lora_shrink and lora_expand instead.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--path apply|split]
                        [--no-cpu-baseline]
-       python bench.py --workload tiny|prefill|vision|mix70b|mixture|swap   (the other workloads; swap: adapter pool)
+       python bench.py --workload tiny|prefill|vision|mix70b|mixture|swap|heads
+                       (the other workloads; swap: adapter pool; heads: per-adapter vision task heads)
        python bench.py --workload prefill|vision --shared-x           (the same with q/k/v reading one x)
        python bench.py --copy-calibration                             (counter calibration under rocprofv3)
        python bench.py --rmw-ceiling                                  (in-place streaming rate of this HBM)
@@ -212,7 +213,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="layer copies the steps rotate over")
     ap.add_argument("--workload", default="decode", choices=["decode", "tiny", "prefill", "vision", "mix70b",
-                                                             "mixture", "swap"],
+                                                             "mixture", "swap", "heads"],
                     help="decode (default) is the benchmark line; the others time shrink+expand (and the "
                          "vision mode switch) of that workload for the kernel tables")
     ap.add_argument("--path", default="apply", choices=["apply", "split"],
@@ -238,6 +239,8 @@ def main():
         return mixture_workload(args)
     if args.workload == "swap":
         return swap_workload(args)
+    if args.workload == "heads":
+        return heads_workload(args)
     if args.workload != "decode":
         return other_workload(args)
     import torch
@@ -638,6 +641,52 @@ def swap_workload(args):
                                         "with_copy_in_us": round(med["compute_with_copy_in"], 1),
                                         "what": "one layer's shrink + expand on the compute stream, alone and "
                                                 "while the pool stream copies 16 adapters in"}}}
+    print(json.dumps(out), flush=True)
+
+
+def heads_workload(args):
+    """Vision task heads (VaLoRA 4.2.2): each of the vision workload's 32
+    adapters carries a head with U{2..128} classes (one linear layer over
+    d 4096), all heads in one launch: logits = x . H_a^T for every row, the
+    shrink kernels with the head's class rows as the A table.  Input: the
+    vision workload's rows and adapter choice; heads drawn like A."""
+    import torch
+    import workloads
+    from heterogeneous_adapter_batching_amd.session import Batch, HipEvent, Rows
+    from workloads.device import to_device
+
+    V = workloads.gen_config(3, n_layers=1)
+    classes = np.random.default_rng([3, 7]).integers(2, 129, size=V.n_adapters).astype(np.int32)
+    W = workloads.gen_custom(3, V.row_adapter, classes, 4096, 64, n_proj=1, layout="dense")
+    dw = to_device(W)
+    p, d = W.projections[0], dw.projections[0]
+    H = Rows(dw.pool, d.A_off, p.A.n_adapters, p.A.max_rank, p.A.row_len, p.A.chunk_len)
+    b = Batch(W.n_rows, W.adapter_rank, 4096, 64).refresh(W.row_adapter)
+    v = [b.new_v(128)]
+    run = b.prepare_shrink([(d.x, H, v[0])])
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ts = []
+    for it in range(args.warmup + args.steps):
+        flush.fill_(it & 0xFF)
+        e = [HipEvent(timing=True) for _ in range(2)]
+        e[0].record()
+        run()
+        e[1].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            ts.append(e[0].elapsed_time(e[1]) * 1e3)
+    act = W.row_adapter[W.row_adapter >= 0]
+    c_act = classes[act].astype(np.int64)
+    distinct = np.unique(act)
+    nbytes = int(act.size * 4096 * 2 + classes[distinct].sum() * 4096 * 2 + c_act.sum() * 4 * b.v_slices)
+    flops = int(2 * 4096 * c_act.sum())
+    us = float(np.median(ts))
+    out = {"workload": "heads", "rows": int(act.size), "heads": int(V.n_adapters),
+           "classes_min_max": [int(classes.min()), int(classes.max())],
+           "kernels": {"heads_shrink": {"us_median": round(us, 2), "alg_bytes": nbytes,
+                                        "GB_s": round(nbytes / us / 1e3, 1),
+                                        "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                                        "TFLOP_s": round(flops / us / 1e6, 2)}}}
     print(json.dumps(out), flush=True)
 
 

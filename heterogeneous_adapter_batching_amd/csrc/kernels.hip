@@ -564,11 +564,12 @@ __device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const l
 // would lower the occupancy of the others).
 template <int MTW, int NTMAX, bool WHOLE_ROWS, int GS>
 __global__ __launch_bounds__(WG) void shrink_rows_kernel(ShrinkArgs args) {
-    // LDS stages: three steps in flight below rank 64 (96 KiB with one
-    // projection per task: one workgroup per CU; measured against two and
-    // three stages: prefill -11%, vision -1%, 70B mix +1%; 160 KiB with
-    // three A tiles per stage), one above
-    constexpr int NBUF = NTMAX == 8 ? 2 : 4;
+    // LDS stages: three steps in flight (96 KiB with one projection per task
+    // and rank <= 64: one workgroup per CU; measured against two and three
+    // stages: prefill -11%, vision -1%, 70B mix +1%; 128 KiB above rank 64,
+    // where one step in flight was 4% slower on the class heads; 160 KiB with
+    // three A tiles per stage)
+    constexpr int NBUF = 4;
     __shared__ u32x4_t sX[NBUF * 64 * MTW * 8];         // NBUF buffers x 64*MTW rows x 8 pieces of 16 B
     __shared__ u32x4_t sA[NBUF * GS * 16 * NTMAX * 8];  // NBUF x GS buffers x 16*NT rank rows x 8 pieces
     const int n_units = GS == 1 ? args.n_proj : args.n_groups;

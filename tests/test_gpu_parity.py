@@ -390,3 +390,41 @@ def test_shared_x_against_separate_copies():
         rel = np.linalg.norm(d_g - d_s) / np.linalg.norm(d_s)
         _say("shared vs separate x, projection", pi, rel)
         assert rel <= 1e-5
+
+
+# ------------------------------------------------------------------ vision task heads
+def test_task_heads_in_one_launch():
+    """Per-adapter vision task heads (VaLoRA 4.2.2: a linear layer that is part
+    of the adapter replaces the LM head for tasks with a small label set) are
+    a shrink whose A rows are the head's class rows: logits = x . H_a^T, with
+    heads of different widths in one launch and the LM-head rows (-1) left
+    alone."""
+    rng = np.random.default_rng(23)
+    classes = np.array([10, 37, 100, 3, 128], np.int32)
+    lens = [300, 2, 270, 1, 40]
+    ra = np.concatenate([np.repeat(np.arange(5), lens), np.full(25, -1)]).astype(np.int32)
+    ra = ra[rng.permutation(ra.shape[0])]
+    d = 2048
+    W = workloads.gen_custom(23, ra, classes, d, 64, n_proj=1, layout="paged", page_elems=512)
+    batch, vs, ys = run_delta(W)   # the expand half is ordinary LoRA work on the same rows
+    p = W.projections[0]
+    _, vref = oracle.apply_ref(W.row_adapter, W.adapter_rank, p.x, p.y0, W.pool, p.A, p.B, W.scale)
+    pos = {int(r): i for i, r in enumerate(batch.segs.row_index)}
+    seg_slices = {}
+    for w in batch.work_expand:
+        for q in range(int(w[0]), int(w[0]) + int(w[1])):
+            seg_slices[q] = int(w[5])
+    worst = 0.0
+    for i in range(W.n_rows):
+        a = int(W.row_adapter[i])
+        if a < 0:
+            assert i not in pos
+            continue
+        c = int(classes[a])
+        logits = vs[0][:seg_slices[pos[i]], pos[i], :].sum(axis=0)
+        ref = vref[i]
+        assert logits.shape[0] >= c and np.all(np.isnan(vs[0][:, pos[i], c:])), "columns past the head's width written"
+        err = np.abs(logits[:c] - ref) / (1e-3 + np.abs(ref).max())
+        worst = max(worst, float(err.max()))
+    _say("task heads: worst relative logit error", worst)
+    assert worst <= 1e-4
