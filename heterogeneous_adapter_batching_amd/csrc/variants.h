@@ -42,6 +42,7 @@ static inline int32_t lv_expand_rows(int shape) {
 #define LV_APPLY_VARIANTS (LV_APPLY_FUSED + 1)
 // The fused kernel covers d_in and d_out up to 8 x half its 1024 threads.
 #define LV_FUSED_MAX_D 4096
+#define LV_FUSED_MAX_ROWRANK 1024  // segments of more than one row are fused while len * rank <= this
 
 // Columns one expand workgroup covers.
 static inline int32_t lv_expand_cols(int shape) { return shape == LV_E_BGMV ? 2048 : 512; }

@@ -254,7 +254,8 @@ def _apply_check(W, ra=None):
 def test_apply_decode_parity(which):
     W = workloads.gen_config(1)
     n_fused = _apply_check(W, W.batches[which])
-    assert n_fused == (64 if which == "hetero" else 0)
+    # hetero: 64 one-row segments; homo: one 64-row rank-16 segment, fused row by row (64 * 16 <= 1024)
+    assert n_fused == 64
 
 
 def test_apply_tiny_and_mixed_lengths():

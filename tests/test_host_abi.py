@@ -300,9 +300,10 @@ def test_batch_prepare_errors_and_size():
 
 
 def test_apply_plan_partitions_segments():
-    """An apply plan fuses exactly the one-row segments with d_in, d_out <= 4096;
-    every other segment is covered by its shrink items (each row x K slice
-    once) and its expand items (each row once); fused items cover one row."""
+    """An apply plan fuses exactly the segments of one row, or of len * rank
+    <= 1024, with d_in, d_out <= 4096 (one item per row); every other segment
+    is covered by its shrink items (each row x K slice once) and its expand
+    items (each row once); fused items cover one row."""
     N_SHRINK = 3 * 4            # shrink variants
     FUSED = N_SHRINK + 5 * 4    # the fused variant follows the expand variants
     rng = np.random.default_rng(12)
@@ -337,10 +338,11 @@ def test_apply_plan_partitions_segments():
             assert info.v_slices <= max(1, info_s.v_slices)
             for s in range(segs.n_seg):
                 lo, hi = int(segs.seg_start[s]), int(segs.seg_start[s + 1])
-                fused = hi - lo == 1 and d_in <= 4096 and d_out <= 4096
-                assert (lo in fused_rows) == fused
+                rk = int(segs.seg_rank[s])
+                fused = (hi - lo == 1 or (hi - lo) * rk <= 1024) and d_in <= 4096 and d_out <= 4096
+                assert all((q in fused_rows) == fused for q in range(lo, hi))
                 if fused:
-                    assert np.all(cov_s[lo] == 0)
+                    assert np.all(cov_s[lo:hi] == 0)
                 else:
                     ns = int(work[[i for i in range(work.shape[0]) if work[i, 0] == lo][0], 5])
                     assert np.all(cov_s[lo:hi, :ns] == 1) and np.all(cov_s[lo:hi, ns:] == 0)
