@@ -15,7 +15,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
-LORA_ABI_VERSION = 7
+LORA_ABI_VERSION = 8
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
 LORA_MAX_RANGES = 48
@@ -66,7 +66,20 @@ class lora_plan_info_t(ctypes.Structure):
 
 
 class lora_launch_t(ctypes.Structure):
-    _fields_ = [("row_index", _vp), ("work", _vp), ("info", lora_plan_info_t)]
+    _fields_ = [("row_index", _vp), ("work", _vp), ("info", lora_plan_info_t), ("live", _vp)]
+
+
+class lora_device_plan_t(ctypes.Structure):
+    _fields_ = [("n_rows", _i32), ("n_adapters", _i32), ("max_rank", _i32), ("d_in", _i32), ("d_out", _i32),
+                ("seg_capacity", _i32), ("work_capacity", _i32), ("reserved", _i32),
+                ("off_row_index", _i64), ("off_seg_start", _i64), ("off_seg_adapter", _i64),
+                ("off_seg_rank", _i64), ("off_scratch", _i64), ("off_work", _i64), ("workspace_bytes", _i64),
+                ("info", lora_plan_info_t)]
+
+
+class lora_device_header_t(ctypes.Structure):
+    _fields_ = [("status", _i32), ("n_seg", _i32), ("n_active", _i32), ("n_work", _i32),
+                ("live", _i32 * LORA_MAX_RANGES)]
 
 
 class lora_batch_t(ctypes.Structure):
@@ -107,6 +120,8 @@ _sig = {
     "lora_mixture_rows": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "lora_batch_prepare": (_i32, [_i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_uint32, _i32, _vp, _vp, _vp, _vp,
                                   _i64, _vp, _vp, _P(lora_batch_t)]),
+    "lora_device_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _P(lora_device_plan_t)]),
+    "lora_batch_build_device": (_i32, [_P(lora_device_plan_t), _vp, _vp, _vp, _vp, _P(lora_launch_t)]),
     "lora_pool_create": (_i32, [_i64, _i32, _i32, _i32, _i32, _vp, _P(_vp)]),
     "lora_pool_destroy": (_i32, [_vp]),
     "lora_pool_acquire": (_i32, [_vp, _i32, _vp, _vp, _vp, _P(_i32)]),
@@ -169,6 +184,29 @@ def lora_batch_prepare(row_adapter, adapter_rank, d_in, d_out, op_mask, staging,
     if not raw:
         _check(st, "lora_batch_prepare")
     return st, out, segs
+
+
+def lora_device_plan(n_rows, n_adapters, max_rank, d_in, d_out, raw=False):
+    """Layout of a device-built apply plan for the given bounds: returns
+    (status, lora_device_plan_t); raises LoraError unless raw=True."""
+    out = lora_device_plan_t()
+    st = _lib.lora_device_plan(int(n_rows), int(n_adapters), int(max_rank), int(d_in), int(d_out),
+                               ctypes.byref(out))
+    if not raw:
+        _check(st, "lora_device_plan")
+    return st, out
+
+
+def lora_batch_build_device(plan, row_adapter_ptr, adapter_rank_ptr, workspace_ptr, stream=None, raw=False):
+    """Enqueue the device plan builder on `stream` (device pointers in,
+    nothing copied).  Returns (status, lora_launch_t); raises LoraError unless
+    raw=True.  The device-side status is in the workspace header."""
+    out = lora_launch_t()
+    st = _lib.lora_batch_build_device(ctypes.byref(plan), row_adapter_ptr, adapter_rank_ptr, workspace_ptr, stream,
+                                      ctypes.byref(out))
+    if not raw:
+        _check(st, "lora_batch_build_device")
+    return st, out
 
 
 class LoraPool:

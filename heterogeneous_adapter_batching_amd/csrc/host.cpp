@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/hetlora.h"
@@ -14,6 +15,7 @@
 #endif
 namespace {
 #include HETLORA_TILE_TABLE
+#include "plan_rules.h"
 }
 
 extern "C" int32_t lora_abi_version(void) { return LORA_ABI_VERSION; }
@@ -79,66 +81,6 @@ extern "C" int32_t lora_build_segments(int32_t n_rows, const int32_t* row_adapte
     return LORA_OK;
 }
 
-namespace {
-
-struct SegCfg {
-    int shape;
-    int32_t slices;
-};
-
-// Shape and K-slice count of a segment for one op.  The slice count always
-// comes from the shrink table (with d_in), so the shrink and expand plans of
-// one batch agree on it.
-SegCfg pick(int32_t op, int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
-    const int lb = lv_len_bucket(len), rb = lv_rank_bucket(rank);
-    const ShrinkCfg sc = kShrinkCfg[lb][rb][lv_d_bucket(d_in)];
-    int32_t slices = sc.slices < 1 ? 1 : sc.slices;
-    if (slices > LORA_MAX_SLICES) slices = LORA_MAX_SLICES;
-    if (slices > d_in / 64) slices = d_in / 64;
-    if (op == LORA_OP_SHRINK) return SegCfg{sc.shape, slices};
-    return SegCfg{kExpandShape[lb][rb][lv_d_bucket(d_out)], slices};
-}
-
-}  // namespace
-
-namespace {
-
-// One segment's share of a plan.
-struct SegPlan {
-    int variant;      // op-local variant id
-    int32_t chunks;   // row chunks
-    int32_t slices;   // K slices of the shrink (1 for expand-only / fused)
-    int32_t mt;       // rows per item
-    bool shrink;      // items carry K slices (one item per chunk x slice)
-};
-
-// Shrink and expand parts of a segment (the expand variant is op-local to an
-// expand plan; an apply plan shifts it by LV_APPLY_EXPAND0).
-SegPlan shrink_part(int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
-    const SegCfg c = pick(LORA_OP_SHRINK, len, rank, d_in, d_out);
-    const int32_t mt = lv_shrink_rows(c.shape);
-    return SegPlan{c.shape * LV_RANK_CLASSES + lv_shrink_class(rank), (len + mt - 1) / mt, c.slices, mt, true};
-}
-SegPlan expand_part(int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
-    const SegCfg c = pick(LORA_OP_EXPAND, len, rank, d_in, d_out);
-    const int32_t mt = lv_expand_rows(c.shape);
-    const int cls = c.shape == LV_E_BGMV ? 0 : lv_expand_class(rank);
-    return SegPlan{c.shape * LV_RANK_CLASSES + cls, (len + mt - 1) / mt, c.slices, mt, false};
-}
-// Segments whose rows' whole reductions fit one workgroup each are fused in
-// an apply plan (one item per row; the shrink result never leaves the chip):
-// one-row segments always, and short segments while len * rank stays small.
-// Each fused row re-reads the adapter's A and B rows (from L2 after the
-// first), which beats the two-kernel path below that product: a 64-row
-// rank-16 segment at d 4096 over q/k/v/o takes 11.1 us fused against 15.5 us
-// as shrink + expand.
-bool fused(int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
-    return (len == 1 || (int64_t)len * rank <= LV_FUSED_MAX_ROWRANK) && d_in <= LV_FUSED_MAX_D &&
-           d_out <= LV_FUSED_MAX_D;
-}
-
-}  // namespace
-
 // Launch plan: every segment is cut into ceil(len / rows_per_item) row chunks
 // whose sizes differ by at most one row; a shrink item is one row chunk x one
 // K slice, an expand item one row chunk.  An apply plan holds, per segment,
@@ -172,17 +114,12 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
     for (int32_t s = 0; s < n_seg; ++s) {
         const int32_t len = seg_start[s + 1] - seg_start[s], r = seg_rank[s];
         SegPlan a{-1, 0, 1, 1, false}, b{-1, 0, 1, 1, false};
-        if (op == LORA_OP_SHRINK) {
-            a = shrink_part(len, r, d_in, d_out);
-        } else if (op == LORA_OP_EXPAND) {
-            a = expand_part(len, r, d_in, d_out);
-        } else if (fused(len, r, d_in, d_out)) {
-            a = SegPlan{LV_APPLY_FUSED, len, 1, 1, false};  // one item per row
-        } else {
-            a = shrink_part(len, r, d_in, d_out);
-            b = expand_part(len, r, d_in, d_out);
-            b.variant += LV_APPLY_EXPAND0;
-        }
+        if (op == LORA_OP_SHRINK)
+            a = lv_shrink_part(len, r, d_in, d_out);
+        else if (op == LORA_OP_EXPAND)
+            a = lv_expand_part(len, r, d_in, d_out);
+        else
+            lv_apply_parts(len, r, d_in, d_out, a, b);
         for (SegPlan* q : {&a, &b}) {
             if (q->variant < 0) continue;
             const int32_t items = q->chunks * (q->shrink ? q->slices : 1);
@@ -310,5 +247,97 @@ extern "C" int32_t lora_mixture_rows(int32_t n_adapters, int32_t max_rank, const
         out_rank[a] = r;
         out_neg_from[a] = a == merged ? rm : ra;
     }
+    return LORA_OK;
+}
+
+// Layout of a device-built apply plan.  A segment's parts depend only on its
+// (length bucket, rank class) box, so the variants a batch can need follow
+// from enumerating the boxes that the bounds allow.  A variant's capacity
+// adds up, over the boxes that reach it, the most items the box's segments
+// can produce: a non-fused segment in a box has at least `lnf` rows, so the
+// box holds at most min(n_adapters, n_rows / lnf) of them, and their row
+// chunks of mt rows number at most n_rows / mt plus one per segment (and at
+// most ceil(len_max / mt) per segment).  Fused items are one per row, so at
+// most n_rows in all.
+namespace {
+constexpr int32_t kLenLo[LV_LEN_BUCKETS] = {1, 2, 5, 9, 17, 33, 65, 257};
+constexpr int32_t kLenHi[LV_LEN_BUCKETS] = {1, 4, 8, 16, 32, 64, 256, INT32_MAX};
+int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+int64_t chunk_bound(int64_t n_rows, int64_t nseg, int32_t len_max, int32_t mt) {
+    const int64_t a = nseg * ((len_max + (int64_t)mt - 1) / mt), b = n_rows / mt + nseg;
+    return a < b ? a : b;
+}
+}  // namespace
+
+extern "C" int32_t lora_device_plan(int32_t n_rows, int32_t n_adapters, int32_t max_rank, int32_t d_in,
+                                    int32_t d_out, lora_device_plan_t* out) {
+    if (out == nullptr || n_rows < 1 || n_rows > 65536 || n_adapters < 1 || n_adapters > 4096) return LORA_EINVAL;
+    if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERANK;
+    if (d_in <= 0 || d_out <= 0 || d_in % 64 != 0 || d_out % 64 != 0) return LORA_ESHAPE;
+    std::vector<int64_t> cap(LV_APPLY_VARIANTS, 0);
+    std::vector<int32_t> rows_per(LV_APPLY_VARIANTS, 1);
+    int32_t v_slices = 1;
+    for (int c = 0; c <= lv_shrink_class(max_rank); ++c) {
+        const int32_t rlo = c == 0 ? 1 : (8 << c) + 1, rhi = (16 << c) < max_rank ? (16 << c) : max_rank;
+        for (int b = 0; b < LV_LEN_BUCKETS; ++b) {
+            const int32_t llo = kLenLo[b], lhi = kLenHi[b] < n_rows ? kLenHi[b] : n_rows;
+            if (llo > lhi) continue;
+            // fusing is monotone: shorter segments and smaller ranks stay fused
+            if (lv_fused(llo, rlo, d_in, d_out)) cap[LV_APPLY_FUSED] = n_rows;
+            if (lv_fused(lhi, rhi, d_in, d_out)) continue;
+            int32_t lnf = llo;  // shortest non-fused segment of the box
+            while (lv_fused(lnf, rhi, d_in, d_out)) ++lnf;
+            const int64_t nseg = std::min<int64_t>(n_adapters, n_rows / lnf);
+            SegPlan sp, ep;
+            lv_apply_parts(lhi, rhi, d_in, d_out, sp, ep);  // same variants for every member of the box
+            cap[(size_t)sp.variant] += chunk_bound(n_rows, nseg, lhi, sp.mt) * sp.slices;
+            cap[(size_t)ep.variant] += chunk_bound(n_rows, nseg, lhi, ep.mt);
+            rows_per[(size_t)sp.variant] = sp.mt;
+            rows_per[(size_t)ep.variant] = ep.mt;
+            if (sp.slices > v_slices) v_slices = sp.slices;
+        }
+    }
+    lora_device_plan_t p;
+    memset(&p, 0, sizeof(p));
+    p.n_rows = n_rows;
+    p.n_adapters = n_adapters;
+    p.max_rank = max_rank;
+    p.d_in = d_in;
+    p.d_out = d_out;
+    p.seg_capacity = n_rows < n_adapters ? n_rows : n_adapters;
+    lora_plan_info_t& I = p.info;
+    I.op = LORA_OP_APPLY;
+    I.n_active = n_rows;
+    I.max_rank = max_rank;
+    I.max_adapter = n_adapters - 1;
+    I.v_slices = v_slices;
+    int64_t begin = 0;
+    for (int v = 0; v < LV_APPLY_VARIANTS; ++v) {
+        if (cap[(size_t)v] == 0) continue;
+        if (I.n_ranges == LORA_MAX_RANGES || begin + cap[(size_t)v] > INT32_MAX / 2) return LORA_EINVAL;
+        lora_range_t& R = I.ranges[I.n_ranges++];
+        R.variant = v;
+        R.begin = (int32_t)begin;
+        R.count = (int32_t)cap[(size_t)v];
+        R.rows_per_item = rows_per[(size_t)v];
+        begin += cap[(size_t)v];
+    }
+    I.n_work = (int32_t)begin;
+    p.work_capacity = (int32_t)begin;
+    int64_t off = align256(sizeof(lora_device_header_t));
+    p.off_row_index = off;
+    off += align256(4 * (int64_t)n_rows);
+    p.off_seg_start = off;
+    off += align256(4 * ((int64_t)p.seg_capacity + 1));
+    p.off_seg_adapter = off;
+    off += align256(4 * (int64_t)p.seg_capacity);
+    p.off_seg_rank = off;
+    off += align256(4 * (int64_t)p.seg_capacity);
+    p.off_scratch = off;
+    off += align256(4 * (int64_t)n_rows);
+    p.off_work = off;
+    off += align256((int64_t)sizeof(lora_work_t) * begin);
+    p.workspace_bytes = off;
+    *out = p;
     return LORA_OK;
 }

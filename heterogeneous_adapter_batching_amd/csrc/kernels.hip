@@ -42,6 +42,7 @@
 #include <mutex>
 
 #include "../../include/hetlora.h"
+#define LV_TABLE_SPACE __constant__
 #include "variants.h"
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -157,6 +158,12 @@ __device__ __forceinline__ bool item_ok(const lora_work_t& it, int32_t n_active,
            (it.adapter < t.n_adapters) & (it.rank >= 1) & (it.rank <= rank_cap) & (it.rank <= t.max_rank) &
            (it.nslices >= 1) & (it.nslices <= v_slices) & (it.kslice >= 0) & (it.kslice < it.nslices);
 }
+// Item `i` of a launch is in use: every item of a host-built plan; for a
+// device-built plan (live != NULL) only those below the range's live count.
+// The item itself may be loaded before this is known: the launch never
+// exceeds the range's capacity, so the load stays inside the work list.
+__device__ __forceinline__ bool item_live(const int32_t* live, int i) { return !live || i < *live; }
+
 // Index into row_off of chunk `c` of row j of adapter a.
 __device__ __forceinline__ int64_t off_index(const Rows& t, int32_t a, int32_t j, int32_t c) {
     return ((int64_t)a * t.max_rank + j) * t.chunks + c;
@@ -174,6 +181,7 @@ struct ShrinkProj {
 struct ShrinkArgs {
     const int32_t* row_index;
     const lora_work_t* work;
+    const int32_t* live;  // device-built plan: items of the range (NULL: all `count`)
     int32_t begin;
     int32_t n_active;
     int32_t v_slices;
@@ -197,7 +205,9 @@ template <int KSPLIT, int MTW, int NT, int U>
 __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
     const lora_work_t it = args.work[args.begin + blockIdx.x];
     const ShrinkProj& P = args.p[blockIdx.y];
-    if (!item_ok(it, args.n_active, args.v_slices, P.A, 16 * NT) || it.nrows > 16 * MTW * (KSPLIT > 1 ? 1 : 4)) return;
+    if (!item_live(args.live, blockIdx.x) || !item_ok(it, args.n_active, args.v_slices, P.A, 16 * NT) ||
+        it.nrows > 16 * MTW * (KSPLIT > 1 ? 1 : 4))
+        return;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int li = lane & 15, lg = lane >> 4;
     const int mbase = KSPLIT > 1 ? 0 : wave * 16 * MTW;
@@ -573,10 +583,11 @@ __global__ __launch_bounds__(WG) void shrink_rows_kernel(ShrinkArgs args) {
     __shared__ u32x4_t sX[NBUF * 64 * MTW * 8];         // NBUF buffers x 64*MTW rows x 8 pieces of 16 B
     __shared__ u32x4_t sA[NBUF * GS * 16 * NTMAX * 8];  // NBUF x GS buffers x 16*NT rank rows x 8 pieces
     const int n_units = GS == 1 ? args.n_proj : args.n_groups;
-    const int ntasks = args.count * n_units;
+    const int count = args.live ? min(args.count, *args.live) : args.count;
+    const int ntasks = count * n_units;
     for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
-        const int unit = task / args.count;
-        const lora_work_t it = args.work[args.begin + task - unit * args.count];
+        const int unit = task / count;
+        const lora_work_t it = args.work[args.begin + task - unit * count];
         int pj[4] = {unit, unit, unit, unit};
         int ng = 1;
         if (GS > 1) {
@@ -632,6 +643,7 @@ struct ExpandProj {
 struct ExpandArgs {
     const int32_t* row_index;
     const lora_work_t* work;
+    const int32_t* live;  // device-built plan: items of the range (NULL: all `count`)
     int32_t begin;
     int32_t n_active;
     int32_t v_slices;
@@ -672,7 +684,9 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     while (pi + 1 < args.n_proj && cg >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
     // uniform over the workgroup, so returning here skips no barrier
-    if (!(item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS) & (it.nrows <= EXPAND_ROWS))) return;
+    if (!(item_live(args.live, item) & item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS) &
+          (it.nrows <= EXPAND_ROWS)))
+        return;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int li = lane & 15, lg = lane >> 4;
     // The wave's 128 columns are two halves of 64 (d_out is a multiple of
@@ -851,7 +865,9 @@ __global__ __launch_bounds__(WG) void bgmv_expand_kernel(ExpandArgs args) {
     int pi = 0;
     while (pi + 1 < args.n_proj && (int)blockIdx.y >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
-    if (!item_ok(it, args.n_active, args.v_slices, P.B, LORA_MAX_RANK) || it.nrows > BGMV_ROWS) return;
+    if (!item_live(args.live, blockIdx.x) || !item_ok(it, args.n_active, args.v_slices, P.B, LORA_MAX_RANK) ||
+        it.nrows > BGMV_ROWS)
+        return;
     const int lane = threadIdx.x & 63;
     const int n0 = ((int)blockIdx.y - P.cg_begin) * 2048 + 8 * (int)threadIdx.x;
     const bool col_ok = n0 < P.d_out;  // lanes past d_out stay: they hold v values for readlane
@@ -962,6 +978,7 @@ struct ApplyProj {
 struct FusedArgs {
     const int32_t* row_index;
     const lora_work_t* work;
+    const int32_t* live;  // device-built plan: items of the range (NULL: every workgroup's)
     int32_t begin;
     int32_t n_active;
     ApplyProj p[LORA_MAX_PROJ];
@@ -1025,7 +1042,8 @@ __global__ __launch_bounds__(FWG) void fused_kernel(FusedArgs args) {
     const lora_work_t it = args.work[args.begin + blockIdx.x];
     const ApplyProj& P = args.p[blockIdx.y];
     // uniform over the workgroup, so returning here skips no barrier
-    if (!(item_ok(it, args.n_active, 1, P.A, LORA_MAX_RANK) & (it.nrows == 1) & (it.adapter < P.B.n_adapters) &
+    if (!(item_live(args.live, blockIdx.x) & item_ok(it, args.n_active, 1, P.A, LORA_MAX_RANK) & (it.nrows == 1) &
+          (it.adapter < P.B.n_adapters) &
           (it.rank <= P.B.max_rank) & (P.d_in <= 8 * FHALF) & (P.d_out <= 8 * FHALF)))
         return;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -1426,8 +1444,8 @@ bool group_shared_x(ShrinkArgs& args, int32_t n_proj) {
     return shared;
 }
 
-hipError_t launch_shrink_ranges(const lora_plan_info_t& info, int r0, int r1, int32_t n_proj, hipStream_t s,
-                                ShrinkArgs& args) {
+hipError_t launch_shrink_ranges(const lora_plan_info_t& info, const int32_t* live, int r0, int r1, int32_t n_proj,
+                                hipStream_t s, ShrinkArgs& args) {
     hipError_t err = hipSuccess;
     args.n_proj = n_proj;
     bool whole = true;  // every projection keeps each A row in one chunk
@@ -1436,6 +1454,7 @@ hipError_t launch_shrink_ranges(const lora_plan_info_t& info, int r0, int r1, in
     for (int r = r0; r < r1;) {
         const lora_range_t& R = info.ranges[r];
         const int shape = R.variant / LV_RANK_CLASSES, cls = R.variant % LV_RANK_CLASSES;
+        args.live = live ? live + r : nullptr;
         if (shape == LV_S_SPLITK16 || cls == LV_RANK_CLASSES - 1) {
             if (R.count > 0) {
                 args.begin = R.begin;
@@ -1454,9 +1473,10 @@ hipError_t launch_shrink_ranges(const lora_plan_info_t& info, int r0, int r1, in
             ++r;
             continue;
         }
-        // ranges r .. e-1: same shape, rank classes below the last one
+        // ranges r .. e-1: same shape, rank classes below the last one (a
+        // device-built plan's ranges have their own live counts: one each)
         int e = r, count = 0;
-        while (e < r1 && info.ranges[e].variant / LV_RANK_CLASSES == shape &&
+        while (e < r1 && (e == r || !live) && info.ranges[e].variant / LV_RANK_CLASSES == shape &&
                info.ranges[e].variant % LV_RANK_CLASSES < LV_RANK_CLASSES - 1 &&
                info.ranges[e].begin == R.begin + count) {
             count += info.ranges[e].count;
@@ -1508,7 +1528,7 @@ extern "C" int32_t lora_shrink(const lora_launch_t* L, int32_t n_proj, const lor
     if (L->info.n_work == 0) return LORA_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     hipError_t err = hipSuccess;
-    err = launch_shrink_ranges(L->info, 0, L->info.n_ranges, n_proj, s, args);
+    err = launch_shrink_ranges(L->info, L->live, 0, L->info.n_ranges, n_proj, s, args);
     return err == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
@@ -1547,6 +1567,7 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
         args.begin = R.begin;
         args.count = R.count;
         args.groups = groups;
+        args.live = L->live ? L->live + r : nullptr;
         const unsigned n1 = (unsigned)((R.count * groups + N_XCD - 1) / N_XCD * N_XCD);
         err = first_error(err, shape == LV_E_BGMV
                                    ? launch(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG), s,
@@ -1592,7 +1613,7 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
     // follow every shrink range on the stream
     int r_shrink = 0;
     while (r_shrink < L->info.n_ranges && L->info.ranges[r_shrink].variant < LV_APPLY_EXPAND0) ++r_shrink;
-    err = launch_shrink_ranges(L->info, 0, r_shrink, n_proj, s, sa);
+    err = launch_shrink_ranges(L->info, L->live, 0, r_shrink, n_proj, s, sa);
     for (int r = r_shrink; r < L->info.n_ranges; ++r) {
         const lora_range_t& R = L->info.ranges[r];
         if (R.count == 0) continue;
@@ -1608,6 +1629,7 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
             ea.begin = R.begin;
             ea.count = R.count;
             ea.groups = groups;
+            ea.live = L->live ? L->live + r : nullptr;
             const unsigned n1 = (unsigned)((R.count * groups + N_XCD - 1) / N_XCD * N_XCD);
             err = first_error(err, shape == LV_E_BGMV
                                        ? launch(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG),
@@ -1615,6 +1637,7 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
                                        : launch(expand_table(ev % LV_RANK_CLASSES), dim3(n1), dim3(WG), s, ea));
         } else {
             fa.begin = R.begin;
+            fa.live = L->live ? L->live + r : nullptr;
             bool uni = true;  // every wave's row offsets are uniform
             for (int i = 0; i < n_proj; ++i)
                 uni = uni && fa.p[i].A.chunk_len % 512 == 0 && fa.p[i].B.chunk_len % 512 == 0;
@@ -1623,6 +1646,364 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
         }
     }
     return err == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
+// ------------------------------------------------------------------ device plan builder
+// The tile-config table and the per-segment rules of the host planner, in
+// constant memory, so the device cuts every segment exactly as lora_plan does.
+#ifndef HETLORA_TILE_TABLE
+#define HETLORA_TILE_TABLE "tile_table.inc"
+#endif
+namespace devplan {
+#include HETLORA_TILE_TABLE
+#include "plan_rules.h"
+}  // namespace devplan
+
+namespace {
+
+#define BWG 1024                 // one workgroup builds the whole plan
+#define BWAVES (BWG / 64)
+#define B_MAX_ADAPTERS 4096
+#define B_ERR_ADAPTER 1
+#define B_ERR_RANK 2
+#define B_ERR_CAPACITY 4
+
+struct BuildArgs {
+    const int32_t* row_adapter;
+    const int32_t* adapter_rank;
+    int32_t n_rows, n_adapters, max_rank, d_in, d_out, n_ranges;
+    lora_device_header_t* hdr;
+    int32_t* row_index;
+    int32_t* seg_start;
+    int32_t* seg_adapter;
+    int32_t* seg_rank;
+    int32_t* scratch;
+    lora_work_t* work;
+    int32_t range_variant[LORA_MAX_RANGES];
+    int32_t range_begin[LORA_MAX_RANGES];
+    int32_t range_cap[LORA_MAX_RANGES];
+};
+
+// Exclusive prefix sum of v over the workgroup's threads in thread order;
+// `total` gets the sum of all.  Every thread must call it.
+__device__ int block_scan(int v, int* s_tmp, int& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < BWAVES; ++i) {
+        const int t = s_tmp[i];
+        before += i < w ? t : 0;
+        tot += t;
+    }
+    __syncthreads();
+    total = tot;
+    return before + x - v;
+}
+
+// The range that holds variant v (-1: none).
+__device__ __forceinline__ int range_of(const int32_t* s_rvar, int n_ranges, int v) {
+    int r = -1;
+    for (int i = 0; i < n_ranges; ++i)
+        if (s_rvar[i] == v) r = i;
+    return v < 0 ? -1 : r;
+}
+
+// Stable counting sort of the rows by adapter id, the segment table, and the
+// apply plan, in five phases separated by barriers:
+//  A  wave w owns rows [w*B, (w+1)*B) and counts them per adapter in its own
+//     LDS column; each row keeps its rank among the equal ids before it in
+//     that block (lanes with equal ids are found by ballot, one id at a time)
+//  B  per adapter, the exclusive prefix over the waves, then over the
+//     adapters: the first row_index slot of each adapter and the segments
+//  C  row i goes to slot first[a] + (rows of a in earlier waves) + its rank
+//  D  per segment, the plan parts (lv_apply_parts, as lora_plan), and per
+//     range an exclusive prefix over the segments in order: each part's
+//     first item in its range
+//  E  each wave writes the items of every 16th segment, lanes in parallel
+// Invalid ids or ranks, or a range over its capacity, leave an error status
+// and every live count 0.
+__global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
+    // phases A-C: per wave and adapter, a row count, then the exclusive
+    // prefix over the waves; phases D-E: 8 ints per segment
+    __shared__ uint32_t s_mem[BWAVES * B_MAX_ADAPTERS / 2];
+    __shared__ int32_t s_first[B_MAX_ADAPTERS];
+    __shared__ int32_t s_tmp[BWAVES];
+    __shared__ int32_t s_live[LORA_MAX_RANGES];
+    __shared__ int32_t s_rvar[LORA_MAX_RANGES], s_rbeg[LORA_MAX_RANGES], s_rcap[LORA_MAX_RANGES];
+    __shared__ int32_t s_err, s_n_active, s_n_seg;
+    uint16_t* s_h = reinterpret_cast<uint16_t*>(s_mem);
+    int32_t* s_rec = reinterpret_cast<int32_t*>(s_mem);
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int NA = a.n_adapters, n_rows = a.n_rows;
+    const int B = ((n_rows + BWAVES - 1) / BWAVES + 63) / 64 * 64;  // rows per wave
+    for (int i = t; i < BWAVES * NA / 2; i += BWG) s_mem[i] = 0;
+    if (t == 0) {
+        s_err = 0;
+        // the range table, copied with constant indices (the argument
+        // block is never indexed at run time)
+#pragma unroll
+        for (int r = 0; r < LORA_MAX_RANGES; ++r) {
+            s_rvar[r] = a.range_variant[r];
+            s_rbeg[r] = a.range_begin[r];
+            s_rcap[r] = a.range_cap[r];
+        }
+    }
+    __syncthreads();
+
+    // A
+    {
+        const int r0 = w * B, r1 = min(n_rows, r0 + B);
+        for (int base = r0; base < r1; base += 64) {
+            const int i = base + lane;
+            int key = -1;
+            if (i < r1) {
+                key = a.row_adapter[i];
+                if (key < -1 || key >= NA) {
+                    atomicOr(&s_err, B_ERR_ADAPTER);
+                    key = -1;
+                }
+            }
+            uint64_t pending = __ballot(key >= 0);
+            int rank_in = 0;
+            while (pending) {
+                const int leader = __ffsll((unsigned long long)pending) - 1;
+                const int k = __shfl(key, leader);
+                const uint64_t m = __ballot(key == k);
+                const int before = s_h[w * NA + k];
+                if (key == k) rank_in = before + __popcll(m & ((1ull << lane) - 1));
+                if (lane == leader) s_h[w * NA + k] = (uint16_t)(before + __popcll(m));
+                pending &= ~m;
+            }
+            if (key >= 0) a.scratch[i] = rank_in;
+        }
+    }
+    __syncthreads();
+
+    // B: prefix over the waves (in place), totals into s_first
+    for (int ad = t; ad < NA; ad += BWG) {
+        int sum = 0;
+        for (int ww = 0; ww < BWAVES; ++ww) {
+            const int c = s_h[ww * NA + ad];
+            s_h[ww * NA + ad] = (uint16_t)sum;
+            sum += c;
+        }
+        s_first[ad] = sum;
+        const int r = a.adapter_rank[ad];
+        if (r < 1 || r > a.max_rank) atomicOr(&s_err, B_ERR_RANK);
+    }
+    __syncthreads();
+    {
+        // thread t owns adapters 4t .. 4t+3
+        constexpr int APT = B_MAX_ADAPTERS / BWG;
+        int cnt[APT], rows = 0, segs = 0;
+#pragma unroll
+        for (int j = 0; j < APT; ++j) {
+            const int ad = APT * t + j;
+            cnt[j] = ad < NA ? s_first[ad] : 0;
+            rows += cnt[j];
+            segs += cnt[j] > 0;
+        }
+        int n_active, n_seg;
+        int row0 = block_scan(rows, s_tmp, n_active);
+        int seg0 = block_scan(segs, s_tmp, n_seg);
+#pragma unroll
+        for (int j = 0; j < APT; ++j) {
+            const int ad = APT * t + j;
+            if (ad < NA) s_first[ad] = row0;
+            if (cnt[j] > 0) {
+                a.seg_start[seg0] = row0;
+                a.seg_adapter[seg0] = ad;
+                a.seg_rank[seg0] = a.adapter_rank[ad];
+                ++seg0;
+            }
+            row0 += cnt[j];
+        }
+        if (t == 0) {
+            a.seg_start[n_seg] = n_active;
+            s_n_active = n_active;
+            s_n_seg = n_seg;
+        }
+    }
+    __syncthreads();
+
+    // C
+    for (int i = t; i < n_rows; i += BWG) {
+        const int key = a.row_adapter[i];
+        if (key < 0 || key >= NA) continue;
+        const int pos = s_first[key] + s_h[(i / B) * NA + key] + a.scratch[i];
+        if (pos >= 0 && pos < n_rows) a.row_index[pos] = i;
+    }
+    __syncthreads();
+
+    // D: thread t owns segments 4t .. 4t+3 (at most B_MAX_ADAPTERS segments)
+    const int n_seg = s_n_seg;
+    {
+        constexpr int SPT = B_MAX_ADAPTERS / BWG;
+        int st[SPT], len[SPT], ad[SPT], rk[SPT], ra[SPT], rb[SPT], ia[SPT], ib[SPT], oa[SPT], ob[SPT];
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int sg = SPT * t + j;
+            ra[j] = rb[j] = -1;
+            ia[j] = ib[j] = oa[j] = ob[j] = 0;
+            st[j] = len[j] = ad[j] = rk[j] = 0;
+            if (sg < n_seg) {
+                st[j] = a.seg_start[sg];
+                len[j] = a.seg_start[sg + 1] - st[j];
+                ad[j] = a.seg_adapter[sg];
+                rk[j] = a.seg_rank[sg];
+                devplan::SegPlan pa, pb;
+                devplan::lv_apply_parts(len[j], rk[j], a.d_in, a.d_out, pa, pb);
+                ra[j] = range_of(s_rvar, a.n_ranges, pa.variant);
+                ia[j] = pa.chunks * (pa.shrink ? pa.slices : 1);
+                if (pb.variant >= 0) {
+                    rb[j] = range_of(s_rvar, a.n_ranges, pb.variant);
+                    ib[j] = pb.chunks;
+                }
+                if (ra[j] < 0 || (pb.variant >= 0 && rb[j] < 0)) atomicOr(&s_err, B_ERR_CAPACITY);
+            }
+        }
+        for (int r = 0; r < a.n_ranges; ++r) {
+            int mine = 0;
+#pragma unroll
+            for (int j = 0; j < SPT; ++j) mine += (ra[j] == r ? ia[j] : 0) + (rb[j] == r ? ib[j] : 0);
+            int total;
+            int run = block_scan(mine, s_tmp, total);
+#pragma unroll
+            for (int j = 0; j < SPT; ++j) {
+                if (ra[j] == r) { oa[j] = run; run += ia[j]; }
+                if (rb[j] == r) { ob[j] = run; run += ib[j]; }
+            }
+            if (t == 0) {
+                s_live[r] = total;
+                if (total > s_rcap[r]) atomicOr(&s_err, B_ERR_CAPACITY);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int sg = SPT * t + j;
+            if (sg >= n_seg) continue;
+            int32_t* rec = s_rec + 8 * sg;
+            rec[0] = st[j];
+            rec[1] = len[j];
+            rec[2] = ad[j];
+            rec[3] = rk[j];
+            rec[4] = ra[j];
+            rec[5] = oa[j];
+            rec[6] = rb[j];
+            rec[7] = ob[j];
+        }
+    }
+    __syncthreads();
+
+    // E
+    for (int sg = w; sg < n_seg; sg += BWAVES) {
+        const int32_t* rec = s_rec + 8 * sg;
+        const int start = rec[0], len = rec[1], adapter = rec[2], rank = rec[3];
+        devplan::SegPlan parts[2];
+        devplan::lv_apply_parts(len, rank, a.d_in, a.d_out, parts[0], parts[1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const devplan::SegPlan& q = parts[h];
+            const int r = rec[4 + 2 * h], o = rec[5 + 2 * h];
+            if (q.variant < 0 || r < 0) continue;
+            const int n = q.chunks * (q.shrink ? q.slices : 1);
+            if (o + n > s_rcap[r]) continue;
+            const int nslices = q.shrink ? q.slices : (q.variant == LV_APPLY_FUSED ? 1 : parts[0].slices);
+            const int base = len / q.chunks, extra = len % q.chunks;
+            for (int i = lane; i < n; i += 64) {
+                const int c = q.shrink ? i / q.slices : i, sl = q.shrink ? i - c * q.slices : 0;
+                const lora_work_t it{start + c * base + min(c, extra), base + (c < extra ? 1 : 0), adapter, rank,
+                                     sl, nslices, {0, 0}};
+                a.work[s_rbeg[r] + o + i] = it;
+            }
+        }
+    }
+    __syncthreads();
+
+    if (t < LORA_MAX_RANGES) a.hdr->live[t] = (s_err == 0 && t < a.n_ranges) ? s_live[t] : 0;
+    if (t == 0) {
+        const int e = s_err;
+        a.hdr->status = (e & B_ERR_ADAPTER) ? LORA_EADAPTER : (e & B_ERR_RANK) ? LORA_ERANK
+                      : (e & B_ERR_CAPACITY) ? LORA_ECAPACITY : LORA_OK;
+        int n_work = 0;
+        for (int r = 0; r < a.n_ranges; ++r) n_work += s_live[r];
+        a.hdr->n_seg = e ? 0 : s_n_seg;
+        a.hdr->n_active = e ? 0 : s_n_active;
+        a.hdr->n_work = e ? 0 : n_work;
+    }
+}
+
+// The plan lora_device_plan writes for the same bounds (so the builder's
+// capacities, which bound every write it makes, can be trusted).
+bool same_plan(const lora_device_plan_t& p, const lora_device_plan_t& q) {
+    if (p.n_rows != q.n_rows || p.n_adapters != q.n_adapters || p.max_rank != q.max_rank || p.d_in != q.d_in ||
+        p.d_out != q.d_out || p.seg_capacity != q.seg_capacity || p.work_capacity != q.work_capacity ||
+        p.off_row_index != q.off_row_index || p.off_seg_start != q.off_seg_start ||
+        p.off_seg_adapter != q.off_seg_adapter || p.off_seg_rank != q.off_seg_rank ||
+        p.off_scratch != q.off_scratch || p.off_work != q.off_work || p.workspace_bytes != q.workspace_bytes)
+        return false;
+    const lora_plan_info_t &a = p.info, &b = q.info;
+    if (a.op != b.op || a.n_work != b.n_work || a.n_active != b.n_active || a.max_rank != b.max_rank ||
+        a.max_adapter != b.max_adapter || a.v_slices != b.v_slices || a.n_ranges != b.n_ranges)
+        return false;
+    for (int r = 0; r < a.n_ranges; ++r)
+        if (a.ranges[r].variant != b.ranges[r].variant || a.ranges[r].begin != b.ranges[r].begin ||
+            a.ranges[r].count != b.ranges[r].count || a.ranges[r].rows_per_item != b.ranges[r].rows_per_item)
+            return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" int32_t lora_batch_build_device(const lora_device_plan_t* plan, const int32_t* row_adapter,
+                                           const int32_t* adapter_rank, void* workspace, void* hip_stream,
+                                           lora_launch_t* out) {
+    if (!plan || !row_adapter || !adapter_rank || !workspace || !out || ((uintptr_t)workspace & 255u) != 0)
+        return LORA_EINVAL;
+    lora_device_plan_t chk;
+    if (lora_device_plan(plan->n_rows, plan->n_adapters, plan->max_rank, plan->d_in, plan->d_out, &chk) != LORA_OK ||
+        !same_plan(chk, *plan))
+        return LORA_EINVAL;
+    char* ws = static_cast<char*>(workspace);
+    BuildArgs args;
+    memset(&args, 0, sizeof(args));
+    args.row_adapter = row_adapter;
+    args.adapter_rank = adapter_rank;
+    args.n_rows = chk.n_rows;
+    args.n_adapters = chk.n_adapters;
+    args.max_rank = chk.max_rank;
+    args.d_in = chk.d_in;
+    args.d_out = chk.d_out;
+    args.n_ranges = chk.info.n_ranges;
+    args.hdr = reinterpret_cast<lora_device_header_t*>(ws);
+    args.row_index = reinterpret_cast<int32_t*>(ws + chk.off_row_index);
+    args.seg_start = reinterpret_cast<int32_t*>(ws + chk.off_seg_start);
+    args.seg_adapter = reinterpret_cast<int32_t*>(ws + chk.off_seg_adapter);
+    args.seg_rank = reinterpret_cast<int32_t*>(ws + chk.off_seg_rank);
+    args.scratch = reinterpret_cast<int32_t*>(ws + chk.off_scratch);
+    args.work = reinterpret_cast<lora_work_t*>(ws + chk.off_work);
+    for (int r = 0; r < chk.info.n_ranges; ++r) {
+        args.range_variant[r] = chk.info.ranges[r].variant;
+        args.range_begin[r] = chk.info.ranges[r].begin;
+        args.range_cap[r] = chk.info.ranges[r].count;
+    }
+    const hipError_t e = launch(build_plan_kernel, dim3(1), dim3(BWG), reinterpret_cast<hipStream_t>(hip_stream), args);
+    if (e != hipSuccess) return LORA_EHIP;
+    memset(out, 0, sizeof(*out));
+    out->row_index = args.row_index;
+    out->work = args.work;
+    out->info = chk.info;
+    out->live = args.hdr->live;
+    return LORA_OK;
 }
 
 // ------------------------------------------------------------------ pool scatter
@@ -1703,6 +2084,7 @@ extern "C" int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter
         L.row_index = dev;
         L.work = reinterpret_cast<const lora_work_t*>(dev + off[op]);
         L.info = info[op];
+        L.live = nullptr;
     }
     if (used == 0) return LORA_OK;
     const hipError_t e = hipMemcpyAsync(dev_staging, staging, (size_t)used * sizeof(int32_t), hipMemcpyHostToDevice,

@@ -8,6 +8,17 @@
 
 #include <stdint.h>
 
+// The helpers below serve the host planner and the device plan builder.
+#ifdef __HIPCC__
+#define LV_HD __host__ __device__
+#else
+#define LV_HD
+#endif
+// Address space of the tile-config table (constant memory where device code reads it).
+#ifndef LV_TABLE_SPACE
+#define LV_TABLE_SPACE
+#endif
+
 #define LV_RANK_CLASSES 4
 
 // Shrink shapes (rows per work item): 4 waves split K over one 16-row tile,
@@ -29,10 +40,10 @@
 #define LV_E_BGMV 4
 #define LV_E_SHAPES 5
 
-static inline int32_t lv_shrink_rows(int shape) {
+static inline LV_HD int32_t lv_shrink_rows(int shape) {
     return shape == LV_S_SPLITK16 ? 16 : shape == LV_S_ROWS64 ? 64 : 128;
 }
-static inline int32_t lv_expand_rows(int shape) {
+static inline LV_HD int32_t lv_expand_rows(int shape) {
     return shape == LV_E_ROWS16 ? 16 : shape == LV_E_ROWS64 ? 64 : shape == LV_E_BGMV ? 2 : 128;
 }
 // Variant ids of an apply plan: the shrink variants, then the expand
@@ -45,15 +56,15 @@ static inline int32_t lv_expand_rows(int shape) {
 #define LV_FUSED_MAX_ROWRANK 1024  // segments of more than one row are fused while len * rank <= this
 
 // Columns one expand workgroup covers.
-static inline int32_t lv_expand_cols(int shape) { return shape == LV_E_BGMV ? 2048 : 512; }
+static inline LV_HD int32_t lv_expand_cols(int shape) { return shape == LV_E_BGMV ? 2048 : 512; }
 
 // Shrink rank classes: N tiles of 16 ranks -> 1, 2, 4, 8 (rank <= 16, 32, 64, 128).
-static inline int lv_shrink_class(int32_t rank) {
+static inline LV_HD int lv_shrink_class(int32_t rank) {
     return rank <= 16 ? 0 : rank <= 32 ? 1 : rank <= 64 ? 2 : 3;
 }
 // Expand rank classes: K steps of 32 ranks -> 1, 2, 4 (rank <= 32, 64, 128);
 // class 3 is unused.
-static inline int lv_expand_class(int32_t rank) {
+static inline LV_HD int lv_expand_class(int32_t rank) {
     return rank <= 32 ? 0 : rank <= 64 ? 1 : 2;
 }
 
@@ -61,9 +72,9 @@ static inline int lv_expand_class(int32_t rank) {
 #define LV_LEN_BUCKETS 8
 #define LV_RANK_BUCKETS 4
 #define LV_D_BUCKETS 4
-static inline int lv_len_bucket(int32_t len) {
+static inline LV_HD int lv_len_bucket(int32_t len) {
     return len <= 1 ? 0 : len <= 4 ? 1 : len <= 8 ? 2 : len <= 16 ? 3 : len <= 32 ? 4 : len <= 64 ? 5
          : len <= 256 ? 6 : 7;
 }
-static inline int lv_rank_bucket(int32_t r) { return r <= 16 ? 0 : r <= 32 ? 1 : r <= 64 ? 2 : 3; }
-static inline int lv_d_bucket(int32_t d) { return d <= 1024 ? 0 : d <= 4096 ? 1 : d <= 8192 ? 2 : 3; }
+static inline LV_HD int lv_rank_bucket(int32_t r) { return r <= 16 ? 0 : r <= 32 ? 1 : r <= 64 ? 2 : 3; }
+static inline LV_HD int lv_d_bucket(int32_t d) { return d <= 1024 ? 0 : d <= 4096 ? 1 : d <= 8192 ? 2 : 3; }

@@ -2,7 +2,8 @@
 
 ``Batch`` has the library build the segment table and the plans on the host
 and upload row_index and the work lists to the device in one pinned
-host->device copy on the caller's stream, all in one call.  ``Batch.prepare_shrink`` / ``prepare_expand`` /
+host->device copy on the caller's stream, all in one call.  ``DeviceBatch``
+builds them on the GPU from a device row -> adapter map instead.  ``Batch.prepare_shrink`` / ``prepare_expand`` /
 ``prepare_merge`` build the C argument structs once and return a callable that
 only issues the library call, so a serving loop pays no per-call marshalling.
 PyTorch only provides memory and streams here.
@@ -15,8 +16,8 @@ import torch
 from . import _lib as _hip  # the HIP runtime the library is linked to (and torch uses)
 from . import (LORA_ECAPACITY, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, LoraPool, Segments,
                batch_prepare, call_apply, call_expand, call_merge, call_shrink, check_status, lora_apply_proj_t,
-               lora_batch_t, lora_expand_proj_t, lora_merge_mat_t, lora_mixture_rows, lora_pool_scatter,
-               lora_shrink_proj_t, make_rows)
+               lora_batch_t, lora_device_header_t, lora_device_plan, lora_expand_proj_t, lora_launch_t,
+               lora_merge_mat_t, lora_mixture_rows, lora_pool_scatter, lora_shrink_proj_t, make_rows)
 
 
 class HipEvent:
@@ -303,6 +304,101 @@ class Batch:
 
     def expand(self, projs, stream=None):
         self.prepare_expand(projs, stream)()
+
+
+class DeviceBatch:
+    """A batch whose segment table and apply plan are built on the GPU.
+
+    The launch shapes come from bounds alone (lora_device_plan: rows,
+    adapters, largest rank, d); ``build(row_adapter, adapter_rank)`` takes
+    both maps as device int32 tensors and enqueues the builder kernel
+    (lora_batch_build_device) on the stream: no host work per batch beyond
+    that one call, and no copy.  The launch struct is the same for every
+    build, so callables from ``prepare_apply`` stay valid.  v buffers are
+    sized for the bounds: fp32 [v_slices, n_rows, ldv]."""
+
+    def __init__(self, n_rows, n_adapters, max_rank, d_in, d_out, device="cuda"):
+        _, self.plan = lora_device_plan(n_rows, n_adapters, max_rank, d_in, d_out)
+        self.device = torch.device(device)
+        self.workspace = torch.empty(self.plan.workspace_bytes, dtype=torch.uint8, device=self.device)
+        assert self.workspace.data_ptr() % 256 == 0
+        self._ws = self.workspace.data_ptr()
+        self._plan_ref = ctypes.byref(self.plan)
+        self._launch = lora_launch_t()
+        self._launch_ref = ctypes.byref(self._launch)
+
+    def build(self, row_adapter, adapter_rank, stream=None):
+        """row_adapter: device int32 [n_rows]; adapter_rank: device int32 [n_adapters]."""
+        assert row_adapter.dtype == torch.int32 and row_adapter.is_contiguous()
+        assert adapter_rank.dtype == torch.int32 and adapter_rank.is_contiguous()
+        assert row_adapter.numel() == self.plan.n_rows and adapter_rank.numel() == self.plan.n_adapters
+        st = _hip.lora_batch_build_device(self._plan_ref, row_adapter.data_ptr(), adapter_rank.data_ptr(), self._ws,
+                                stream_handle(stream), self._launch_ref)
+        check_status(st, "lora_batch_build_device")
+        return self
+
+    @property
+    def apply_launch(self):
+        return self._launch
+
+    @property
+    def info_apply(self):
+        return self.plan.info
+
+    @property
+    def v_slices(self):
+        return self.plan.info.v_slices
+
+    def new_v(self, ldv, fill=None):
+        shape = (self.v_slices, self.plan.n_rows, ldv)
+        if fill is None:
+            return torch.empty(shape, dtype=torch.float32, device=self.device)
+        return torch.full(shape, fill, dtype=torch.float32, device=self.device)
+
+    def header(self):
+        """The builder's header (waits for the device): status, n_seg,
+        n_active, n_work and the live count of every range."""
+        h = lora_device_header_t()
+        raw = self.workspace[:ctypes.sizeof(h)].cpu().numpy().tobytes()
+        ctypes.memmove(ctypes.addressof(h), raw, len(raw))
+        return h
+
+    def read(self):
+        """Everything the builder wrote (waits for the device): header,
+        row_index [n_active], the segment table, and per range its live work
+        items (int32 [live, WORK_INTS])."""
+        h = self.header()
+        ws = self.workspace.cpu().numpy()
+        p = self.plan
+
+        def ints(off, n):
+            return ws[off:off + 4 * n].view(np.int32)
+        segs = Segments(ints(p.off_row_index, h.n_active).copy(), ints(p.off_seg_start, h.n_seg + 1).copy(),
+                        ints(p.off_seg_adapter, h.n_seg).copy(), ints(p.off_seg_rank, h.n_seg).copy())
+        work = ints(p.off_work, WORK_INTS * p.work_capacity).reshape(-1, WORK_INTS)
+        items = {r.variant: work[r.begin:r.begin + h.live[i]].copy()
+                 for i, r in enumerate(p.info.ranges[:p.info.n_ranges])}
+        return h, segs, items
+
+    def prepare_apply(self, projs, stream=None):
+        """projs as for Batch.prepare_apply; v buffers from new_v."""
+        arr = (lora_apply_proj_t * len(projs))(*[
+            lora_apply_proj_t(x.data_ptr(), x.stride(0), x.shape[1], A.c(), v.data_ptr(), v.stride(1), B.c(),
+                              y.shape[1], y.data_ptr(), y.stride(0), float(s))
+            for x, A, v, B, y, s in projs])
+        for p in projs:
+            v = p[2]
+            assert v.dtype == torch.float32 and v.is_contiguous() and v.dim() == 3
+            assert v.shape[0] >= self.v_slices and v.shape[1] == self.plan.n_rows
+        h, n, L = stream_handle(stream), len(projs), self._launch
+
+        def run():
+            call_apply(L, arr, n, h)
+        run.keep = (projs, arr)
+        return run
+
+    def apply(self, projs, stream=None):
+        self.prepare_apply(projs, stream)()
 
 
 def merge_mats(mats):

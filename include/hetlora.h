@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 7
+#define LORA_ABI_VERSION 8
 #define LORA_MAX_RANK 128   /* ranks are 1..128                              */
 #define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
 #define LORA_MAX_RANGES 48  /* kernel variants in one plan                   */
@@ -150,11 +150,17 @@ typedef struct lora_plan_info {
     lora_range_t ranges[LORA_MAX_RANGES];
 } lora_plan_info_t;
 
-/* What lora_shrink / lora_expand need to launch one plan. */
+/* What lora_shrink / lora_expand need to launch one plan.
+ *   live  NULL for a plan built on the host.  For a plan built on the device
+ *         (lora_batch_build_device): device int32 [info.n_ranges], the items
+ *         range r really holds; info.ranges[r].count is then the range's
+ *         capacity, every launch is sized for it, and items at or past
+ *         live[r] are skipped on the device without being read. */
 typedef struct lora_launch {
     const int32_t* row_index;   /* device int32 [info.n_active] (lora_build_segments) */
     const lora_work_t* work;    /* device [info.n_work] (lora_plan, same op)           */
     lora_plan_info_t info;      /* host copy of the plan summary                      */
+    const int32_t* live;        /* see above                                          */
 } lora_launch_t;
 
 /* One projection of a shrink: v[p][j] = sum_k x[row_index[p]][k] * A_a[j][k],
@@ -312,6 +318,85 @@ int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter,
                            int32_t* seg_adapter, int32_t* seg_rank,
                            int32_t* staging, int64_t staging_capacity,
                            void* dev_staging, void* hip_stream, lora_batch_t* out);
+
+/* Device-built batches: the segment table and the apply plan of a batch
+ * whose row -> adapter map is already in device memory, built by one kernel
+ * on the stream, with no host round trip and no host-to-device copy (the
+ * grouping of rows by adapter identity of the BEE-30060 page, Punica
+ * paragraph, and the run-time tile lookup of the VaLoRA blog, section 4.3.2,
+ * done on the GPU).  The host fixes the launch shapes in advance from bounds
+ * alone (rows, adapters, largest rank, d): lora_device_plan lists every
+ * kernel variant a batch within those bounds can need, as one range per
+ * variant with room for the most items such a batch can put there.  The
+ * builder fills each range with exactly the items lora_plan(LORA_OP_APPLY)
+ * gives that variant for the same batch, in the same order, and stores the
+ * count; lora_apply then launches every range at its capacity and the
+ * workgroups past the count return at once.  Results are bit-identical to
+ * lora_apply with the host-built plan of the same batch.
+ *
+ * lora_device_plan (host only): the layout for given bounds.
+ *   n_rows      rows of row_adapter, 1 .. 65536
+ *   n_adapters  adapter ids are in [0, n_adapters), 1 .. 4096
+ *   max_rank    bound on every adapter's rank, 1 .. LORA_MAX_RANK
+ *   d_in, d_out as in lora_plan (the largest over the projections)
+ *   out         the layout: seg_capacity = min(n_rows, n_adapters);
+ *               info (op LORA_OP_APPLY, n_active = n_rows, max_rank,
+ *               max_adapter = n_adapters - 1, v_slices = the most K slices a
+ *               segment can get, one range per variant: begin, count = its
+ *               capacity, rows_per_item); byte offsets of each part of the
+ *               workspace and its size (256-byte aligned parts)
+ * Errors: LORA_EINVAL (bounds out of range), LORA_ERANK, LORA_ESHAPE.
+ *
+ * lora_batch_build_device: enqueue the builder on hip_stream.
+ *   plan          as written by lora_device_plan
+ *   row_adapter   device int32 [plan->n_rows], each in [-1, n_adapters)
+ *   adapter_rank  device int32 [plan->n_adapters], each in [1, max_rank]
+ *   workspace     device, plan->workspace_bytes, 256-byte aligned; holds the
+ *                 header (lora_device_header_t, offset 0), row_index, the
+ *                 segment table (seg_start [seg_capacity + 1], seg_adapter,
+ *                 seg_rank [seg_capacity], as lora_build_segments writes
+ *                 them), a scratch part and the work items.  Only the
+ *                 header's counts say which entries are current.
+ *   out           host: a ready lora_launch_t (op LORA_OP_APPLY) whose
+ *                 row_index, work and live point into the workspace
+ * The inputs are checked on the device: an adapter id outside [-1,
+ * n_adapters) or a rank outside [1, max_rank] leaves status LORA_EADAPTER /
+ * LORA_ERANK in the header and an empty plan (every live count 0), so the
+ * launches that follow do nothing; the caller reads the header when it
+ * wants to know.  Host-side errors: LORA_EINVAL (null or misaligned
+ * pointer, a plan lora_device_plan did not write), LORA_EHIP. */
+typedef struct lora_device_plan {
+    int32_t n_rows;
+    int32_t n_adapters;
+    int32_t max_rank;
+    int32_t d_in;
+    int32_t d_out;
+    int32_t seg_capacity;
+    int32_t work_capacity;      /* items over all ranges                     */
+    int32_t reserved;
+    int64_t off_row_index;      /* byte offsets into the workspace           */
+    int64_t off_seg_start;
+    int64_t off_seg_adapter;
+    int64_t off_seg_rank;
+    int64_t off_scratch;
+    int64_t off_work;
+    int64_t workspace_bytes;
+    lora_plan_info_t info;
+} lora_device_plan_t;
+
+typedef struct lora_device_header {
+    int32_t status;             /* LORA_OK or the error found on the device  */
+    int32_t n_seg;
+    int32_t n_active;
+    int32_t n_work;             /* items over all ranges                     */
+    int32_t live[LORA_MAX_RANGES];
+} lora_device_header_t;
+
+int32_t lora_device_plan(int32_t n_rows, int32_t n_adapters, int32_t max_rank, int32_t d_in,
+                         int32_t d_out, lora_device_plan_t* out);
+int32_t lora_batch_build_device(const lora_device_plan_t* plan, const int32_t* row_adapter,
+                                const int32_t* adapter_rank, void* workspace, void* hip_stream,
+                                lora_launch_t* out);
 
 /* Shrink for n_proj projections (1..LORA_MAX_PROJ) sharing one plan
  * (launch->info.op == LORA_OP_SHRINK): one kernel launch per variant range.

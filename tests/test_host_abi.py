@@ -48,39 +48,10 @@ def _same(a, b):
 
 @pytest.mark.parametrize("k", [0, 1, 2, 3, 4])
 def test_build_segments_matches_oracle_on_workloads(k):
-    # structure only: avoid drawing the big tensors of the large workloads
-    rng = np.random.default_rng([k, 0])
-    W = workloads.gen_config(k) if k <= 1 else None
-    if W is not None:
-        batches = list(W.batches.values())
-        ranks = W.adapter_rank
-    else:
-        gen = {2: workloads.gen_prefill, 3: workloads.gen_vision, 4: workloads.gen_mix70b}[k]
-        batches, ranks = _structure_only(gen, k)
-    for ra in batches:
-        _same(hl.lora_build_segments(ra, ranks), oracle.build_segments_ref(ra, ranks))
-
-
-def _structure_only(gen, seed):
-    """Replay a generator's structure draws without drawing tensors."""
-    import math
-    rng = np.random.default_rng([seed, 0])
-    if gen is workloads.gen_prefill:
-        z = rng.standard_normal(16)
-        lens = np.clip(np.rint(np.exp(math.log(512.0) + 0.6 * z)), 32, 2048).astype(np.int64)
-        ranks = rng.choice(np.array([8, 16, 32, 64]), size=16)
-        ad = workloads._zipf_choice(rng, 16, 16)
-        return [np.repeat(ad, lens)], ranks
-    if gen is workloads.gen_vision:
-        lens = rng.integers(256, 1025, size=24) + 32
-        ad = workloads._zipf_choice(rng, 32, 24)
-        return [np.repeat(ad, lens)], np.full(32, 64)
-    ranks = rng.choice(np.array([16, 32, 64]), size=128)
-    dec = rng.integers(0, 128, size=256)
-    released = rng.choice(256, size=128, replace=False)
-    dec[released] = -1
-    pre = np.repeat(rng.integers(0, 128, size=8), 1024)
-    return [np.concatenate([dec, pre])], ranks
+    # structure only: the big workloads' tensors are not drawn
+    S = workloads.structure(k)
+    for ra in S.batches.values():
+        _same(hl.lora_build_segments(ra, S.adapter_rank), oracle.build_segments_ref(ra, S.adapter_rank))
 
 
 def test_build_segments_matches_oracle_random():

@@ -49,7 +49,7 @@ import math
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
-from typing import Callable, Dict, List, Optional
+from typing import Callable, Dict, List, NamedTuple, Optional
 
 import numpy as np
 
@@ -221,6 +221,29 @@ def _zipf_choice(rng, n_ids, size, s=1.1):
     return rng.choice(n_ids, size=size, p=p)
 
 
+class Structure(NamedTuple):
+    """A workload's batch structure: no tensors drawn."""
+    name: str
+    row_adapter: np.ndarray
+    adapter_rank: np.ndarray
+    projs: list          # (name, d_in, d_out)
+    batches: dict
+
+
+_structure_only = False
+
+
+def structure(k: int, seed: Optional[int] = None, **kw) -> Structure:
+    """Row map(s), ranks and projection shapes of workload k, from the same
+    draws as gen_config(k, seed) but without drawing its tensors."""
+    global _structure_only
+    _structure_only = True
+    try:
+        return gen_config(k, seed, **kw)
+    finally:
+        _structure_only = False
+
+
 def _make(name, seed, row_adapter, ranks, projs, layout, page_elems, rng,
           batches=None, merge=None, scale=2.0, shared_x=()):
     """shared_x: groups of projection indices that take the same x (one
@@ -228,6 +251,9 @@ def _make(name, seed, row_adapter, ranks, projs, layout, page_elems, rng,
     transformer layer."""
     row_adapter = np.asarray(row_adapter, dtype=np.int32)
     ranks = np.asarray(ranks, dtype=np.int32)
+    if _structure_only:
+        return Structure(name, row_adapter, ranks, [(pn, di, do) for pn, di, do in projs],
+                         batches or {"main": row_adapter})
     n_rows, n_ad = row_adapter.shape[0], ranks.shape[0]
     max_rank = int(ranks.max())
     x_of = {}
