@@ -218,6 +218,9 @@ def main():
                          "vision mode switch) of that workload for the kernel tables")
     ap.add_argument("--path", default="apply", choices=["apply", "split"],
                     help="apply (default): lora_apply, one-row segments fused; split: lora_shrink then lora_expand")
+    ap.add_argument("--metadata", default="host", choices=["host", "device"],
+                    help="decode: host (default) prepares each batch with lora_batch_prepare and one copy; "
+                         "device builds it on the GPU (lora_batch_build_device) from device-resident row maps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shared-x", action="store_true",
                     help="with --workload prefill|vision: q, k and v take one x (the layer input), o its own")
@@ -245,7 +248,7 @@ def main():
         return other_workload(args)
     import torch
     import workloads
-    from heterogeneous_adapter_batching_amd.session import Batch, HipEvent, Rows, prepare_merge
+    from heterogeneous_adapter_batching_amd.session import Batch, DeviceBatch, HipEvent, Rows, prepare_merge
     from workloads.device import bits_to_device, to_device
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -265,10 +268,20 @@ def main():
     het, homo = W.batches["hetero"], W.batches["homo"]
     r_m = int(W.adapter_rank[W.merge.adapter])
     ldv = 16
-    bh = Batch(64, W.adapter_rank, 4096, 4096).refresh(het)
-    bo = Batch(64, W.adapter_rank, 4096, 4096).refresh(homo)
-    vs = {id(b): [b.new_v(ldv) for _ in W.projections] for b in (bh, bo)}
     stream = torch.cuda.current_stream()
+    on_device = args.metadata == "device"
+    if on_device:
+        assert args.path == "apply", "device-built plans are apply plans"
+        rk_d = torch.from_numpy(np.asarray(W.adapter_rank, np.int32)).to(dev)
+        het_d = torch.from_numpy(np.asarray(het, np.int32)).to(dev)
+        homo_d = torch.from_numpy(np.asarray(homo, np.int32)).to(dev)
+        max_rank = int(W.adapter_rank.max())
+        bh = DeviceBatch(64, len(W.adapter_rank), max_rank, 4096, 4096).build(het_d, rk_d)
+        bo = DeviceBatch(64, len(W.adapter_rank), max_rank, 4096, 4096).build(homo_d, rk_d)
+    else:
+        bh = Batch(64, W.adapter_rank, 4096, 4096).refresh(het)
+        bo = Batch(64, W.adapter_rank, 4096, 4096).refresh(homo)
+    vs = {id(b): [b.new_v(ldv) for _ in W.projections] for b in (bh, bo)}
     split = args.path == "split"
     for L in layers:
         L["calls"] = []
@@ -293,15 +306,26 @@ def main():
         groups = ["hetero_shrink", "hetero_expand", "homo_shrink", "homo_expand", "merge_unmerge"]
     else:
         groups = ["hetero_apply", "homo_apply", "merge_unmerge"]
+    if on_device:
+        groups = ["metadata"] + groups
+        build_h, build_o = bh.prepare_build(het_d, rk_d, stream), bo.prepare_build(homo_d, rk_d, stream)
 
-    # group g runs between events g and g + 1; both batches are prepared (host
-    # plan + metadata upload) before the first event
+    # group g runs between events g and g + 1; host metadata: both batches are
+    # prepared (host plan + metadata upload) before the first event; device
+    # metadata: both builder kernels are the first group
     def step(ev, k):
         L = layers[k % len(layers)]
-        bh.refresh(het, stream)
-        bo.refresh(homo, stream)
-        ev[0].record(stream)
-        g = 0
+        if on_device:
+            ev[0].record(stream)
+            build_h()
+            build_o()
+            ev[1].record(stream)
+            g = 1
+        else:
+            bh.refresh(het, stream)
+            bo.refresh(homo, stream)
+            ev[0].record(stream)
+            g = 0
         for fns in L["calls"]:
             for fn in fns:
                 fn()
@@ -339,12 +363,17 @@ def main():
            "homo_expand": (co["expand_bytes"], co["flops"] * 0.5),
            "hetero_apply": (ch["shrink_bytes"] + ch["expand_bytes"], ch["flops"]),
            "homo_apply": (co["shrink_bytes"] + co["expand_bytes"], co["flops"]),
-           "merge_unmerge": (2 * mc["bytes"], 2 * mc["flops"])}
+           "merge_unmerge": (2 * mc["bytes"], 2 * mc["flops"]),
+           "metadata": (0, 0)}
     alg = {g: alg[g] for g in groups}
     step_bytes = sum(b for b, _ in alg.values())
     kernels = {}
     for g in groups:
         b, f = alg[g]
+        if g == "metadata":  # the builder kernels: no HBM traffic to speak of
+            kernels[g] = {"us_median": round(med[g], 3), "us_p10": round(float(np.percentile(us[g], 10)), 3),
+                          "us_p90": round(float(np.percentile(us[g], 90)), 3), "launches": 2}
+            continue
         gbs = b / (med[g] * 1e-6) / 1e9
         kernels[g] = {"us_median": round(med[g], 3), "us_p10": round(float(np.percentile(us[g], 10)), 3),
                       "us_p90": round(float(np.percentile(us[g], 90)), 3), "alg_bytes": int(b),
@@ -352,7 +381,7 @@ def main():
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     # dominant kernel: largest share of GPU time; merge and unmerge are the same kernel
     mavg = med["merge_unmerge"] / 2
-    dom = max(groups, key=lambda g: med[g])
+    dom = max((g for g in groups if g != "metadata"), key=lambda g: med[g])
     traffic = None
     if dom == "merge_unmerge":
         d_us, d_bytes, name = mavg, mc["bytes"], "merge_kernel (merge/unmerge, 4 x W[4096x4096], rank 16)"
@@ -381,6 +410,7 @@ def main():
         "hetero_over_homo": round(sum(med[g] for g in groups if g.startswith("hetero")) /
                                   sum(med[g] for g in groups if g.startswith("homo")), 3),
         "path": args.path,
+        "metadata": args.metadata,
         "merge_us_per_layer": round(mavg, 3),
         "step_alg_bytes": int(step_bytes),
     }
@@ -439,6 +469,35 @@ def other_workload(args):
     nb = c["shrink_bytes"] + c["expand_bytes"]
     out["shrink_expand_us"] = round(float(tot), 2)
     out["shrink_expand_hbm_frac"] = round(nb / tot / 1e3 / HBM_PEAK_GBS, 4)
+    if args.metadata == "device":
+        # lora_apply with the host-built plan, against the builder kernel plus
+        # lora_apply with the device-built plan (every range launched at its
+        # capacity), each from a flushed cache
+        from heterogeneous_adapter_batching_amd.session import DeviceBatch
+        va = [b.new_v(ldv) for _ in W.projections]
+        do_a = b.prepare_apply([(d.x, A[i], va[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
+        db = DeviceBatch(W.n_rows, len(W.adapter_rank), int(W.adapter_rank.max()), d_in, d_out)
+        ra_d = torch.from_numpy(np.asarray(W.row_adapter, np.int32)).cuda()
+        rk_d = torch.from_numpy(np.asarray(W.adapter_rank, np.int32)).cuda()
+        db.build(ra_d, rk_d)
+        vd = [db.new_v(ldv) for _ in W.projections]
+        do_d = db.prepare_apply([(d.x, A[i], vd[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
+        r2 = {"apply_host_plan": [], "build": [], "apply_device_plan": []}
+        for it in range(args.warmup + args.steps):
+            e = [HipEvent(timing=True) for _ in range(5)]
+            flush.fill_(it & 0xFF)
+            e[0].record(); do_a(); e[1].record()
+            flush.fill_((it + 1) & 0xFF)
+            e[2].record(); db.build(ra_d, rk_d); e[3].record(); do_d(); e[4].record()
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                r2["apply_host_plan"].append(e[0].elapsed_time(e[1]) * 1e3)
+                r2["build"].append(e[2].elapsed_time(e[3]) * 1e3)
+                r2["apply_device_plan"].append(e[3].elapsed_time(e[4]) * 1e3)
+        assert db.header().status == 0
+        out["device_metadata"] = {g: round(float(np.median(r2[g])), 2) for g in r2}
+        out["device_metadata"]["ranges"] = db.plan.info.n_ranges
+        out["device_metadata"]["work_capacity"] = db.plan.work_capacity
     if k == 3:
         spec = W.merge
         r = int(W.adapter_rank[spec.adapter])

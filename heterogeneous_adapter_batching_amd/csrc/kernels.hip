@@ -202,10 +202,10 @@ struct ShrinkArgs {
 // rows [16*MTW*w, 16*MTW*(w+1)); long segments use shrink_rows_kernel.)
 // NT = number of 16-wide rank tiles; U = K blocks loaded ahead per step.
 template <int KSPLIT, int MTW, int NT, int U>
-__global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
-    const lora_work_t it = args.work[args.begin + blockIdx.x];
-    const ShrinkProj& P = args.p[blockIdx.y];
-    if (!item_live(args.live, blockIdx.x) || !item_ok(it, args.n_active, args.v_slices, P.A, 16 * NT) ||
+__device__ __forceinline__ void shrink_item(const ShrinkArgs& args, const int bx, const int by) {
+    const lora_work_t it = args.work[args.begin + bx];
+    const ShrinkProj& P = args.p[by];
+    if (!item_live(args.live, bx) || !item_ok(it, args.n_active, args.v_slices, P.A, 16 * NT) ||
         it.nrows > 16 * MTW * (KSPLIT > 1 ? 1 : 4))
         return;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -354,6 +354,21 @@ __global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
                 if (m < it.nrows) vout[(int64_t)(it.row0 + m) * P.ldv + j] = j >= jneg ? -acc[t][n][e] : acc[t][n][e];
             }
         }
+}
+template <int KSPLIT, int MTW, int NT, int U>
+__global__ __launch_bounds__(WG) void shrink_kernel(ShrinkArgs args) {
+    shrink_item<KSPLIT, MTW, NT, U>(args, blockIdx.x, blockIdx.y);
+}
+// Device-built plans: a grid of at most the resident workgroups walks the
+// range's live items (every wave reaches each barrier of an item, and the
+// barrier after it keeps the next item's LDS writes behind its reads).
+template <int KSPLIT, int MTW, int NT, int U>
+__global__ __launch_bounds__(WG) void shrink_loop_kernel(ShrinkArgs args) {
+    const int live = *args.live;
+    for (int bx = blockIdx.x; bx < live; bx += gridDim.x) {
+        shrink_item<KSPLIT, MTW, NT, U>(args, bx, blockIdx.y);
+        __syncthreads();
+    }
 }
 
 // Barrier for LDS traffic only: waits for this wave's LDS operations, not for
@@ -672,11 +687,10 @@ __device__ __forceinline__ int xcd_block(int wg, int n_wg) { return (wg % N_XCD)
 // written in fp32.
 #define EXPAND_ROWS 128
 template <int KS>
-__global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
+__device__ __forceinline__ void expand_item(const ExpandArgs& args, const int lid) {
     constexpr int G = 4 * KS;  // groups of 8 ranks
     __shared__ int32_t s_rows[EXPAND_ROWS];          // the item's y row indices
     __shared__ u32x4_t s_v[EXPAND_ROWS * 2 * G];     // per row: (hi, lo) x G groups, XOR-swizzled
-    const int lid = xcd_block((int)blockIdx.x, (int)gridDim.x);
     if (lid >= args.count * args.groups) return;      // padding of the grid to a multiple of 8
     const int item = lid / args.groups, cg = lid - item * args.groups;
     const lora_work_t it = args.work[args.begin + item];
@@ -684,7 +698,7 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     while (pi + 1 < args.n_proj && cg >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
     // uniform over the workgroup, so returning here skips no barrier
-    if (!(item_live(args.live, item) & item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS) &
+    if (!(item_live(args.live, item) && item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS) &
           (it.nrows <= EXPAND_ROWS)))
         return;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -852,6 +866,21 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
         if (++mt >= ntiles) break;
     }
 }
+template <int KS>
+__global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
+    expand_item<KS>(args, xcd_block((int)blockIdx.x, (int)gridDim.x));
+}
+// Device-built plans: the grid (a multiple of 8, at most the resident
+// workgroups) walks the live (item, column group) pairs, each XCD a
+// contiguous block of them per round.
+template <int KS>
+__global__ __launch_bounds__(WG) void expand_loop_kernel(ExpandArgs args) {
+    const int total = *args.live * args.groups;
+    for (int lid = xcd_block((int)blockIdx.x, (int)gridDim.x); lid < total; lid += gridDim.x) {
+        expand_item<KS>(args, lid);
+        __syncthreads();
+    }
+}
 
 // One workgroup = one work item of at most BGMV_ROWS rows x one 2048-column
 // group of one projection (decode rows: BGMV).  Lane t owns columns
@@ -860,16 +889,16 @@ __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
 // wave (its K slices summed in slice order) and broadcast with readlane; B is
 // read 16 rank rows at a time (row offsets first, then the rows).
 #define BGMV_ROWS 2
-__global__ __launch_bounds__(WG) void bgmv_expand_kernel(ExpandArgs args) {
-    const lora_work_t it = args.work[args.begin + blockIdx.x];
+__device__ __forceinline__ void bgmv_item(const ExpandArgs& args, const int bx, const int by) {
+    const lora_work_t it = args.work[args.begin + bx];
     int pi = 0;
-    while (pi + 1 < args.n_proj && (int)blockIdx.y >= args.p[pi + 1].cg_begin) ++pi;
+    while (pi + 1 < args.n_proj && by >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
-    if (!item_live(args.live, blockIdx.x) || !item_ok(it, args.n_active, args.v_slices, P.B, LORA_MAX_RANK) ||
+    if (!item_live(args.live, bx) || !item_ok(it, args.n_active, args.v_slices, P.B, LORA_MAX_RANK) ||
         it.nrows > BGMV_ROWS)
         return;
     const int lane = threadIdx.x & 63;
-    const int n0 = ((int)blockIdx.y - P.cg_begin) * 2048 + 8 * (int)threadIdx.x;
+    const int n0 = (by - P.cg_begin) * 2048 + 8 * (int)threadIdx.x;
     const bool col_ok = n0 < P.d_out;  // lanes past d_out stay: they hold v values for readlane
     const int nc = col_ok ? n0 : 0;
     const int cchunk = nc / P.B.chunk_len, cin = nc - cchunk * P.B.chunk_len;
@@ -962,6 +991,14 @@ __global__ __launch_bounds__(WG) void bgmv_expand_kernel(ExpandArgs args) {
         stf4(yrow[p] + 4, o1);
     }
 }
+__global__ __launch_bounds__(WG) void bgmv_expand_kernel(ExpandArgs args) {
+    bgmv_item(args, blockIdx.x, blockIdx.y);
+}
+// Device-built plans: a grid of at most the resident workgroups walks the live items.
+__global__ __launch_bounds__(WG) void bgmv_expand_loop_kernel(ExpandArgs args) {
+    const int live = *args.live;
+    for (int bx = blockIdx.x; bx < live; bx += gridDim.x) bgmv_item(args, bx, blockIdx.y);
+}
 
 // ------------------------------------------------------------------ fused (apply)
 struct ApplyProj {
@@ -1035,14 +1072,14 @@ __device__ __forceinline__ float wave_sum8(const float (&in)[8], int lane) {
 #define FWG 1024
 #define FHALF (FWG / 2)
 template <bool UNI>
-__global__ __launch_bounds__(FWG) void fused_kernel(FusedArgs args) {
+__device__ __forceinline__ void fused_item(const FusedArgs& args, const int bx, const int by) {
     __shared__ float s_part[FWG / 64][8];
     __shared__ float s_v[16];
     __shared__ f32x4_t s_acc[FHALF][2];
-    const lora_work_t it = args.work[args.begin + blockIdx.x];
-    const ApplyProj& P = args.p[blockIdx.y];
+    const lora_work_t it = args.work[args.begin + bx];
+    const ApplyProj& P = args.p[by];
     // uniform over the workgroup, so returning here skips no barrier
-    if (!(item_live(args.live, blockIdx.x) & item_ok(it, args.n_active, 1, P.A, LORA_MAX_RANK) & (it.nrows == 1) &
+    if (!(item_live(args.live, bx) && item_ok(it, args.n_active, 1, P.A, LORA_MAX_RANK) & (it.nrows == 1) &
           (it.adapter < P.B.n_adapters) &
           (it.rank <= P.B.max_rank) & (P.d_in <= 8 * FHALF) & (P.d_out <= 8 * FHALF)))
         return;
@@ -1162,6 +1199,21 @@ __global__ __launch_bounds__(FWG) void fused_kernel(FusedArgs args) {
         }
         stf4(yp, o0);
         stf4(yp + 4, o1);
+    }
+}
+template <bool UNI>
+__global__ __launch_bounds__(FWG) void fused_kernel(FusedArgs args) {
+    fused_item<UNI>(args, blockIdx.x, blockIdx.y);
+}
+// Device-built plans: a grid of at most the resident workgroups walks the
+// live rows (the barrier after each keeps the next row's LDS writes behind
+// this one's reads).
+template <bool UNI>
+__global__ __launch_bounds__(FWG) void fused_loop_kernel(FusedArgs args) {
+    const int live = *args.live;
+    for (int bx = blockIdx.x; bx < live; bx += gridDim.x) {
+        fused_item<UNI>(args, bx, blockIdx.y);
+        __syncthreads();
     }
 }
 
@@ -1355,20 +1407,26 @@ constexpr int unroll_for() {
     return KSPLIT > 1 ? (NT == 1 ? 4 : NT == 2 ? 2 : 1) : ((MTW + NT) <= 2 ? 2 : 1);
 }
 template <int KSPLIT, int MTW, int NT>
-shrink_fn shrink_inst() {
-    return shrink_kernel<KSPLIT, MTW, NT, unroll_for<KSPLIT, MTW, NT>()>;
+shrink_fn shrink_inst(bool loop) {
+    return loop ? shrink_loop_kernel<KSPLIT, MTW, NT, unroll_for<KSPLIT, MTW, NT>()>
+                : shrink_kernel<KSPLIT, MTW, NT, unroll_for<KSPLIT, MTW, NT>()>;
 }
-// Short-segment (SPLITK16) shrink kernels by rank class.
-shrink_fn shrink_table(int variant) {
-    static const shrink_fn t[LV_RANK_CLASSES] = {shrink_inst<4, 1, 1>(), shrink_inst<4, 1, 2>(),
-                                                 shrink_inst<4, 1, 4>(), shrink_inst<4, 1, 8>()};
-    return t[variant % LV_RANK_CLASSES];
+// Short-segment (SPLITK16) shrink kernels by rank class (loop: the
+// grid-stride form for device-built plans).
+shrink_fn shrink_table(int variant, bool loop) {
+    static const shrink_fn t[2][LV_RANK_CLASSES] = {
+        {shrink_inst<4, 1, 1>(false), shrink_inst<4, 1, 2>(false), shrink_inst<4, 1, 4>(false),
+         shrink_inst<4, 1, 8>(false)},
+        {shrink_inst<4, 1, 1>(true), shrink_inst<4, 1, 2>(true), shrink_inst<4, 1, 4>(true),
+         shrink_inst<4, 1, 8>(true)}};
+    return t[loop][variant % LV_RANK_CLASSES];
 }
 
 typedef void (*expand_fn)(ExpandArgs);
-expand_fn expand_table(int rank_class) {
-    static const expand_fn t[3] = {expand_kernel<1>, expand_kernel<2>, expand_kernel<4>};
-    return t[rank_class];
+expand_fn expand_table(int rank_class, bool loop) {
+    static const expand_fn t[2][3] = {{expand_kernel<1>, expand_kernel<2>, expand_kernel<4>},
+                                      {expand_loop_kernel<1>, expand_loop_kernel<2>, expand_loop_kernel<4>}};
+    return t[loop][rank_class];
 }
 
 // Launches `fn` and returns the status of this launch alone
@@ -1387,9 +1445,9 @@ inline hipError_t first_error(hipError_t acc, hipError_t e) { return acc != hipS
 // shape with ranks up to 64 are consecutive in the work list and share one
 // launch (the kernel picks the rank tiles per item), ranks above 64 get their
 // own.
-// Workgroups of `fn` (WG threads) that the current device holds at once:
-// CUs x resident workgroups per CU, cached per (device, kernel).
-int resident_slots(const void* fn) {
+// Workgroups of `fn` (`block` threads) that the current device holds at
+// once: CUs x resident workgroups per CU, cached per (device, kernel).
+int resident_slots(const void* fn, int block = WG) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
     static std::mutex mu;
@@ -1400,7 +1458,7 @@ int resident_slots(const void* fn) {
         if (cache[i].dev == dev && cache[i].fn == fn) return cache[i].slots;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, WG, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
     const int slots = cus * per_cu;
     if (n_cache < 64) cache[n_cache++] = Entry{dev, fn, slots};
     return slots;
@@ -1414,6 +1472,14 @@ unsigned persistent_grid(const void* fn, int64_t tasks) {
     const int64_t slots = resident_slots(fn);
     const int64_t rounds = (tasks + slots - 1) / slots;
     return (unsigned)((tasks + rounds - 1) / rounds);
+}
+
+// grid.x of a grid-stride launch (device-built plans) over `count` items
+// with grid.y = ny: at most one round of resident workgroups, at least one.
+unsigned loop_grid_x(const void* fn, int64_t count, int ny, int block = WG) {
+    int64_t gx = resident_slots(fn, block) / ny;
+    if (gx > count) gx = count;
+    return (unsigned)(gx > 0 ? gx : 1);
 }
 
 // Groups of up to SHRINK_GROUP projections with the same x (pointer, ldx
@@ -1460,8 +1526,10 @@ hipError_t launch_shrink_ranges(const lora_plan_info_t& info, const int32_t* liv
                 args.begin = R.begin;
                 args.count = R.count;
                 if (shape == LV_S_SPLITK16) {
-                    err = first_error(err, launch(shrink_table(R.variant), dim3((unsigned)R.count, (unsigned)n_proj),
-                                                  dim3(WG), s, args));
+                    const shrink_fn fn = shrink_table(R.variant, live != nullptr);
+                    const unsigned gx =
+                        live ? loop_grid_x(reinterpret_cast<const void*>(fn), R.count, n_proj) : (unsigned)R.count;
+                    err = first_error(err, launch(fn, dim3(gx, (unsigned)n_proj), dim3(WG), s, args));
                 } else {
                     shrink_fn fn = shape == LV_S_ROWS64
                                        ? (whole ? shrink_rows_kernel<1, 8, true, 1> : shrink_rows_kernel<1, 8, false, 1>)
@@ -1503,6 +1571,37 @@ hipError_t launch_shrink_ranges(const lora_plan_info_t& info, const int32_t* liv
         r = e;
     }
     return err;
+}
+
+// Expand launch of one range: op-local variant `ev` (shape x rank class),
+// items [begin, begin + count); live != NULL for a device-built plan.
+hipError_t launch_expand_range(int ev, int32_t begin, int32_t count, const int32_t* live, int32_t n_proj,
+                               hipStream_t s, ExpandArgs& args) {
+    const int shape = ev / LV_RANK_CLASSES;
+    const int32_t width = lv_expand_cols(shape);
+    int32_t groups = 0;  // column groups of every projection, back to back on grid.y
+    for (int i = 0; i < n_proj; ++i) {
+        args.p[i].cg_begin = groups;
+        groups += (args.p[i].d_out + width - 1) / width;
+    }
+    args.begin = begin;
+    args.count = count;
+    args.groups = groups;
+    args.live = live;
+    if (shape == LV_E_BGMV) {
+        const auto fn = live ? bgmv_expand_loop_kernel : bgmv_expand_kernel;
+        const unsigned gx =
+            live ? loop_grid_x(reinterpret_cast<const void*>(fn), count, groups) : (unsigned)count;
+        return launch(fn, dim3(gx, (unsigned)groups), dim3(WG), s, args);
+    }
+    const expand_fn fn = expand_table(ev % LV_RANK_CLASSES, live != nullptr);
+    int64_t n1 = (int64_t)count * groups;
+    if (live) {
+        const int64_t slots = resident_slots(reinterpret_cast<const void*>(fn));
+        if (n1 > slots) n1 = slots;
+    }
+    n1 = (n1 + N_XCD - 1) / N_XCD * N_XCD;  // xcd_block needs a multiple of 8
+    return launch(fn, dim3((unsigned)n1), dim3(WG), s, args);
 }
 
 }  // namespace
@@ -1557,22 +1656,8 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
     for (int r = 0; r < L->info.n_ranges; ++r) {
         const lora_range_t& R = L->info.ranges[r];
         if (R.count == 0) continue;
-        const int shape = R.variant / LV_RANK_CLASSES;
-        const int32_t width = lv_expand_cols(shape);
-        int32_t groups = 0;  // column groups of every projection, back to back on grid.y
-        for (int i = 0; i < n_proj; ++i) {
-            args.p[i].cg_begin = groups;
-            groups += (args.p[i].d_out + width - 1) / width;
-        }
-        args.begin = R.begin;
-        args.count = R.count;
-        args.groups = groups;
-        args.live = L->live ? L->live + r : nullptr;
-        const unsigned n1 = (unsigned)((R.count * groups + N_XCD - 1) / N_XCD * N_XCD);
-        err = first_error(err, shape == LV_E_BGMV
-                                   ? launch(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG), s,
-                                            args)
-                                   : launch(expand_table(R.variant % LV_RANK_CLASSES), dim3(n1), dim3(WG), s, args));
+        err = first_error(err, launch_expand_range(R.variant, R.begin, R.count, L->live ? L->live + r : nullptr,
+                                                   n_proj, s, args));
     }
     return err == hipSuccess ? LORA_OK : LORA_EHIP;
 }
@@ -1618,31 +1703,19 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
         const lora_range_t& R = L->info.ranges[r];
         if (R.count == 0) continue;
         if (R.variant < LV_APPLY_FUSED) {
-            const int ev = R.variant - LV_APPLY_EXPAND0;
-            const int shape = ev / LV_RANK_CLASSES;
-            const int32_t width = lv_expand_cols(shape);
-            int32_t groups = 0;
-            for (int i = 0; i < n_proj; ++i) {
-                ea.p[i].cg_begin = groups;
-                groups += (ea.p[i].d_out + width - 1) / width;
-            }
-            ea.begin = R.begin;
-            ea.count = R.count;
-            ea.groups = groups;
-            ea.live = L->live ? L->live + r : nullptr;
-            const unsigned n1 = (unsigned)((R.count * groups + N_XCD - 1) / N_XCD * N_XCD);
-            err = first_error(err, shape == LV_E_BGMV
-                                       ? launch(bgmv_expand_kernel, dim3((unsigned)R.count, (unsigned)groups), dim3(WG),
-                                                s, ea)
-                                       : launch(expand_table(ev % LV_RANK_CLASSES), dim3(n1), dim3(WG), s, ea));
+            err = first_error(err, launch_expand_range(R.variant - LV_APPLY_EXPAND0, R.begin, R.count,
+                                                       L->live ? L->live + r : nullptr, n_proj, s, ea));
         } else {
             fa.begin = R.begin;
             fa.live = L->live ? L->live + r : nullptr;
             bool uni = true;  // every wave's row offsets are uniform
             for (int i = 0; i < n_proj; ++i)
                 uni = uni && fa.p[i].A.chunk_len % 512 == 0 && fa.p[i].B.chunk_len % 512 == 0;
-            err = first_error(err, launch(uni ? fused_kernel<true> : fused_kernel<false>,
-                                          dim3((unsigned)R.count, (unsigned)n_proj), dim3(FWG), s, fa));
+            const auto fn = fa.live ? (uni ? fused_loop_kernel<true> : fused_loop_kernel<false>)
+                                    : (uni ? fused_kernel<true> : fused_kernel<false>);
+            const unsigned gx = fa.live ? loop_grid_x(reinterpret_cast<const void*>(fn), R.count, n_proj, FWG)
+                                        : (unsigned)R.count;
+            err = first_error(err, launch(fn, dim3(gx, (unsigned)n_proj), dim3(FWG), s, fa));
         }
     }
     return err == hipSuccess ? LORA_OK : LORA_EHIP;
@@ -1708,36 +1781,37 @@ __device__ int block_scan(int v, int* s_tmp, int& total) {
     return before + x - v;
 }
 
-// The range that holds variant v (-1: none).
-__device__ __forceinline__ int range_of(const int32_t* s_rvar, int n_ranges, int v) {
-    int r = -1;
-    for (int i = 0; i < n_ranges; ++i)
-        if (s_rvar[i] == v) r = i;
-    return v < 0 ? -1 : r;
-}
 
 // Stable counting sort of the rows by adapter id, the segment table, and the
-// apply plan, in five phases separated by barriers:
-//  A  wave w owns rows [w*B, (w+1)*B) and counts them per adapter in its own
-//     LDS column; each row keeps its rank among the equal ids before it in
-//     that block (lanes with equal ids are found by ballot, one id at a time)
-//  B  per adapter, the exclusive prefix over the waves, then over the
-//     adapters: the first row_index slot of each adapter and the segments
-//  C  row i goes to slot first[a] + (rows of a in earlier waves) + its rank
-//  D  per segment, the plan parts (lv_apply_parts, as lora_plan), and per
-//     range an exclusive prefix over the segments in order: each part's
+// apply plan.  Thread t owns adapters 4t .. 4t+3 and so the segments of those
+// adapters (segments come in adapter order); wave w owns rows [w*B, (w+1)*B).
+//  A  each wave counts its rows per adapter in its own LDS column: lanes with
+//     equal ids are found by ballot, one id at a time, and the id's first
+//     lane adds the count; each row keeps (id, rank among the equal ids before
+//     it in the block), in LDS when it fits, else in the scratch part
+//  B  per owned adapter, the exclusive prefix over the waves; then prefix
+//     sums over the adapters: each adapter's first row_index slot and each
+//     segment's id (the segment table is written here)
+//  D  per owned segment, its plan parts (lv_apply_parts, as lora_plan), and
+//     per range an exclusive prefix over the segments in order: each part's
 //     first item in its range
+//  C  row i goes to slot first[a] + (rows of a in earlier waves) + its rank
 //  E  each wave writes the items of every 16th segment, lanes in parallel
+// Only phase A reads global memory (the ids and the ranks, loaded together).
 // Invalid ids or ranks, or a range over its capacity, leave an error status
 // and every live count 0.
 __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
-    // phases A-C: per wave and adapter, a row count, then the exclusive
-    // prefix over the waves; phases D-E: 8 ints per segment
+    // A-C: per wave and adapter a row count, then the exclusive prefix over
+    // the waves (16 x NA uint16), then per row (id << 16 | rank in block) when
+    // it fits; E: 8 ints per segment
     __shared__ uint32_t s_mem[BWAVES * B_MAX_ADAPTERS / 2];
     __shared__ int32_t s_first[B_MAX_ADAPTERS];
     __shared__ int32_t s_tmp[BWAVES];
     __shared__ int32_t s_live[LORA_MAX_RANGES];
     __shared__ int32_t s_rvar[LORA_MAX_RANGES], s_rbeg[LORA_MAX_RANGES], s_rcap[LORA_MAX_RANGES];
+    __shared__ int32_t s_vrange[LV_APPLY_VARIANTS];  // the range of each variant (-1: none)
+    __shared__ devplan::ShrinkCfg s_stab[LV_LEN_BUCKETS][LV_RANK_BUCKETS][LV_D_BUCKETS];
+    __shared__ int8_t s_etab[LV_LEN_BUCKETS][LV_RANK_BUCKETS][LV_D_BUCKETS];
     __shared__ int32_t s_err, s_n_active, s_n_seg;
     uint16_t* s_h = reinterpret_cast<uint16_t*>(s_mem);
     int32_t* s_rec = reinterpret_cast<int32_t*>(s_mem);
@@ -1745,6 +1819,14 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int NA = a.n_adapters, n_rows = a.n_rows;
     const int B = ((n_rows + BWAVES - 1) / BWAVES + 63) / 64 * 64;  // rows per wave
+    // per-row data: after the counters in LDS if it fits, else the scratch part
+    const bool rows_in_lds = n_rows <= BWAVES * B_MAX_ADAPTERS / 2 - BWAVES * NA / 2;
+    uint32_t* rowdat = rows_in_lds ? s_mem + BWAVES * NA / 2 : reinterpret_cast<uint32_t*>(a.scratch);
+
+    constexpr int APT = B_MAX_ADAPTERS / BWG;  // adapters (and segments) per thread
+    int rk[APT];
+#pragma unroll
+    for (int j = 0; j < APT; ++j) rk[j] = APT * t + j < NA ? a.adapter_rank[APT * t + j] : 1;
     for (int i = t; i < BWAVES * NA / 2; i += BWG) s_mem[i] = 0;
     if (t == 0) {
         s_err = 0;
@@ -1756,7 +1838,21 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
             s_rbeg[r] = a.range_begin[r];
             s_rcap[r] = a.range_cap[r];
         }
+#pragma unroll
+        for (int v = 0; v < LV_APPLY_VARIANTS; ++v) s_vrange[v] = -1;
+        for (int r = 0; r < a.n_ranges; ++r) s_vrange[s_rvar[r]] = r;  // variants are in [0, LV_APPLY_VARIANTS)
     }
+    {  // the tile table, copied to LDS byte by byte (phase B looks it up per segment)
+        constexpr int NS = (int)sizeof(s_stab), NE = (int)sizeof(s_etab);
+        if (t < NS)
+            reinterpret_cast<uint8_t*>(&s_stab[0][0][0])[t] = reinterpret_cast<const uint8_t*>(devplan::kShrinkCfg)[t];
+        else if (t < NS + NE)
+            reinterpret_cast<uint8_t*>(&s_etab[0][0][0])[t - NS] =
+                reinterpret_cast<const uint8_t*>(devplan::kExpandShape)[t - NS];
+    }
+    // the ids, loaded by all threads at once (each wave's walk below then
+    // reads them from LDS or L2 instead of waiting on HBM chunk by chunk)
+    for (int i = t; i < n_rows; i += BWG) rowdat[i] = (uint32_t)a.row_adapter[i];
     __syncthreads();
 
     // A
@@ -1766,164 +1862,186 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
             const int i = base + lane;
             int key = -1;
             if (i < r1) {
-                key = a.row_adapter[i];
+                key = (int)rowdat[i];
                 if (key < -1 || key >= NA) {
                     atomicOr(&s_err, B_ERR_ADAPTER);
                     key = -1;
                 }
             }
             uint64_t pending = __ballot(key >= 0);
-            int rank_in = 0;
+            int below = 0, leader = lane, cnt = 0;
             while (pending) {
-                const int leader = __ffsll((unsigned long long)pending) - 1;
-                const int k = __shfl(key, leader);
+                const int l = __ffsll((unsigned long long)pending) - 1;
+                const int k = __builtin_amdgcn_readlane(key, l);
                 const uint64_t m = __ballot(key == k);
-                const int before = s_h[w * NA + k];
-                if (key == k) rank_in = before + __popcll(m & ((1ull << lane) - 1));
-                if (lane == leader) s_h[w * NA + k] = (uint16_t)(before + __popcll(m));
+                if (key == k) {
+                    below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                    leader = l;
+                    cnt = __popcll(m);
+                }
                 pending &= ~m;
             }
-            if (key >= 0) a.scratch[i] = rank_in;
-        }
-    }
-    __syncthreads();
-
-    // B: prefix over the waves (in place), totals into s_first
-    for (int ad = t; ad < NA; ad += BWG) {
-        int sum = 0;
-        for (int ww = 0; ww < BWAVES; ++ww) {
-            const int c = s_h[ww * NA + ad];
-            s_h[ww * NA + ad] = (uint16_t)sum;
-            sum += c;
-        }
-        s_first[ad] = sum;
-        const int r = a.adapter_rank[ad];
-        if (r < 1 || r > a.max_rank) atomicOr(&s_err, B_ERR_RANK);
-    }
-    __syncthreads();
-    {
-        // thread t owns adapters 4t .. 4t+3
-        constexpr int APT = B_MAX_ADAPTERS / BWG;
-        int cnt[APT], rows = 0, segs = 0;
-#pragma unroll
-        for (int j = 0; j < APT; ++j) {
-            const int ad = APT * t + j;
-            cnt[j] = ad < NA ? s_first[ad] : 0;
-            rows += cnt[j];
-            segs += cnt[j] > 0;
-        }
-        int n_active, n_seg;
-        int row0 = block_scan(rows, s_tmp, n_active);
-        int seg0 = block_scan(segs, s_tmp, n_seg);
-#pragma unroll
-        for (int j = 0; j < APT; ++j) {
-            const int ad = APT * t + j;
-            if (ad < NA) s_first[ad] = row0;
-            if (cnt[j] > 0) {
-                a.seg_start[seg0] = row0;
-                a.seg_adapter[seg0] = ad;
-                a.seg_rank[seg0] = a.adapter_rank[ad];
-                ++seg0;
+            int before = 0;
+            if (key >= 0 && lane == leader) {  // one lane per id: distinct addresses
+                before = s_h[w * NA + key];
+                s_h[w * NA + key] = (uint16_t)(before + cnt);
             }
-            row0 += cnt[j];
-        }
-        if (t == 0) {
-            a.seg_start[n_seg] = n_active;
-            s_n_active = n_active;
-            s_n_seg = n_seg;
+            before = __shfl(before, leader);
+            if (i < r1) rowdat[i] = key >= 0 ? ((uint32_t)key << 16) | (uint32_t)(before + below) : 0xFFFFFFFFu;
         }
     }
     __syncthreads();
 
-    // C
-    for (int i = t; i < n_rows; i += BWG) {
-        const int key = a.row_adapter[i];
-        if (key < 0 || key >= NA) continue;
-        const int pos = s_first[key] + s_h[(i / B) * NA + key] + a.scratch[i];
-        if (pos >= 0 && pos < n_rows) a.row_index[pos] = i;
-    }
-    __syncthreads();
-
-    // D: thread t owns segments 4t .. 4t+3 (at most B_MAX_ADAPTERS segments)
-    const int n_seg = s_n_seg;
-    {
-        constexpr int SPT = B_MAX_ADAPTERS / BWG;
-        int st[SPT], len[SPT], ad[SPT], rk[SPT], ra[SPT], rb[SPT], ia[SPT], ib[SPT], oa[SPT], ob[SPT];
+    // B
+    int cnt[APT], rows = 0, segs = 0;
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const int sg = SPT * t + j;
+    for (int j = 0; j < APT; ++j) {
+        const int ad = APT * t + j;
+        int sum = 0;
+        if (ad < NA) {
+            int c[BWAVES];  // all loads first, then the prefix
+#pragma unroll
+            for (int ww = 0; ww < BWAVES; ++ww) c[ww] = s_h[ww * NA + ad];
+#pragma unroll
+            for (int ww = 0; ww < BWAVES; ++ww) {
+                s_h[ww * NA + ad] = (uint16_t)sum;
+                sum += c[ww];
+            }
+            if (rk[j] < 1 || rk[j] > a.max_rank) atomicOr(&s_err, B_ERR_RANK);
+        }
+        cnt[j] = sum;
+        rows += sum;
+        segs += sum > 0;
+    }
+    // one scan for both: rows (<= 65536, 17 bits) and segments above them
+    int tot;
+    const int pre = block_scan(rows | (segs << 17), s_tmp, tot);
+    const int n_active = tot & 0x1FFFF, n_seg = tot >> 17;
+    int st[APT], sid[APT], ra[APT], rb[APT], ia[APT], ib[APT], sl[APT];
+    {
+        int r = pre & 0x1FFFF, sg = pre >> 17;
+#pragma unroll
+        for (int j = 0; j < APT; ++j) {
+            const int ad = APT * t + j;
+            st[j] = r;
+            sid[j] = cnt[j] > 0 ? sg : -1;
             ra[j] = rb[j] = -1;
-            ia[j] = ib[j] = oa[j] = ob[j] = 0;
-            st[j] = len[j] = ad[j] = rk[j] = 0;
-            if (sg < n_seg) {
-                st[j] = a.seg_start[sg];
-                len[j] = a.seg_start[sg + 1] - st[j];
-                ad[j] = a.seg_adapter[sg];
-                rk[j] = a.seg_rank[sg];
+            ia[j] = ib[j] = 0;
+            sl[j] = 1;
+            if (ad < NA) s_first[ad] = r;
+            if (cnt[j] > 0) {
+                a.seg_start[sg] = r;
+                a.seg_adapter[sg] = ad;
+                a.seg_rank[sg] = rk[j];
+                ++sg;
+                // the segment's plan parts (as lora_plan cuts them)
                 devplan::SegPlan pa, pb;
-                devplan::lv_apply_parts(len[j], rk[j], a.d_in, a.d_out, pa, pb);
-                ra[j] = range_of(s_rvar, a.n_ranges, pa.variant);
+                devplan::lv_apply_parts(cnt[j], rk[j], a.d_in, a.d_out, pa, pb, s_stab, s_etab);
+                sl[j] = pa.slices;
+                ra[j] = s_vrange[pa.variant];
                 ia[j] = pa.chunks * (pa.shrink ? pa.slices : 1);
                 if (pb.variant >= 0) {
-                    rb[j] = range_of(s_rvar, a.n_ranges, pb.variant);
+                    rb[j] = s_vrange[pb.variant];
                     ib[j] = pb.chunks;
                 }
                 if (ra[j] < 0 || (pb.variant >= 0 && rb[j] < 0)) atomicOr(&s_err, B_ERR_CAPACITY);
             }
+            r += cnt[j];
         }
-        for (int r = 0; r < a.n_ranges; ++r) {
-            int mine = 0;
+    }
+    if (t == 0) {
+        a.seg_start[n_seg] = n_active;
+        s_n_active = n_active;
+        s_n_seg = n_seg;
+    }
+    __syncthreads();  // s_first and the wave prefixes are complete
+
+    // C
+    for (int i = t; i < n_rows; i += BWG) {
+        const uint32_t d = rowdat[i];
+        const int key = (int)(d >> 16);
+        if (key >= NA) continue;  // released (or an invalid id)
+        const int pos = s_first[key] + s_h[(i / B) * NA + key] + (int)(d & 0xFFFFu);
+        if (pos >= 0 && pos < n_rows) a.row_index[pos] = i;
+    }
+    __syncthreads();  // LDS is free for the segment records
+
+    // segment records: start, len, adapter, rank | K slices << 16,
+    // range of part a | range of part b << 8 (0xFF: none), then the parts'
+    // item counts (replaced by their first item in the range below)
 #pragma unroll
-            for (int j = 0; j < SPT; ++j) mine += (ra[j] == r ? ia[j] : 0) + (rb[j] == r ? ib[j] : 0);
-            int total;
-            int run = block_scan(mine, s_tmp, total);
+    for (int j = 0; j < APT; ++j) {
+        if (sid[j] < 0) continue;
+        int32_t* rec = s_rec + 8 * sid[j];
+        rec[0] = st[j];
+        rec[1] = cnt[j];
+        rec[2] = APT * t + j;
+        rec[3] = (rk[j] & 0xFFFF) | (sl[j] << 16);
+        rec[4] = (ra[j] & 0xFF) | ((rb[j] & 0xFF) << 8);
+        rec[5] = ia[j];
+        rec[6] = ib[j];
+    }
+    __syncthreads();
+
+    // D: wave w takes ranges w, w+16, ...: an exclusive prefix of the item
+    // counts over the segments in order (64 at a time)
+    for (int r = w; r < a.n_ranges; r += BWAVES) {
+        int run = 0;
+        for (int base = 0; base < n_seg; base += 64) {
+            const int sg = base + lane;
+            int c = 0, slot = -1;
+            if (sg < n_seg) {
+                const int32_t* rec = s_rec + 8 * sg;
+                const int rr = rec[4];
+                if ((int8_t)(rr & 0xFF) == r) slot = 5;
+                else if ((int8_t)((rr >> 8) & 0xFF) == r) slot = 6;
+                if (slot >= 0) c = rec[slot];
+            }
+            int x = c;
 #pragma unroll
-            for (int j = 0; j < SPT; ++j) {
-                if (ra[j] == r) { oa[j] = run; run += ia[j]; }
-                if (rb[j] == r) { ob[j] = run; run += ib[j]; }
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o);
+                if (lane >= o) x += y;
             }
-            if (t == 0) {
-                s_live[r] = total;
-                if (total > s_rcap[r]) atomicOr(&s_err, B_ERR_CAPACITY);
-            }
+            if (slot >= 0) s_rec[8 * sg + slot] = run + x - c;
+            run += __shfl(x, 63);
         }
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const int sg = SPT * t + j;
-            if (sg >= n_seg) continue;
-            int32_t* rec = s_rec + 8 * sg;
-            rec[0] = st[j];
-            rec[1] = len[j];
-            rec[2] = ad[j];
-            rec[3] = rk[j];
-            rec[4] = ra[j];
-            rec[5] = oa[j];
-            rec[6] = rb[j];
-            rec[7] = ob[j];
+        if (lane == 0) {
+            s_live[r] = run;
+            if (run > s_rcap[r]) atomicOr(&s_err, B_ERR_CAPACITY);
         }
     }
     __syncthreads();
 
-    // E
-    for (int sg = w; sg < n_seg; sg += BWAVES) {
-        const int32_t* rec = s_rec + 8 * sg;
-        const int start = rec[0], len = rec[1], adapter = rec[2], rank = rec[3];
-        devplan::SegPlan parts[2];
-        devplan::lv_apply_parts(len, rank, a.d_in, a.d_out, parts[0], parts[1]);
+    // E: small parts one thread each, larger ones a wave each (lanes over items)
+    for (int pass = 0; pass < 2; ++pass) {
+        const int first = pass == 0 ? t : w, stride = pass == 0 ? BWG : BWAVES;
+        for (int sg = first; sg < n_seg; sg += stride) {
+            const int32_t* rec = s_rec + 8 * sg;
+            const int start = rec[0], len = rec[1], adapter = rec[2], rank = (int16_t)(rec[3] & 0xFFFF);
+            const int slices = rec[3] >> 16;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const devplan::SegPlan& q = parts[h];
-            const int r = rec[4 + 2 * h], o = rec[5 + 2 * h];
-            if (q.variant < 0 || r < 0) continue;
-            const int n = q.chunks * (q.shrink ? q.slices : 1);
-            if (o + n > s_rcap[r]) continue;
-            const int nslices = q.shrink ? q.slices : (q.variant == LV_APPLY_FUSED ? 1 : parts[0].slices);
-            const int base = len / q.chunks, extra = len % q.chunks;
-            for (int i = lane; i < n; i += 64) {
-                const int c = q.shrink ? i / q.slices : i, sl = q.shrink ? i - c * q.slices : 0;
-                const lora_work_t it{start + c * base + min(c, extra), base + (c < extra ? 1 : 0), adapter, rank,
-                                     sl, nslices, {0, 0}};
-                a.work[s_rbeg[r] + o + i] = it;
+            for (int h = 0; h < 2; ++h) {
+                const int r = (int8_t)((rec[4] >> (8 * h)) & 0xFF), o = rec[5 + h];
+                if (r < 0) continue;
+                // the part's shape follows from its range's variant
+                const int v = s_rvar[r];
+                const bool fused = v == LV_APPLY_FUSED, shrink = v < LV_APPLY_EXPAND0;
+                const int mt = fused ? 1 : shrink ? lv_shrink_rows(v / LV_RANK_CLASSES)
+                                                  : lv_expand_rows((v - LV_APPLY_EXPAND0) / LV_RANK_CLASSES);
+                const int lg = __builtin_ctz(mt);  // rows per item are powers of two
+                const int chunks = (len + mt - 1) >> lg;
+                const int per = shrink ? slices : 1;  // items per row chunk
+                const int n = chunks * per;
+                if (o + n > s_rcap[r] || (n <= 4) != (pass == 0)) continue;
+                const int nslices = shrink ? slices : (fused ? 1 : slices);
+                const int base = len / chunks, extra = len - base * chunks;
+                for (int i = pass == 0 ? 0 : lane; i < n; i += pass == 0 ? 1 : 64) {
+                    const int c = per == 1 ? i : i / per, ks = i - c * per;
+                    const lora_work_t it{start + c * base + min(c, extra), base + (c < extra ? 1 : 0), adapter, rank,
+                                         ks, nslices, {0, 0}};
+                    a.work[s_rbeg[r] + o + i] = it;
+                }
             }
         }
     }
@@ -1969,10 +2087,31 @@ extern "C" int32_t lora_batch_build_device(const lora_device_plan_t* plan, const
                                            lora_launch_t* out) {
     if (!plan || !row_adapter || !adapter_rank || !workspace || !out || ((uintptr_t)workspace & 255u) != 0)
         return LORA_EINVAL;
+    // the capacities bound every write of the builder, so the plan must be
+    // one lora_device_plan wrote; plans verified before are remembered (the
+    // layout costs a few microseconds to recompute, a serving loop calls this
+    // every step)
+    static std::mutex mu;
+    static lora_device_plan_t verified[8];
+    static int n_verified = 0, next_slot = 0;
+    bool known = false;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < n_verified && !known; ++i) known = same_plan(verified[i], *plan);
+    }
     lora_device_plan_t chk;
-    if (lora_device_plan(plan->n_rows, plan->n_adapters, plan->max_rank, plan->d_in, plan->d_out, &chk) != LORA_OK ||
-        !same_plan(chk, *plan))
-        return LORA_EINVAL;
+    if (!known) {
+        if (lora_device_plan(plan->n_rows, plan->n_adapters, plan->max_rank, plan->d_in, plan->d_out, &chk) !=
+                LORA_OK ||
+            !same_plan(chk, *plan))
+            return LORA_EINVAL;
+        std::lock_guard<std::mutex> lock(mu);
+        verified[next_slot] = chk;
+        next_slot = (next_slot + 1) % 8;
+        if (n_verified < 8) ++n_verified;
+    } else {
+        chk = *plan;
+    }
     char* ws = static_cast<char*>(workspace);
     BuildArgs args;
     memset(&args, 0, sizeof(args));

@@ -1,8 +1,13 @@
 // Per-segment plan rules, shared by the host planner (lora_plan) and the
 // device plan builder (lora_batch_build_device), so that both cut a segment
 // into the same work items.  Include after the tile-config table
-// (kShrinkCfg, kExpandShape), inside the namespace that holds it.
+// (kShrinkCfg, kExpandShape), inside the namespace that holds it.  Every rule
+// takes the table's two parts by pointer (the device builder passes a copy
+// in LDS); they default to the table itself.
 #pragma once
+
+typedef const ShrinkCfg (*ShrinkTab)[LV_RANK_BUCKETS][LV_D_BUCKETS];
+typedef const int8_t (*ExpandTab)[LV_RANK_BUCKETS][LV_D_BUCKETS];
 
 struct SegCfg {
     int shape;
@@ -12,14 +17,15 @@ struct SegCfg {
 // Shape and K-slice count of a segment for one op.  The slice count always
 // comes from the shrink table (with d_in), so the shrink and expand plans of
 // one batch agree on it.
-static inline LV_HD SegCfg lv_pick(int32_t op, int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
+static inline LV_HD SegCfg lv_pick(int32_t op, int32_t len, int32_t rank, int32_t d_in, int32_t d_out,
+                                   ShrinkTab st, ExpandTab et) {
     const int lb = lv_len_bucket(len), rb = lv_rank_bucket(rank);
-    const ShrinkCfg sc = kShrinkCfg[lb][rb][lv_d_bucket(d_in)];
+    const ShrinkCfg sc = st[lb][rb][lv_d_bucket(d_in)];
     int32_t slices = sc.slices < 1 ? 1 : sc.slices;
     if (slices > LORA_MAX_SLICES) slices = LORA_MAX_SLICES;
     if (slices > d_in / 64) slices = d_in / 64;
     if (op == LORA_OP_SHRINK) return SegCfg{sc.shape, slices};
-    return SegCfg{kExpandShape[lb][rb][lv_d_bucket(d_out)], slices};
+    return SegCfg{et[lb][rb][lv_d_bucket(d_out)], slices};
 }
 
 // One segment's share of a plan.
@@ -33,13 +39,15 @@ struct SegPlan {
 
 // Shrink and expand parts of a segment (the expand variant is op-local to an
 // expand plan; an apply plan shifts it by LV_APPLY_EXPAND0).
-static inline LV_HD SegPlan lv_shrink_part(int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
-    const SegCfg c = lv_pick(LORA_OP_SHRINK, len, rank, d_in, d_out);
+static inline LV_HD SegPlan lv_shrink_part(int32_t len, int32_t rank, int32_t d_in, int32_t d_out,
+                                           ShrinkTab st = kShrinkCfg, ExpandTab et = kExpandShape) {
+    const SegCfg c = lv_pick(LORA_OP_SHRINK, len, rank, d_in, d_out, st, et);
     const int32_t mt = lv_shrink_rows(c.shape);
     return SegPlan{c.shape * LV_RANK_CLASSES + lv_shrink_class(rank), (len + mt - 1) / mt, c.slices, mt, true};
 }
-static inline LV_HD SegPlan lv_expand_part(int32_t len, int32_t rank, int32_t d_in, int32_t d_out) {
-    const SegCfg c = lv_pick(LORA_OP_EXPAND, len, rank, d_in, d_out);
+static inline LV_HD SegPlan lv_expand_part(int32_t len, int32_t rank, int32_t d_in, int32_t d_out,
+                                           ShrinkTab st = kShrinkCfg, ExpandTab et = kExpandShape) {
+    const SegCfg c = lv_pick(LORA_OP_EXPAND, len, rank, d_in, d_out, st, et);
     const int32_t mt = lv_expand_rows(c.shape);
     const int cls = c.shape == LV_E_BGMV ? 0 : lv_expand_class(rank);
     return SegPlan{c.shape * LV_RANK_CLASSES + cls, (len + mt - 1) / mt, c.slices, mt, false};
@@ -60,13 +68,13 @@ static inline LV_HD bool lv_fused(int32_t len, int32_t rank, int32_t d_in, int32
 // row), or a shrink part and an expand part (variant shifted by
 // LV_APPLY_EXPAND0).
 static inline LV_HD void lv_apply_parts(int32_t len, int32_t rank, int32_t d_in, int32_t d_out, SegPlan& a,
-                                        SegPlan& b) {
+                                        SegPlan& b, ShrinkTab st = kShrinkCfg, ExpandTab et = kExpandShape) {
     if (lv_fused(len, rank, d_in, d_out)) {
         a = SegPlan{LV_APPLY_FUSED, len, 1, 1, false};
         b = SegPlan{-1, 0, 1, 1, false};
     } else {
-        a = lv_shrink_part(len, rank, d_in, d_out);
-        b = lv_expand_part(len, rank, d_in, d_out);
+        a = lv_shrink_part(len, rank, d_in, d_out, st, et);
+        b = lv_expand_part(len, rank, d_in, d_out, st, et);
         b.variant += LV_APPLY_EXPAND0;
     }
 }

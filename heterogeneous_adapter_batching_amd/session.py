@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import _lib as _hip  # the HIP runtime the library is linked to (and torch uses)
-from . import (LORA_ECAPACITY, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, LoraPool, Segments,
+from . import (LORA_ECAPACITY, LORA_OK, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, LoraPool, Segments,
                batch_prepare, call_apply, call_expand, call_merge, call_shrink, check_status, lora_apply_proj_t,
                lora_batch_t, lora_device_header_t, lora_device_plan, lora_expand_proj_t, lora_launch_t,
                lora_merge_mat_t, lora_mixture_rows, lora_pool_scatter, lora_shrink_proj_t, make_rows)
@@ -327,14 +327,27 @@ class DeviceBatch:
         self._launch = lora_launch_t()
         self._launch_ref = ctypes.byref(self._launch)
 
-    def build(self, row_adapter, adapter_rank, stream=None):
-        """row_adapter: device int32 [n_rows]; adapter_rank: device int32 [n_adapters]."""
+    def prepare_build(self, row_adapter, adapter_rank, stream=None):
+        """row_adapter: device int32 [n_rows]; adapter_rank: device int32
+        [n_adapters].  Returns fn() that enqueues the builder for the maps'
+        current contents (one library call)."""
         assert row_adapter.dtype == torch.int32 and row_adapter.is_contiguous()
         assert adapter_rank.dtype == torch.int32 and adapter_rank.is_contiguous()
         assert row_adapter.numel() == self.plan.n_rows and adapter_rank.numel() == self.plan.n_adapters
-        st = _hip.lora_batch_build_device(self._plan_ref, row_adapter.data_ptr(), adapter_rank.data_ptr(), self._ws,
-                                stream_handle(stream), self._launch_ref)
-        check_status(st, "lora_batch_build_device")
+        args = (self._plan_ref, row_adapter.data_ptr(), adapter_rank.data_ptr(), self._ws, stream_handle(stream),
+                self._launch_ref)
+        call = _hip.lora_batch_build_device
+
+        def run():
+            st = call(*args)
+            if st != LORA_OK:
+                check_status(st, "lora_batch_build_device")
+        run.keep = (row_adapter, adapter_rank)
+        return run
+
+    def build(self, row_adapter, adapter_rank, stream=None):
+        """Enqueue the builder once (see prepare_build)."""
+        self.prepare_build(row_adapter, adapter_rank, stream)()
         return self
 
     @property

@@ -182,3 +182,20 @@ def test_apply_device_padded_rows_untouched():
     _, yh = run_apply(W)
     _, yd = run_apply_device(W, n_rows=256)
     assert np.array_equal(yh[0], yd[0])
+
+
+def test_apply_device_more_items_than_resident_workgroups():
+    """Each grid-stride kernel walks several items per workgroup: 1500 rows on
+    400 adapters (segments of ~4 rows).  At d 1024 every segment is fused
+    (1500 fused rows); with d_in 8192 none is, so the split-K short shrink
+    (8 K slices), the BGMV expand and the 16-row expand take them."""
+    rng = np.random.default_rng(77)
+    ra = rng.integers(0, 400, 1500).astype(np.int32)
+    ranks = rng.choice([4, 8, 16], 400).astype(np.int32)
+    W = workloads.gen_custom(35, ra, ranks, 1024, 1024, n_proj=2)
+    hb, _ = _same_as_host(W)
+    assert sum(c for v, b, c, m in hb.info_apply.range_list() if v == 32) == 1500
+    W = workloads.gen_custom(36, ra, ranks, 8192, 1024, n_proj=2)
+    hb, _ = _same_as_host(W)
+    variants = {v: c for v, b, c, m in hb.info_apply.range_list()}
+    assert 32 not in variants and sum(c for v, c in variants.items() if v < 4) > 1000
