@@ -311,16 +311,25 @@ extern "C" int32_t lora_device_plan(int32_t n_rows, int32_t n_adapters, int32_t 
     I.max_rank = max_rank;
     I.max_adapter = n_adapters - 1;
     I.v_slices = v_slices;
-    int64_t begin = 0;
+    // one range per launch group, keyed by its smallest variant
+    std::vector<int64_t> gcap(LV_APPLY_VARIANTS, 0);
+    std::vector<int32_t> grows(LV_APPLY_VARIANTS, 0);
     for (int v = 0; v < LV_APPLY_VARIANTS; ++v) {
         if (cap[(size_t)v] == 0) continue;
-        if (I.n_ranges == LORA_MAX_RANGES || begin + cap[(size_t)v] > INT32_MAX / 2) return LORA_EINVAL;
+        const int g = lv_launch_group(v);
+        gcap[(size_t)g] += cap[(size_t)v];
+        grows[(size_t)g] = std::max(grows[(size_t)g], rows_per[(size_t)v]);
+    }
+    int64_t begin = 0;
+    for (int g = 0; g < LV_APPLY_VARIANTS; ++g) {
+        if (gcap[(size_t)g] == 0) continue;
+        if (I.n_ranges == LORA_MAX_RANGES || begin + gcap[(size_t)g] > INT32_MAX / 2) return LORA_EINVAL;
         lora_range_t& R = I.ranges[I.n_ranges++];
-        R.variant = v;
+        R.variant = g;
         R.begin = (int32_t)begin;
-        R.count = (int32_t)cap[(size_t)v];
-        R.rows_per_item = rows_per[(size_t)v];
-        begin += cap[(size_t)v];
+        R.count = (int32_t)gcap[(size_t)g];
+        R.rows_per_item = grows[(size_t)g];
+        begin += gcap[(size_t)g];
     }
     I.n_work = (int32_t)begin;
     p.work_capacity = (int32_t)begin;

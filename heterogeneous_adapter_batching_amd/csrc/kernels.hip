@@ -1809,7 +1809,7 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
     __shared__ int32_t s_tmp[BWAVES];
     __shared__ int32_t s_live[LORA_MAX_RANGES];
     __shared__ int32_t s_rvar[LORA_MAX_RANGES], s_rbeg[LORA_MAX_RANGES], s_rcap[LORA_MAX_RANGES];
-    __shared__ int32_t s_vrange[LV_APPLY_VARIANTS];  // the range of each variant (-1: none)
+    __shared__ int32_t s_vrange[LV_APPLY_VARIANTS];  // the range (launch group) of each variant (-1: none)
     __shared__ devplan::ShrinkCfg s_stab[LV_LEN_BUCKETS][LV_RANK_BUCKETS][LV_D_BUCKETS];
     __shared__ int8_t s_etab[LV_LEN_BUCKETS][LV_RANK_BUCKETS][LV_D_BUCKETS];
     __shared__ int32_t s_err, s_n_active, s_n_seg;
@@ -1840,7 +1840,10 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
         }
 #pragma unroll
         for (int v = 0; v < LV_APPLY_VARIANTS; ++v) s_vrange[v] = -1;
-        for (int r = 0; r < a.n_ranges; ++r) s_vrange[s_rvar[r]] = r;  // variants are in [0, LV_APPLY_VARIANTS)
+        // ranges are keyed by their group's smallest variant (in [0, LV_APPLY_VARIANTS))
+        for (int r = 0; r < a.n_ranges; ++r) s_vrange[s_rvar[r]] = r;
+#pragma unroll
+        for (int v = 0; v < LV_APPLY_VARIANTS; ++v) s_vrange[v] = s_vrange[lv_launch_group(v)];  // key <= v
     }
     {  // the tile table, copied to LDS byte by byte (phase B looks it up per segment)
         constexpr int NS = (int)sizeof(s_stab), NE = (int)sizeof(s_etab);
@@ -1917,7 +1920,7 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
     int tot;
     const int pre = block_scan(rows | (segs << 17), s_tmp, tot);
     const int n_active = tot & 0x1FFFF, n_seg = tot >> 17;
-    int st[APT], sid[APT], ra[APT], rb[APT], ia[APT], ib[APT], sl[APT];
+    int st[APT], sid[APT], va[APT], vb[APT], ia[APT], ib[APT], sl[APT];
     {
         int r = pre & 0x1FFFF, sg = pre >> 17;
 #pragma unroll
@@ -1925,7 +1928,7 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
             const int ad = APT * t + j;
             st[j] = r;
             sid[j] = cnt[j] > 0 ? sg : -1;
-            ra[j] = rb[j] = -1;
+            va[j] = vb[j] = -1;
             ia[j] = ib[j] = 0;
             sl[j] = 1;
             if (ad < NA) s_first[ad] = r;
@@ -1938,13 +1941,12 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
                 devplan::SegPlan pa, pb;
                 devplan::lv_apply_parts(cnt[j], rk[j], a.d_in, a.d_out, pa, pb, s_stab, s_etab);
                 sl[j] = pa.slices;
-                ra[j] = s_vrange[pa.variant];
+                va[j] = pa.variant;
+                vb[j] = pb.variant;
                 ia[j] = pa.chunks * (pa.shrink ? pa.slices : 1);
-                if (pb.variant >= 0) {
-                    rb[j] = s_vrange[pb.variant];
-                    ib[j] = pb.chunks;
-                }
-                if (ra[j] < 0 || (pb.variant >= 0 && rb[j] < 0)) atomicOr(&s_err, B_ERR_CAPACITY);
+                ib[j] = pb.variant >= 0 ? pb.chunks : 0;
+                if (s_vrange[pa.variant] < 0 || (pb.variant >= 0 && s_vrange[pb.variant] < 0))
+                    atomicOr(&s_err, B_ERR_CAPACITY);
             }
             r += cnt[j];
         }
@@ -1967,8 +1969,8 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
     __syncthreads();  // LDS is free for the segment records
 
     // segment records: start, len, adapter, rank | K slices << 16,
-    // range of part a | range of part b << 8 (0xFF: none), then the parts'
-    // item counts (replaced by their first item in the range below)
+    // variant of part a | variant of part b << 8 (0xFF: none), then the
+    // parts' item counts (replaced by their first item in the range below)
 #pragma unroll
     for (int j = 0; j < APT; ++j) {
         if (sid[j] < 0) continue;
@@ -1977,34 +1979,39 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
         rec[1] = cnt[j];
         rec[2] = APT * t + j;
         rec[3] = (rk[j] & 0xFFFF) | (sl[j] << 16);
-        rec[4] = (ra[j] & 0xFF) | ((rb[j] & 0xFF) << 8);
+        rec[4] = (va[j] & 0xFF) | ((vb[j] & 0xFF) << 8);
         rec[5] = ia[j];
         rec[6] = ib[j];
     }
     __syncthreads();
 
-    // D: wave w takes ranges w, w+16, ...: an exclusive prefix of the item
-    // counts over the segments in order (64 at a time)
+    // D: wave w takes ranges w, w+16, ...: the range's variants in order,
+    // each an exclusive prefix of the item counts over the segments in order
+    // (64 at a time), continuing from the variant before
     for (int r = w; r < a.n_ranges; r += BWAVES) {
         int run = 0;
-        for (int base = 0; base < n_seg; base += 64) {
-            const int sg = base + lane;
-            int c = 0, slot = -1;
-            if (sg < n_seg) {
-                const int32_t* rec = s_rec + 8 * sg;
-                const int rr = rec[4];
-                if ((int8_t)(rr & 0xFF) == r) slot = 5;
-                else if ((int8_t)((rr >> 8) & 0xFF) == r) slot = 6;
-                if (slot >= 0) c = rec[slot];
-            }
-            int x = c;
+        for (int m = 0; m < LV_RANK_CLASSES; ++m) {
+            const int v = lv_group_member(s_rvar[r], m);
+            if (v < 0) break;
+            for (int base = 0; base < n_seg; base += 64) {
+                const int sg = base + lane;
+                int c = 0, slot = -1;
+                if (sg < n_seg) {
+                    const int32_t* rec = s_rec + 8 * sg;
+                    const int vv = rec[4];
+                    if ((int8_t)(vv & 0xFF) == v) slot = 5;
+                    else if ((int8_t)((vv >> 8) & 0xFF) == v) slot = 6;
+                    if (slot >= 0) c = rec[slot];
+                }
+                int x = c;
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o);
-                if (lane >= o) x += y;
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(x, o);
+                    if (lane >= o) x += y;
+                }
+                if (slot >= 0) s_rec[8 * sg + slot] = run + x - c;
+                run += __shfl(x, 63);
             }
-            if (slot >= 0) s_rec[8 * sg + slot] = run + x - c;
-            run += __shfl(x, 63);
         }
         if (lane == 0) {
             s_live[r] = run;
@@ -2022,10 +2029,11 @@ __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
             const int slices = rec[3] >> 16;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int r = (int8_t)((rec[4] >> (8 * h)) & 0xFF), o = rec[5 + h];
+                const int v = (int8_t)((rec[4] >> (8 * h)) & 0xFF), o = rec[5 + h];
+                if (v < 0) continue;
+                const int r = s_vrange[v];
                 if (r < 0) continue;
-                // the part's shape follows from its range's variant
-                const int v = s_rvar[r];
+                // the part's shape follows from its variant
                 const bool fused = v == LV_APPLY_FUSED, shrink = v < LV_APPLY_EXPAND0;
                 const int mt = fused ? 1 : shrink ? lv_shrink_rows(v / LV_RANK_CLASSES)
                                                   : lv_expand_rows((v - LV_APPLY_EXPAND0) / LV_RANK_CLASSES);

@@ -1,7 +1,7 @@
 """Device-built plans, host side (CPU only): the layout lora_device_plan fixes
 from bounds must hold the host planner's plan of every batch within those
-bounds, range by range.  The GPU tests check that the builder fills it with
-exactly those items."""
+bounds, launch group by launch group.  The GPU tests check that the builder
+fills it with exactly those items."""
 import ctypes
 import os
 import subprocess
@@ -14,6 +14,24 @@ import heterogeneous_adapter_batching_amd as hl
 REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 LEN_EDGES = [1, 2, 4, 5, 8, 9, 16, 17, 32, 33, 64, 65, 256, 257]
+FUSED = 3 * 4 + 5 * 4   # apply variants: 3 shrink shapes x 4 rank classes, 5 expand shapes x 4, then fused
+
+
+def launch_group(v):
+    """The launch group of an apply variant in a device-built plan, keyed by
+    its smallest variant: the long-segment shrink (shapes 1, 2) of ranks up to
+    64 shares one launch per shape, the MFMA expand (shapes 0-3) one launch
+    per rank class; the split-K shrink, ranks above 64 of the long shrink,
+    the BGMV expand and the fused rows are launches of their own."""
+    if v < 12:
+        shape, cls = divmod(v, 4)
+        return shape * 4 if shape != 0 and cls < 3 else v
+    if v < FUSED:
+        shape, cls = divmod(v - 12, 4)
+        return v if shape == 4 else 12 + cls
+    return v
+
+
 RANK_EDGES = [1, 8, 16, 17, 32, 33, 64, 65, 128]
 
 
@@ -24,16 +42,20 @@ def host_plan(row_adapter, ranks, d_in, d_out):
 
 
 def check_fits(row_adapter, ranks, bounds, d_in, d_out):
-    """Every range of the host apply plan fits the device layout's range of
-    the same variant."""
+    """The host apply plan's items of every launch group fit the device
+    layout's range of that group."""
     n_rows, n_adapters, max_rank = bounds
     _, plan = hl.lora_device_plan(n_rows, n_adapters, max_rank, d_in, d_out)
-    dev = {v: (b, c, m) for v, b, c, m in plan.info.range_list()}
+    dev = {g: (b, c, m) for g, b, c, m in plan.info.range_list()}
     _, _, info = host_plan(row_adapter, ranks, d_in, d_out)
+    need = {}
     for v, _, count, rows_per in info.range_list():
-        assert v in dev, (v, sorted(dev))
-        assert count <= dev[v][1], (v, count, dev[v][1])
-        assert rows_per == dev[v][2]
+        g = launch_group(v)
+        assert g in dev, (v, g, sorted(dev))
+        assert rows_per <= dev[g][2]
+        need[g] = need.get(g, 0) + count
+    for g, n in need.items():
+        assert n <= dev[g][1], (g, n, dev[g][1])
     assert info.v_slices <= plan.info.v_slices
     return plan, info
 
@@ -96,13 +118,20 @@ def test_decode_layout_is_one_fused_range():
     """64 one-token rows, rank <= 16, d 4096: every segment is fused whatever
     the adapters, so the device layout is the fused range alone, 64 items."""
     _, plan = hl.lora_device_plan(64, 1024, 16, 4096, 4096)
-    assert plan.info.range_list() == [(hl_fused_variant(), 0, 64, 1)]
+    assert plan.info.range_list() == [(FUSED, 0, 64, 1)]
     assert plan.info.v_slices == 1 and plan.info.n_active == 64 and plan.info.max_adapter == 1023
 
 
-def hl_fused_variant():
-    # LV_APPLY_FUSED: 3 shrink shapes x 4 rank classes, then 5 expand shapes x 4
-    return 3 * 4 + 5 * 4
+def test_launch_groups():
+    """Each range is keyed by its group's smallest variant, groups are
+    disjoint, and the prefill-sized layout needs 7 launches."""
+    for v in range(FUSED + 1):
+        g = launch_group(v)
+        assert g <= v and launch_group(g) == g
+    _, plan = hl.lora_device_plan(9436, 16, 64, 4096, 4096)
+    keys = [g for g, *_ in plan.info.range_list()]
+    assert keys == sorted(set(keys)) and all(launch_group(g) == g for g in keys)
+    assert keys == [1, 2, 4, 8, 12, 13, FUSED]
 
 
 def test_layout_offsets_and_sizes():
@@ -178,3 +207,31 @@ def test_struct_layouts_match_header(tmp_path):
         assert int(got[name]) == ctypes.sizeof(cls), name
         for fname, _ in cls._fields_:
             assert int(got[f"{name}.{fname}"]) == getattr(cls, fname).offset, (name, fname)
+
+
+def test_launch_group_rules_match_the_library(tmp_path):
+    """The C rules (lv_launch_group, lv_group_member in variants.h) against
+    the statement above: every variant's group and every group's members."""
+    src = tmp_path / "groups.c"
+    src.write_text('''#include <stdio.h>
+#include "hetlora.h"
+#include "variants.h"
+int main(void) {
+    for (int v = 0; v < LV_APPLY_VARIANTS; ++v) printf("g %d %d\\n", v, lv_launch_group(v));
+    for (int key = 0; key < LV_APPLY_VARIANTS; ++key)
+        for (int i = 0; i < 8 && lv_group_member(key, i) >= 0; ++i) printf("m %d %d\\n", key, lv_group_member(key, i));
+    return 0;
+}
+''')
+    exe = tmp_path / "groups"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(REPO, "include"), "-I",
+                    os.path.join(REPO, "heterogeneous_adapter_batching_amd", "csrc"), str(src), "-o", str(exe)],
+                   check=True)
+    lines = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    groups = {int(v): int(g) for k, v, g in (l.split() for l in lines if l.startswith("g"))}
+    assert groups == {v: launch_group(v) for v in range(FUSED + 1)}
+    members = {}
+    for k, key, v in (l.split() for l in lines if l.startswith("m")):
+        members.setdefault(int(key), []).append(int(v))
+    for key in set(groups.values()):
+        assert members[key] == sorted(v for v in groups if groups[v] == key), key

@@ -16,6 +16,7 @@ from heterogeneous_adapter_batching_amd.session import DeviceBatch
 from workloads.device import to_device
 
 from gpu_helpers import check_delta, rows_of, run_apply
+from test_device_plan import launch_group
 
 pytestmark = pytest.mark.gpu
 
@@ -48,10 +49,13 @@ def build_and_compare(ra, ranks, d_in, d_out, n_rows=None, max_rank=None, db=Non
     assert (h.n_seg, h.n_active, h.n_work) == (hs.n_seg, hs.n_active, info.n_work)
     for k in ("row_index", "seg_start", "seg_adapter", "seg_rank"):
         assert np.array_equal(getattr(segs, k), getattr(hs, k)), k
-    assert set(host_items) <= set(items)
-    for v, got in items.items():
-        exp = host_items.get(v, np.zeros((0, hl.WORK_INTS), np.int32))
-        assert np.array_equal(got, exp), v
+    # each range (launch group) holds the host plan's items of its variants,
+    # variant after variant
+    assert {launch_group(v) for v in host_items} <= set(items)
+    for g, got in items.items():
+        parts = [host_items[v] for v in sorted(host_items) if launch_group(v) == g]
+        exp = np.concatenate(parts) if parts else np.zeros((0, hl.WORK_INTS), np.int32)
+        assert np.array_equal(got, exp), g
     return db
 
 
