@@ -870,13 +870,16 @@ template <int KS>
 __global__ __launch_bounds__(WG) void expand_kernel(ExpandArgs args) {
     expand_item<KS>(args, xcd_block((int)blockIdx.x, (int)gridDim.x));
 }
-// Device-built plans: the grid (a multiple of 8, at most the resident
-// workgroups) walks the live (item, column group) pairs, each XCD a
-// contiguous block of them per round.
+// Device-built plans: the live (item, column group) pairs are split into 8
+// contiguous shares, one per XCD (workgroup b runs on XCD b mod 8), and the
+// XCD's workgroups walk its share; the grid is a multiple of 8 and need not
+// match the live count.
 template <int KS>
 __global__ __launch_bounds__(WG) void expand_loop_kernel(ExpandArgs args) {
     const int total = *args.live * args.groups;
-    for (int lid = xcd_block((int)blockIdx.x, (int)gridDim.x); lid < total; lid += gridDim.x) {
+    const int x = (int)blockIdx.x % N_XCD, per_xcd = (int)gridDim.x / N_XCD;
+    const int lo = (int)((int64_t)x * total / N_XCD), hi = (int)((int64_t)(x + 1) * total / N_XCD);
+    for (int lid = lo + (int)blockIdx.x / N_XCD; lid < hi; lid += per_xcd) {
         expand_item<KS>(args, lid);
         __syncthreads();
     }
@@ -1573,6 +1576,9 @@ hipError_t launch_shrink_ranges(const lora_plan_info_t& info, const int32_t* liv
     return err;
 }
 
+#ifndef EXPAND_LOOP_ROUNDS
+#define EXPAND_LOOP_ROUNDS 8
+#endif
 // Expand launch of one range: op-local variant `ev` (shape x rank class),
 // items [begin, begin + count); live != NULL for a device-built plan.
 hipError_t launch_expand_range(int ev, int32_t begin, int32_t count, const int32_t* live, int32_t n_proj,
@@ -1597,8 +1603,10 @@ hipError_t launch_expand_range(int ev, int32_t begin, int32_t count, const int32
     const expand_fn fn = expand_table(ev % LV_RANK_CLASSES, live != nullptr);
     int64_t n1 = (int64_t)count * groups;
     if (live) {
-        const int64_t slots = resident_slots(reinterpret_cast<const void*>(fn));
-        if (n1 > slots) n1 = slots;
+        // a launch group mixes items of 16 to 128 rows: several rounds of
+        // workgroups let the dispatcher even out the load
+        const int64_t cap = EXPAND_LOOP_ROUNDS * (int64_t)resident_slots(reinterpret_cast<const void*>(fn));
+        if (n1 > cap) n1 = cap;
     }
     n1 = (n1 + N_XCD - 1) / N_XCD * N_XCD;  // xcd_block needs a multiple of 8
     return launch(fn, dim3((unsigned)n1), dim3(WG), s, args);
