@@ -326,12 +326,14 @@ int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter,
  * paragraph, and the run-time tile lookup of the VaLoRA blog, section 4.3.2,
  * done on the GPU).  The host fixes the launch shapes in advance from bounds
  * alone (rows, adapters, largest rank, d): lora_device_plan lists every
- * kernel variant a batch within those bounds can need, as one range per
- * variant with room for the most items such a batch can put there.  The
- * builder fills each range with exactly the items lora_plan(LORA_OP_APPLY)
- * gives that variant for the same batch, in the same order, and stores the
- * count; lora_apply then launches every range at its capacity and the
- * workgroups past the count return at once.  Results are bit-identical to
+ * kernel variant a batch within those bounds can need, grouped into one
+ * range per launch (variants one kernel runs share a range: the long-segment
+ * shrink of ranks <= 64 per row shape, the MFMA expand per rank class), each
+ * with room for the most items such a batch can put there.  The builder
+ * fills a range with exactly the items lora_plan(LORA_OP_APPLY) gives its
+ * variants for the same batch, variant after variant in ascending order, and
+ * stores the count; lora_apply then walks each range's live items with a
+ * grid of at most the resident workgroups.  Results are bit-identical to
  * lora_apply with the host-built plan of the same batch.
  *
  * lora_device_plan (host only): the layout for given bounds.
@@ -342,9 +344,10 @@ int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter,
  *   out         the layout: seg_capacity = min(n_rows, n_adapters);
  *               info (op LORA_OP_APPLY, n_active = n_rows, max_rank,
  *               max_adapter = n_adapters - 1, v_slices = the most K slices a
- *               segment can get, one range per variant: begin, count = its
- *               capacity, rows_per_item); byte offsets of each part of the
- *               workspace and its size (256-byte aligned parts)
+ *               segment can get, one range per launch group: variant = the
+ *               group's smallest variant, begin, count = its capacity,
+ *               rows_per_item = its largest); byte offsets of each part of
+ *               the workspace and its size (256-byte aligned parts)
  * Errors: LORA_EINVAL (bounds out of range), LORA_ERANK, LORA_ESHAPE.
  *
  * lora_batch_build_device: enqueue the builder on hip_stream.
