@@ -221,6 +221,9 @@ def main():
     ap.add_argument("--metadata", default="host", choices=["host", "device"],
                     help="decode: host (default) prepares each batch with lora_batch_prepare and one copy; "
                          "device builds it on the GPU (lora_batch_build_device) from device-resident row maps")
+    ap.add_argument("--twin", action="store_true",
+                    help="with --workload prefill|vision|mix70b: also time the homogeneous twin (the same rows on one "
+                         "adapter of the token-weighted mean rank) and report the heterogeneous / homogeneous ratio")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shared-x", action="store_true",
                     help="with --workload prefill|vision: q, k and v take one x (the layer input), o its own")
@@ -349,6 +352,17 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
+    # launch floor: one near-empty kernel (a 1-element fill) between the same
+    # kind of events, on the same stream
+    tiny = torch.zeros(1, dtype=torch.int32, device=dev)
+    floor = []
+    for k in range(40):
+        a, z = HipEvent(timing=True), HipEvent(timing=True)
+        a.record(stream); tiny.fill_(k); z.record(stream)
+        z.synchronize()
+        if k >= 10:
+            floor.append(a.elapsed_time(z) * 1e3)
+
     us = {g: [] for g in groups}
     for ev in evs:
         for gi, g in enumerate(groups):
@@ -412,6 +426,7 @@ def main():
         "path": args.path,
         "metadata": args.metadata,
         "merge_us_per_layer": round(mavg, 3),
+        "launch_floor_us": round(float(np.median(floor)), 3),
         "step_alg_bytes": int(step_bytes),
     }
     if not args.no_cpu_baseline:
@@ -434,28 +449,38 @@ def other_workload(args):
     if getattr(args, "shared_x", False):
         assert k in (2, 3), "--shared-x applies to the prefill and vision workloads (q/k/v share x)"
         kw["shared_qkv"] = True
-    W = workloads.gen_config(k, **kw)
-    dw = to_device(W)
-    rows = lambda desc, off: Rows(dw.pool, off, desc.n_adapters, desc.max_rank, desc.row_len, desc.chunk_len)
-    A = [rows(p.A, d.A_off) for p, d in zip(W.projections, dw.projections)]
-    B = [rows(p.B, d.B_off) for p, d in zip(W.projections, dw.projections)]
-    d_in = max(p.d_in for p in W.projections)
-    d_out = max(p.d_out for p in W.projections)
-    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out).refresh(W.row_adapter)
-    ldv = -(-int(W.adapter_rank.max()) // 4) * 4
-    v = [b.new_v(ldv) for _ in W.projections]
-    do_s = b.prepare_shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)])
-    do_e = b.prepare_expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")   # Infinity Cache flush between steps
-    res = {"shrink": [], "expand": []}
-    for it in range(args.warmup + args.steps):
-        flush.fill_(it & 0xFF)
-        e = [HipEvent(timing=True) for _ in range(3)]
-        e[0].record(); do_s(); e[1].record(); do_e(); e[2].record()
-        torch.cuda.synchronize()
-        if it >= args.warmup:
-            res["shrink"].append(e[0].elapsed_time(e[1]) * 1e3)
-            res["expand"].append(e[1].elapsed_time(e[2]) * 1e3)
+
+    def setup(W):
+        dw = to_device(W)
+        rows = lambda desc, off: Rows(dw.pool, off, desc.n_adapters, desc.max_rank, desc.row_len, desc.chunk_len)
+        A = [rows(p.A, d.A_off) for p, d in zip(W.projections, dw.projections)]
+        B = [rows(p.B, d.B_off) for p, d in zip(W.projections, dw.projections)]
+        d_in = max(p.d_in for p in W.projections)
+        d_out = max(p.d_out for p in W.projections)
+        b = Batch(W.n_rows, W.adapter_rank, d_in, d_out).refresh(W.row_adapter)
+        ldv = -(-int(W.adapter_rank.max()) // 4) * 4
+        return dw, A, B, d_in, d_out, b, ldv
+
+    def time_split(W, dw, A, B, b, ldv):
+        """Median shrink and expand µs over the timed steps (cold cache)."""
+        v = [b.new_v(ldv) for _ in W.projections]
+        do_s = b.prepare_shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)])
+        do_e = b.prepare_expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
+        res = {"shrink": [], "expand": []}
+        for it in range(args.warmup + args.steps):
+            flush.fill_(it & 0xFF)
+            e = [HipEvent(timing=True) for _ in range(3)]
+            e[0].record(); do_s(); e[1].record(); do_e(); e[2].record()
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                res["shrink"].append(e[0].elapsed_time(e[1]) * 1e3)
+                res["expand"].append(e[1].elapsed_time(e[2]) * 1e3)
+        return res
+
+    W = workloads.gen_config(k, **kw)
+    dw, A, B, d_in, d_out, b, ldv = setup(W)
+    res = time_split(W, dw, A, B, b, ldv)
     c = delta_cost(W, W.row_adapter)
     out = {"workload": args.workload + ("+shared-x" if getattr(args, "shared_x", False) else ""),
            "rows": W.n_rows, "active": int((W.row_adapter >= 0).sum()),
@@ -469,6 +494,20 @@ def other_workload(args):
     nb = c["shrink_bytes"] + c["expand_bytes"]
     out["shrink_expand_us"] = round(float(tot), 2)
     out["shrink_expand_hbm_frac"] = round(nb / tot / 1e3 / HBM_PEAK_GBS, 4)
+    if getattr(args, "twin", False):
+        assert k in (2, 3, 4), "--twin applies to the prefill, vision and 70B workloads"
+        Wt = workloads.gen_twin(k)
+        dwt, At, Bt, _, _, bt, ldvt = setup(Wt)
+        rt = time_split(Wt, dwt, At, Bt, bt, ldvt)
+        ct = delta_cost(Wt, Wt.row_adapter)
+        tt = sum(np.median(rt[g]) for g in rt)
+        nbt = ct["shrink_bytes"] + ct["expand_bytes"]
+        out["twin"] = {"rank": int(Wt.adapter_rank[0]), "shrink_us": round(float(np.median(rt["shrink"])), 2),
+                       "expand_us": round(float(np.median(rt["expand"])), 2), "shrink_expand_us": round(float(tt), 2),
+                       "alg_bytes": int(nbt), "hbm_frac": round(nbt / tt / 1e3 / HBM_PEAK_GBS, 4),
+                       "hetero_over_homo_time": round(float(tot / tt), 3),
+                       "hetero_over_homo_bytes": round(nb / nbt, 3)}
+        del dwt, bt
     if args.metadata == "device":
         # lora_apply with the host-built plan, against the builder kernel plus
         # lora_apply with the device-built plan (every range launched at its

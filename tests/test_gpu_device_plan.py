@@ -203,3 +203,14 @@ def test_apply_device_more_items_than_resident_workgroups():
     hb, _ = _same_as_host(W)
     variants = {v: c for v, b, c, m in hb.info_apply.range_list()}
     assert 32 not in variants and sum(c for v, c in variants.items() if v < 4) > 1000
+
+
+def test_apply_device_shared_x_bit_identical():
+    """q, k and v read one x: the device-built launch runs the grouped
+    long-segment shrink (tasks = item x group, counted from the live count)."""
+    ra = np.repeat([0, 1, 2, 3], [300, 1, 150, 520])
+    W = workloads.gen_custom(41, ra, [16, 64, 32, 8], 4096, 4096, n_proj=4, shared_x=[(0, 1, 2)])
+    _same_as_host(W)
+    W = workloads.gen_custom(42, ra, [16, 64, 32, 8], 1024, 8192, n_proj=3, layout="paged", page_elems=1024,
+                             shared_x=[(0, 1, 2)])
+    _same_as_host(W)

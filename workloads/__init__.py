@@ -228,6 +228,8 @@ class Structure(NamedTuple):
     adapter_rank: np.ndarray
     projs: list          # (name, d_in, d_out)
     batches: dict
+    layout: str
+    page_elems: int
 
 
 _structure_only = False
@@ -253,7 +255,7 @@ def _make(name, seed, row_adapter, ranks, projs, layout, page_elems, rng,
     ranks = np.asarray(ranks, dtype=np.int32)
     if _structure_only:
         return Structure(name, row_adapter, ranks, [(pn, di, do) for pn, di, do in projs],
-                         batches or {"main": row_adapter})
+                         batches or {"main": row_adapter}, layout, page_elems)
     n_rows, n_ad = row_adapter.shape[0], ranks.shape[0]
     max_rank = int(ranks.max())
     x_of = {}
@@ -370,6 +372,20 @@ GENERATORS = {0: gen_tiny, 1: gen_decode, 2: gen_prefill, 3: gen_vision, 4: gen_
 def gen_config(k: int, seed: Optional[int] = None, **kw) -> Workload:
     """Workload k (0 tiny, 1 decode, 2 prefill, 3 vision, 4 70B mix); the seeded instance uses seed = k."""
     return GENERATORS[k](k if seed is None else seed, **kw)
+
+
+def gen_twin(k: int, seed: Optional[int] = None) -> Workload:
+    """Homogeneous twin of workload k: the same rows and projections, every
+    active row on one adapter whose rank is the token-weighted mean rank of
+    the heterogeneous batch (flop-matched), released rows still released."""
+    S = structure(k, seed)
+    ra = S.row_adapter
+    active = ra >= 0
+    r = int(round(float(S.adapter_rank[ra[active]].mean())))
+    twin = np.where(active, 0, -1).astype(np.int32)
+    sd = k if seed is None else seed
+    rng = np.random.default_rng([sd, 1])
+    return _make(S.name + "-twin", sd, twin, np.array([r], np.int32), S.projs, S.layout, S.page_elems, rng)
 
 
 def gen_custom(seed, row_adapter, ranks, d_in, d_out, n_proj=1, layout="dense",
