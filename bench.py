@@ -8,8 +8,8 @@ of the whole path over that batch, on one layer:
   1. fully heterogeneous batch (row i -> adapter i, 64 adapters):
      segment build + plans (host, C) -> metadata upload -> lora_apply (every
      segment is one row, so shrink and expand run fused in one kernel)
-  2. homogeneous batch (all rows -> adapter 0): the same (one 64-row segment:
-     lora_apply runs the shrink and the expand kernels)
+  2. homogeneous batch (all rows -> adapter 0): the same (one 64-row
+     rank-16 segment: lora_apply fuses it row by row, 64 x 16 <= 1024)
   3. mode switch of the layer: merge adapter 0 into the four W[4096x4096],
      then unmerge it (one launch each, four matrices per launch)
 
@@ -20,21 +20,27 @@ layers; layer copy 0 is the seeded decode instance the parity tests check.
 Inputs are resident in HBM before the timed region.  `value` is the step's
 algorithmic bytes (what the method must move: x rows, each distinct adapter's
 A and B once, v written and read, y read and written in fp32, W read and
-written in bf16) divided by the wall-clock time per step.  Per-kernel times
-come from HIP events recorded on the stream the kernels run on, inside the
-timed steps (events without the system-scope fence: a default event writes
-back and invalidates the GPU caches when it completes, which idles the GPU
-between the kernels it separates); `roofline` describes the kernel with the largest share of the
-step time.  `cpu_baseline` times the CPU oracle on a bounded sample of the
-same workload.
+written in bf16) divided by the wall-clock time per step.  The timed steps
+record one pair of HIP events each, on the stream the kernels run on, around
+the merge and unmerge: `roofline` describes that kernel (the largest share of
+the step) from those events.  The per-group table comes from as many steps
+again, after the timed ones, with an event between every group.  All events
+are recorded without the system-scope fence: a default event writes back and
+invalidates the GPU caches when it completes, which idles the GPU between
+the kernels it separates.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
 
-With --path split the step calls lora_shrink and lora_expand instead.
+With --path split the step calls lora_shrink and lora_expand instead; with
+--metadata device both batches are built on the GPU (lora_batch_build_device)
+from device-resident row maps, and the builder launches are the first group.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--path apply|split]
-                       [--no-cpu-baseline]
+                       [--metadata host|device] [--no-cpu-baseline]
        python bench.py --workload tiny|prefill|vision|mix70b|mixture|swap|heads
                        (the other workloads; swap: adapter pool; heads: per-adapter vision task heads)
        python bench.py --workload prefill|vision --shared-x           (the same with q/k/v reading one x)
+       python bench.py --workload prefill|vision|mix70b --twin        (and the homogeneous twin, hetero/homo ratio)
+       python bench.py --workload prefill|vision|mix70b --metadata device  (apply: host- vs device-built plan)
        python bench.py --copy-calibration                             (counter calibration under rocprofv3)
        python bench.py --rmw-ceiling                                  (in-place streaming rate of this HBM)
 """
@@ -313,44 +319,58 @@ def main():
         groups = ["metadata"] + groups
         build_h, build_o = bh.prepare_build(het_d, rk_d, stream), bo.prepare_build(homo_d, rk_d, stream)
 
-    # group g runs between events g and g + 1; host metadata: both batches are
-    # prepared (host plan + metadata upload) before the first event; device
-    # metadata: both builder kernels are the first group
-    def step(ev, k):
+    # One step, two ways.  Timed steps record one event pair, around the
+    # merge and unmerge (the roofline kernel): nothing else is added to the
+    # timed region.  Profiled steps (after the timed ones, untimed) record an
+    # event between every group: group g runs between events g and g + 1.
+    # Host metadata: both batches are prepared (host plan + metadata upload)
+    # before the first group; device metadata: both builder kernels are the
+    # first group.
+    def step(ev, k, every_group):
         L = layers[k % len(layers)]
+        g = 0
         if on_device:
-            ev[0].record(stream)
+            if every_group:
+                ev[0].record(stream)
             build_h()
             build_o()
-            ev[1].record(stream)
             g = 1
         else:
             bh.refresh(het, stream)
             bo.refresh(homo, stream)
-            ev[0].record(stream)
-            g = 0
+        if every_group:
+            ev[g].record(stream)
         for fns in L["calls"]:
             for fn in fns:
                 fn()
                 g += 1
-                ev[g].record(stream)
+                if every_group:
+                    ev[g].record(stream)
+        if not every_group:
+            ev[0].record(stream)
         L["merge"]()
         L["unmerge"]()
-        ev[g + 1].record(stream)
+        ev[g + 1 if every_group else 1].record(stream)
 
-    def new_events():
-        return [HipEvent(timing=True) for _ in range(len(groups) + 1)]
+    def new_events(n):
+        return [HipEvent(timing=True) for _ in range(n)]
 
     for k in range(args.warmup):
-        step(new_events(), k)
+        step(new_events(2), k, False)
     torch.cuda.synchronize()
-    evs = [new_events() for _ in range(args.steps)]
+    evs = [new_events(2) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(evs[k], args.warmup + k)
+        step(evs[k], args.warmup + k, False)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    merge_pair_us = [ev[0].elapsed_time(ev[1]) * 1e3 for ev in evs]
+
+    pevs = [new_events(len(groups) + 1) for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(pevs[k], args.warmup + args.steps + k, True)
+    torch.cuda.synchronize()
 
     # launch floor: one near-empty kernel (a 1-element fill) between the same
     # kind of events, on the same stream
@@ -364,10 +384,13 @@ def main():
             floor.append(a.elapsed_time(z) * 1e3)
 
     us = {g: [] for g in groups}
-    for ev in evs:
+    for ev in pevs:
         for gi, g in enumerate(groups):
             us[g].append(ev[gi].elapsed_time(ev[gi + 1]) * 1e3)
     med = {g: float(np.median(us[g])) for g in groups}
+    # the roofline kernel from the timed steps themselves
+    us["merge_unmerge"] = merge_pair_us
+    med["merge_unmerge"] = float(np.median(merge_pair_us))
 
     ch, co = delta_cost(W, het), delta_cost(W, homo)
     mc = merge_cost(4096, 4096, r_m, n_mats)
