@@ -11,12 +11,13 @@ import pytest
 import torch
 
 import heterogeneous_adapter_batching_amd as hl
+import oracle
 import workloads
 from heterogeneous_adapter_batching_amd.session import DeviceBatch
 from workloads.device import to_device
 
 from gpu_helpers import check_delta, rows_of, run_apply
-from test_device_plan import launch_group
+from test_device_plan import FUSED, launch_group
 
 pytestmark = pytest.mark.gpu
 
@@ -37,8 +38,29 @@ def _padded(ra, n_rows):
     return out
 
 
+def check_against_oracle(ra, ranks, segs, items, v_slices):
+    """The device-built segment table against the oracle's, bit for bit, and
+    the device-built work lists against the oracle's coverage invariants: the
+    shrink items and the fused rows cover every (active row, K slice) pair of
+    its segment once, the expand items and the fused rows every active row
+    once, each with its segment's adapter and rank."""
+    ref = oracle.build_segments_ref(ra, ranks)
+    for k in ("row_index", "seg_start", "seg_adapter", "seg_rank"):
+        assert np.array_equal(getattr(segs, k), np.asarray(getattr(ref, k))), k
+    for side in ("shrink", "expand"):
+        keys = [g for g in sorted(items) if g == FUSED or (g < 12) == (side == "shrink")]
+        work = [items[g] for g in keys]
+        begin, ranges = 0, []
+        for g, w in zip(keys, work):
+            ranges.append((g, begin, w.shape[0], 128))
+            begin += w.shape[0]
+        work = np.concatenate(work) if work else np.zeros((0, hl.WORK_INTS), np.int32)
+        oracle.check_plan_coverage(ref, work, ranges, side == "shrink", v_slices)
+
+
 def build_and_compare(ra, ranks, d_in, d_out, n_rows=None, max_rank=None, db=None):
-    """Build on the device and compare with the host planner; returns the DeviceBatch."""
+    """Build on the device and compare with the host planner and the oracle;
+    returns the DeviceBatch."""
     ranks = np.asarray(ranks, np.int32)
     ra = _padded(np.asarray(ra, np.int32), n_rows or len(ra))
     db = db or DeviceBatch(len(ra), len(ranks), max_rank or int(ranks.max()), d_in, d_out)
@@ -56,6 +78,7 @@ def build_and_compare(ra, ranks, d_in, d_out, n_rows=None, max_rank=None, db=Non
         parts = [host_items[v] for v in sorted(host_items) if launch_group(v) == g]
         exp = np.concatenate(parts) if parts else np.zeros((0, hl.WORK_INTS), np.int32)
         assert np.array_equal(got, exp), g
+    check_against_oracle(ra, ranks, segs, items, db.plan.info.v_slices)
     return db
 
 
