@@ -4,6 +4,10 @@
 //   expand  y[row_index[p]][n] += s * sum_j v[p][j] * B_a[j][n]
 //   merge   W[n][k]  = RNE_bf16(W[n][k] + s * sum_j B_a[j][n] * A_a[j][k])
 //
+// plus the adapter-pool scatter and the device-side plan builder (the
+// segment table and the apply plan built on the GPU from a row -> adapter
+// map, for lora_apply's grid-stride launches).
+//
 // (BEE-30060 "Multi-LoRA serving", Punica paragraph: per-request delta
 // x_i A_i B_i, requests grouped by adapter; VaLoRA blog section 4.4.1:
 // Delta W = B x A added once; S-LoRA article, Unified Paging: adapter rows are

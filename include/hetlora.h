@@ -51,11 +51,14 @@
  * GPU work is enqueued on the given hipStream_t (passed as void*; NULL = the
  * null stream) and is asynchronous: no call synchronises.  All functions are
  * re-entrant (a pool manager serves one thread at a time); the only global
- * state is constant tables and a per-device occupancy cache.
+ * state is constant tables, a per-device occupancy cache and a small cache of
+ * device-plan layouts already checked (lora_batch_build_device).
  * Arguments are validated before anything is launched; on error nothing is
  * launched and no output is written, except that the counts of
  * lora_build_segments / lora_plan are written on LORA_ECAPACITY so the caller
- * can resize.  An empty batch (no active rows) is LORA_OK and launches nothing.
+ * can resize.  Inputs that only the device sees (the row map and ranks of
+ * lora_batch_build_device) are checked there, and an invalid batch becomes
+ * an empty plan with an error status in the workspace header.  An empty batch (no active rows) is LORA_OK and launches nothing.
  * Device array contents (row_index, work, row_off) are trusted: they must be
  * what lora_build_segments / lora_plan / the caller's page table produced for
  * the host-side summary passed alongside.  x must not alias y; v must not
