@@ -146,17 +146,37 @@ def test_dense_vs_paged_bit_identical(page):
     check_delta(Wp, batch, vp, yp)
 
 
-def test_repeat_runs_bit_identical():
-    ra = np.repeat([0, 1, 2], [1, 33, 513])
-    W = workloads.gen_custom(25, ra, [16, 96, 64], 1024, 1024, n_proj=3)
+@pytest.mark.parametrize("path", ["split", "apply", "apply_shared_x"])
+def test_repeat_runs_bit_identical(path):
+    """10 runs from the same inputs give the same bits (a race on LDS or a
+    reduction whose order depends on timing would show up here): one-row,
+    short and long segments, several K slices, three projections."""
+    from gpu_helpers import run_apply
+    from workloads.device import reset_outputs
+    ra = np.repeat([0, 1, 2, 3], [1, 33, 513, 700])
+    shared = [(0, 1, 2)] if path == "apply_shared_x" else ()
+    W = workloads.gen_custom(25, ra, [16, 96, 64, 40], 4096, 1024, n_proj=3, shared_x=shared)
     dw = to_device(W)
-    _, _, y1 = run_delta(W, dw=dw)
-    for _ in range(3):
-        from workloads.device import reset_outputs
+    run = (lambda: run_delta(W, dw=dw)[2]) if path == "split" else (lambda: run_apply(W, dw=dw)[1])
+    y1 = run()
+    for _ in range(9):
         reset_outputs(W, dw)
-        _, _, y2 = run_delta(W, dw=dw)
-        for a, b in zip(y1, y2):
+        for a, b in zip(y1, run()):
             assert np.array_equal(a, b)
+
+
+def test_repeat_merge_bit_identical():
+    """10 merges of a 4096 x 4096 W (many tiles, rank 16) give the same bits."""
+    W = workloads.gen_config(1)
+    dw = to_device(W)
+    p, d = W.projections[0], dw.projections[0]
+    w = W.merge.weight(0, 0)
+    r = int(W.adapter_rank[W.merge.adapter])
+    descs = [(p.A, d.A_off, p.B, d.B_off)]
+    first, _ = run_merge([w], dw, descs, W.merge.adapter, r, W.scale)
+    for _ in range(9):
+        again, _ = run_merge([w], dw, descs, W.merge.adapter, r, W.scale)
+        assert np.array_equal(first[0], again[0])
 
 
 def test_empty_batch_no_work():
