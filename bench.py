@@ -153,12 +153,20 @@ def merge_cost(d_out, d_in, r, n):
     return {"bytes": n * (4 * d_out * d_in + r * (d_in + d_out) * 2), "flops": n * 2 * r * d_out * d_in}
 
 
-def cpu_baseline(W, batches, merge_ws, min_seconds=10.0, max_seconds=30.0):
+def cpu_baseline(W, batches, merge_ws, gpu=None, min_seconds=10.0, max_seconds=30.0):
     """The oracle as it stands, on a bounded sample of the same workload: work
     units (the oracle delta for all rows and projections of one batch, or the
     oracle merge + unmerge of one of the layer's W) are run in turn until at
     least `min_seconds` have passed and every unit has run once; the rate is
-    the units' algorithmic bytes over the elapsed time."""
+    the units' algorithmic bytes over the elapsed time.  `gpu` holds the GPU
+    results of the same units (y per batch and projection from y0, merged W
+    bits), which each unit's first oracle result is compared with (the
+    comparison's own time is left out of the rate): the returned `parity`
+    reports the delta's relative Frobenius and max abs error against the
+    4e-3 / 2e-2 bounds, and for the merge the fraction of bits identical to
+    the oracle's and the worst error against the exact W + s*B^T A over its
+    bound (half a bf16 ulp plus the fp32 accumulation allowance; <= 1 is
+    within)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -168,10 +176,24 @@ def cpu_baseline(W, batches, merge_ws, min_seconds=10.0, max_seconds=30.0):
     p0 = W.projections[0]
     r = int(W.adapter_rank[W.merge.adapter])
 
-    def delta_unit(ra):
+    parity = {"delta_relF_max": 0.0, "delta_abs_max": 0.0, "merge_equal_fraction_min": 1.0,
+              "merge_worst_over_bound": 0.0, "checked": []}
+    check_s = [0.0]
+
+    def delta_unit(name, ra):
         def run():
-            for p in W.projections:
-                oracle.apply_ref(ra, W.adapter_rank, p.x, p.y0, W.pool, p.A, p.B, W.scale)
+            for pi, p in enumerate(W.projections):
+                yrows, _ = oracle.apply_ref(ra, W.adapter_rank, p.x, p.y0, W.pool, p.A, p.B, W.scale)
+                if gpu is not None and (name, pi) not in parity["checked"]:
+                    t_check = time.perf_counter()
+                    yref = np.stack([yrows[i] for i in range(len(ra))])
+                    yg = gpu["delta"][name][pi].astype(np.float64)
+                    d_ref, d_gpu = yref - p.y0, yg - p.y0
+                    relf = float(np.linalg.norm(d_gpu - d_ref) / max(np.linalg.norm(d_ref), 1e-300))
+                    parity["delta_relF_max"] = max(parity["delta_relF_max"], relf)
+                    parity["delta_abs_max"] = max(parity["delta_abs_max"], float(np.max(np.abs(yg - yref))))
+                    parity["checked"].append((name, pi))
+                    check_s[0] += time.perf_counter() - t_check
             c = delta_cost(W, ra)
             return c["shrink_bytes"] + c["expand_bytes"], "delta"
         return run
@@ -180,11 +202,28 @@ def cpu_baseline(W, batches, merge_ws, min_seconds=10.0, max_seconds=30.0):
         def run():
             p = W.projections[W.merge.projs[i]]
             wm = oracle.merge_ref(merge_ws[i], W.pool, p.A, p.B, W.merge.adapter, r, W.scale)
+            if gpu is not None and ("merge", i) not in parity["checked"] and i < len(gpu["merge"]):
+                t_check = time.perf_counter()
+                a, b = np.asarray(wm, np.uint16), gpu["merge"][i]
+                parity["merge_equal_fraction_min"] = min(parity["merge_equal_fraction_min"], float(np.mean(a == b)))
+                Aa = oracle.gather_rows_ref(W.pool, p.A.row_off, p.A.max_rank, p.A.row_len, p.A.chunk_len,
+                                            W.merge.adapter, r)
+                Ba = oracle.gather_rows_ref(W.pool, p.B.row_off, p.B.max_rank, p.B.row_len, p.B.chunk_len,
+                                            W.merge.adapter, r)
+                exact = oracle.bf16_to_f64(merge_ws[i]) + W.scale * (Ba.T @ Aa)
+                got = oracle.bf16_to_f64(b)
+                ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(got), 2.0 ** -126))) - 7)
+                bound = (0.5 * ulp + (r + 4) * 2.0 ** -23 * abs(W.scale) * (np.abs(Ba).T @ np.abs(Aa)) +
+                         2.0 ** -23 * np.abs(exact))
+                parity["merge_worst_over_bound"] = max(parity["merge_worst_over_bound"],
+                                                       float(np.max(np.abs(got - exact) / bound)))
+                parity["checked"].append(("merge", i))
+                check_s[0] += time.perf_counter() - t_check
             oracle.unmerge_ref(wm, W.pool, p.A, p.B, W.merge.adapter, r, W.scale)
             return 2 * merge_cost(p.d_out, p.d_in, r, 1)["bytes"], "merge"
         return run
 
-    units = [delta_unit(ra) for ra in batches.values()] + [merge_unit(i) for i in range(len(merge_ws))]
+    units = [delta_unit(n, ra) for n, ra in batches.items()] + [merge_unit(i) for i in range(len(merge_ws))]
     t0 = time.perf_counter()
     nbytes, done, k = 0, {"delta": 0, "merge": 0}, 0
     while True:
@@ -192,14 +231,18 @@ def cpu_baseline(W, batches, merge_ws, min_seconds=10.0, max_seconds=30.0):
         nbytes += b
         done[kind] += 1
         k += 1
-        dt = time.perf_counter() - t0
+        dt = time.perf_counter() - t0 - check_s[0]
         if (k >= len(units) and dt >= min_seconds) or dt >= max_seconds:
             break
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": "%d oracle delta passes (all 64 rows x q/k/v/o of the hetero or homo batch) and %d oracle "
                       "merge+unmerge passes of one W[4096x4096], run in turn for %.1f s"
                       % (done["delta"], done["merge"], dt),
-            "seconds": round(dt, 3), "cpu_model": _cpu_model()}
+            "seconds": round(dt, 3), "cpu_model": _cpu_model(),
+            "parity": None if gpu is None else dict(
+                parity, checked=len(parity["checked"]),
+                within_bounds=bool(parity["delta_relF_max"] <= 4e-3 and parity["delta_abs_max"] <= 2e-2 and
+                                   parity["merge_worst_over_bound"] <= 1.0))}
 
 
 def _cpu_model():
@@ -355,6 +398,28 @@ def main():
     def new_events(n):
         return [HipEvent(timing=True) for _ in range(n)]
 
+    # the GPU results the CPU baseline leg checks against the oracle: layer 0's
+    # batches from y0 and its merged W (both restored afterwards)
+    gpu_results = None
+    if not args.no_cpu_baseline:
+        L0 = layers[0]
+        gpu_results = {"delta": {}, "merge": []}
+        for name, fns in zip(("hetero", "homo"), L0["calls"]):
+            for p, d in zip(W.projections, L0["dw"].projections):
+                d.y.copy_(torch.from_numpy(p.y0))
+            for fn in fns:
+                fn()
+            torch.cuda.synchronize()
+            gpu_results["delta"][name] = [d.y.cpu().numpy() for d in L0["dw"].projections]
+        for p, d in zip(W.projections, L0["dw"].projections):
+            d.y.copy_(torch.from_numpy(p.y0))
+        L0["merge"]()
+        torch.cuda.synchronize()
+        gpu_results["merge"] = [w.cpu().numpy().view(np.uint16).copy() for w in L0["Wt"]]
+        for w, h in zip(L0["Wt"], L0["merge_host"]):
+            w.copy_(torch.from_numpy(np.ascontiguousarray(h).view(np.int16)))
+        torch.cuda.synchronize()
+
     for k in range(args.warmup):
         step(new_events(2), k, False)
     torch.cuda.synchronize()
@@ -453,7 +518,7 @@ def main():
         "step_alg_bytes": int(step_bytes),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(W, {"hetero": het, "homo": homo}, merge_host)
+        out["cpu_baseline"] = cpu_baseline(W, {"hetero": het, "homo": homo}, merge_host, gpu_results)
     print(json.dumps(out), flush=True)
 
 
