@@ -550,14 +550,16 @@ def other_workload(args):
         ldv = -(-int(W.adapter_rank.max()) // 4) * 4
         return dw, A, B, d_in, d_out, b, ldv
 
-    def time_split(W, dw, A, B, b, ldv):
-        """Median shrink and expand µs over the timed steps (cold cache)."""
+    def time_split(W, dw, A, B, b, ldv, cold=True):
+        """Shrink and expand µs over the timed steps: cold (a cache-flushing
+        fill before each step) or warm (the same launches back to back)."""
         v = [b.new_v(ldv) for _ in W.projections]
         do_s = b.prepare_shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)])
         do_e = b.prepare_expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
         res = {"shrink": [], "expand": []}
         for it in range(args.warmup + args.steps):
-            flush.fill_(it & 0xFF)
+            if cold:
+                flush.fill_(it & 0xFF)
             e = [HipEvent(timing=True) for _ in range(3)]
             e[0].record(); do_s(); e[1].record(); do_e(); e[2].record()
             torch.cuda.synchronize()
@@ -569,6 +571,7 @@ def other_workload(args):
     W = workloads.gen_config(k, **kw)
     dw, A, B, d_in, d_out, b, ldv = setup(W)
     res = time_split(W, dw, A, B, b, ldv)
+    warm = time_split(W, dw, A, B, b, ldv, cold=False)
     c = delta_cost(W, W.row_adapter)
     out = {"workload": args.workload + ("+shared-x" if getattr(args, "shared_x", False) else ""),
            "rows": W.n_rows, "active": int((W.row_adapter >= 0).sum()),
@@ -577,7 +580,10 @@ def other_workload(args):
         us = float(np.median(res[g]))
         out["kernels"][g] = {"us_median": round(us, 2), "alg_bytes": int(nb), "GB_s": round(nb / us / 1e3, 1),
                              "hbm_frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
-                             "TFLOP_s": round(fl / us / 1e6, 2)}
+                             "TFLOP_s": round(fl / us / 1e6, 2),
+                             "us_p10": round(float(np.percentile(res[g], 10)), 2),
+                             "us_p90": round(float(np.percentile(res[g], 90)), 2),
+                             "warm_us_median": round(float(np.median(warm[g])), 2)}
     tot = sum(np.median(res[g]) for g in res)
     nb = c["shrink_bytes"] + c["expand_bytes"]
     out["shrink_expand_us"] = round(float(tot), 2)
