@@ -364,7 +364,10 @@ int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter,
  *                 them), a scratch part and the work items.  Only the
  *                 header's counts say which entries are current.
  *   out           host: a ready lora_launch_t (op LORA_OP_APPLY) whose
- *                 row_index, work and live point into the workspace
+ *                 row_index, work and live point into the workspace; the
+ *                 launches that use it must follow the builder on the device
+ *                 (the same stream, or one ordered after it by an event), and
+ *                 the next build into this workspace must follow them
  * The inputs are checked on the device: an adapter id outside [-1,
  * n_adapters) or a rank outside [1, max_rank] leaves status LORA_EADAPTER /
  * LORA_ERANK in the header and an empty plan (every live count 0), so the
