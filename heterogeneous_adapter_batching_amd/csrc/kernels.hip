@@ -1797,19 +1797,22 @@ __device__ int block_scan(int v, int* s_tmp, int& total) {
 // Stable counting sort of the rows by adapter id, the segment table, and the
 // apply plan.  Thread t owns adapters 4t .. 4t+3 and so the segments of those
 // adapters (segments come in adapter order); wave w owns rows [w*B, (w+1)*B).
+// Before A, every thread loads its share of the ids and its adapters' ranks
+// (the only global reads), and the tile table is copied to LDS.
 //  A  each wave counts its rows per adapter in its own LDS column: lanes with
 //     equal ids are found by ballot, one id at a time, and the id's first
 //     lane adds the count; each row keeps (id, rank among the equal ids before
 //     it in the block), in LDS when it fits, else in the scratch part
-//  B  per owned adapter, the exclusive prefix over the waves; then prefix
-//     sums over the adapters: each adapter's first row_index slot and each
-//     segment's id (the segment table is written here)
-//  D  per owned segment, its plan parts (lv_apply_parts, as lora_plan), and
-//     per range an exclusive prefix over the segments in order: each part's
-//     first item in its range
+//  B  per owned adapter, the exclusive prefix over the waves; one prefix sum
+//     over the adapters gives each adapter's first row_index slot and each
+//     segment's id (the segment table is written here); each owned segment is
+//     cut into its plan parts (lv_apply_parts, as lora_plan cuts it)
 //  C  row i goes to slot first[a] + (rows of a in earlier waves) + its rank
-//  E  each wave writes the items of every 16th segment, lanes in parallel
-// Only phase A reads global memory (the ids and the ranks, loaded together).
+//  then the segment records go to LDS (it is free once C is done)
+//  D  wave w takes ranges w, w+16, ...: over the range's variants in order,
+//     an exclusive prefix of the item counts over the segments in order gives
+//     each part its first item in the range
+//  E  the items: small parts one thread each, larger ones a wave each
 // Invalid ids or ranks, or a range over its capacity, leave an error status
 // and every live count 0.
 __global__ __launch_bounds__(BWG) void build_plan_kernel(BuildArgs a) {
