@@ -1447,11 +1447,6 @@ hipError_t launch(void (*fn)(A), dim3 grid, dim3 block, hipStream_t s, A& args) 
 // The first failure of a sequence of launches.
 inline hipError_t first_error(hipError_t acc, hipError_t e) { return acc != hipSuccess ? acc : e; }
 
-// Shrink launches for the plan's ranges [r0, r1) (shrink variants only).
-// Short-segment ranges get one launch each; the long-segment ranges of one
-// shape with ranks up to 64 are consecutive in the work list and share one
-// launch (the kernel picks the rank tiles per item), ranks above 64 get their
-// own.
 // Workgroups of `fn` (`block` threads) that the current device holds at
 // once: CUs x resident workgroups per CU, cached per (device, kernel).
 int resident_slots(const void* fn, int block = WG) {
@@ -1517,6 +1512,12 @@ bool group_shared_x(ShrinkArgs& args, int32_t n_proj) {
     return shared;
 }
 
+// Shrink launches for the plan's ranges [r0, r1) (shrink variants only).
+// Short-segment ranges get one launch each; the long-segment ranges of one
+// shape with ranks up to 64 are consecutive in the work list and share one
+// launch (the kernel picks the rank tiles per item), ranks above 64 get their
+// own.  A device-built plan (live != NULL) already has one range per launch
+// group: each range is one launch, bounded by its live count.
 hipError_t launch_shrink_ranges(const lora_plan_info_t& info, const int32_t* live, int r0, int r1, int32_t n_proj,
                                 hipStream_t s, ShrinkArgs& args) {
     hipError_t err = hipSuccess;
