@@ -267,9 +267,11 @@ def main():
                          "vision mode switch) of that workload for the kernel tables")
     ap.add_argument("--path", default="apply", choices=["apply", "split"],
                     help="apply (default): lora_apply, one-row segments fused; split: lora_shrink then lora_expand")
-    ap.add_argument("--metadata", default="host", choices=["host", "device"],
-                    help="decode: host (default) prepares each batch with lora_batch_prepare and one copy; "
-                         "device builds it on the GPU (lora_batch_build_device) from device-resident row maps")
+    ap.add_argument("--metadata", default="inline", choices=["host", "inline", "device"],
+                    help="decode: inline (default) prepares each batch with lora_batch_prepare on the host and "
+                         "passes the small all-fused plan in the kernel's launch arguments (no copy); host "
+                         "copies the prepared metadata to the device instead; device builds it on the GPU (lora_batch_build_device) "
+                         "from device-resident row maps")
     ap.add_argument("--twin", action="store_true",
                     help="with --workload prefill|vision|mix70b: also time the homogeneous twin (the same rows on one "
                          "adapter of the token-weighted mean rank) and report the heterogeneous / homogeneous ratio")
@@ -331,8 +333,12 @@ def main():
         bh = DeviceBatch(64, len(W.adapter_rank), max_rank, 4096, 4096).build(het_d, rk_d)
         bo = DeviceBatch(64, len(W.adapter_rank), max_rank, 4096, 4096).build(homo_d, rk_d)
     else:
-        bh = Batch(64, W.adapter_rank, 4096, 4096).refresh(het)
-        bo = Batch(64, W.adapter_rank, 4096, 4096).refresh(homo)
+        inline = args.metadata == "inline"
+        assert not inline or args.path == "apply", "inline plans are apply plans"
+        bh = Batch(64, W.adapter_rank, 4096, 4096, inline=inline).refresh(het)
+        bo = Batch(64, W.adapter_rank, 4096, 4096, inline=inline).refresh(homo)
+        # both decode plans are all fused and small: they must travel inline
+        assert not inline or not (bh.apply_launch.work or bo.apply_launch.work), "plan did not go inline"
     vs = {id(b): [b.new_v(ldv) for _ in W.projections] for b in (bh, bo)}
     split = args.path == "split"
     for L in layers:

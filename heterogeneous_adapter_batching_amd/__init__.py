@@ -15,12 +15,14 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
-LORA_ABI_VERSION = 8
+LORA_ABI_VERSION = 9
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
 LORA_MAX_RANGES = 48
 LORA_MAX_MERGE = 8
 LORA_MAX_SLICES = 16
+LORA_INLINE_ITEMS = 64
+LORA_PREPARE_INLINE = 0x100
 WORK_INTS = 8  # int32 fields of lora_work_t
 LORA_OK, LORA_EINVAL, LORA_EADAPTER, LORA_ERANK, LORA_ESHAPE, LORA_ECAPACITY, LORA_EHIP = 0, -1, -2, -3, -4, -5, -6
 LORA_OP_SHRINK, LORA_OP_EXPAND, LORA_OP_APPLY = 0, 1, 2
@@ -66,7 +68,8 @@ class lora_plan_info_t(ctypes.Structure):
 
 
 class lora_launch_t(ctypes.Structure):
-    _fields_ = [("row_index", _vp), ("work", _vp), ("info", lora_plan_info_t), ("live", _vp)]
+    _fields_ = [("row_index", _vp), ("work", _vp), ("info", lora_plan_info_t), ("live", _vp),
+                ("host_work", _vp), ("host_row_index", _vp)]
 
 
 class lora_device_plan_t(ctypes.Structure):

@@ -1026,7 +1026,23 @@ struct FusedArgs {
     int32_t begin;
     int32_t n_active;
     ApplyProj p[LORA_MAX_PROJ];
+    __device__ lora_work_t item(int i) const { return work[begin + i]; }
+    __device__ int32_t row(int j) const { return row_index[j]; }
 };
+// The same for a small all-fused plan carried in the launch arguments: the
+// items and the row index are read from the argument block (scalar loads),
+// so the plan needs no device copy.
+struct FusedInlineArgs {
+    const int32_t* live;  // always NULL
+    int32_t begin;        // always 0
+    int32_t n_active;
+    ApplyProj p[LORA_MAX_PROJ];
+    lora_work_t w[LORA_INLINE_ITEMS];
+    int32_t rows[LORA_INLINE_ITEMS];
+    __device__ lora_work_t item(int i) const { return w[i]; }
+    __device__ int32_t row(int j) const { return rows[j]; }
+};
+static_assert(sizeof(FusedInlineArgs) <= 4096, "a kernel's arguments are at most 4 KiB");
 
 // Wave-uniform read through the scalar data cache (row tables are read-only
 // for the whole launch).  `i` must be the same in every lane of the wave.
@@ -1078,12 +1094,12 @@ __device__ __forceinline__ float wave_sum8(const float (&in)[8], int lane) {
 // offsets are wave-uniform and come through the scalar cache.
 #define FWG 1024
 #define FHALF (FWG / 2)
-template <bool UNI>
-__device__ __forceinline__ void fused_item(const FusedArgs& args, const int bx, const int by) {
+template <bool UNI, typename Args>
+__device__ __forceinline__ void fused_item(const Args& args, const int bx, const int by) {
     __shared__ float s_part[FWG / 64][8];
     __shared__ float s_v[16];
     __shared__ f32x4_t s_acc[FHALF][2];
-    const lora_work_t it = args.work[args.begin + bx];
+    const lora_work_t it = args.item(bx);
     const ApplyProj& P = args.p[by];
     // uniform over the workgroup, so returning here skips no barrier
     if (!(item_live(args.live, bx) && item_ok(it, args.n_active, 1, P.A, LORA_MAX_RANK) & (it.nrows == 1) &
@@ -1120,7 +1136,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& args, const int bx, 
                 boff[e] = P.B.row_off[off_index(P.B, it.adapter, j, cb)];
             }
         }
-        if (g0 == 0) row = args.row_index[it.row0];
+        if (g0 == 0) row = args.row(it.row0);
         issue_fence();
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -1210,6 +1226,10 @@ __device__ __forceinline__ void fused_item(const FusedArgs& args, const int bx, 
 }
 template <bool UNI>
 __global__ __launch_bounds__(FWG) void fused_kernel(FusedArgs args) {
+    fused_item<UNI>(args, blockIdx.x, blockIdx.y);
+}
+template <bool UNI>
+__global__ __launch_bounds__(FWG) void fused_inline_kernel(FusedInlineArgs args) {
     fused_item<UNI>(args, blockIdx.x, blockIdx.y);
 }
 // Device-built plans: a grid of at most the resident workgroups walks the
@@ -1390,12 +1410,23 @@ Rows to_rows(const lora_rows_t& r) {
                 r.neg_from};
 }
 
+// A plan lora_apply carries in its launch arguments: one range of the fused
+// variant, at most LORA_INLINE_ITEMS items (one row each).
+bool plan_inlines(const lora_plan_info_t& I) {
+    return I.op == LORA_OP_APPLY && I.n_ranges == 1 && I.ranges[0].variant == LV_APPLY_FUSED &&
+           I.ranges[0].begin == 0 && I.ranges[0].count == I.n_work && I.n_work <= LORA_INLINE_ITEMS &&
+           I.n_active <= LORA_INLINE_ITEMS;
+}
+bool launch_inlines(const lora_launch_t* L) {
+    return !L->live && L->host_work && L->host_row_index && plan_inlines(L->info);
+}
+
 int32_t check_launch(const lora_launch_t* L, int32_t op, int32_t n_proj) {
     if (!L || n_proj < 1 || n_proj > LORA_MAX_PROJ) return LORA_EINVAL;
     const lora_plan_info_t& I = L->info;
     if (I.op != op || I.n_work < 0 || I.n_ranges < 0 || I.n_ranges > LORA_MAX_RANGES) return LORA_EINVAL;
     if (I.v_slices < 1 || I.v_slices > LORA_MAX_SLICES || I.n_active < 0) return LORA_EINVAL;
-    if (I.n_work > 0 && (!L->row_index || !L->work)) return LORA_EINVAL;
+    if (I.n_work > 0 && (!L->row_index || !L->work) && !(op == LORA_OP_APPLY && launch_inlines(L))) return LORA_EINVAL;
     if (I.max_rank > LORA_MAX_RANK) return LORA_ERANK;
     const int n_variants = op == LORA_OP_SHRINK ? LV_S_SHAPES * LV_RANK_CLASSES
                          : op == LORA_OP_EXPAND ? LV_E_SHAPES * LV_RANK_CLASSES
@@ -1706,6 +1737,20 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
     }
     if (L->info.n_work == 0) return LORA_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    bool uni = true;  // every wave's row offsets are uniform
+    for (int i = 0; i < n_proj; ++i) uni = uni && fa.p[i].A.chunk_len % 512 == 0 && fa.p[i].B.chunk_len % 512 == 0;
+    if (launch_inlines(L)) {  // the plan goes in the launch arguments
+        FusedInlineArgs ia{};
+        ia.live = nullptr;
+        ia.begin = 0;
+        ia.n_active = L->info.n_active;
+        for (int i = 0; i < n_proj; ++i) ia.p[i] = fa.p[i];
+        memcpy(ia.w, L->host_work, sizeof(lora_work_t) * (size_t)L->info.n_work);
+        memcpy(ia.rows, L->host_row_index, sizeof(int32_t) * (size_t)L->info.n_active);
+        const hipError_t e = launch(uni ? fused_inline_kernel<true> : fused_inline_kernel<false>,
+                                    dim3((unsigned)L->info.n_work, (unsigned)n_proj), dim3(FWG), s, ia);
+        return e == hipSuccess ? LORA_OK : LORA_EHIP;
+    }
     hipError_t err = hipSuccess;
     // ranges come in variant order: shrink, expand, fused; the expand ranges
     // follow every shrink range on the stream
@@ -1721,9 +1766,6 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
         } else {
             fa.begin = R.begin;
             fa.live = L->live ? L->live + r : nullptr;
-            bool uni = true;  // every wave's row offsets are uniform
-            for (int i = 0; i < n_proj; ++i)
-                uni = uni && fa.p[i].A.chunk_len % 512 == 0 && fa.p[i].B.chunk_len % 512 == 0;
             const auto fn = fa.live ? (uni ? fused_loop_kernel<true> : fused_loop_kernel<false>)
                                     : (uni ? fused_kernel<true> : fused_kernel<false>);
             const unsigned gx = fa.live ? loop_grid_x(reinterpret_cast<const void*>(fn), R.count, n_proj, FWG)
@@ -2207,6 +2249,8 @@ extern "C" int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter
                                       int32_t* seg_rank, int32_t* staging, int64_t staging_capacity,
                                       void* dev_staging, void* hip_stream, lora_batch_t* out) {
     constexpr int64_t wi = sizeof(lora_work_t) / sizeof(int32_t);
+    const bool want_inline = (op_mask & LORA_PREPARE_INLINE) != 0;
+    op_mask &= ~LORA_PREPARE_INLINE;
     if (!out || !staging || !dev_staging || op_mask == 0 || (op_mask & ~7u) || staging_capacity < 0 || n_rows < 0)
         return LORA_EINVAL;
     if (staging_capacity < n_rows) {  // row_index goes first
@@ -2236,6 +2280,8 @@ extern "C" int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter
     }
     out->n_staged = used;
     if (!fits) return LORA_ECAPACITY;
+    // a small all-fused apply plan travels in the launch arguments: no copy
+    const bool inline_only = want_inline && op_mask == (1u << LORA_OP_APPLY) && plan_inlines(info[LORA_OP_APPLY]);
     int32_t* dev = static_cast<int32_t*>(dev_staging);
     for (int op = 0; op < 3; ++op) {
         lora_launch_t& L = out->launch[op];
@@ -2244,12 +2290,14 @@ extern "C" int32_t lora_batch_prepare(int32_t n_rows, const int32_t* row_adapter
             L.info.op = -1;
             continue;
         }
-        L.row_index = dev;
-        L.work = reinterpret_cast<const lora_work_t*>(dev + off[op]);
+        L.row_index = inline_only ? nullptr : dev;
+        L.work = inline_only ? nullptr : reinterpret_cast<const lora_work_t*>(dev + off[op]);
         L.info = info[op];
         L.live = nullptr;
+        L.host_row_index = staging;
+        L.host_work = reinterpret_cast<const lora_work_t*>(staging + off[op]);
     }
-    if (used == 0) return LORA_OK;
+    if (used == 0 || inline_only) return LORA_OK;
     const hipError_t e = hipMemcpyAsync(dev_staging, staging, (size_t)used * sizeof(int32_t), hipMemcpyHostToDevice,
                                         reinterpret_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? LORA_OK : LORA_EHIP;

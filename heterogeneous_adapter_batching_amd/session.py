@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import _lib as _hip  # the HIP runtime the library is linked to (and torch uses)
-from . import (LORA_ECAPACITY, LORA_OK, LORA_OP_APPLY, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, LoraPool, Segments,
+from . import (LORA_ECAPACITY, LORA_OK, LORA_OP_APPLY, LORA_PREPARE_INLINE, LORA_OP_EXPAND, LORA_OP_SHRINK, WORK_INTS, LoraPool, Segments,
                batch_prepare, call_apply, call_expand, call_merge, call_shrink, check_status, lora_apply_proj_t,
                lora_batch_t, lora_device_header_t, lora_device_plan, lora_expand_proj_t, lora_launch_t,
                lora_merge_mat_t, lora_mixture_rows, lora_pool_scatter, lora_shrink_proj_t, make_rows)
@@ -107,9 +107,14 @@ class Batch:
     table, the three plans, and their upload from a pinned staging buffer on
     the caller's stream), reusing the host arrays and both buffers; the launch
     structs live in the library's output struct and are updated in place, so
-    callables from ``prepare_*`` stay valid across refreshes."""
+    callables from ``prepare_*`` stay valid across refreshes.
 
-    def __init__(self, n_rows_max, adapter_rank, d_in, d_out, device="cuda"):
+    ``inline=True`` plans the apply op only, with LORA_PREPARE_INLINE: a
+    small all-fused plan (decode batches) is then not copied at all but
+    handed to the kernel in its launch arguments; a larger plan is copied as
+    usual.  The shrink and expand launches are then unavailable."""
+
+    def __init__(self, n_rows_max, adapter_rank, d_in, d_out, device="cuda", inline=False):
         self.adapter_rank = np.ascontiguousarray(adapter_rank, dtype=np.int32)
         self.d_in, self.d_out = int(d_in), int(d_out)
         self.device = torch.device(device)
@@ -123,6 +128,7 @@ class Batch:
         self._pending = False
         self._stream, self._stream_h = None, None
         self._n_active, self._v_slices = 0, 1
+        self._op_mask = ((1 << LORA_OP_APPLY) | LORA_PREPARE_INLINE) if inline else 7
         self._alloc(n + WORK_INTS * 10 * n)  # grown on demand
 
     def _alloc_segs(self, cap):
@@ -151,7 +157,7 @@ class Batch:
             self._copied.synchronize()   # the staging buffer may still be in flight
         while True:
             st = batch_prepare(ra.shape[0], ra.ctypes.data, self.adapter_rank.shape[0], self._rank_ptr,
-                               self.d_in, self.d_out, 7, self._seg_cap, *self._seg_ptr, self._host_ptr,
+                               self.d_in, self.d_out, self._op_mask, self._seg_cap, *self._seg_ptr, self._host_ptr,
                                self._host.shape[0], self._dev_ptr, self._stream_h, self._b_ref)
             if st != LORA_ECAPACITY:
                 break
@@ -165,7 +171,8 @@ class Batch:
         self._copied.record(stream)
         self._pending = True
         self._n_active = self._b.n_active
-        self._v_slices = self._launch[LORA_OP_SHRINK].info.v_slices
+        planned = self._launch[LORA_OP_SHRINK] if self._op_mask & 1 else self._launch[LORA_OP_APPLY]
+        self._v_slices = max(1, planned.info.v_slices)
         return self
 
     @property
@@ -200,7 +207,7 @@ class Batch:
 
     def _work(self, op):
         L = self._launch[op]
-        off = (L.work - self._dev_ptr) // 4
+        off = (L.host_work - self._host_ptr) // 4
         return self._hnp[off:off + WORK_INTS * L.info.n_work].reshape(-1, WORK_INTS)
 
     @property

@@ -73,12 +73,13 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 8
+#define LORA_ABI_VERSION 9
 #define LORA_MAX_RANK 128   /* ranks are 1..128                              */
 #define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
 #define LORA_MAX_RANGES 48  /* kernel variants in one plan                   */
 #define LORA_MAX_MERGE 8    /* weight matrices per merge/unmerge call        */
 #define LORA_MAX_SLICES 16  /* K slices of one shrink segment                */
+#define LORA_INLINE_ITEMS 64 /* fused items a plan may carry in its launch     */
 
 /* Status codes (int32_t return value of every call except the two getters). */
 #define LORA_OK         0  /* success                                                  */
@@ -154,6 +155,13 @@ typedef struct lora_plan_info {
 } lora_plan_info_t;
 
 /* What lora_shrink / lora_expand need to launch one plan.
+ *   host_work, host_row_index  host copies of work and row_index (the
+ *         staging buffer lora_batch_prepare wrote), or NULL.  lora_apply
+ *         passes a small all-fused plan (one range of the fused variant, at
+ *         most LORA_INLINE_ITEMS items) to its kernel in the launch
+ *         arguments from these, and then reads neither device array; with
+ *         LORA_PREPARE_INLINE, lora_batch_prepare copies nothing for such a
+ *         plan and leaves row_index and work NULL.
  *   live  NULL for a plan built on the host.  For a plan built on the device
  *         (lora_batch_build_device): device int32 [info.n_ranges], the items
  *         range r really holds; info.ranges[r].count is then the range's
@@ -164,6 +172,8 @@ typedef struct lora_launch {
     const lora_work_t* work;    /* device [info.n_work] (lora_plan, same op)           */
     lora_plan_info_t info;      /* host copy of the plan summary                      */
     const int32_t* live;        /* see above                                          */
+    const lora_work_t* host_work;      /* see above                                   */
+    const int32_t* host_row_index;     /* see above                                   */
 } lora_launch_t;
 
 /* One projection of a shrink: v[p][j] = sum_k x[row_index[p]][k] * A_a[j][k],
@@ -290,7 +300,12 @@ int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
  *   staging layout (int32 elements):  row_index [n_active], then the plan of
  *       each requested op in LORA_OP_* order (info.n_work lora_work_t each)
  *   op_mask      bit (1 << op) for each of LORA_OP_SHRINK / _EXPAND / _APPLY
- *                to plan; at least one
+ *                to plan; at least one.  With LORA_PREPARE_INLINE added and
+ *                LORA_OP_APPLY the only op, a plan lora_apply can carry in
+ *                its launch arguments (see lora_launch_t) is not copied: the
+ *                launch's row_index and work stay NULL, its host_* pointers
+ *                point into staging, and staging must then stay unchanged
+ *                until the lora_apply calls that use it have been made
  *   seg_*        host int32 outputs as in lora_build_segments (seg_start
  *                [seg_capacity + 1], seg_adapter / seg_rank [seg_capacity])
  *   staging      host int32 [staging_capacity]; pinned memory makes the copy
@@ -307,6 +322,8 @@ int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
  * out->n_staged is 0) or staging_capacity is (out->n_staged holds the size
  * needed); nothing is copied then.  LORA_EHIP when the copy cannot be
  * enqueued. */
+#define LORA_PREPARE_INLINE 0x100u
+
 typedef struct lora_batch {
     int32_t n_seg;
     int32_t n_active;

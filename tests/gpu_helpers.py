@@ -34,14 +34,15 @@ def run_delta(W, row_adapter=None, dw=None, scale=None, ldv=None):
     return batch, [v.cpu().numpy() for v in vs], [dp.y.cpu().numpy() for dp in dw.projections]
 
 
-def run_apply(W, row_adapter=None, dw=None, scale=None, ldv=None):
+def run_apply(W, row_adapter=None, dw=None, scale=None, ldv=None, inline=False):
     """lora_apply (fused where the plan says so) for every projection of W;
-    returns (batch, y list) on the host."""
+    returns (batch, y list) on the host.  inline: the batch is prepared with
+    LORA_PREPARE_INLINE (a small all-fused plan rides in the launch arguments)."""
     dw = dw if dw is not None else to_device(W)
     ra = W.row_adapter if row_adapter is None else np.asarray(row_adapter, np.int32)
     d_in = max(p.d_in for p in W.projections)
     d_out = max(p.d_out for p in W.projections)
-    batch = Batch(max(1, W.n_rows), W.adapter_rank, d_in, d_out).refresh(ra)
+    batch = Batch(max(1, W.n_rows), W.adapter_rank, d_in, d_out, inline=inline).refresh(ra)
     ldv = ldv or -(-int(W.adapter_rank.max()) // 4) * 4
     s = W.scale if scale is None else scale
     vs = [batch.new_v(ldv, fill=float("nan")) for _ in W.projections]

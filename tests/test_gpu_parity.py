@@ -304,6 +304,29 @@ def test_apply_matches_shrink_expand_when_nothing_fuses():
     assert np.array_equal(ya[0], yd[0])
 
 
+@pytest.mark.parametrize("case", ["hetero", "homo", "tiny", "not_inline"])
+def test_apply_inline_plan_bit_identical(case):
+    """A plan carried in the launch arguments gives the same bits as the
+    copied one; a plan too large or not all fused falls back to the copy."""
+    from gpu_helpers import run_apply
+    if case in ("hetero", "homo"):
+        W = workloads.gen_config(1)
+        ra = W.batches[case]
+    elif case == "tiny":
+        W, ra = workloads.gen_config(0), None
+    else:  # a long rank-64 segment: shrink + expand ranges, copied
+        ra = np.repeat([0, 1, 2], [1, 3, 200])
+        W = workloads.gen_custom(34, ra, [16, 8, 64], 4096, 4096, n_proj=2)
+    b0, y0 = run_apply(W, ra)
+    b1, y1 = run_apply(W, ra, inline=True)
+    L = b1.apply_launch
+    assert bool(L.work) == (case == "not_inline") and bool(L.row_index) == (case == "not_inline")
+    for a, b in zip(y0, y1):
+        assert np.array_equal(a, b)
+    rep = check_delta(W, b0, None, y1, row_adapter=ra, check_v=False)
+    _say("inline", case, rep)
+
+
 # ------------------------------------------------------------------ batch preparation
 def test_batch_prepare_layout_and_upload():
     """lora_batch_prepare writes row_index and the requested plans back to back

@@ -381,3 +381,28 @@ def test_mixture_rows_errors():
     assert st == hl.LORA_ERANK                       # 70 + 8 > out_max_rank
     st, off, crank, neg = hl.lora_mixture_rows(rank, 2, 1, row_off, 80, 128, raw=True)
     assert st == hl.LORA_OK and crank.tolist() == [72, 78, 8] and neg.tolist() == [64, 70, 8]
+
+
+def test_batch_prepare_inline_copies_nothing():
+    """With LORA_PREPARE_INLINE and the apply op alone, a small all-fused plan
+    (64 one-token rows, rank 16, d 4096) is left in the staging buffer: no
+    copy is enqueued (so this runs without a GPU), the launch's device arrays
+    are NULL and its host pointers point into staging."""
+    import ctypes
+    staging = np.zeros(4096, np.int32)
+    ra = np.arange(64, dtype=np.int32)
+    st, out, segs = hl.lora_batch_prepare(ra, np.full(64, 16), 4096, 4096,
+                                          (1 << hl.LORA_OP_APPLY) | hl.LORA_PREPARE_INLINE, staging, 0x1000)
+    assert st == hl.LORA_OK
+    L = out.launch[hl.LORA_OP_APPLY]
+    assert not L.row_index and not L.work
+    assert L.host_row_index == staging.ctypes.data
+    assert L.host_work == staging.ctypes.data + 4 * 64
+    assert L.info.n_work == 64 and L.info.range_list() == [(3 * 4 + 5 * 4, 0, 64, 1)]
+    assert out.n_staged == 64 + hl.WORK_INTS * 64
+    assert np.array_equal(staging[:64], np.arange(64))
+    assert out.launch[hl.LORA_OP_SHRINK].info.op == -1 and out.launch[hl.LORA_OP_EXPAND].info.op == -1
+    # a flag bit the call does not know
+    st, *_ = hl.lora_batch_prepare(ra, np.full(64, 16), 4096, 4096, (1 << hl.LORA_OP_APPLY) | 0x200, staging,
+                                   0x1000, raw=True)
+    assert st == hl.LORA_EINVAL
