@@ -1,7 +1,7 @@
 """Guard canaries around every output (GPU): y, v and W are views into larger
 buffers (rows above and below, a row stride wider than the row), filled with
 a NaN bit pattern beforehand.  After the shrink, the expand, lora_apply
-(host- and device-built plans, fused and split segments) and merge/unmerge,
+(host-built, inline and device-built plans, fused and split segments) and merge/unmerge,
 every guard word, every released row and every column past the output's
 width must hold its old bits; the outputs themselves match the unguarded
 runs bit for bit."""
@@ -36,7 +36,14 @@ def _workload():
     return workloads.gen_custom(61, ra, [16, 64, 8, 128, 40], 1024, 960, n_proj=2)
 
 
-def _apply_guarded(W, device_plan):
+def _fused_workload():
+    # every segment fused (one row, or len * rank <= 1024) and released rows,
+    # so the plan is small enough to travel in the launch arguments
+    ra = np.array([0, -1, -1, 1, 2, 2, 2, 3, -1, 4, 4], np.int32)
+    return workloads.gen_custom(62, ra, [16, 64, 8, 128, 40], 1024, 960, n_proj=2)
+
+
+def _apply_guarded(W, device_plan, inline=False):
     dw = to_device(W)
     ys, bigs = [], []
     for p, d in zip(W.projections, dw.projections):
@@ -51,7 +58,8 @@ def _apply_guarded(W, device_plan):
         b.build(torch.from_numpy(W.row_adapter.astype(np.int32)).cuda(),
                 torch.from_numpy(W.adapter_rank.astype(np.int32)).cuda())
     else:
-        b = Batch(W.n_rows, W.adapter_rank, 1024, 960).refresh(W.row_adapter)
+        b = Batch(W.n_rows, W.adapter_rank, 1024, 960, inline=inline).refresh(W.row_adapter)
+        assert not inline or not b.apply_launch.work, "plan did not go inline"
     vs = [b.new_v(ldv, fill=float("nan")) for _ in W.projections]
     b.apply([(d.x, rows_of(dw.pool, p.A, d.A_off), v, rows_of(dw.pool, p.B, d.B_off), y, W.scale)
              for p, d, v, y in zip(W.projections, dw.projections, vs, ys)])
@@ -59,11 +67,11 @@ def _apply_guarded(W, device_plan):
     return ys, bigs
 
 
-@pytest.mark.parametrize("device_plan", [False, True])
-def test_apply_writes_nothing_outside_y(device_plan):
-    W = _workload()
+@pytest.mark.parametrize("plan", ["host", "device", "inline"])
+def test_apply_writes_nothing_outside_y(plan):
+    W = _fused_workload() if plan == "inline" else _workload()
     _, ref = run_apply(W)
-    ys, bigs = _apply_guarded(W, device_plan)
+    ys, bigs = _apply_guarded(W, plan == "device", inline=plan == "inline")
     for p, y, big, yr in zip(W.projections, ys, bigs, ref):
         assert np.array_equal(y.cpu().numpy(), yr)
         b = big.cpu().numpy()
