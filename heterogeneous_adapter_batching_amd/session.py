@@ -155,6 +155,7 @@ class Batch:
             self._stream, self._stream_h = stream, stream.cuda_stream
         if self._pending:
             self._copied.synchronize()   # the staging buffer may still be in flight
+            self._pending = False
         while True:
             st = batch_prepare(ra.shape[0], ra.ctypes.data, self.adapter_rank.shape[0], self._rank_ptr,
                                self.d_in, self.d_out, self._op_mask, self._seg_cap, *self._seg_ptr, self._host_ptr,
@@ -168,8 +169,11 @@ class Batch:
             else:
                 break
         check_status(st, "lora_batch_prepare")
-        self._copied.record(stream)
-        self._pending = True
+        # an inline plan stays on the host (lora_apply copies it into the
+        # launch arguments), so nothing is in flight to wait for next time
+        if not (self._op_mask & LORA_PREPARE_INLINE) or self._launch[LORA_OP_APPLY].work:
+            self._copied.record(stream)
+            self._pending = True
         self._n_active = self._b.n_active
         planned = self._launch[LORA_OP_SHRINK] if self._op_mask & 1 else self._launch[LORA_OP_APPLY]
         self._v_slices = max(1, planned.info.v_slices)
