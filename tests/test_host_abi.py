@@ -402,6 +402,32 @@ def test_batch_prepare_inline_copies_nothing():
     assert out.n_staged == 64 + hl.WORK_INTS * 64
     assert np.array_equal(staging[:64], np.arange(64))
     assert out.launch[hl.LORA_OP_SHRINK].info.op == -1 and out.launch[hl.LORA_OP_EXPAND].info.op == -1
+    # lora_apply refuses, before any HIP call, a launch with neither device
+    # arrays nor a complete inline plan
+    lib = hl._lib
+    arr = (hl.lora_apply_proj_t * 1)(hl.lora_apply_proj_t(0x30000, 4096, 4096, _rows(4096, 4096, 16, 64),
+                                                         0x40000, 16, _rows(4096, 4096, 16, 64), 4096, 0x50000,
+                                                         4096, 1.0))
+
+    def apply_with(edit):
+        L2 = hl.lora_launch_t.from_buffer_copy(L)
+        edit(L2)
+        return lib.lora_apply(ctypes.byref(L2), 1, arr, None)
+
+    def no_host_work(L2):
+        L2.host_work = None
+
+    def no_host_rows(L2):
+        L2.host_row_index = None
+
+    def too_many(L2):  # 65 items: past what the launch arguments hold
+        L2.info.n_work = L2.info.ranges[0].count = hl.LORA_INLINE_ITEMS + 1
+
+    def not_fused(L2):
+        L2.info.ranges[0].variant = 0
+
+    for edit in (no_host_work, no_host_rows, too_many, not_fused):
+        assert apply_with(edit) == hl.LORA_EINVAL, edit.__name__
     # a flag bit the call does not know
     st, *_ = hl.lora_batch_prepare(ra, np.full(64, 16), 4096, 4096, (1 << hl.LORA_OP_APPLY) | 0x200, staging,
                                    0x1000, raw=True)
