@@ -15,7 +15,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
-LORA_ABI_VERSION = 9
+LORA_ABI_VERSION = 10
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
 LORA_MAX_RANGES = 48
@@ -60,7 +60,7 @@ class lora_range_t(ctypes.Structure):
 
 class lora_plan_info_t(ctypes.Structure):
     _fields_ = [("op", _i32), ("n_work", _i32), ("n_active", _i32), ("max_rank", _i32),
-                ("max_adapter", _i32), ("v_slices", _i32), ("n_ranges", _i32),
+                ("max_adapter", _i32), ("v_slices", _i32), ("d_in", _i32), ("d_out", _i32), ("n_ranges", _i32),
                 ("ranges", lora_range_t * LORA_MAX_RANGES)]
 
     def range_list(self):

@@ -142,6 +142,8 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
     out.max_rank = 0;
     out.max_adapter = -1;
     out.v_slices = v_slices;
+    out.d_in = d_in;
+    out.d_out = d_out;
     int32_t begin = 0;
     for (int v = 0; v < n_variants; ++v) {
         if (per_variant[(size_t)v] == 0) continue;
@@ -311,6 +313,8 @@ extern "C" int32_t lora_device_plan(int32_t n_rows, int32_t n_adapters, int32_t 
     I.max_rank = max_rank;
     I.max_adapter = n_adapters - 1;
     I.v_slices = v_slices;
+    I.d_in = d_in;
+    I.d_out = d_out;
     // one range per launch group, keyed by its smallest variant
     std::vector<int64_t> gcap(LV_APPLY_VARIANTS, 0);
     std::vector<int32_t> grows(LV_APPLY_VARIANTS, 0);

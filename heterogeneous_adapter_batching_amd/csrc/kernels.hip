@@ -56,12 +56,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 #define WG 256
 
-// Compile-time tuning constants (measured on MI355X; the per-shape choices
-// are made at plan time from the tile table).
-#ifndef HETLORA_HW_CVT
-#define HETLORA_HW_CVT 1          // fp32 -> bf16 with the hardware convert (round to nearest even)
-#endif
-
 namespace {
 
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -108,20 +102,12 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Two fp32 -> packed bf16 bits, round to nearest, ties to even.
+// Two fp32 -> packed bf16 bits, round to nearest, ties to even (the
+// hardware convert, v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-#if HETLORA_HW_CVT
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, p);
-#else
-    auto rne = [](float f) -> uint32_t {
-        const uint32_t u = __float_as_uint(f);
-        if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-        return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    };
-    return rne(lo) | (rne(hi) << 16);
-#endif
 }
 
 // 8 rows (r[e] = 8 consecutive bf16 columns of row e) -> 8 columns
@@ -543,7 +529,7 @@ __device__ __forceinline__ void shrink_rows_task(const ShrinkArgs& args, const l
     // on neither which item holds it nor how A is paged.
     const int nb = kend - kbeg;
     const unsigned h = (unsigned)it.adapter * 2654435761u ^ ((unsigned)pj[0] * 40503u + (unsigned)it.kslice * 977u);
-    const int rot = (int)((h >> 7) % (unsigned)nb);
+    const int rot = nb > 0 ? (int)((h >> 7) % (unsigned)nb) : 0;  // nb = 0: a slice past a narrow projection's d_in
     auto step = [&](int i) { return kbeg + (i + rot < nb ? i + rot : i + rot - nb); };
 #pragma unroll
     for (int b = 0; b < NBUF - 1; ++b)
@@ -1421,6 +1407,20 @@ bool launch_inlines(const lora_launch_t* L) {
     return !L->live && L->host_work && L->host_row_index && plan_inlines(L->info);
 }
 
+// An expand variant (op-local id) that a kernel runs: the MFMA shapes in
+// rank classes 0..2 (rank <= 32, 64, 128), the VALU decode shape in class 0.
+bool expand_variant_ok(int ev) {
+    if (ev < 0 || ev >= LV_E_SHAPES * LV_RANK_CLASSES) return false;
+    const int shape = ev / LV_RANK_CLASSES, cls = ev % LV_RANK_CLASSES;
+    return shape == LV_E_BGMV ? cls == 0 : cls < LV_RANK_CLASSES - 1;
+}
+bool variant_ok(int32_t op, int v) {
+    if (op == LORA_OP_SHRINK) return v >= 0 && v < LV_S_SHAPES * LV_RANK_CLASSES;
+    if (op == LORA_OP_EXPAND) return expand_variant_ok(v);
+    if (v >= 0 && v < LV_APPLY_EXPAND0) return true;
+    return v == LV_APPLY_FUSED || expand_variant_ok(v - LV_APPLY_EXPAND0);
+}
+
 int32_t check_launch(const lora_launch_t* L, int32_t op, int32_t n_proj) {
     if (!L || n_proj < 1 || n_proj > LORA_MAX_PROJ) return LORA_EINVAL;
     const lora_plan_info_t& I = L->info;
@@ -1428,12 +1428,10 @@ int32_t check_launch(const lora_launch_t* L, int32_t op, int32_t n_proj) {
     if (I.v_slices < 1 || I.v_slices > LORA_MAX_SLICES || I.n_active < 0) return LORA_EINVAL;
     if (I.n_work > 0 && (!L->row_index || !L->work) && !(op == LORA_OP_APPLY && launch_inlines(L))) return LORA_EINVAL;
     if (I.max_rank > LORA_MAX_RANK) return LORA_ERANK;
-    const int n_variants = op == LORA_OP_SHRINK ? LV_S_SHAPES * LV_RANK_CLASSES
-                         : op == LORA_OP_EXPAND ? LV_E_SHAPES * LV_RANK_CLASSES
-                                                : LV_APPLY_VARIANTS;
+    if (I.d_in <= 0 || I.d_out <= 0 || I.d_in % 64 != 0 || I.d_out % 64 != 0) return LORA_ESHAPE;
     for (int r = 0; r < I.n_ranges; ++r) {
         const lora_range_t& R = I.ranges[r];
-        if (R.variant < 0 || R.variant >= n_variants || R.begin < 0 || R.count < 0 || R.begin + R.count > I.n_work)
+        if (!variant_ok(op, R.variant) || R.begin < 0 || R.count < 0 || R.begin + R.count > I.n_work)
             return LORA_EINVAL;
     }
     return LORA_OK;
@@ -1663,7 +1661,7 @@ extern "C" int32_t lora_shrink(const lora_launch_t* L, int32_t n_proj, const lor
     for (int i = 0; i < n_proj; ++i) {
         const lora_shrink_proj_t& p = projs[i];
         if (!p.x || !p.v || !aligned16(p.x) || !aligned16(p.v)) return LORA_EINVAL;
-        if (p.d_in <= 0 || p.d_in % 64 != 0) return LORA_ESHAPE;
+        if (p.d_in <= 0 || p.d_in % 64 != 0 || p.d_in > L->info.d_in) return LORA_ESHAPE;
         if (p.ldx < p.d_in || p.ldx % 8 != 0 || p.ldv % 4 != 0 || p.ldv < L->info.max_rank) return LORA_EINVAL;
         if ((st = check_rows(p.A, p.d_in, L->info.max_rank, L->info.max_adapter)) != LORA_OK) return st;
         args.p[i] = ShrinkProj{p.x, p.ldx, to_rows(p.A), p.d_in, p.v, p.ldv};
@@ -1689,7 +1687,7 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
     for (int i = 0; i < n_proj; ++i) {
         const lora_expand_proj_t& p = projs[i];
         if (!p.v || !p.y || !aligned16(p.v) || !aligned16(p.y)) return LORA_EINVAL;
-        if (p.d_out <= 0 || p.d_out % 64 != 0) return LORA_ESHAPE;
+        if (p.d_out <= 0 || p.d_out % 64 != 0 || p.d_out > L->info.d_out) return LORA_ESHAPE;
         if (p.ldy < p.d_out || p.ldy % 4 != 0 || p.ldv % 4 != 0 || p.ldv < L->info.max_rank) return LORA_EINVAL;
         if ((st = check_rows(p.B, p.d_out, L->info.max_rank, L->info.max_adapter)) != LORA_OK) return st;
         args.p[i] = ExpandProj{p.v, p.ldv, to_rows(p.B), p.d_out, p.y, p.ldy, p.scale, 0};
@@ -1712,8 +1710,12 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
     if (st != LORA_OK) return st;
     if (!projs) return LORA_EINVAL;
     bool need_v = false;  // any shrink or expand range (segments that are not fused)
-    for (int r = 0; r < L->info.n_ranges; ++r)
-        if (L->info.ranges[r].variant != LV_APPLY_FUSED && L->info.ranges[r].count > 0) need_v = true;
+    bool fused = false;   // any fused range
+    for (int r = 0; r < L->info.n_ranges; ++r) {
+        if (L->info.ranges[r].count == 0) continue;
+        if (L->info.ranges[r].variant != LV_APPLY_FUSED) need_v = true;
+        else fused = true;
+    }
     ShrinkArgs sa;
     ExpandArgs ea;
     FusedArgs fa;
@@ -1728,6 +1730,10 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
         if (!p.x || !p.y || !aligned16(p.x) || !aligned16(p.y)) return LORA_EINVAL;
         if (need_v && (!p.v || !aligned16(p.v) || p.ldv % 4 != 0 || p.ldv < mr)) return LORA_EINVAL;
         if (p.d_in <= 0 || p.d_in % 64 != 0 || p.d_out <= 0 || p.d_out % 64 != 0) return LORA_ESHAPE;
+        if (p.d_in > L->info.d_in || p.d_out > L->info.d_out) return LORA_ESHAPE;
+        // the fused kernel covers d_in and d_out up to LV_FUSED_MAX_D (a plan
+        // lora_plan made never fuses past it; a hand-made one is refused)
+        if (fused && (p.d_in > LV_FUSED_MAX_D || p.d_out > LV_FUSED_MAX_D)) return LORA_ESHAPE;
         if (p.ldx < p.d_in || p.ldx % 8 != 0 || p.ldy < p.d_out || p.ldy % 4 != 0) return LORA_EINVAL;
         if ((st = check_rows(p.A, p.d_in, mr, ma)) != LORA_OK) return st;
         if ((st = check_rows(p.B, p.d_out, mr, ma)) != LORA_OK) return st;
@@ -2137,7 +2143,8 @@ bool same_plan(const lora_device_plan_t& p, const lora_device_plan_t& q) {
         return false;
     const lora_plan_info_t &a = p.info, &b = q.info;
     if (a.op != b.op || a.n_work != b.n_work || a.n_active != b.n_active || a.max_rank != b.max_rank ||
-        a.max_adapter != b.max_adapter || a.v_slices != b.v_slices || a.n_ranges != b.n_ranges)
+        a.max_adapter != b.max_adapter || a.v_slices != b.v_slices || a.d_in != b.d_in || a.d_out != b.d_out ||
+        a.n_ranges != b.n_ranges)
         return false;
     for (int r = 0; r < a.n_ranges; ++r)
         if (a.ranges[r].variant != b.ranges[r].variant || a.ranges[r].begin != b.ranges[r].begin ||

@@ -63,7 +63,8 @@ struct lora_pool {
 extern "C" int32_t lora_pool_create(int64_t n_pages, int32_t page_elems, int32_t n_adapters, int32_t max_rank,
                                     int32_t n_tables, const int32_t* row_len, lora_pool_t** out) {
     if (!out || !row_len || n_pages <= 0 || n_adapters <= 0 || n_tables < 1 || n_tables > 64) return LORA_EINVAL;
-    if (page_elems <= 0 || page_elems % 64 != 0) return LORA_ESHAPE;
+    // pages up to 65536 elements: the scatter kernel's piece limit
+    if (page_elems <= 0 || page_elems % 64 != 0 || page_elems > 65536) return LORA_ESHAPE;
     if (max_rank < 1 || max_rank > LORA_MAX_RANK) return LORA_ERANK;
     for (int32_t t = 0; t < n_tables; ++t)
         if (row_len[t] <= 0 || row_len[t] % 64 != 0) return LORA_ESHAPE;

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 9
+#define LORA_ABI_VERSION 10
 #define LORA_MAX_RANK 128   /* ranks are 1..128                              */
 #define LORA_MAX_PROJ 8     /* projections per shrink/expand call            */
 #define LORA_MAX_RANGES 48  /* kernel variants in one plan                   */
@@ -150,6 +150,8 @@ typedef struct lora_plan_info {
     int32_t max_rank;     /* largest rank among the items                */
     int32_t max_adapter;  /* largest adapter id among the items (-1 if none) */
     int32_t v_slices;     /* v slices the shrink writes / the expand reads (>= 1) */
+    int32_t d_in;         /* d_in and d_out the plan was made for: the calls  */
+    int32_t d_out;        /* reject projections wider than these (LORA_ESHAPE) */
     int32_t n_ranges;
     lora_range_t ranges[LORA_MAX_RANGES];
 } lora_plan_info_t;
@@ -426,13 +428,15 @@ int32_t lora_batch_build_device(const lora_device_plan_t* plan, const int32_t* r
 
 /* Shrink for n_proj projections (1..LORA_MAX_PROJ) sharing one plan
  * (launch->info.op == LORA_OP_SHRINK): one kernel launch per variant range.
- * Errors: LORA_EINVAL, LORA_ESHAPE, LORA_EADAPTER / LORA_ERANK (summary does
- * not fit the row tables), LORA_EHIP. */
+ * Errors: LORA_EINVAL (also: a range whose variant no kernel runs),
+ * LORA_ESHAPE (also: a projection's d_in above the plan's info.d_in),
+ * LORA_EADAPTER / LORA_ERANK (summary does not fit the row tables), LORA_EHIP. */
 int32_t lora_shrink(const lora_launch_t* launch, int32_t n_proj,
                     const lora_shrink_proj_t* projs, void* hip_stream);
 
 /* Expand for n_proj projections sharing one plan
- * (launch->info.op == LORA_OP_EXPAND).  Same errors as lora_shrink. */
+ * (launch->info.op == LORA_OP_EXPAND).  Same errors as lora_shrink, with
+ * d_out checked against info.d_out. */
 int32_t lora_expand(const lora_launch_t* launch, int32_t n_proj,
                     const lora_expand_proj_t* projs, void* hip_stream);
 
@@ -442,7 +446,8 @@ int32_t lora_expand(const lora_launch_t* launch, int32_t n_proj,
  * d_out into a single kernel that keeps v on chip; the other segments run the
  * shrink and expand kernels of lora_shrink / lora_expand through v.  The
  * result is the same delta within rounding (the fused kernel reduces over
- * d_in in another order).  Errors: as lora_shrink and lora_expand. */
+ * d_in in another order).  Errors: as lora_shrink and lora_expand (d_in and
+ * d_out both checked against the plan's). */
 int32_t lora_apply(const lora_launch_t* launch, int32_t n_proj,
                    const lora_apply_proj_t* projs, void* hip_stream);
 
@@ -528,7 +533,8 @@ typedef struct lora_pool lora_pool_t;
 
 /* Errors: LORA_EINVAL (null out, non-positive sizes, n_tables outside
  * [1, 64]), LORA_ESHAPE (page_elems or a row_len not a positive multiple of
- * 64), LORA_ERANK (max_rank outside [1, LORA_MAX_RANK]). */
+ * 64, or page_elems above 65536, the longest piece lora_pool_scatter copies),
+ * LORA_ERANK (max_rank outside [1, LORA_MAX_RANK]). */
 int32_t lora_pool_create(int64_t n_pages, int32_t page_elems, int32_t n_adapters,
                          int32_t max_rank, int32_t n_tables, const int32_t* row_len,
                          lora_pool_t** out);

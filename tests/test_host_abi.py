@@ -169,6 +169,7 @@ def _launch(op, n_work=1, max_rank=16, max_adapter=0):
     info = hl.lora_plan_info_t()
     info.op, info.n_work, info.n_active, info.max_rank, info.max_adapter = op, n_work, n_work, max_rank, max_adapter
     info.v_slices = 1
+    info.d_in = info.d_out = 512
     info.n_ranges = 1
     info.ranges[0].variant, info.ranges[0].begin, info.ranges[0].count, info.ranges[0].rows_per_item = 0, 0, n_work, 16
     return hl.lora_launch_t(0x1000, 0x2000, info)
@@ -232,6 +233,77 @@ def test_shrink_expand_merge_validation_errors():
     assert merge(ldw=256) == (hl.LORA_EINVAL,) * 2
     assert lib.lora_merge(0, None, None) == hl.LORA_EINVAL
     assert lib.lora_merge(9, None, None) == hl.LORA_EINVAL
+
+
+def test_launch_rejects_variants_no_kernel_runs():
+    """Expand variants of rank class 3 exist only for the VALU decode shape's
+    numbering; no MFMA expand kernel runs them (its rank classes stop at 128
+    ranks in class 2), and the decode shape has class 0 only.  A hand-made
+    launch that names one is refused before anything is launched, for the
+    expand and for the expand part of an apply plan."""
+    lib = hl._lib
+    n_rc = 4
+    e_shapes, bgmv = 5, 4
+    expand0, fused = 3 * n_rc, 3 * n_rc + 5 * n_rc
+    earr = (hl.lora_expand_proj_t * 1)(hl.lora_expand_proj_t(0x40000, 16, _rows(), 512, 0x50000, 512, 2.0))
+    aarr = (hl.lora_apply_proj_t * 1)(hl.lora_apply_proj_t(0x30000, 512, 512, _rows(), 0x40000, 16, _rows(),
+                                                           512, 0x50000, 512, 2.0))
+    bad = [s * n_rc + 3 for s in range(e_shapes)] + [bgmv * n_rc + c for c in (1, 2)] + [-1, e_shapes * n_rc]
+    for ev in bad:
+        LE = _launch(hl.LORA_OP_EXPAND)
+        LE.info.ranges[0].variant = ev
+        assert lib.lora_expand(ctypes.byref(LE), 1, earr, None) == hl.LORA_EINVAL, ev
+        LA = _launch(hl.LORA_OP_APPLY)
+        LA.info.ranges[0].variant = expand0 + ev
+        if expand0 + ev not in (fused,) and not 0 <= expand0 + ev < expand0:
+            assert lib.lora_apply(ctypes.byref(LA), 1, aarr, None) == hl.LORA_EINVAL, ev
+    LA = _launch(hl.LORA_OP_APPLY)
+    LA.info.ranges[0].variant = fused + 1
+    assert lib.lora_apply(ctypes.byref(LA), 1, aarr, None) == hl.LORA_EINVAL
+    LS = _launch(hl.LORA_OP_SHRINK)
+    LS.info.ranges[0].variant = 3 * n_rc
+    sarr = (hl.lora_shrink_proj_t * 1)(hl.lora_shrink_proj_t(0x30000, 512, 512, _rows(), 0x40000, 16))
+    assert lib.lora_shrink(ctypes.byref(LS), 1, sarr, None) == hl.LORA_EINVAL
+
+
+def test_launch_rejects_projections_wider_than_the_plan():
+    """A plan is cut for the d_in / d_out it was made with (its K slices, and
+    whether a segment is fused): a wider projection is refused, as is a
+    fused range at a width the fused kernel does not cover, and a plan
+    summary with no widths."""
+    lib = hl._lib
+    LS = _launch(hl.LORA_OP_SHRINK)
+    arr = (hl.lora_shrink_proj_t * 1)(hl.lora_shrink_proj_t(0x30000, 1024, 1024, _rows(1024, 1024), 0x40000, 16))
+    assert lib.lora_shrink(ctypes.byref(LS), 1, arr, None) == hl.LORA_ESHAPE
+    LE = _launch(hl.LORA_OP_EXPAND)
+    arr = (hl.lora_expand_proj_t * 1)(hl.lora_expand_proj_t(0x40000, 16, _rows(1024, 1024), 1024, 0x50000, 1024, 2.0))
+    assert lib.lora_expand(ctypes.byref(LE), 1, arr, None) == hl.LORA_ESHAPE
+    LE.info.d_out = 0
+    assert lib.lora_expand(ctypes.byref(LE), 1, arr, None) == hl.LORA_ESHAPE
+    fused = 3 * 4 + 5 * 4
+    for d_in, d_out in ((8192, 4096), (4096, 28672)):
+        LA = _launch(hl.LORA_OP_APPLY)
+        LA.info.ranges[0].variant = fused
+        LA.info.d_in, LA.info.d_out = d_in, d_out
+        arr = (hl.lora_apply_proj_t * 1)(hl.lora_apply_proj_t(0x30000, d_in, d_in, _rows(d_in, d_in), 0x40000, 16,
+                                                             _rows(d_out, d_out), d_out, 0x50000, d_out, 2.0))
+        assert lib.lora_apply(ctypes.byref(LA), 1, arr, None) == hl.LORA_ESHAPE, (d_in, d_out)
+
+
+def test_plan_records_its_widths():
+    segs = hl.lora_build_segments([0, 0, 1], [8, 16])
+    for op in (hl.LORA_OP_SHRINK, hl.LORA_OP_EXPAND, hl.LORA_OP_APPLY):
+        _, info = hl.lora_plan(op, segs, 1024, 28672)
+        assert (info.d_in, info.d_out) == (1024, 28672)
+    _, dp = hl.lora_device_plan(64, 8, 16, 2048, 512)
+    assert (dp.info.d_in, dp.info.d_out) == (2048, 512)
+
+
+def test_pool_rejects_pages_past_the_scatter_piece():
+    with pytest.raises(hl.LoraError) as e:
+        hl.LoraPool(4, 65536 + 64, 2, 16, [512])
+    assert e.value.code == hl.LORA_ESHAPE
+    hl.LoraPool(4, 65536, 2, 16, [512])
 
 
 def test_empty_batch_launches_nothing():
