@@ -1,45 +1,44 @@
 #!/usr/bin/env python3
 """Benchmark of the heterogeneous LoRA hot path on one MI355X.
 
-Workload (the decode configuration): a Llama-7B-shaped layer, 64 one-token
-rows, d = 4096, q/k/v/o projections, rank-16 adapters.  One step is one pass
-of the whole path over that batch, on one layer:
+The benchmark line (default, `--workload mix70b`): the 70B-shaped paged mix,
+the largest configuration.  One step = one pass of the whole path over one
+batch of 8,448 rows (256 decode rows, 128 of them released; 8 prefill
+segments of 1024 rows) on q/o (8192 -> 8192) and up (8192 -> 28672), with
+128 adapters of ranks 16/32/64 held in a pool of 8192-element pages under a
+random page table: the host builds the segment table and the apply plan and
+copies them to the device (lora_batch_prepare), then lora_apply runs the
+shrink and expand over the active rows.  Steps alternate between two device
+copies of the inputs (same values, other addresses), so every step streams
+from HBM.  `value` is the step's algorithmic bytes (x rows, each distinct
+adapter's A and B rows once, v written and read, y read and written in fp32)
+over the wall-clock time per step.  lora_apply is issued in pieces split at
+its launch boundaries (all shrink ranges, then each expand range, then the
+fused range: the launches lora_apply makes, in its order), so that the
+timed steps can hold one pair of HIP events around the dominant launch:
+`roofline` describes it.  The same line carries the vision workload's mode
+switch (merge, then unmerge, of its rank-64 adapter into 32 layers x q/k/v/o
+W[4096x4096], each phase cold) as `merge_us_per_layer`, the ratio against
+the homogeneous twin, a per-piece table, and `cpu_baseline`: the CPU oracle
+timed on a bounded sample of the same work and checked against the GPU's
+results.  All events are recorded without the system-scope fence: a default
+event writes back and invalidates the GPU caches when it completes, which
+idles the GPU between the kernels it separates.
 
-  1. fully heterogeneous batch (row i -> adapter i, 64 adapters):
-     segment build + plans (host, C) -> metadata upload -> lora_apply (every
-     segment is one row, so shrink and expand run fused in one kernel)
-  2. homogeneous batch (all rows -> adapter 0): the same (one 64-row
-     rank-16 segment: lora_apply fuses it row by row, 64 x 16 <= 1024)
-  3. mode switch of the layer: merge adapter 0 into the four W[4096x4096],
-     then unmerge it (one launch each, four matrices per launch)
+`--workload decode`: the decode configuration, a Llama-7B-shaped layer of 64
+one-token rows at d 4096 (q/k/v/o, rank 16).  One step: the fully
+heterogeneous batch (64 adapters) and the homogeneous batch (1 adapter)
+through lora_apply, then merge and unmerge of adapter 0 into the layer's four
+W[4096x4096]; steps rotate over 8 layer copies (cold Infinity Cache).  With
+--path split it calls lora_shrink and lora_expand instead; with --metadata
+device both batches are built on the GPU (lora_batch_build_device).
 
-Step k works on layer copy k mod L (default L = 8: each copy has its own
-adapters, x, y and W, about 200 MB), so the working set exceeds the 256 MB
-Infinity Cache and the kernels stream from HBM as they would over a model's
-layers; layer copy 0 is the seeded decode instance the parity tests check.
-Inputs are resident in HBM before the timed region.  `value` is the step's
-algorithmic bytes (what the method must move: x rows, each distinct adapter's
-A and B once, v written and read, y read and written in fp32, W read and
-written in bf16) divided by the wall-clock time per step.  The timed steps
-record one pair of HIP events each, on the stream the kernels run on, around
-the merge and unmerge: `roofline` describes that kernel (the largest share of
-the step) from those events.  The per-group table comes from as many steps
-again, after the timed ones, with an event between every group.  All events
-are recorded without the system-scope fence: a default event writes back and
-invalidates the GPU caches when it completes, which idles the GPU between
-the kernels it separates.  `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload.
-
-With --path split the step calls lora_shrink and lora_expand instead; with
---metadata device both batches are built on the GPU (lora_batch_build_device)
-from device-resident row maps, and the builder launches are the first group.
-
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--path apply|split]
-                       [--metadata host|device] [--no-cpu-baseline]
-       python bench.py --workload tiny|prefill|vision|mix70b|mixture|swap|heads
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --workload decode [--layers L] [--path apply|split] [--metadata host|inline|device]
+       python bench.py --workload tiny|prefill|vision|mixture|swap|heads
                        (the other workloads; swap: adapter pool; heads: per-adapter vision task heads)
        python bench.py --workload prefill|vision --shared-x           (the same with q/k/v reading one x)
-       python bench.py --workload prefill|vision|mix70b --twin        (and the homogeneous twin, hetero/homo ratio)
+       python bench.py --workload prefill|vision|mix70b --twin        (shrink/expand tables and the twin ratio)
        python bench.py --workload prefill|vision|mix70b --metadata device  (apply: host- vs device-built plan)
        python bench.py --copy-calibration                             (counter calibration under rocprofv3)
        python bench.py --rmw-ceiling                                  (in-place streaming rate of this HBM)
@@ -261,10 +260,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=8, help="layer copies the steps rotate over")
-    ap.add_argument("--workload", default="decode", choices=["decode", "tiny", "prefill", "vision", "mix70b",
+    ap.add_argument("--workload", default="mix70b", choices=["decode", "tiny", "prefill", "vision", "mix70b",
                                                              "mixture", "swap", "heads"],
-                    help="decode (default) is the benchmark line; the others time shrink+expand (and the "
-                         "vision mode switch) of that workload for the kernel tables")
+                    help="mix70b (default) is the benchmark line (with the vision mode switch); decode is the "
+                         "decode layer's line; the others time shrink+expand of that workload for the kernel "
+                         "tables")
     ap.add_argument("--path", default="apply", choices=["apply", "split"],
                     help="apply (default): lora_apply, one-row segments fused; split: lora_shrink then lora_expand")
     ap.add_argument("--metadata", default="inline", choices=["host", "inline", "device"],
@@ -298,8 +298,16 @@ def main():
         return swap_workload(args)
     if args.workload == "heads":
         return heads_workload(args)
+    if args.workload == "mix70b" and not (args.twin or args.metadata == "device"):
+        return headline(args)
     if args.workload != "decode":
         return other_workload(args)
+    return decode_workload(args)
+
+
+def decode_workload(args):
+    """The decode configuration's line (see the module docstring's last
+    paragraph)."""
     import torch
     import workloads
     from heterogeneous_adapter_batching_amd.session import Batch, DeviceBatch, HipEvent, Rows, prepare_merge
@@ -525,6 +533,478 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, {"hetero": het, "homo": homo}, merge_host, gpu_results)
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# The benchmark line: the 70B-shaped paged mix, plus the vision mode switch
+# ---------------------------------------------------------------------------
+APPLY_EXPAND0, APPLY_FUSED = 3 * 4, 3 * 4 + 5 * 4   # apply-plan variant numbering (shrink, expand, fused)
+EXPAND_SHAPES = {0: 16, 1: 64, 2: 128, 3: 128, 4: 2}
+MIX70B_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mix70b_dominant_traffic.json")
+
+
+def kernel_section_digest(name):
+    """sha256 of one section of kernels.hip (the kernel's device code)."""
+    src = open(KERNELS_SRC).read()
+    a = src.index(SECTION + name + "\n")
+    b = src.index(SECTION, a + len(SECTION))
+    return hashlib.sha256(src[a:b].encode()).hexdigest()
+
+
+def recorded_traffic(path, kernel):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counters
+    (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, one pass each, each
+    scaled by a plain copy's bytes over the same counter's reading); None when
+    there is no record for this kernel or its source section has changed."""
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel") != kernel or rec.get("source_sha256") != kernel_section_digest(rec.get("section", "")):
+        return None
+    c = rec["copy"]
+    return round(rec["fetch_kib"] * c["bytes"] / c["fetch_kib"] + rec["write_kib"] * c["bytes"] / c["write_kib"])
+
+
+def piece_name(variant):
+    if variant < APPLY_EXPAND0:
+        return "shrink"
+    if variant < APPLY_FUSED:
+        ev = variant - APPLY_EXPAND0
+        shape, cls = divmod(ev, 4)
+        if shape == 4:
+            return "bgmv_expand_kernel"
+        return "expand_kernel<%d> (items of <= %d rows)" % ((1, 2, 4)[cls], EXPAND_SHAPES[shape])
+    return "fused_kernel"
+
+
+def piece_cost(W, work, parts):
+    """Algorithmic bytes and flops of a set of apply-plan items over every
+    projection of W.  parts: which halves the items compute ("shrink",
+    "expand" or both for fused items): x rows (bf16) read and v written by
+    the shrink; v read, y read and written (fp32) by the expand; each
+    distinct adapter's A rows (shrink) and B rows (expand) once."""
+    nb = fl = 0
+    rows_r = []          # (row, rank) of every row the items cover, once
+    seen, adapters = set(), set()
+    for w in work:
+        row0, nrows, a, r = int(w[0]), int(w[1]), int(w[2]), int(w[3])
+        adapters.add((a, r))
+        for q in range(row0, row0 + nrows):
+            if q not in seen:
+                seen.add(q)
+                rows_r.append(r)
+    rows_r = np.asarray(rows_r, np.int64)
+    n = rows_r.size
+    for p in W.projections:
+        if "shrink" in parts:
+            nb += n * p.d_in * 2 + sum(r * p.d_in * 2 for _, r in adapters) + int(rows_r.sum()) * 4
+            fl += 2 * int(rows_r.sum()) * p.d_in
+        if "expand" in parts:
+            nb += int(rows_r.sum()) * 4 + sum(r * p.d_out * 2 for _, r in adapters) + n * p.d_out * 8
+            fl += 2 * int(rows_r.sum()) * p.d_out
+    return nb, fl
+
+
+def apply_pieces(batch, projs):
+    """lora_apply of the batch's current apply plan issued in pieces, each a
+    lora_apply call on a copy of the launch that keeps some of its ranges:
+    all shrink ranges (one call: the launcher groups them exactly as
+    lora_apply does), then every expand range alone, then the fused range.
+    lora_apply itself makes the same launches in the same order (one launch
+    per expand range), so the pieces are the call split at its launch
+    boundaries, which lets events sit between them.  Returns [(name,
+    range indices, fn, items)]."""
+    import ctypes
+    from heterogeneous_adapter_batching_amd import lora_apply_proj_t, lora_launch_t, call_apply
+    from heterogeneous_adapter_batching_amd.session import stream_handle
+    L = batch.apply_launch
+    info = L.info
+    ranges = info.range_list()
+    groups = []
+    sh = [i for i, (v, _, c, _) in enumerate(ranges) if v < APPLY_EXPAND0 and c > 0]
+    if sh:
+        groups.append(("shrink", sh))
+    for i, (v, _, c, _) in enumerate(ranges):
+        if APPLY_EXPAND0 <= v < APPLY_FUSED and c > 0:
+            groups.append((piece_name(v), [i]))
+    for i, (v, _, c, _) in enumerate(ranges):
+        if v == APPLY_FUSED and c > 0:
+            groups.append(("fused_kernel", [i]))
+    arr = (lora_apply_proj_t * len(projs))(*[
+        lora_apply_proj_t(x.data_ptr(), x.stride(0), x.shape[1], A.c(), v.data_ptr(), v.stride(1), B.c(),
+                          y.shape[1], y.data_ptr(), y.stride(0), float(s))
+        for x, A, v, B, y, s in projs])
+    h = stream_handle()
+    work = batch.work_apply.copy()
+    out = []
+    for name, idx in groups:
+        sub = lora_launch_t.from_buffer_copy(L)
+        sub.info.n_ranges = len(idx)
+        for j, i in enumerate(idx):
+            sub.info.ranges[j] = L.info.ranges[i]
+        items = np.concatenate([work[ranges[i][1]:ranges[i][1] + ranges[i][2]] for i in idx])
+
+        def fn(sub=sub):
+            call_apply(sub, arr, len(projs), h)
+        fn.keep = (sub, arr, projs)
+        out.append((name, idx, fn, items))
+    return out
+
+
+def cpu_baseline_mix(W, gpu_y, V, vision_merge, min_seconds=10.0, max_seconds=30.0):
+    """The oracle as it stands, timed on a bounded sample of the benchmark's
+    work on the host cores, and checked against the GPU's results of the same
+    work.  Units, run in turn until `min_seconds` have passed and every unit
+    ran once: (1) the oracle delta of a 1-in-16 sample of the 70B mix's rows
+    (every 16th row, released ones included: they cost a copy) for one
+    projection, cycling over q, o and up; (2) the oracle merge + unmerge of
+    one vision W[4096x4096] with the rank-64 adapter.  The rate is the units'
+    algorithmic bytes (the same definitions as the GPU figures) over the
+    elapsed time; the comparisons' own time is left out."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    ra = np.asarray(W.row_adapter)
+    sample = np.arange(0, W.n_rows, 16)
+    act = sample[ra[sample] >= 0]
+    distinct = np.unique(ra[act])
+    r_act = W.adapter_rank[ra[act]].astype(np.int64)
+    parity = {"delta_relF_max": 0.0, "delta_abs_max": 0.0, "rows_checked": 0, "released_untouched": True,
+              "merge_equal_fraction": None, "merge_worst_over_bound": None}
+    check_s = [0.0]
+
+    def delta_unit(pi):
+        def run():
+            p = W.projections[pi]
+            yrows, _ = oracle.apply_ref(ra, W.adapter_rank, p.x, p.y0, W.pool, p.A, p.B, W.scale, rows=sample)
+            if ("delta", pi) not in done_checks:
+                t0 = time.perf_counter()
+                yg = gpu_y[pi]
+                num = den = 0.0
+                for i in sample:
+                    if ra[i] < 0:
+                        parity["released_untouched"] &= bool(np.array_equal(yg[i], p.y0[i]))
+                        continue
+                    dr = yrows[i] - p.y0[i]
+                    dg = yg[i].astype(np.float64) - p.y0[i]
+                    num += float(np.sum((dg - dr) ** 2))
+                    den += float(np.sum(dr ** 2))
+                    parity["delta_abs_max"] = max(parity["delta_abs_max"], float(np.max(np.abs(dg - dr))))
+                    parity["rows_checked"] += 1
+                parity["delta_relF_max"] = max(parity["delta_relF_max"], (num / den) ** 0.5)
+                done_checks.add(("delta", pi))
+                check_s[0] += time.perf_counter() - t0
+            nb = act.size * p.d_in * 2 + act.size * p.d_out * 8 + int(r_act.sum()) * 8 + \
+                int(W.adapter_rank[distinct].sum()) * (p.d_in + p.d_out) * 2
+            return nb, "delta"
+        return run
+
+    def merge_unit():
+        spec = V.merge
+        p = V.projections[spec.projs[0]]
+        r = int(V.adapter_rank[spec.adapter])
+        w0, got = vision_merge
+
+        def run():
+            wm = oracle.merge_ref(w0, V.pool, p.A, p.B, spec.adapter, r, V.scale)
+            if "merge" not in done_checks:
+                t0 = time.perf_counter()
+                parity["merge_equal_fraction"] = float(np.mean(np.asarray(wm, np.uint16) == got))
+                Aa = oracle.gather_rows_ref(V.pool, p.A.row_off, p.A.max_rank, p.A.row_len, p.A.chunk_len,
+                                            spec.adapter, r)
+                Ba = oracle.gather_rows_ref(V.pool, p.B.row_off, p.B.max_rank, p.B.row_len, p.B.chunk_len,
+                                            spec.adapter, r)
+                exact = oracle.bf16_to_f64(w0) + V.scale * (Ba.T @ Aa)
+                g = oracle.bf16_to_f64(got)
+                ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(g), 2.0 ** -126))) - 7)
+                bound = (0.5 * ulp + (r + 4) * 2.0 ** -23 * abs(V.scale) * (np.abs(Ba).T @ np.abs(Aa)) +
+                         2.0 ** -23 * np.abs(exact))
+                parity["merge_worst_over_bound"] = float(np.max(np.abs(g - exact) / bound))
+                done_checks.add("merge")
+                check_s[0] += time.perf_counter() - t0
+            oracle.unmerge_ref(wm, V.pool, p.A, p.B, spec.adapter, r, V.scale)
+            return 2 * merge_cost(p.d_out, p.d_in, r, 1)["bytes"], "merge"
+        return run
+
+    done_checks = set()
+    units = [delta_unit(pi) for pi in range(len(W.projections))] + [merge_unit()]
+    t0 = time.perf_counter()
+    nbytes, done, k = 0, {"delta": 0, "merge": 0}, 0
+    while True:
+        b, kind = units[k % len(units)]()
+        nbytes += b
+        done[kind] += 1
+        k += 1
+        dt = time.perf_counter() - t0 - check_s[0]
+        if (k >= len(units) and dt >= min_seconds) or dt >= max_seconds:
+            break
+    parity["within_bounds"] = bool(parity["delta_relF_max"] <= 4e-3 and parity["delta_abs_max"] <= 2e-2 and
+                                   parity["released_untouched"] and parity["merge_worst_over_bound"] <= 1.0)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d oracle delta passes over every 16th row of the 70B mix (%d rows, %d active) for one "
+                      "projection each (q, o, up in turn) and %d oracle merge+unmerge passes of one vision "
+                      "W[4096x4096] with the rank-64 adapter, run in turn for %.1f s"
+                      % (done["delta"], sample.size, act.size, done["merge"], dt),
+            "seconds": round(dt, 3), "cpu_model": _cpu_model(), "parity": parity}
+
+
+def headline(args):
+    """The benchmark line.  Workload: the 70B-shaped paged mix (d 8192; q and
+    o 8192 -> 8192, up 8192 -> 28672; 256 decode rows of which 128 are
+    released, plus 8 prefill segments of 1024 rows; 128 adapters of ranks
+    16/32/64 in a paged pool of 8192-element pages).  One step = one pass of
+    the whole path over that batch: the host builds the segment table and the
+    apply plan and copies them to the device (lora_batch_prepare), then
+    lora_apply runs the shrink and expand of every projection over the
+    active rows, gathering adapter rows through the page table.  Steps
+    alternate between two device copies of the inputs (same values, other
+    addresses), so no step finds the previous one's data in the Infinity
+    Cache.  Inputs are resident in HBM before the timed region.
+
+    Beside it, in the same line: the vision workload's mode switch (merge of
+    its rank-64 adapter into 32 layers x q/k/v/o W[4096x4096], then unmerge),
+    as merge and unmerge µs per layer, each phase cold (it streams 4.3 GB of
+    W); and the heterogeneous / homogeneous time ratio against the mix's
+    homogeneous twin (the same rows on one adapter of the token-weighted
+    mean rank), both cold (a 512 MB fill before each timed call)."""
+    import torch
+    import workloads
+    from heterogeneous_adapter_batching_amd.session import Batch, HipEvent, Rows, prepare_merge
+    from workloads.device import bits_to_device, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    t_setup = time.perf_counter()
+    W = workloads.gen_config(4)
+    d_in = max(p.d_in for p in W.projections)
+    d_out = max(p.d_out for p in W.projections)
+    ldv = -(-int(W.adapter_rank.max()) // 4) * 4
+    dw0 = to_device(W)
+    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out, inline=True).refresh(W.row_adapter)
+    copies = []
+    for c in range(2):
+        if c == 0:
+            pool, xs, ys = dw0.pool, [d.x for d in dw0.projections], [d.y for d in dw0.projections]
+            offs = [(d.A_off, d.B_off) for d in dw0.projections]
+        else:
+            pool = dw0.pool.clone()
+            xs = [d.x.clone() for d in dw0.projections]
+            ys = [d.y.clone() for d in dw0.projections]
+            offs = [(d.A_off.clone(), d.B_off.clone()) for d in dw0.projections]
+        projs = []
+        for p, x, y, (ao, bo) in zip(W.projections, xs, ys, offs):
+            A = Rows(pool, ao, p.A.n_adapters, p.A.max_rank, p.A.row_len, p.A.chunk_len)
+            B = Rows(pool, bo, p.B.n_adapters, p.B.max_rank, p.B.row_len, p.B.chunk_len)
+            projs.append((x, A, b.new_v(ldv), B, y, W.scale))
+        copies.append(dict(pool=pool, projs=projs, run=b.prepare_apply(projs), pieces=apply_pieces(b, projs)))
+    names = [n for n, _, _, _ in copies[0]["pieces"]]
+
+    # GPU results the CPU baseline checks (copy 0, one lora_apply from y0)
+    gpu_y = None
+    if not args.no_cpu_baseline:
+        copies[0]["run"]()
+        torch.cuda.synchronize()
+        gpu_y = [d.y.cpu().numpy() for d in dw0.projections]
+        for p, d in zip(W.projections, dw0.projections):
+            d.y.copy_(torch.from_numpy(p.y0))
+        torch.cuda.synchronize()
+
+    def step(k, ev=None, dom=None):
+        """One step on copy k mod 2: host preparation, then the pieces; with
+        `ev` an event before every piece and one after the last (all pieces),
+        or around piece `dom` only."""
+        C = copies[k % 2]
+        b.refresh(W.row_adapter, stream)
+        for i, (_, _, fn, _) in enumerate(C["pieces"]):
+            if ev is not None and (dom is None or i == dom):
+                ev[0 if dom is not None else i].record(stream)
+            fn()
+            if ev is not None and dom == i:
+                ev[1].record(stream)
+        if ev is not None and dom is None:
+            ev[len(C["pieces"])].record(stream)
+
+    new_events = lambda n: [HipEvent(timing=True) for _ in range(n)]
+    # warm-up steps, with an event between every piece: they name the dominant piece
+    wev = [new_events(len(names) + 1) for _ in range(max(1, args.warmup))]
+    for k in range(max(1, args.warmup)):
+        step(k, wev[k])
+    torch.cuda.synchronize()
+    wmed = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in wev])) for i in range(len(names))]
+    dom = int(np.argmax(wmed))
+
+    # timed steps: one event pair, around the dominant piece
+    evs = [new_events(2) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, evs[k], dom)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    dom_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+
+    # per-piece table: as many steps again, an event between every piece
+    pev = [new_events(len(names) + 1) for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(k, pev[k])
+    torch.cuda.synchronize()
+    piece_us = [[e[i].elapsed_time(e[i + 1]) * 1e3 for e in pev] for i in range(len(names))]
+    # the whole lora_apply as one call, between one event pair (same steps)
+    aev = [new_events(2) for _ in range(args.steps)]
+    for k in range(args.steps):
+        C = copies[k % 2]
+        b.refresh(W.row_adapter, stream)
+        aev[k][0].record(stream)
+        C["run"]()
+        aev[k][1].record(stream)
+    torch.cuda.synchronize()
+    apply_us = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in aev]))
+
+    cost = delta_cost(W, W.row_adapter)
+    step_bytes = cost["shrink_bytes"] + cost["expand_bytes"]
+    pieces = {}
+    for i, (name, idx, _, items) in enumerate(copies[0]["pieces"]):
+        parts = ("shrink",) if name == "shrink" else ("shrink", "expand") if name == "fused_kernel" else ("expand",)
+        nb, fl = piece_cost(W, items, parts)
+        us = float(np.median(piece_us[i]))
+        key = name if name not in pieces else "%s #%d" % (name, i)
+        pieces[key] = {"us_median": round(us, 2), "us_p10": round(float(np.percentile(piece_us[i], 10)), 2),
+                       "us_p90": round(float(np.percentile(piece_us[i], 90)), 2), "items": int(items.shape[0]),
+                       "alg_bytes": int(nb), "GB_s": round(nb / us / 1e3, 1),
+                       "hbm_frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "TFLOP_s": round(fl / us / 1e6, 2)}
+    dname, _, _, ditems = copies[0]["pieces"][dom]
+    dparts = ("shrink",) if dname == "shrink" else ("shrink", "expand") if dname == "fused_kernel" else ("expand",)
+    d_bytes, d_flops = piece_cost(W, ditems, dparts)
+    d_us = float(np.median(dom_us))
+    achieved = d_bytes / (d_us * 1e-6) / 1e9
+    kernel_label = dname.split(" ")[0]
+    traffic = recorded_traffic(MIX70B_TRAFFIC_FILE, kernel_label)
+
+    # homogeneous twin, cold: lora_apply between an event pair after a 512 MB fill
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    Wt = workloads.gen_twin(4)
+    dwt = to_device(Wt)
+    bt = Batch(Wt.n_rows, Wt.adapter_rank, d_in, d_out, inline=True).refresh(Wt.row_adapter)
+    ldvt = -(-int(Wt.adapter_rank.max()) // 4) * 4
+    run_t = bt.prepare_apply([(d.x, Rows(dwt.pool, d.A_off, p.A.n_adapters, p.A.max_rank, p.A.row_len, p.A.chunk_len),
+                               bt.new_v(ldvt), Rows(dwt.pool, d.B_off, p.B.n_adapters, p.B.max_rank, p.B.row_len,
+                                                    p.B.chunk_len), d.y, Wt.scale)
+                              for p, d in zip(Wt.projections, dwt.projections)])
+    cold = {"hetero": [], "homo": []}
+    for it in range(args.warmup + args.steps):
+        for name, fn in (("hetero", copies[0]["run"]), ("homo", run_t)):
+            flush.fill_(it & 0xFF)
+            e = new_events(2)
+            e[0].record(stream); fn(); e[1].record(stream)
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                cold[name].append(e[0].elapsed_time(e[1]) * 1e3)
+    ct = delta_cost(Wt, Wt.row_adapter)
+    twin = {"rank": int(Wt.adapter_rank[0]), "hetero_us": round(float(np.median(cold["hetero"])), 2),
+            "homo_us": round(float(np.median(cold["homo"])), 2),
+            "hetero_over_homo_time": round(float(np.median(cold["hetero"]) / np.median(cold["homo"])), 3),
+            "hetero_over_homo_bytes": round(step_bytes / (ct["shrink_bytes"] + ct["expand_bytes"]), 3)}
+    del dwt, bt, run_t
+
+    # the vision mode switch: merge adapter 0 (rank 64) into 32 layers x
+    # q/k/v/o W[4096x4096], then unmerge; each layer's matrices are copies of
+    # the seeded layer-0 draws (same values, own addresses: 4.3 GB streamed
+    # per phase, far past the Infinity Cache)
+    V = workloads.gen_config(3, n_layers=32)
+    dv = to_device(V)
+    spec = V.merge
+    rv = int(V.adapter_rank[spec.adapter])
+    Av = [Rows(dv.pool, d.A_off, p.A.n_adapters, p.A.max_rank, p.A.row_len, p.A.chunk_len)
+          for p, d in zip(V.projections, dv.projections)]
+    Bv = [Rows(dv.pool, d.B_off, p.B.n_adapters, p.B.max_rank, p.B.row_len, p.B.chunk_len)
+          for p, d in zip(V.projections, dv.projections)]
+    w_host = [spec.weight(0, pi) for pi in spec.projs]
+    w_dev0 = [bits_to_device(w) for w in w_host]
+    mats = [[w_dev0[i] if l == 0 else w_dev0[i].clone() for i in range(len(spec.projs))] for l in range(spec.n_layers)]
+    calls = [(prepare_merge([(mats[l][i], Av[pi], Bv[pi], spec.adapter, rv, V.scale)
+                             for i, pi in enumerate(spec.projs)]),
+              prepare_merge([(mats[l][i], Av[pi], Bv[pi], spec.adapter, rv, V.scale)
+                             for i, pi in enumerate(spec.projs)], unmerge=True)) for l in range(spec.n_layers)]
+    calls[0][0]()
+    torch.cuda.synchronize()
+    vision_merged = mats[0][0].cpu().numpy().view(np.uint16).copy()
+    calls[0][1]()
+    torch.cuda.synchronize()
+    sw = []
+    for rep in range(4):
+        e = new_events(3)
+        e[0].record(stream)
+        for m, _ in calls:
+            m()
+        e[1].record(stream)
+        for _, u in calls:
+            u()
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if rep > 0:
+            sw.append((e[0].elapsed_time(e[1]) * 1e3, e[1].elapsed_time(e[2]) * 1e3))
+    mb = merge_cost(4096, 4096, rv, len(spec.projs) * spec.n_layers)
+    mus, uus = float(np.median([t[0] for t in sw])), float(np.median([t[1] for t in sw]))
+    switch = {"layers": spec.n_layers, "matrices": len(spec.projs) * spec.n_layers, "rank": rv,
+              "merge_us_per_layer": round(mus / spec.n_layers, 2), "unmerge_us_per_layer": round(uus / spec.n_layers, 2),
+              "switch_ms": round((mus + uus) / 1e3, 3), "alg_bytes_per_phase": int(mb["bytes"]),
+              "merge_hbm_frac": round(mb["bytes"] / mus / 1e3 / HBM_PEAK_GBS, 4),
+              "unmerge_hbm_frac": round(mb["bytes"] / uus / 1e3 / HBM_PEAK_GBS, 4),
+              "merge_TFLOP_s": round(mb["flops"] / mus / 1e6, 2)}
+    del mats, calls, w_dev0
+
+    # launch floor: one near-empty kernel between the same kind of events
+    tiny = torch.zeros(1, dtype=torch.int32, device=dev)
+    floor = []
+    for k in range(40):
+        a_, z_ = HipEvent(timing=True), HipEvent(timing=True)
+        a_.record(stream); tiny.fill_(k); z_.record(stream)
+        z_.synchronize()
+        if k >= 10:
+            floor.append(a_.elapsed_time(z_) * 1e3)
+
+    ms = dt / args.steps * 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(step_bytes / (dt / args.steps) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "70B-shaped paged mix: 256 decode rows (128 released) + 8 prefill segments of 1024 "
+                               "rows; q/o 8192->8192 and up 8192->28672; 128 adapters of ranks 16/32/64 in a pool of "
+                               "8192-element pages under a random page table; step = host segment table + apply "
+                               "plan + upload, then lora_apply (shrink + expand, all projections); plus the vision "
+                               "mode switch (merge/unmerge of a rank-64 adapter into 32 x 4 W[4096x4096])",
+                   "rows": int(W.n_rows), "active_rows": int((W.row_adapter >= 0).sum()),
+                   "segments": int(b.segs.n_seg), "d": 8192, "d_up": 28672, "adapters": int(W.n_adapters),
+                   "projections": len(W.projections), "input_copies": 2},
+        "step_alg_bytes": int(step_bytes), "step_flops": int(cost["flops"]),
+        "TFLOP_s": round(cost["flops"] / (ms * 1e-3) / 1e12, 2),
+        "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "%s, %s" % (dname, "lora_apply's launch over %d items x %d "
+                                                           "projections" % (ditems.shape[0], len(W.projections))),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "us_per_launch": round(d_us, 3), "alg_bytes_per_launch": int(d_bytes)},
+        "pieces": pieces,
+        "lora_apply_one_call_us": round(apply_us, 2),
+        "twin": twin,
+        "switch": switch,
+        "merge_us_per_layer": switch["merge_us_per_layer"],
+        "launch_floor_us": round(float(np.median(floor)), 3),
+        "setup_s": round(time.perf_counter() - t_setup, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_mix(W, gpu_y, V, (w_host[0], vision_merged))
     print(json.dumps(out), flush=True)
 
 

@@ -10,6 +10,17 @@ from workloads.device import bits_to_device, to_device
 REL_F_TOL = 4e-3      # contract bound (relative Frobenius of the delta)
 ABS_TOL = 2e-2        # contract bound (max abs error of y)
 REL_F_EXPECT = 1e-4   # fp32 sums of exact bf16 products with a hi+lo split v land near 1e-6
+# Bit equality with the oracle's single rounding of the exact fp64 value.  The
+# kernel accumulates Delta W in fp32, and where the fp32 value straddles a
+# rounding boundary the bits differ (every element stays within the error
+# bound check_merge_bits also applies).  An unmerge cancels W' against
+# s*Delta W, so its result is small where the merge's was large and more
+# elements straddle: an fp32 accumulation of Delta W in rank order, emulated
+# in numpy on the vision switch's 4096 x 4096 rank-64 matrices, gives
+# 0.99995 equal for the merge and 0.99985 for the unmerge; the kernel
+# measures 0.99996 and 0.99987.
+MERGE_MIN_EQUAL = 0.9999
+UNMERGE_MIN_EQUAL = 0.9995
 
 
 def rows_of(pool, desc, off):
@@ -107,7 +118,7 @@ def ulp_compare(got_bits, ref_bits):
     return float(eq.mean()), int(np.max(np.abs(g - r))) if not eq.all() else 0
 
 
-def check_merge_bits(got_bits, W_bits, Aa, Ba, scale, min_equal=0.9999):
+def check_merge_bits(got_bits, W_bits, Aa, Ba, scale, min_equal=MERGE_MIN_EQUAL):
     """Merged W from the GPU against the oracle.
 
     The oracle rounds the exact W + s*B^T A once to bf16.  The kernel rounds
