@@ -119,7 +119,7 @@ _sig = {
     "lora_merge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
     "lora_unmerge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
     "lora_rows_dense_offsets": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _P(_i64)]),
-    "lora_mixture_row_adapter": (_i32, [_i32, _vp, _i32, _vp]),
+    "lora_mixture_row_adapter": (_i32, [_i32, _vp, _i32, _i32, _vp]),
     "lora_mixture_rows": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "lora_batch_prepare": (_i32, [_i32, _vp, _i32, _vp, _i32, _i32, ctypes.c_uint32, _i32, _vp, _vp, _vp, _vp,
                                   _i64, _vp, _vp, _P(lora_batch_t)]),
@@ -424,12 +424,14 @@ def lora_rows_dense_offsets(rank, max_rank, row_len, chunk_len):
     return off[:rk.shape[0] * int(max_rank) * chunks].copy(), pe.value
 
 
-def lora_mixture_row_adapter(row_adapter, merged, raw=False):
-    """deLoRA mixture batch (host): rows on the merged adapter -> -1.  With
-    raw=True returns (status, out) instead of raising."""
+def lora_mixture_row_adapter(row_adapter, merged, base_rows=True, raw=False):
+    """deLoRA mixture batch (host): rows on the merged adapter -> -1; released
+    rows -> the merged adapter's composite (minus the merged adapter: the
+    backbone output) when base_rows, else left released.  With raw=True
+    returns (status, out) instead of raising."""
     ra = np.ascontiguousarray(row_adapter, dtype=np.int32)
     out = np.empty(max(1, ra.shape[0]), np.int32)
-    st = _lib.lora_mixture_row_adapter(ra.shape[0], _ptr(ra), int(merged), out.ctypes.data)
+    st = _lib.lora_mixture_row_adapter(ra.shape[0], _ptr(ra), int(merged), int(bool(base_rows)), out.ctypes.data)
     if raw:
         return st, out[:ra.shape[0]]
     _check(st, "lora_mixture_row_adapter")

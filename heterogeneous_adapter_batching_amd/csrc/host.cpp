@@ -209,17 +209,24 @@ extern "C" int32_t lora_rows_dense_offsets(int32_t n_adapters, int32_t max_rank,
 
 // deLoRA mixture (VaLoRA blog, section 4.4.2): rows on the merged adapter
 // get no delta; every other row keeps its adapter, which the composite
-// tables below turn into "adapter a, minus the merged one".
+// tables below turn into "adapter a, minus the merged one".  A released row
+// (no adapter: served by the backbone, LoRazor article, mechanism section)
+// becomes composite adapter `merged`, which the tables make "minus the
+// merged adapter": the backbone output x W = x (W_merge - Delta W_m).
 extern "C" int32_t lora_mixture_row_adapter(int32_t n_rows, const int32_t* row_adapter, int32_t merged,
-                                            int32_t* out_row_adapter) {
+                                            int32_t base_rows, int32_t* out_row_adapter) {
     if (n_rows < 0 || merged < 0 || (n_rows > 0 && (row_adapter == nullptr || out_row_adapter == nullptr)))
         return LORA_EINVAL;
-    for (int32_t i = 0; i < n_rows; ++i) out_row_adapter[i] = row_adapter[i] == merged ? -1 : row_adapter[i];
+    for (int32_t i = 0; i < n_rows; ++i) {
+        const int32_t a = row_adapter[i];
+        out_row_adapter[i] = a == merged ? -1 : (a == -1 && base_rows) ? merged : a;
+    }
     return LORA_OK;
 }
 
 // Composite row table: adapter a's rows, then the merged adapter's rows;
-// the merged adapter's part is marked negative through neg_from.
+// the merged adapter's part is marked negative through neg_from.  The
+// merged adapter's own composite holds its rows, all negated.
 extern "C" int32_t lora_mixture_rows(int32_t n_adapters, int32_t max_rank, const int32_t* rank, int32_t merged,
                                      int32_t chunks, const int64_t* row_off, int32_t out_max_rank,
                                      int64_t* out_row_off, int32_t* out_rank, int32_t* out_neg_from) {
@@ -247,7 +254,7 @@ extern "C" int32_t lora_mixture_rows(int32_t n_adapters, int32_t max_rank, const
                     j < r ? row_off[((int64_t)src_a * max_rank + src_j) * chunks + c] : 0;
         }
         out_rank[a] = r;
-        out_neg_from[a] = a == merged ? rm : ra;
+        out_neg_from[a] = a == merged ? 0 : ra;
     }
     return LORA_OK;
 }

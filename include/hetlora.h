@@ -477,13 +477,19 @@ int32_t lora_rows_dense_offsets(int32_t n_adapters, int32_t max_rank,
  * Mode"): while adapter `merged` (m) is merged into the weights, a request
  * on adapter x != m is served with W_merge - Delta W_m + Delta W_x, i.e. on
  * the delta path y += s (x A_x^T) B_x - s (x A_m^T) B_m, and a request on m
- * needs no delta at all.  The two calls below express this as an ordinary
- * heterogeneous batch over "composite" adapters, so every call above
- * (lora_apply, lora_shrink + lora_expand) serves it in one pass:
+ * needs no delta at all.  A request with no adapter (a released one, which
+ * the LoRazor article's mechanism section serves on the backbone alone) is
+ * the same formula with Delta W_x = 0: y += -s (x A_m^T) B_m, giving x W.
+ * The two calls below express this as an ordinary heterogeneous batch over
+ * "composite" adapters, so every call above (lora_apply, lora_shrink +
+ * lora_expand) serves it in one pass:
  *
  * lora_mixture_row_adapter: host.  out_row_adapter[i] = -1 where
- *   row_adapter[i] == merged, else row_adapter[i] (rows on the merged
- *   adapter get no work; released rows stay released).
+ *   row_adapter[i] == merged (no work: W_merge serves the row); `merged`
+ *   where row_adapter[i] == -1 and base_rows != 0 (composite adapter m is
+ *   "minus the merged adapter": the row gets the backbone output); -1 where
+ *   row_adapter[i] == -1 and base_rows == 0 (a row whose output is not
+ *   wanted, e.g. padding, stays untouched); else row_adapter[i].
  *   row_adapter, out_row_adapter: host int32 [n_rows] (may be the same
  *   array).  Errors: LORA_EINVAL (null pointer, n_rows < 0, merged < 0).
  *
@@ -491,7 +497,7 @@ int32_t lora_rows_dense_offsets(int32_t n_adapters, int32_t max_rank,
  *   matrix kind (call it once for A and once for B) from the table of the
  *   real adapters: composite adapter a (a != m) has rank r_a + r_m, rows
  *   j < r_a are adapter a's rows and rows r_a + i are the merged adapter's
- *   row i; composite adapter m keeps m's own rows.
+ *   row i; composite adapter m has m's own r_m rows, all negated.
  *   rank        host int32 [n_adapters], ranks of the real adapters
  *   row_off     host int64 [n_adapters * max_rank * chunks], the real table
  *   out_row_off host int64 [n_adapters * out_max_rank * chunks]; slots past
@@ -499,14 +505,14 @@ int32_t lora_rows_dense_offsets(int32_t n_adapters, int32_t max_rank,
  *   out_rank    host int32 [n_adapters] (composite ranks; the adapter_rank
  *               argument of lora_build_segments for the mixture batch)
  *   out_neg_from host int32 [n_adapters]: r_a for a != m (the merged
- *               adapter's rows enter negated), r_m for m; upload it and pass
- *               it as the A side's neg_from
+ *               adapter's rows enter negated), 0 for m (every row negated);
+ *               upload it and pass it as the A side's neg_from
  *   Outputs are written only on LORA_OK.  Errors: LORA_EINVAL (null
  *   pointer, n_adapters < 1, chunks < 1, merged outside [0, n_adapters)),
  *   LORA_ERANK (a rank outside [1, max_rank], or r_a + r_m > out_max_rank
  *   or > LORA_MAX_RANK).                                                    */
 int32_t lora_mixture_row_adapter(int32_t n_rows, const int32_t* row_adapter,
-                                 int32_t merged, int32_t* out_row_adapter);
+                                 int32_t merged, int32_t base_rows, int32_t* out_row_adapter);
 int32_t lora_mixture_rows(int32_t n_adapters, int32_t max_rank,
                           const int32_t* rank, int32_t merged, int32_t chunks,
                           const int64_t* row_off, int32_t out_max_rank,

@@ -7,12 +7,20 @@ W_merge - Delta W_deLoRA_m + Delta W_x, where Delta W_deLoRA_m equals
 Delta W_m: the merged adapter is subtracted and the wanted one added, with no
 change to the weights in memory.
 
+A request with no adapter runs on the backbone alone: the LoRazor article's
+mechanism section releases a request's adapter early and serves the request
+on the backbone from then on.  With W_merge resident, the backbone weights
+are W_merge - Delta W_m: the formula above with Delta W_x = 0.
+
 On the delta path the merged GEMM y0 = x * W_merge^T is shared by all rows, so
 row i with adapter a = row_adapter[i] gets
 
     y[i] = y0[i] + s * (x_i A_a^T) B_a - s * (x_i A_m^T) B_m     (a >= 0, a != m)
     y[i] = y0[i]                                                  (a == m: served by W_merge)
-    y[i] = y0[i]                                                  (a == -1: released row, no work)
+    y[i] = y0[i] - s * (x_i A_m^T) B_m                            (a == -1: released, backbone)
+
+``base_rows=False`` leaves released rows at y0 instead (rows whose output is
+not wanted, such as padding).
 
 fp64 arithmetic on the exact values of the bf16 inputs, as in ``lora``.
 """
@@ -22,7 +30,7 @@ from .bf16 import bf16_to_f64
 from .lora import gather_rows_ref
 
 
-def mixture_ref(row_adapter, adapter_rank, merged, x_bits, y0, pool, A, B, scale, rows=None):
+def mixture_ref(row_adapter, adapter_rank, merged, x_bits, y0, pool, A, B, scale, rows=None, base_rows=True):
     """Returns {i: fp64 y row} for each i in ``rows`` (default: all rows)."""
     rows = range(len(row_adapter)) if rows is None else rows
 
@@ -42,5 +50,8 @@ def mixture_ref(row_adapter, adapter_rank, merged, x_bits, y0, pool, A, B, scale
             add = (Aa @ xi) @ Ba          # s-free delta of the wanted adapter
             sub = (Am @ xi) @ Bm          # and of the merged one
             y += scale * add - scale * sub
+        elif a == -1 and base_rows:
+            xi = bf16_to_f64(x_bits[i])
+            y -= scale * ((Am @ xi) @ Bm)  # back to the backbone: minus the merged adapter
         out[i] = y
     return out

@@ -132,7 +132,7 @@ static void offsets_and_mixture() {
         CHECK(lora_mixture_rows(n_ad, mr, rk.data(), merged, chunks, off.p, out_mr, o2.p, r2.p, n2.p) == LORA_OK);
         std::vector<int32_t> ra(uni(0, 50)), ra2(ra.size());
         for (auto& v : ra) v = uni(-1, n_ad - 1);
-        CHECK(lora_mixture_row_adapter((int32_t)ra.size(), ra.data(), merged, ra2.data()) == LORA_OK);
+        CHECK(lora_mixture_row_adapter((int32_t)ra.size(), ra.data(), merged, (int32_t)(iter & 1), ra2.data()) == LORA_OK);
     }
     int64_t pe;
     const int32_t rk[1] = {4};

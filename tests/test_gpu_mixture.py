@@ -1,7 +1,8 @@
 """GPU parity of deLoRA mixture inference (VaLoRA blog, section 4.4.2): with
 adapter m merged, rows on other adapters get y += s x A_x^T B_x - s x A_m^T B_m
 through composite adapters (lora_mixture_rows, neg_from on the A side), rows
-on m and released rows are untouched.  Compared with the oracle's
+on m are untouched, and released rows get the backbone output y += -s x A_m^T
+B_m (or stay untouched with base_rows=False).  Compared with the oracle's
 mixture_ref; tolerances as in test_gpu_parity (contract bounds plus the
 precision check), untouched rows bit-exact."""
 import sys
@@ -25,9 +26,9 @@ def _say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _run_mixture(W, m, path):
+def _run_mixture(W, m, path, base_rows=True):
     dw = to_device(W)
-    ra = hl.lora_mixture_row_adapter(W.row_adapter, m)
+    ra = hl.lora_mixture_row_adapter(W.row_adapter, m, base_rows=base_rows)
     out_max = int(max(W.adapter_rank[a] + (W.adapter_rank[m] if a != m else 0) for a in range(len(W.adapter_rank))))
     out_max = -(-out_max // 4) * 4
     projs, crank = [], None
@@ -51,13 +52,14 @@ def _run_mixture(W, m, path):
     return b, [d.y.cpu().numpy() for d, _, _, _ in projs]
 
 
-def _check(W, m, ys):
+def _check(W, m, ys, base_rows=True):
     for p, y in zip(W.projections, ys):
-        ref = oracle.mixture_ref(W.row_adapter, W.adapter_rank, m, p.x, p.y0, W.pool, p.A, p.B, W.scale)
+        ref = oracle.mixture_ref(W.row_adapter, W.adapter_rank, m, p.x, p.y0, W.pool, p.A, p.B, W.scale,
+                                 base_rows=base_rows)
         num = den = amax = 0.0
         for i in range(W.n_rows):
             a = int(W.row_adapter[i])
-            if a < 0 or a == m:
+            if (a < 0 and not base_rows) or a == m:
                 assert np.array_equal(y[i], p.y0[i]), f"row {i} (adapter {a}) must be untouched"
                 continue
             d_ref = ref[i] - p.y0[i].astype(np.float64)
@@ -71,14 +73,15 @@ def _check(W, m, ys):
         _say(p.name, "relF", relF, "max abs", amax)
 
 
-@pytest.mark.parametrize("path", ["apply", "split"])
-def test_mixture_decode_rows(path):
-    """One-token rows on 48 adapters, adapter 5 merged (lora_apply: the fused kernel)."""
-    ra = np.array(list(range(48)) + [5, 5, -1, 7], np.int32)
+@pytest.mark.parametrize("path,base_rows", [("apply", True), ("split", True), ("apply", False)])
+def test_mixture_decode_rows(path, base_rows):
+    """One-token rows on 48 adapters, adapter 5 merged (lora_apply: the fused
+    kernel), two released rows (backbone output, or untouched)."""
+    ra = np.array(list(range(48)) + [5, 5, -1, 7, -1], np.int32)
     W = workloads.gen_custom(31, ra, np.full(48, 16), 4096, 4096, n_proj=2)
-    _say("mixture decode", path)
-    _, ys = _run_mixture(W, 5, path)
-    _check(W, 5, ys)
+    _say("mixture decode", path, "base rows", base_rows)
+    _, ys = _run_mixture(W, 5, path, base_rows)
+    _check(W, 5, ys, base_rows)
 
 
 @pytest.mark.parametrize("layout", ["dense", "paged"])

@@ -412,7 +412,9 @@ def test_one_hip_runtime_in_process():
 
 def test_mixture_row_adapter():
     ra = np.array([0, 2, -1, 2, 1, 0, 2], np.int32)
-    out = hl.lora_mixture_row_adapter(ra, 2)
+    out = hl.lora_mixture_row_adapter(ra, 2)               # released row -> minus the merged adapter
+    assert out.tolist() == [0, -1, 2, -1, 1, 0, -1]
+    out = hl.lora_mixture_row_adapter(ra, 2, base_rows=False)   # released row stays untouched
     assert out.tolist() == [0, -1, -1, -1, 1, 0, -1]
     st, _ = hl.lora_mixture_row_adapter(ra, -1, raw=True)
     assert st == hl.LORA_EINVAL
@@ -421,7 +423,7 @@ def test_mixture_row_adapter():
 @pytest.mark.parametrize("chunks", [1, 3])
 def test_mixture_rows_composite_table(chunks):
     """Composite adapter a != m: rows j < r_a are a's, rows r_a + i are m's row i;
-    m keeps its own rows; neg_from = r_a (m: r_m)."""
+    m keeps its own rows, all negated; neg_from = r_a (m: 0)."""
     rng = np.random.default_rng(chunks)
     rank = np.array([3, 8, 5, 1], np.int32)
     max_rank, m, out_max = 8, 2, 16
@@ -430,7 +432,7 @@ def test_mixture_rows_composite_table(chunks):
     R = lambda t, a, j, c, mr: t[(a * mr + j) * chunks + c]
     for a in range(len(rank)):
         r = rank[m] if a == m else rank[a] + rank[m]
-        assert crank[a] == r and neg[a] == (rank[m] if a == m else rank[a])
+        assert crank[a] == r and neg[a] == (0 if a == m else rank[a])
         for j in range(out_max):
             for c in range(chunks):
                 if j >= r:
@@ -452,7 +454,7 @@ def test_mixture_rows_errors():
     st, *_ = hl.lora_mixture_rows(rank, 2, 1, row_off, 80, 64, raw=True)
     assert st == hl.LORA_ERANK                       # 70 + 8 > out_max_rank
     st, off, crank, neg = hl.lora_mixture_rows(rank, 2, 1, row_off, 80, 128, raw=True)
-    assert st == hl.LORA_OK and crank.tolist() == [72, 78, 8] and neg.tolist() == [64, 70, 8]
+    assert st == hl.LORA_OK and crank.tolist() == [72, 78, 8] and neg.tolist() == [64, 70, 0]
 
 
 def test_batch_prepare_inline_copies_nothing():

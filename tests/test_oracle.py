@@ -302,14 +302,19 @@ def test_mixture_rank1_closed_form_bit_exact():
                            p["A"], p["B"], 2.0)
     assert y[0].tolist() == [4.0, -1.0, -26.0, 34.0]     # 2*(5*b1 - 3*b0)
     assert y[1].tolist() == [0.0] * 4                     # on the merged adapter: W_merge serves it
-    assert y[2].tolist() == [0.0] * 4                     # released
+    assert y[2].tolist() == [-6.0] * 4                    # released: backbone, -2*3*b0
+    y = oracle.mixture_ref(p["row_adapter"], p["adapter_rank"], 0, p["x_bits"], p["y0"], p["pool"],
+                           p["A"], p["B"], 2.0, base_rows=False)
+    assert y[2].tolist() == [0.0] * 4                     # released, output not wanted: untouched
 
 
 @pytest.mark.parametrize("layout", ["dense", "paged"])
 def test_mixture_equals_unmerged_inference(layout):
     """VaLoRA's identity: x (W_merge - dW_m + dW_x)^T with W_merge = W + dW_m equals the
     unmerged output x W^T + s x A_x^T B_x, for rows on any adapter; rows on m get
-    x W_merge^T; released rows keep y0.  Exact real arithmetic, so fp64 agrees to rounding."""
+    x W_merge^T; released rows get the backbone output x W^T (the identity with
+    dW_x = 0), or keep y0 with base_rows=False.  Exact real arithmetic, so fp64
+    agrees to rounding."""
     rng = np.random.default_rng(11)
     d_in, d_out, s, m = 96, 64, 2.0, 1
     ranks = [4, 8, 3]
@@ -323,9 +328,12 @@ def test_mixture_equals_unmerged_inference(layout):
     Wm = Wb + s * Be[m].T @ Ae[m]                          # merged weights (unrounded)
     y0 = xe @ Wm.T                                         # shared merged GEMM
     y = oracle.mixture_ref(ra, p["adapter_rank"], m, p["x_bits"], y0, p["pool"], p["A"], p["B"], s)
+    y_pad = oracle.mixture_ref(ra, p["adapter_rank"], m, p["x_bits"], y0, p["pool"], p["A"], p["B"], s,
+                               base_rows=False)
     for i, a in enumerate(ra):
         if a < 0:
-            want = y0[i]
+            want = xe[i] @ Wb.T                                  # backbone alone
+            np.testing.assert_array_equal(y_pad[i], y0[i])
         elif a == m:
             want = xe[i] @ Wm.T
         else:
