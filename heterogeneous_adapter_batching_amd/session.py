@@ -127,7 +127,7 @@ class Batch:
         self._copied = HipEvent()   # the last staging copy
         self._pending = False
         self._stream, self._stream_h = None, None
-        self._n_active, self._v_slices = 0, 1
+        self._n_active, self._v_slices, self._op_slices = 0, 1, [0, 0, 0]
         self._op_mask = ((1 << LORA_OP_APPLY) | LORA_PREPARE_INLINE) if inline else 7
         self._alloc(n + WORK_INTS * 10 * n)  # grown on demand
 
@@ -175,8 +175,11 @@ class Batch:
             self._copied.record(stream)
             self._pending = True
         self._n_active = self._b.n_active
-        planned = self._launch[LORA_OP_SHRINK] if self._op_mask & 1 else self._launch[LORA_OP_APPLY]
-        self._v_slices = max(1, planned.info.v_slices)
+        # v buffers from new_v serve every planned op (the library trusts the
+        # size of v, so each call checks its own plan's slices below)
+        self._op_slices = [self._launch[op].info.v_slices if self._launch[op].info.op == op else 0
+                           for op in (LORA_OP_SHRINK, LORA_OP_EXPAND, LORA_OP_APPLY)]
+        self._v_slices = max(1, *self._op_slices)
         return self
 
     @property
@@ -249,11 +252,14 @@ class Batch:
             assert v.dtype == torch.float32 and v.is_contiguous() and v.dim() == 3
         return [(int(v.shape[0]), int(v.shape[1])) for v in vs]
 
-    def _check_v(self, shapes):
+    def _check_v(self, shapes, op):
+        """The library trusts v's size: check it against the plan of `op`
+        before every call (v_slices of that plan, n_active rows)."""
         rows = max(1, self._n_active)
+        need = self._op_slices[op]
         for s0, s1 in shapes:
-            if s0 < self._v_slices or s1 != rows:
-                raise AssertionError("v buffer does not match the batch (v_slices, n_active)")
+            if s0 < need or s1 != rows:
+                raise AssertionError("v buffer does not match the batch's plan (v_slices, n_active)")
 
     def prepare_shrink(self, projs, stream=None):
         """projs: list of (x tensor bf16 [*, ldx], Rows A, v tensor fp32 [v_slices, n_active, ldv]).
@@ -267,7 +273,7 @@ class Batch:
         shapes, n, L = self._v_shapes(vs), len(vs), self._launch[LORA_OP_SHRINK]
 
         def run():
-            self._check_v(shapes)
+            self._check_v(shapes, LORA_OP_SHRINK)
             call_shrink(L, arr, n, h)
         run.keep = (projs, arr)
         return run
@@ -283,7 +289,7 @@ class Batch:
         shapes, n, L = self._v_shapes(vs), len(vs), self._launch[LORA_OP_EXPAND]
 
         def run():
-            self._check_v(shapes)
+            self._check_v(shapes, LORA_OP_EXPAND)
             call_expand(L, arr, n, h)
         run.keep = (projs, arr)
         return run
@@ -302,7 +308,7 @@ class Batch:
         shapes, n, L = self._v_shapes(vs), len(vs), self._launch[LORA_OP_APPLY]
 
         def run():
-            self._check_v(shapes)
+            self._check_v(shapes, LORA_OP_APPLY)
             call_apply(L, arr, n, h)
         run.keep = (projs, arr)
         return run
