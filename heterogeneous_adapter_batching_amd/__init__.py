@@ -16,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhetlora.so")
 
 LORA_ABI_VERSION = 10
+LORA_STATIC_SCRATCH_BYTES = 64 << 20
 LORA_MAX_RANK = 128
 LORA_MAX_PROJ = 8
 LORA_MAX_RANGES = 48
@@ -116,6 +117,7 @@ _sig = {
     "lora_shrink": (_i32, [_P(lora_launch_t), _i32, _P(lora_shrink_proj_t), _vp]),
     "lora_expand": (_i32, [_P(lora_launch_t), _i32, _P(lora_expand_proj_t), _vp]),
     "lora_apply": (_i32, [_P(lora_launch_t), _i32, _P(lora_apply_proj_t), _vp]),
+    "lora_apply_static": (_i32, [_P(lora_launch_t), _i32, _P(lora_apply_proj_t), _vp]),
     "lora_merge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
     "lora_unmerge": (_i32, [_i32, _P(lora_merge_mat_t), _vp]),
     "lora_rows_dense_offsets": (_i32, [_i32, _i32, _vp, _i32, _i32, _vp, _P(_i64)]),

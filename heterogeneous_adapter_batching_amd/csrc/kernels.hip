@@ -1704,8 +1704,8 @@ extern "C" int32_t lora_expand(const lora_launch_t* L, int32_t n_proj, const lor
     return err == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
-extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora_apply_proj_t* projs,
-                              void* hip_stream) {
+namespace {
+int32_t apply_impl(const lora_launch_t* L, int32_t n_proj, const lora_apply_proj_t* projs, void* hip_stream) {
     int32_t st = check_launch(L, LORA_OP_APPLY, n_proj);
     if (st != LORA_OK) return st;
     if (!projs) return LORA_EINVAL;
@@ -1780,6 +1780,62 @@ extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora
         }
     }
     return err == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+}  // namespace
+
+extern "C" int32_t lora_apply(const lora_launch_t* L, int32_t n_proj, const lora_apply_proj_t* projs,
+                              void* hip_stream) {
+    return apply_impl(L, n_proj, projs, hip_stream);
+}
+
+// ------------------------------------------------------------------ lora_apply without a workspace
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid allocation): lora_apply with v taken
+// from this file-scope array instead of the caller's buffers.  Each device
+// the library runs on holds its own copy until the process ends.  In host
+// code the array's name is not a device address: its address on the current
+// device comes from hipGetSymbolAddress (once per device, kept below) and
+// is the only form of it the host ever passes on.
+static __device__ __align__(256) float scratch[LORA_STATIC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+// Address of `scratch` on the current device (nullptr if the lookup fails).
+float* scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    static std::mutex mu;
+    static void* addr[64] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev] = p;
+    }
+    return static_cast<float*>(addr[dev]);
+}
+}  // namespace
+
+extern "C" int32_t lora_apply_static(const lora_launch_t* L, int32_t n_proj, const lora_apply_proj_t* projs,
+                                     void* hip_stream) {
+    if (!L || !projs || n_proj < 1 || n_proj > LORA_MAX_PROJ) return LORA_EINVAL;
+    // each projection's v: [v_slices][n_active][ldv] floats, ldv the plan's
+    // largest rank rounded up to 4, back to back in the array
+    const int64_t ldv = L->info.max_rank < 1 ? 4 : ((int64_t)L->info.max_rank + 3) / 4 * 4;
+    const int64_t rows = L->info.n_active < 1 ? 1 : L->info.n_active;
+    const int64_t per = (int64_t)(L->info.v_slices < 1 ? 1 : L->info.v_slices) * rows * ldv;
+    const int64_t region = (per + 63) / 64 * 64;  // 256-byte aligned regions
+    if (L->info.n_active < 0 || L->info.v_slices > LORA_MAX_SLICES || L->info.max_rank > LORA_MAX_RANK ||
+        region * n_proj > (int64_t)(LORA_STATIC_SCRATCH_BYTES / sizeof(float)))
+        return LORA_ECAPACITY;
+    float* base = scratch_on_current_device();
+    if (!base) return LORA_EHIP;
+    lora_apply_proj_t p[LORA_MAX_PROJ];
+    for (int i = 0; i < n_proj; ++i) {
+        p[i] = projs[i];
+        p[i].v = base + region * i;
+        p[i].ldv = ldv;
+    }
+    return apply_impl(L, n_proj, p, hip_stream);
 }
 
 // ------------------------------------------------------------------ device plan builder

@@ -451,6 +451,23 @@ int32_t lora_expand(const lora_launch_t* launch, int32_t n_proj,
 int32_t lora_apply(const lora_launch_t* launch, int32_t n_proj,
                    const lora_apply_proj_t* projs, void* hip_stream);
 
+/* lora_apply without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid allocation.  The same as lora_apply, except that projs[i].v
+ * and projs[i].ldv are ignored: v lives in an array the library holds on
+ * each device it runs on (LORA_STATIC_SCRATCH_BYTES, kept until the process
+ * ends), projection i in its own region of info.v_slices * max(1, n_active)
+ * * ldv floats, ldv = info.max_rank rounded up to 4.  Nothing is allocated
+ * and nothing needs to start at zero.  Every call on a device shares that
+ * device's array, so calls that overlap in time on one device (other
+ * streams, other threads) race and must not be made; the array keeps the
+ * last call's contents.  Errors: as lora_apply; LORA_ECAPACITY when n_proj
+ * regions do not fit the array (nothing is launched); LORA_EHIP when the
+ * array's address on the current device cannot be found. */
+#define LORA_STATIC_SCRATCH_BYTES (64u << 20)
+int32_t lora_apply_static(const lora_launch_t* launch, int32_t n_proj,
+                          const lora_apply_proj_t* projs, void* hip_stream);
+
 /* Merge n_mats (1..LORA_MAX_MERGE) adapters into their weights in place, one
  * launch: W <- RNE_bf16(W + scale * B_a^T A_a), with Delta W accumulated in
  * fp32 and a single rounding to bf16.  Matrices must not overlap.

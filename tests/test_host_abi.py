@@ -306,6 +306,23 @@ def test_pool_rejects_pages_past_the_scatter_piece():
     hl.LoraPool(4, 65536, 2, 16, [512])
 
 
+def test_static_apply_refuses_plans_past_its_array():
+    """lora_apply_static checks that every projection's v region fits the
+    library's array before it touches the device (so this runs without a
+    GPU): 8 projections x 16 slices x 65,536 rows x 128 ranks do not fit."""
+    lib = hl._lib
+    L = _launch(hl.LORA_OP_APPLY)
+    L.info.n_active, L.info.v_slices, L.info.max_rank = 65536, 16, 128
+    arr = (hl.lora_apply_proj_t * 8)(*[hl.lora_apply_proj_t(0x30000, 512, 512, _rows(), None, 0, _rows(), 512,
+                                                            0x50000, 512, 2.0) for _ in range(8)])
+    assert lib.lora_apply_static(ctypes.byref(L), 8, arr, None) == hl.LORA_ECAPACITY
+    # one projection of 16 x 8192 x 128 floats (64 MiB) still fits; two do not
+    L.info.n_active, L.info.v_slices, L.info.max_rank = 8192, 16, 128
+    assert lib.lora_apply_static(ctypes.byref(L), 2, arr, None) == hl.LORA_ECAPACITY
+    assert lib.lora_apply_static(None, 1, arr, None) == hl.LORA_EINVAL
+    assert lib.lora_apply_static(ctypes.byref(L), 0, arr, None) == hl.LORA_EINVAL
+
+
 def test_empty_batch_launches_nothing():
     # n_work == 0 returns OK before any HIP call (works without a GPU)
     lib = hl._lib
