@@ -41,6 +41,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --workload prefill|vision|mix70b --twin        (shrink/expand tables and the twin ratio)
        python bench.py --workload prefill|vision|mix70b --metadata device  (apply: host- vs device-built plan)
        python bench.py --copy-calibration                             (counter calibration under rocprofv3)
+       python bench.py --traffic-record PMC_DIR --traffic-grid N      (write the dominant launch's traffic record)
        python bench.py --rmw-ceiling                                  (in-place streaming rate of this HBM)
 """
 import argparse
@@ -282,7 +283,13 @@ def main():
                     help="run one 1 GiB device copy (counter calibration under rocprofv3 --pmc) and exit")
     ap.add_argument("--rmw-ceiling", action="store_true",
                     help="time a plain in-place read-modify-write stream of the merge's size (cold) and exit")
+    ap.add_argument("--traffic-record", default=None, metavar="PMC_DIR",
+                    help="(no GPU) write the dominant launch's traffic record from the --pmc runs under PMC_DIR")
+    ap.add_argument("--traffic-kernel", default="expand_kernel<1>")
+    ap.add_argument("--traffic-grid", type=int, default=0, help="workgroups of the recorded launch")
     args = ap.parse_args()
+    if args.traffic_record:
+        return traffic_record(args)
     if args.copy_calibration:
         return copy_calibration()
     if args.rmw_ceiling:
@@ -552,19 +559,89 @@ def kernel_section_digest(name):
     return hashlib.sha256(src[a:b].encode()).hexdigest()
 
 
+PLAN_SOURCES = [os.path.join(ROOT, "heterogeneous_adapter_batching_amd", "csrc", f)
+                for f in ("tile_table.inc", "plan_rules.h", "variants.h")]
+
+
+def plan_digest():
+    """sha256 of the sources that decide which items a launch holds (the tile
+    table and the plan rules): a launch's counters describe that launch only
+    while they are unchanged."""
+    h = hashlib.sha256()
+    for f in PLAN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def recorded_traffic(path, kernel):
     """HBM bytes per launch of `kernel` from committed rocprofv3 counters
     (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, one pass each, each
     scaled by a plain copy's bytes over the same counter's reading); None when
-    there is no record for this kernel or its source section has changed."""
+    there is no record for this kernel, or its source section, the tile table
+    or the plan rules have changed since."""
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
     if rec.get("kernel") != kernel or rec.get("source_sha256") != kernel_section_digest(rec.get("section", "")):
         return None
+    if rec.get("plan_sha256") != plan_digest():
+        return None
     c = rec["copy"]
     return round(rec["fetch_kib"] * c["bytes"] / c["fetch_kib"] + rec["write_kib"] * c["bytes"] / c["write_kib"])
+
+
+def _pmc_groups(path):
+    """rocprofv3 --pmc counter CSV -> {(kernel, grid workgroups): [value per dispatch]}."""
+    import csv
+    import re
+    g = {}
+    for r in csv.DictReader(open(path)):
+        name = re.sub(r"\(anonymous namespace\)::", "", r["Kernel_Name"])
+        name = re.sub(r"\([A-Za-z]*Args\)$", "", re.sub(r"^void ", "", name))
+        wg = int(r.get("Workgroup_Size", r.get("Workgroup_Size_X", 256)) or 256)
+        grid = int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0) // max(wg, 1)
+        g.setdefault((name, grid), []).append(float(r["Counter_Value"]))
+    return g
+
+
+def traffic_record(args):
+    """Write the committed traffic record of the 70B-mix step's dominant launch
+    from four rocprofv3 --pmc runs under args.traffic_record: bench_FETCH_SIZE,
+    bench_WRITE_SIZE (this script's default line) and copy_FETCH_SIZE,
+    copy_WRITE_SIZE (--copy-calibration), each holding run_counter_collection.csv.
+    The launch is the one of kernel args.traffic_kernel over args.traffic_grid
+    workgroups (the grid the kernel trace shows for it)."""
+    d = args.traffic_record
+
+    def mean(op, counter, key):
+        g = _pmc_groups(os.path.join(d, "%s_%s" % (op, counter), "run_counter_collection.csv"))
+        v = g[key] if key is not None else max(g.values(), key=np.mean)   # the copy: the largest dispatches
+        return float(np.mean(v)), len(v)
+    key = (args.traffic_kernel, args.traffic_grid)
+    f, n = mean("bench", "FETCH_SIZE", key)
+    w, _ = mean("bench", "WRITE_SIZE", key)
+    cf, _ = mean("copy", "FETCH_SIZE", None)
+    cw, _ = mean("copy", "WRITE_SIZE", None)
+    section = args.traffic_kernel.split("_kernel")[0]
+    rec = {"what": "rocprofv3 --pmc counters (KiB per dispatch, mean over dispatches), one counter per run: the "
+                   "dominant launch of the 70B-mix benchmark step (%s over %d workgroups) and one plain 1 GiB "
+                   "device copy for calibration" % key,
+           "kernel": args.traffic_kernel, "section": section,
+           "source_sha256": kernel_section_digest(section), "plan_sha256": plan_digest(),
+           "grid_workgroups": args.traffic_grid, "fetch_kib": round(f, 1), "write_kib": round(w, 1),
+           "dispatches": n,
+           "copy": {"bytes": 1 << 30, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+                    "kernel": "the largest dispatch group of the calibration run (the 1 GiB copy)"},
+           "commands": ["rocprofv3 --pmc %s --output-format csv -d %s/bench_%s -o run -- python3 bench.py "
+                        "--no-cpu-baseline --steps 4 --warmup 2" % (c, d, c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                       + ["rocprofv3 --pmc %s --output-format csv -d %s/copy_%s -o run -- python3 bench.py "
+                          "--copy-calibration" % (c, d, c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                       + ["python bench.py --traffic-record %s --traffic-kernel '%s' --traffic-grid %d"
+                          % (d, args.traffic_kernel, args.traffic_grid)]}
+    with open(MIX70B_TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def piece_name(variant):

@@ -114,6 +114,7 @@ _sig = {
     "lora_status_string": (ctypes.c_char_p, [_i32]),
     "lora_build_segments": (_i32, [_i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _P(_i32), _P(_i32)]),
     "lora_plan": (_i32, [_i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _P(lora_plan_info_t)]),
+    "lora_plan_table": (_i32, [_i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _P(lora_plan_info_t)]),
     "lora_shrink": (_i32, [_P(lora_launch_t), _i32, _P(lora_shrink_proj_t), _vp]),
     "lora_expand": (_i32, [_P(lora_launch_t), _i32, _P(lora_expand_proj_t), _vp]),
     "lora_apply": (_i32, [_P(lora_launch_t), _i32, _P(lora_apply_proj_t), _vp]),
@@ -360,6 +361,25 @@ def lora_plan(op, segs, d_in, d_out, work_capacity=None, work_out=None, info_out
     _check(st, "lora_plan")
     if work_out is not None:
         return work[:info.n_work], info
+    return work[:info.n_work].copy(), info
+
+
+def lora_plan_table(op, segs, d_in, d_out, shrink_table, expand_table, raw=False):
+    """Launch plan with the caller's tile table (the offline tile search's
+    planner): shrink_table int8 [8][4][4][2] of (shape, slices), expand_table
+    int8 [8][4][4].  Returns (work, info), or (status, work, info) with raw=True."""
+    st_tab = np.ascontiguousarray(shrink_table, dtype=np.int8)
+    ex_tab = np.ascontiguousarray(expand_table, dtype=np.int8)
+    assert st_tab.shape == (8, 4, 4, 2) and ex_tab.shape == (8, 4, 4)
+    cap = (LORA_MAX_SLICES + 1) * max(1, segs.n_active)
+    work = np.zeros((cap, WORK_INTS), np.int32)
+    info = lora_plan_info_t()
+    st = _lib.lora_plan_table(int(op), segs.n_seg, segs.seg_start.ctypes.data, _ptr(segs.seg_adapter),
+                              _ptr(segs.seg_rank), int(d_in), int(d_out), st_tab.ctypes.data, ex_tab.ctypes.data,
+                              cap, work.ctypes.data, ctypes.byref(info))
+    if raw:
+        return st, work[:max(0, info.n_work)].copy(), info
+    _check(st, "lora_plan_table")
     return work[:info.n_work].copy(), info
 
 

@@ -87,10 +87,12 @@ extern "C" int32_t lora_build_segments(int32_t n_rows, const int32_t* row_adapte
 // either one fused item or the segment's shrink and expand items.  Items are
 // grouped by variant (in ascending variant id, segments in order inside a
 // variant) so that each variant is one launch over a contiguous range.
-extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
-                             const int32_t* seg_adapter, const int32_t* seg_rank,
-                             int32_t d_in, int32_t d_out, int32_t work_capacity,
-                             lora_work_t* work, lora_plan_info_t* info) {
+namespace {
+// Every segment's shape and K slices from the tile table st / et (the
+// compiled-in one, or a caller's for the offline search).
+int32_t plan_impl(int32_t op, int32_t n_seg, const int32_t* seg_start, const int32_t* seg_adapter,
+                  const int32_t* seg_rank, int32_t d_in, int32_t d_out, int32_t work_capacity, lora_work_t* work,
+                  lora_plan_info_t* info, ShrinkTab st, ExpandTab et) {
     if ((op != LORA_OP_SHRINK && op != LORA_OP_EXPAND && op != LORA_OP_APPLY) || n_seg < 0 ||
         work_capacity < 0 || info == nullptr || seg_start == nullptr)
         return LORA_EINVAL;
@@ -115,11 +117,11 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
         const int32_t len = seg_start[s + 1] - seg_start[s], r = seg_rank[s];
         SegPlan a{-1, 0, 1, 1, false}, b{-1, 0, 1, 1, false};
         if (op == LORA_OP_SHRINK)
-            a = lv_shrink_part(len, r, d_in, d_out);
+            a = lv_shrink_part(len, r, d_in, d_out, st, et);
         else if (op == LORA_OP_EXPAND)
-            a = lv_expand_part(len, r, d_in, d_out);
+            a = lv_expand_part(len, r, d_in, d_out, st, et);
         else
-            lv_apply_parts(len, r, d_in, d_out, a, b);
+            lv_apply_parts(len, r, d_in, d_out, a, b, st, et);
         for (SegPlan* q : {&a, &b}) {
             if (q->variant < 0) continue;
             const int32_t items = q->chunks * (q->shrink ? q->slices : 1);
@@ -180,6 +182,33 @@ extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start
     }
     *info = out;
     return LORA_OK;
+}
+}  // namespace
+
+extern "C" int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
+                             const int32_t* seg_adapter, const int32_t* seg_rank,
+                             int32_t d_in, int32_t d_out, int32_t work_capacity,
+                             lora_work_t* work, lora_plan_info_t* info) {
+    return plan_impl(op, n_seg, seg_start, seg_adapter, seg_rank, d_in, d_out, work_capacity, work, info,
+                     kShrinkCfg, kExpandShape);
+}
+
+// The offline tile search's planner: lora_plan with the caller's table, so
+// every candidate table can be timed with the library as built.
+extern "C" int32_t lora_plan_table(int32_t op, int32_t n_seg, const int32_t* seg_start,
+                                   const int32_t* seg_adapter, const int32_t* seg_rank, int32_t d_in,
+                                   int32_t d_out, const int8_t* shrink_table, const int8_t* expand_table,
+                                   int32_t work_capacity, lora_work_t* work, lora_plan_info_t* info) {
+    static_assert(sizeof(ShrinkCfg) == 2, "a shrink entry is (shape, slices)");
+    if (shrink_table == nullptr || expand_table == nullptr) return LORA_EINVAL;
+    const int n = LV_LEN_BUCKETS * LV_RANK_BUCKETS * LV_D_BUCKETS;
+    for (int i = 0; i < n; ++i) {
+        if (shrink_table[2 * i] < 0 || shrink_table[2 * i] >= LV_S_SHAPES || shrink_table[2 * i + 1] < 1 ||
+            shrink_table[2 * i + 1] > LORA_MAX_SLICES || expand_table[i] < 0 || expand_table[i] >= LV_E_SHAPES)
+            return LORA_EINVAL;
+    }
+    return plan_impl(op, n_seg, seg_start, seg_adapter, seg_rank, d_in, d_out, work_capacity, work, info,
+                     reinterpret_cast<ShrinkTab>(shrink_table), reinterpret_cast<ExpandTab>(expand_table));
 }
 
 extern "C" int32_t lora_rows_dense_offsets(int32_t n_adapters, int32_t max_rank,

@@ -294,6 +294,23 @@ int32_t lora_plan(int32_t op, int32_t n_seg, const int32_t* seg_start,
                   int32_t d_in, int32_t d_out, int32_t work_capacity,
                   lora_work_t* work, lora_plan_info_t* info);
 
+/* lora_plan with the caller's tile table, for the offline tiling search
+ * (VaLoRA blog, section 4.3.2: input shapes are profiled offline and the
+ * best tiling of each kept in a table looked up at run time), so candidate
+ * tables can be timed with the library as built.  The tables have the
+ * compiled-in table's layout (csrc/tile_table.inc), indexed [length bucket
+ * 8][rank bucket 4][d bucket 4]:
+ *   shrink_table  host int8 [8][4][4][2]: (shrink shape 0..2, K slices 1..16)
+ *   expand_table  host int8 [8][4][4]: expand shape 0..4
+ * A segment's K-slice count is min(slices, d_in / 64), as with the compiled
+ * table.  Everything else as lora_plan.  Errors: as lora_plan; LORA_EINVAL
+ * also for a null table or an entry outside those ranges. */
+int32_t lora_plan_table(int32_t op, int32_t n_seg, const int32_t* seg_start,
+                        const int32_t* seg_adapter, const int32_t* seg_rank,
+                        int32_t d_in, int32_t d_out, const int8_t* shrink_table,
+                        const int8_t* expand_table, int32_t work_capacity,
+                        lora_work_t* work, lora_plan_info_t* info);
+
 /* Everything the host does for one batch, in one call: the segment table
  * (lora_build_segments), the plans of the ops in op_mask (lora_plan), all
  * written into one caller buffer laid out for a single host-to-device copy,

@@ -124,14 +124,22 @@ def test_decode_layout_is_one_fused_range():
 
 def test_launch_groups():
     """Each range is keyed by its group's smallest variant, groups are
-    disjoint, and the prefill-sized layout needs 7 launches."""
+    disjoint, and the prefill-sized layout holds exactly the launch groups
+    that some segment within its bounds reaches (from the host planner, one
+    segment of each length-bucket edge and rank edge at a time)."""
     for v in range(FUSED + 1):
         g = launch_group(v)
         assert g <= v and launch_group(g) == g
     _, plan = hl.lora_device_plan(9436, 16, 64, 4096, 4096)
     keys = [g for g, *_ in plan.info.range_list()]
     assert keys == sorted(set(keys)) and all(launch_group(g) == g for g in keys)
-    assert keys == [1, 2, 4, 8, 12, 13, FUSED]
+    reach = set()
+    for n in LEN_EDGES + [9436]:
+        for r in [e for e in RANK_EDGES if e <= 64]:
+            _, _, info = host_plan(np.zeros(n, np.int32), [r], 4096, 4096)
+            reach |= {launch_group(v) for v, *_ in info.range_list()}
+    assert keys == sorted(reach)
+    assert FUSED in keys and len(keys) <= 10
 
 
 def test_layout_offsets_and_sizes():

@@ -127,6 +127,76 @@ def test_plan_coverage_invariants():
             assert slices[0] == slices[1], "shrink and expand agree on K slices"
 
 
+def test_table_plans_follow_the_given_table():
+    """lora_plan_table (the tile search's planner): with the compiled-in table
+    it plans exactly as lora_plan for every op; with a table that holds one
+    choice everywhere every segment gets that shape and K-slice count (capped
+    at d_in/64), its plans pass the oracle's coverage checker, and its items
+    stay within the shape's rows; tables with entries out of range, null
+    tables and widths it cannot plan are refused."""
+    from heterogeneous_adapter_batching_amd.tile_search import read_table
+    st0, ex0 = read_table()
+    rng = np.random.default_rng(21)
+    ra = np.repeat(rng.permutation(6), [1, 2, 3, 17, 300, 70])
+    ranks = np.array([8, 16, 64, 128, 32, 1], np.int32)
+    segs = hl.lora_build_segments(ra, ranks)
+    for op in (hl.LORA_OP_SHRINK, hl.LORA_OP_EXPAND, hl.LORA_OP_APPLY):
+        for d_in, d_out in ((1024, 2048), (4096, 4096), (8192, 28672)):
+            w0, i0 = hl.lora_plan(op, segs, d_in, d_out)
+            w1, i1 = hl.lora_plan_table(op, segs, d_in, d_out, st0, ex0)
+            assert np.array_equal(w0, w1) and i0.range_list() == i1.range_list() and i0.v_slices == i1.v_slices
+    rows = {hl.LORA_OP_SHRINK: {0: 16, 1: 64, 2: 128}, hl.LORA_OP_EXPAND: {0: 16, 1: 64, 2: 128, 4: 2}}
+    for op, shapes in rows.items():
+        for shape, mt in shapes.items():
+            for sl in (1, 2, 4, 8, 16):
+                for d_in in (256, 4096):
+                    st, ex = st0.copy(), ex0.copy()
+                    st[...] = (shape if op == hl.LORA_OP_SHRINK else 0, sl)
+                    ex[...] = shape if op == hl.LORA_OP_EXPAND else 0
+                    if shape == 4:   # the VALU expand takes segments of at most 2 rows
+                        segs2 = hl.lora_build_segments([0, 1, 1, 2], [8, 16, 64])
+                    else:
+                        segs2 = segs
+                    work, info = hl.lora_plan_table(op, segs2, d_in, 2048, st, ex)
+                    ns = oracle.check_plan_coverage(segs2, work, info.range_list(), op == hl.LORA_OP_SHRINK,
+                                                    info.v_slices)
+                    want = min(sl, d_in // 64)
+                    assert set(ns.values()) == {want} and info.v_slices == want
+                    assert all(1 <= w[1] <= mt for w in work)
+                    assert all(v // 4 == shape for v, *_ in info.range_list())
+    bad = []
+    for i, v in ((0, -1), (0, 3), (1, 0), (1, 17)):
+        st = st0.copy()
+        st[7, 2, 1, i] = v
+        bad.append((st, ex0))
+    for v in (-1, 5):
+        ex = ex0.copy()
+        ex[0, 0, 0] = v
+        bad.append((st0, ex))
+    for st, ex in bad:
+        status, _, _ = hl.lora_plan_table(hl.LORA_OP_SHRINK, segs, 1024, 2048, st, ex, raw=True)
+        assert status == hl.LORA_EINVAL
+    st_null = hl._lib.lora_plan_table(hl.LORA_OP_SHRINK, segs.n_seg, segs.seg_start.ctypes.data,
+                                      segs.seg_adapter.ctypes.data, segs.seg_rank.ctypes.data, 1024, 2048, None,
+                                      ex0.ctypes.data, 0, None, ctypes.byref(hl.lora_plan_info_t()))
+    assert st_null == hl.LORA_EINVAL
+    status, _, _ = hl.lora_plan_table(hl.LORA_OP_SHRINK, segs, 1000, 2048, st0, ex0, raw=True)
+    assert status == hl.LORA_ESHAPE
+
+
+def test_tile_table_source_round_trips(tmp_path):
+    """The tile search reads the compiled-in table's source and writes it back
+    unchanged but for its note line."""
+    from heterogeneous_adapter_batching_amd import tile_search
+    st0, ex0 = tile_search.read_table()
+    out = tmp_path / "t.inc"
+    tile_search.write_table(st0, ex0, str(out), "note")
+    st1, ex1 = tile_search.read_table(str(out))
+    assert np.array_equal(st0, st1) and np.array_equal(ex0, ex1)
+    keep = [ln for ln in open(tile_search.TABLE).read().splitlines() if not ln.startswith("// Written by")]
+    assert [ln for ln in out.read_text().splitlines() if ln != "// note"] == keep
+
+
 def test_plan_errors():
     segs = hl.lora_build_segments([0, 0, 1], [8, 16])
     with pytest.raises(hl.LoraError) as e:

@@ -238,12 +238,21 @@ _structure_only = False
 def structure(k: int, seed: Optional[int] = None, **kw) -> Structure:
     """Row map(s), ranks and projection shapes of workload k, from the same
     draws as gen_config(k, seed) but without drawing its tensors."""
+    return _structure_of(gen_config, k, seed, **kw)
+
+
+def structure_twin(k: int, seed: Optional[int] = None) -> Structure:
+    """Row map, rank and projection shapes of gen_twin(k, seed), no tensors drawn."""
+    return _structure_of(gen_twin, k, seed)
+
+
+def _structure_of(gen, *a, **kw):
     global _structure_only
-    _structure_only = True
+    prev, _structure_only = _structure_only, True
     try:
-        return gen_config(k, seed, **kw)
+        return gen(*a, **kw)
     finally:
-        _structure_only = False
+        _structure_only = prev
 
 
 def _make(name, seed, row_adapter, ranks, projs, layout, page_elems, rng,
