@@ -93,6 +93,12 @@ __device__ __forceinline__ u32x4_t sel(bool ok, u32x4_t v) {
 // is emitted.
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
+// Wave-uniform read through the scalar data cache (row tables are read-only
+// for the whole launch).  `i` must be the same in every lane of the wave.
+__device__ __forceinline__ int64_t ld_uniform(const int64_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int64_t*)p)[i];
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar)
 // value.  Branches on it are then scalar branches: an MFMA inside a branch the
 // compiler takes for divergent runs under EXEC = 0 when no lane takes the
@@ -898,122 +904,159 @@ __global__ __launch_bounds__(WG) void expand_loop_kernel(ExpandArgs args) {
     }
 }
 
-// One workgroup = one work item of at most BGMV_ROWS rows x one 2048-column
-// group of one projection (decode rows: BGMV).  Lane t owns columns
-// 8t .. 8t+7 of the group and forms y[row][n] += s * sum_j v[row][j] * B[j][n]
-// with fp32 FMAs in rank order.  v[row][j] is loaded by lane j % 64 of every
-// wave (its K slices summed in slice order) and broadcast with readlane; B is
-// read 16 rank rows at a time (row offsets first, then the rows).
+// One workgroup = one work item of at most BGMV_ROWS rows x one 512-column
+// group of one projection (decode rows: BGMV).  Lane l of every wave owns
+// columns 8l .. 8l+7 of the group; wave w takes the rank groups w and w + 4
+// (16 ranks each: ranks 16w .. 16w+15, then 64+16w ..), so the B rows of up
+// to 64 ranks are in flight at once, one round trip for their row offsets and
+// one for the rows.  Each wave forms its partial sum_j v[row][j] * B[j][n]
+// over its ranks with fp32 FMAs in rank order (v[row][j] loaded by one lane,
+// its K slices summed in slice order, and broadcast with readlane); the
+// partials of the four waves are added in wave order through LDS, and
+// y[row][n] += s * that sum, each wave storing 128 of the columns.  With UNI
+// (every chunk_len a multiple of 512, so that the group's 512 columns lie in
+// one chunk of B) the row offsets are wave-uniform and come through the
+// scalar cache.
 #define BGMV_ROWS 2
+#define BGMV_COLS 512
+template <bool UNI>
 __device__ __forceinline__ void bgmv_item(const ExpandArgs& args, const int bx, const int by) {
+    __shared__ f32x4_t s_part[4][BGMV_ROWS][2][64];  // [wave][row][half][lane]: 16 KiB
     const lora_work_t it = args.work[args.begin + bx];
     int pi = 0;
     while (pi + 1 < args.n_proj && by >= args.p[pi + 1].cg_begin) ++pi;
     const ExpandProj& P = args.p[pi];
+    // uniform over the workgroup, so returning here skips no barrier
     if (!item_live(args.live, bx) || !item_ok(it, args.n_active, args.v_slices, P.B, LORA_MAX_RANK) ||
         it.nrows > BGMV_ROWS)
         return;
-    const int lane = threadIdx.x & 63;
-    const int n0 = (by - P.cg_begin) * 2048 + 8 * (int)threadIdx.x;
-    const bool col_ok = n0 < P.d_out;  // lanes past d_out stay: they hold v values for readlane
-    const int nc = col_ok ? n0 : 0;
-    const int cchunk = nc / P.B.chunk_len, cin = nc - cchunk * P.B.chunk_len;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int g0 = (by - P.cg_begin) * BGMV_COLS;
+    const int n0 = g0 + 8 * lane;
+    const bool col_ok = n0 < P.d_out;
+    const int nc = col_ok ? n0 : g0;  // g0 < d_out: the grid covers d_out
+    const int cchunk = (UNI ? __builtin_amdgcn_readfirstlane(nc) : nc) / P.B.chunk_len;
+    const int cin = nc - cchunk * P.B.chunk_len;
     const int64_t vslice = (int64_t)args.n_active * P.ldv;
 
-    // first batch: y row indices, v (lane j holds ranks j and j + 64), first B row offsets
-    int32_t yidx[BGMV_ROWS];
+    // this wave's rank groups: j0 = 16w (and 64 + 16w for ranks above 64)
+    const int ja = 16 * wave, jb = 64 + 16 * wave;
+    // lane l < 16 holds v[row][ja + l], lane 16 <= l < 32 v[row][jb + l - 16]
+    float vsum[BGMV_ROWS];
+    {
+        const int j = lane < 16 ? ja + lane : jb + lane - 16;
+        const bool jok = lane < 32 && j < it.rank;
 #pragma unroll
-    for (int p = 0; p < BGMV_ROWS; ++p) yidx[p] = args.row_index[it.row0 + min(p, it.nrows - 1)];
-    float vsum[BGMV_ROWS][2];
-#pragma unroll
-    for (int p = 0; p < BGMV_ROWS; ++p)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int j = lane + 64 * h;
-            const bool ok = p < it.nrows && j < it.rank;
+        for (int p = 0; p < BGMV_ROWS; ++p) {
+            const bool ok = jok && p < it.nrows;
             const float* vp = P.v + (int64_t)(it.row0 + min(p, it.nrows - 1)) * P.ldv + (ok ? j : 0);
             float t = 0.f;
-            for (int s0 = 0; s0 < it.nslices; s0 += 4) {
-                float sv[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    sv[q] = 0.f;
-                    if (ok && s0 + q < it.nslices) sv[q] = vp[(s0 + q) * vslice];
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (s0 + q < it.nslices) t += sv[q];
-            }
-            vsum[p][h] = t;
+            for (int sl = 0; sl < it.nslices; ++sl)
+                if (ok) t += vp[sl * vslice];
+            vsum[p] = t;
         }
-    int64_t boff[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) boff[e] = P.B.row_off[off_index(P.B, it.adapter, min(e, it.rank - 1), cchunk)];
-    issue_fence();
-    // second batch: y rows
-    float* yrow[BGMV_ROWS];
-    f32x4_t y0[BGMV_ROWS], y1[BGMV_ROWS];
-#pragma unroll
-    for (int p = 0; p < BGMV_ROWS; ++p) {
-        yrow[p] = P.y + (int64_t)yidx[p] * P.ldy + nc;
-        const bool ok = col_ok && p < it.nrows;
-        y0[p] = ldf4_if(ok, yrow[p]);
-        y1[p] = ldf4_if(ok, yrow[p] + 4);
     }
     f32x4_t acc0[BGMV_ROWS], acc1[BGMV_ROWS];
 #pragma unroll
     for (int p = 0; p < BGMV_ROWS; ++p) acc0[p] = acc1[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int j0 = 0; j0 < it.rank; j0 += 16) {
-        if (j0 > 0) {
+    // y of the columns this thread stores (see below), loaded with the first
+    // group's B rows
+    const int q = 16 * wave + (lane >> 2), part = lane & 3;
+    const int nq = g0 + 8 * q + 2 * part;
+    const bool q_ok = nq < P.d_out;
+    int32_t yidx[BGMV_ROWS];
+    float2 y0[BGMV_ROWS];
+    // one rank group: row offsets, the 16 rows, then the FMAs in rank order
+    auto group = [&](int j0, int vl0) {
+        int64_t boff[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                boff[e] = P.B.row_off[off_index(P.B, it.adapter, min(j0 + e, it.rank - 1), cchunk)];
-            issue_fence();
+        for (int e = 0; e < 16; ++e) {
+            const int64_t i = off_index(P.B, it.adapter, min(j0 + e, it.rank - 1), cchunk);
+            boff[e] = UNI ? ld_uniform(P.B.row_off, i) : P.B.row_off[i];
         }
+        issue_fence();
         u32x4_t rows[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) rows[e] = ld16_if(col_ok && j0 + e < it.rank, P.B.pool + boff[e] + cin);
+        if (vl0 == 0) {
 #pragma unroll
-        for (int p = 0; p < BGMV_ROWS; ++p) {
-            if (p >= it.nrows) break;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int j = j0 + e;  // wave-uniform
-                const float vj = __builtin_amdgcn_readlane(__float_as_int(j < 64 ? vsum[p][0] : vsum[p][1]), j & 63);
-                const float w = j < it.rank ? __int_as_float(vj) : 0.f;
-                const u32x4_t r = rows[e];
-                acc0[p][0] = __builtin_fmaf(w, bf16_lo(r[0]), acc0[p][0]);
-                acc0[p][1] = __builtin_fmaf(w, bf16_hi(r[0]), acc0[p][1]);
-                acc0[p][2] = __builtin_fmaf(w, bf16_lo(r[1]), acc0[p][2]);
-                acc0[p][3] = __builtin_fmaf(w, bf16_hi(r[1]), acc0[p][3]);
-                acc1[p][0] = __builtin_fmaf(w, bf16_lo(r[2]), acc1[p][0]);
-                acc1[p][1] = __builtin_fmaf(w, bf16_hi(r[2]), acc1[p][1]);
-                acc1[p][2] = __builtin_fmaf(w, bf16_lo(r[3]), acc1[p][2]);
-                acc1[p][3] = __builtin_fmaf(w, bf16_hi(r[3]), acc1[p][3]);
+            for (int p = 0; p < BGMV_ROWS; ++p) {
+                const bool ok = q_ok && p < it.nrows;
+                y0[p] = ok ? *reinterpret_cast<const float2*>(P.y + (int64_t)yidx[p] * P.ldy + nq) : float2{0.f, 0.f};
             }
         }
-    }
+        issue_fence();
+        // rank by rank: each row's 8 values are widened once and used for
+        // both output rows (row-major would keep all 16 rows widened)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const u32x4_t r = rows[e];
+            const float f[8] = {bf16_lo(r[0]), bf16_hi(r[0]), bf16_lo(r[1]), bf16_hi(r[1]),
+                                bf16_lo(r[2]), bf16_hi(r[2]), bf16_lo(r[3]), bf16_hi(r[3])};
+#pragma unroll
+            for (int p = 0; p < BGMV_ROWS; ++p) {
+                const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vsum[p]), vl0 + e));
+                const float w = j0 + e < it.rank ? vj : 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc0[p][c] = __builtin_fmaf(w, f[c], acc0[p][c]);
+                    acc1[p][c] = __builtin_fmaf(w, f[4 + c], acc1[p][c]);
+                }
+            }
+        }
+    };
 #pragma unroll
     for (int p = 0; p < BGMV_ROWS; ++p) {
-        if (p >= it.nrows || !col_ok) continue;
-        f32x4_t o0, o1;
+        yidx[p] = args.row_index[it.row0 + min(p, it.nrows - 1)];
+        y0[p] = float2{0.f, 0.f};
+    }
+    // the wave's groups in turn (a loop, so that the second group's rows do
+    // not take registers of their own)
+    for (int j0 = ja, vl0 = 0; j0 < it.rank; j0 += 64, vl0 += 16) group(j0, vl0);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            o0[c] = __builtin_fmaf(P.scale, acc0[p][c], y0[p][c]);
-            o1[c] = __builtin_fmaf(P.scale, acc1[p][c], y1[p][c]);
+    for (int p = 0; p < BGMV_ROWS; ++p) {
+        s_part[wave][p][0][lane] = acc0[p];
+        s_part[wave][p][1][lane] = acc1[p];
+    }
+    // y: wave w stores the columns of lanes 16w .. 16w+15 (128 columns):
+    // thread t = 64w + l handles lane q = 16w + l / 4, part (l & 3) of its
+    // 8 columns (2 columns each)
+    if (ja >= it.rank) {  // no group: load this thread's y here
+#pragma unroll
+        for (int p = 0; p < BGMV_ROWS; ++p) {
+            const bool ok = q_ok && p < it.nrows;
+            y0[p] = ok ? *reinterpret_cast<const float2*>(P.y + (int64_t)yidx[p] * P.ldy + nq) : float2{0.f, 0.f};
         }
-        stf4(yrow[p], o0);
-        stf4(yrow[p] + 4, o1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < BGMV_ROWS; ++p) {
+        if (p >= it.nrows || !q_ok) continue;
+        float2 sum = {0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const f32x4_t v = s_part[w][p][part >> 1][q];
+            sum.x += (part & 1) ? v[2] : v[0];
+            sum.y += (part & 1) ? v[3] : v[1];
+        }
+        float2 o;
+        o.x = __builtin_fmaf(P.scale, sum.x, y0[p].x);
+        o.y = __builtin_fmaf(P.scale, sum.y, y0[p].y);
+        *reinterpret_cast<float2*>(P.y + (int64_t)yidx[p] * P.ldy + nq) = o;
     }
 }
+template <bool UNI>
 __global__ __launch_bounds__(WG) void bgmv_expand_kernel(ExpandArgs args) {
-    bgmv_item(args, blockIdx.x, blockIdx.y);
+    bgmv_item<UNI>(args, blockIdx.x, blockIdx.y);
 }
 // Device-built plans: a grid of at most the resident workgroups walks the live items.
+template <bool UNI>
 __global__ __launch_bounds__(WG) void bgmv_expand_loop_kernel(ExpandArgs args) {
     const int live = *args.live;
-    for (int bx = blockIdx.x; bx < live; bx += gridDim.x) bgmv_item(args, bx, blockIdx.y);
+    for (int bx = blockIdx.x; bx < live; bx += gridDim.x) {
+        bgmv_item<UNI>(args, bx, blockIdx.y);
+        __syncthreads();  // the next item's LDS writes wait for this one's reads
+    }
 }
 
 // ------------------------------------------------------------------ fused (apply)
@@ -1053,11 +1096,6 @@ struct FusedInlineArgs {
 };
 static_assert(sizeof(FusedInlineArgs) <= 4096, "a kernel's arguments are at most 4 KiB");
 
-// Wave-uniform read through the scalar data cache (row tables are read-only
-// for the whole launch).  `i` must be the same in every lane of the wave.
-__device__ __forceinline__ int64_t ld_uniform(const int64_t* p, int64_t i) {
-    return ((const __attribute__((address_space(4))) int64_t*)p)[i];
-}
 
 // Sums of 8 values over the 64 lanes of a wave by reduce-scatter: at the
 // steps 32, 16, 8 a lane keeps half of its remaining values and adds its
@@ -1666,7 +1704,10 @@ hipError_t launch_expand_range(int ev, int32_t begin, int32_t count, const int32
     args.groups = groups;
     args.live = live;
     if (shape == LV_E_BGMV) {
-        const auto fn = live ? bgmv_expand_loop_kernel : bgmv_expand_kernel;
+        bool uni = true;  // every wave's row offsets are uniform
+        for (int i = 0; i < n_proj; ++i) uni = uni && args.p[i].B.chunk_len % 512 == 0;
+        const auto fn = live ? (uni ? bgmv_expand_loop_kernel<true> : bgmv_expand_loop_kernel<false>)
+                             : (uni ? bgmv_expand_kernel<true> : bgmv_expand_kernel<false>);
         const unsigned gx =
             live ? loop_grid_x(reinterpret_cast<const void*>(fn), count, groups) : (unsigned)count;
         return launch(fn, dim3(gx, (unsigned)groups), dim3(WG), s, args);

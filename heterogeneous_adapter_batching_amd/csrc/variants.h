@@ -85,8 +85,8 @@ static inline LV_HD int lv_group_member(int key, int i) {
     return i == 0 ? key : -1;
 }
 
-// Columns one expand workgroup covers.
-static inline LV_HD int32_t lv_expand_cols(int shape) { return shape == LV_E_BGMV ? 2048 : 512; }
+// Columns per workgroup (a column group) of the expand kernels: 512 for both.
+static inline LV_HD int32_t lv_expand_cols(int shape) { return shape >= 0 ? 512 : 0; }
 
 // Shrink rank classes: N tiles of 16 ranks -> 1, 2, 4, 8 (rank <= 16, 32, 64, 128).
 static inline LV_HD int lv_shrink_class(int32_t rank) {
