@@ -1197,10 +1197,13 @@ def other_workload(args):
     if k == 3:
         spec = W.merge
         r = int(W.adapter_rank[spec.adapter])
+        # each layer's matrices are copies of the seeded layer-0 draws (same
+        # values, own addresses: every phase streams all of them from HBM)
+        w0 = {pi: bits_to_device(spec.weight(0, pi)) for pi in spec.projs}
         mats = {}
         for l in range(spec.n_layers):
             for pi in spec.projs:
-                mats[(l, pi)] = (torch.randn(4096, 4096, device="cuda") / 64).to(torch.bfloat16).view(torch.int16)
+                mats[(l, pi)] = w0[pi] if l == 0 else w0[pi].clone()
         calls = [(prepare_merge([(mats[(l, pi)], A[pi], B[pi], spec.adapter, r, W.scale) for pi in spec.projs]),
                   prepare_merge([(mats[(l, pi)], A[pi], B[pi], spec.adapter, r, W.scale) for pi in spec.projs],
                                 unmerge=True)) for l in range(spec.n_layers)]
