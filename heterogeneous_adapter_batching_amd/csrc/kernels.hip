@@ -378,6 +378,25 @@ __global__ __launch_bounds__(WG) void shrink_classes_kernel(ShrinkArgs args) {
     else
         shrink_item<KSPLIT, MTW, 4, unroll_for<KSPLIT, MTW, 4>()>(args, bx, blockIdx.y);
 }
+// The same for a device-built plan's launch group of those classes: a grid of
+// at most the resident workgroups walks the group's live items, heaviest
+// class first (the barrier after each item keeps the next item's LDS writes
+// behind its reads).
+template <int KSPLIT, int MTW>
+__global__ __launch_bounds__(WG) void shrink_classes_loop_kernel(ShrinkArgs args) {
+    const int live = *args.live;
+    for (int i = blockIdx.x; i < live; i += gridDim.x) {
+        const int bx = live - 1 - i;
+        const int rank = __builtin_amdgcn_readfirstlane(args.work[args.begin + bx].rank);
+        if (rank <= 16)
+            shrink_item<KSPLIT, MTW, 1, unroll_for<KSPLIT, MTW, 1>()>(args, bx, blockIdx.y);
+        else if (rank <= 32)
+            shrink_item<KSPLIT, MTW, 2, unroll_for<KSPLIT, MTW, 2>()>(args, bx, blockIdx.y);
+        else
+            shrink_item<KSPLIT, MTW, 4, unroll_for<KSPLIT, MTW, 4>()>(args, bx, blockIdx.y);
+        __syncthreads();
+    }
+}
 // Device-built plans: a grid of at most the resident workgroups walks the
 // range's live items (every wave reaches each barrier of an item, and the
 // barrier after it keeps the next item's LDS writes behind its reads).
@@ -1638,7 +1657,9 @@ hipError_t launch_shrink_ranges(const lora_plan_info_t& info, const int32_t* liv
                 args.begin = R.begin;
                 args.count = R.count;
                 if (shape == LV_S_SPLITK16) {
-                    const shrink_fn fn = shrink_table(R.variant, live != nullptr);
+                    // a device-built plan's range of classes 0-2 is one launch group
+                    const shrink_fn fn = live && cls < LV_RANK_CLASSES - 1 ? shrink_classes_loop_kernel<4, 1>
+                                                                         : shrink_table(R.variant, live != nullptr);
                     const unsigned gx =
                         live ? loop_grid_x(reinterpret_cast<const void*>(fn), R.count, n_proj) : (unsigned)R.count;
                     err = first_error(err, launch(fn, dim3(gx, (unsigned)n_proj), dim3(WG), s, args));

@@ -56,15 +56,14 @@ static inline LV_HD int32_t lv_expand_rows(int shape) {
 #define LV_FUSED_MAX_ROWRANK 1024  // segments of more than one row are fused while len * rank <= this
 
 // Launch group of an apply-plan variant in a device-built plan: variants one
-// launch can run share a group (the long-segment shrink of one shape with
-// ranks up to 64, whose kernel picks the rank tiles per item; the MFMA
-// expand of one rank class, whose kernel takes items of any row count); every
-// other variant is a group of its own.  The key is the group's smallest
-// variant.
+// launch can run share a group (the shrink of one shape with ranks up to 64,
+// whose kernels pick the rank tiles per item; the MFMA expand of one rank
+// class, whose kernel takes items of any row count); every other variant is
+// a group of its own.  The key is the group's smallest variant.
 static inline LV_HD int lv_launch_group(int v) {
     if (v < LV_APPLY_EXPAND0) {
         const int shape = v / LV_RANK_CLASSES, cls = v % LV_RANK_CLASSES;
-        return shape != LV_S_SPLITK16 && cls < LV_RANK_CLASSES - 1 ? shape * LV_RANK_CLASSES : v;
+        return cls < LV_RANK_CLASSES - 1 ? shape * LV_RANK_CLASSES : v;
     }
     if (v < LV_APPLY_FUSED) {
         const int ev = v - LV_APPLY_EXPAND0, shape = ev / LV_RANK_CLASSES, cls = ev % LV_RANK_CLASSES;
@@ -76,8 +75,7 @@ static inline LV_HD int lv_launch_group(int v) {
 // Member i (in ascending order) of the launch group keyed by `key`, or -1.
 static inline LV_HD int lv_group_member(int key, int i) {
     if (key < LV_APPLY_EXPAND0) {
-        const int shape = key / LV_RANK_CLASSES, cls = key % LV_RANK_CLASSES;
-        const int n = shape != LV_S_SPLITK16 && cls == 0 ? LV_RANK_CLASSES - 1 : 1;
+        const int n = key % LV_RANK_CLASSES == 0 ? LV_RANK_CLASSES - 1 : 1;
         return i < n ? key + i : -1;
     }
     if (key < LV_APPLY_EXPAND0 + LV_RANK_CLASSES)  // MFMA expand of one rank class: shapes 0 .. LV_E_SPARE

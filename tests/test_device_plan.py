@@ -19,13 +19,13 @@ FUSED = 3 * 4 + 5 * 4   # apply variants: 3 shrink shapes x 4 rank classes, 5 ex
 
 def launch_group(v):
     """The launch group of an apply variant in a device-built plan, keyed by
-    its smallest variant: the long-segment shrink (shapes 1, 2) of ranks up to
-    64 shares one launch per shape, the MFMA expand (shapes 0-3) one launch
-    per rank class; the split-K shrink, ranks above 64 of the long shrink,
-    the BGMV expand and the fused rows are launches of their own."""
+    its smallest variant: the shrink of ranks up to 64 shares one launch per
+    shape (split-K, 64-row and 128-row items), the MFMA expand (shapes 0-3)
+    one launch per rank class; ranks above 64 of the shrink, the BGMV expand
+    and the fused rows are launches of their own."""
     if v < 12:
         shape, cls = divmod(v, 4)
-        return shape * 4 if shape != 0 and cls < 3 else v
+        return shape * 4 if cls < 3 else v
     if v < FUSED:
         shape, cls = divmod(v - 12, 4)
         return v if shape == 4 else 12 + cls
