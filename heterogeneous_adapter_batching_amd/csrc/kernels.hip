@@ -200,7 +200,7 @@ struct ShrinkArgs {
 template <int KSPLIT, int MTW, int NT, int U>
 __device__ __forceinline__ void shrink_item(const ShrinkArgs& args, const int bx, const int by) {
     const lora_work_t it = args.work[args.begin + bx];
-    const ShrinkProj& P = args.p[by];
+    const ShrinkProj P = args.p[by];  // by value: its fields load in one batch
     if (!item_live(args.live, bx) || !item_ok(it, args.n_active, args.v_slices, P.A, 16 * NT) ||
         it.nrows > 16 * MTW * (KSPLIT > 1 ? 1 : 4))
         return;
@@ -706,6 +706,16 @@ struct ExpandArgs {
     ExpandProj p[LORA_MAX_PROJ];
 };
 
+// The projection that column group `cg` belongs to: a count of the
+// projections whose groups start at or before it, so that the launch's
+// start columns are read in one batch rather than one after the other.
+__device__ __forceinline__ int proj_of_group(const ExpandArgs& args, int cg) {
+    int pi = 0;
+#pragma unroll
+    for (int i = 1; i < LORA_MAX_PROJ; ++i) pi += (i < args.n_proj) & (cg >= args.p[i].cg_begin);
+    return pi;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
 // L2.  The MFMA expand's 1-D grid (a multiple of 8) is remapped so that XCD x
 // takes the contiguous block x*G/8 .. (x+1)*G/8 - 1 of logical ids, ordered
@@ -732,9 +742,9 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& args, const int li
     if (lid >= args.count * args.groups) return;      // padding of the grid to a multiple of 8
     const int item = lid / args.groups, cg = lid - item * args.groups;
     const lora_work_t it = args.work[args.begin + item];
-    int pi = 0;
-    while (pi + 1 < args.n_proj && cg >= args.p[pi + 1].cg_begin) ++pi;
-    const ExpandProj& P = args.p[pi];
+    // the projection by value: its fields are loaded in one batch, before
+    // the checks branch on them
+    const ExpandProj P = args.p[proj_of_group(args, cg)];
     // uniform over the workgroup, so returning here skips no barrier
     if (!(item_live(args.live, item) && item_ok(it, args.n_active, args.v_slices, P.B, 32 * KS) &
           (it.nrows <= EXPAND_ROWS)))
@@ -942,9 +952,7 @@ template <bool UNI>
 __device__ __forceinline__ void bgmv_item(const ExpandArgs& args, const int bx, const int by) {
     __shared__ f32x4_t s_part[4][BGMV_ROWS][2][64];  // [wave][row][half][lane]: 16 KiB
     const lora_work_t it = args.work[args.begin + bx];
-    int pi = 0;
-    while (pi + 1 < args.n_proj && by >= args.p[pi + 1].cg_begin) ++pi;
-    const ExpandProj& P = args.p[pi];
+    const ExpandProj P = args.p[proj_of_group(args, by)];  // by value, as in expand_item
     // uniform over the workgroup, so returning here skips no barrier
     if (!item_live(args.live, bx) || !item_ok(it, args.n_active, args.v_slices, P.B, LORA_MAX_RANK) ||
         it.nrows > BGMV_ROWS)
@@ -1104,7 +1112,7 @@ struct FusedArgs {
 // items and the row index are read from the argument block (scalar loads),
 // so the plan needs no device copy.
 struct FusedInlineArgs {
-    const int32_t* live;  // always NULL
+    static constexpr const int32_t* live = nullptr;  // every item is in use
     int32_t begin;        // always 0
     int32_t n_active;
     ApplyProj p[LORA_MAX_PROJ];
@@ -1165,8 +1173,10 @@ __device__ __forceinline__ void fused_item(const Args& args, const int bx, const
     __shared__ float s_part[FWG / 64][8];
     __shared__ float s_v[16];
     __shared__ f32x4_t s_acc[FHALF][2];
+    // the item and the projection by value: every field the workgroup needs
+    // is loaded in one batch, before the checks branch on them
     const lora_work_t it = args.item(bx);
-    const ApplyProj& P = args.p[by];
+    const ApplyProj P = args.p[by];
     // uniform over the workgroup, so returning here skips no barrier
     if (!(item_live(args.live, bx) && item_ok(it, args.n_active, 1, P.A, LORA_MAX_RANK) & (it.nrows == 1) &
           (it.adapter < P.B.n_adapters) &
@@ -1846,7 +1856,6 @@ int32_t apply_impl(const lora_launch_t* L, int32_t n_proj, const lora_apply_proj
     for (int i = 0; i < n_proj; ++i) uni = uni && fa.p[i].A.chunk_len % 512 == 0 && fa.p[i].B.chunk_len % 512 == 0;
     if (launch_inlines(L)) {  // the plan goes in the launch arguments
         FusedInlineArgs ia{};
-        ia.live = nullptr;
         ia.begin = 0;
         ia.n_active = L->info.n_active;
         for (int i = 0; i < n_proj; ++i) ia.p[i] = fa.p[i];
