@@ -41,6 +41,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --workload prefill|vision|mix70b --twin        (shrink/expand tables and the twin ratio)
        python bench.py --workload prefill|vision|mix70b --metadata device  (apply: host- vs device-built plan)
        python bench.py --copy-calibration                             (counter calibration under rocprofv3)
+       python bench.py --flush-study                                  (the prefill shrink after a write or read cache flush)
        python bench.py --traffic-record PMC_DIR --traffic-grid N      (write the dominant launch's traffic record)
        python bench.py --rmw-ceiling                                  (in-place streaming rate of this HBM)
 """
@@ -59,6 +60,101 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 METRIC = "hetero-LoRA shrink+expand µs, GB/s & TFLOP/s vs roofline; merge µs/layer"
+
+
+class ColdCache:
+    """Evicts the 256 MB Infinity Cache before a cold timing by reading a
+    512 MB buffer (one reduction over it).  A write-based flush (a fill)
+    would leave the cache full of dirty lines, and the kernel timed next
+    would pay their write-back on its own reads: the prefill shrink takes
+    ~116 us after a 1 GiB fill against ~67 us after a 1 GiB read
+    (`--flush-study`)."""
+
+    def __init__(self, device="cuda"):
+        import torch
+        self.buf = torch.ones(128 << 20, dtype=torch.int32, device=device)
+
+    def __call__(self):
+        self.sink = self.buf.max()
+
+
+def flush_study():
+    """The prefill workload's lora_shrink (9,436 rows, q/k/v/o at d 4096:
+    326 MB of algorithmic bytes) timed after three cache states: after a
+    1 GiB fill (the Infinity Cache left full of dirty lines), after a 1 GiB
+    read (evicted, clean), and right after the batch's own lora_expand (y
+    just written: the state a step leaves behind); and the decode layer's
+    heterogeneous lora_apply (the fused kernel) after the first two."""
+    import torch
+    import workloads
+    from heterogeneous_adapter_batching_amd.session import Batch, HipEvent, Rows
+    from workloads.device import to_device
+    W = workloads.gen_config(2)
+    dw = to_device(W)
+    d_in = max(p.d_in for p in W.projections)
+    d_out = max(p.d_out for p in W.projections)
+    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out).refresh(W.row_adapter)
+    ldv = -(-int(W.adapter_rank.max()) // 4) * 4
+    A = [Rows(dw.pool, d.A_off, p.A.n_adapters, p.A.max_rank, p.A.row_len, p.A.chunk_len)
+         for p, d in zip(W.projections, dw.projections)]
+    B = [Rows(dw.pool, d.B_off, p.B.n_adapters, p.B.max_rank, p.B.row_len, p.B.chunk_len)
+         for p, d in zip(W.projections, dw.projections)]
+    v = [b.new_v(ldv) for _ in W.projections]
+    do_s = b.prepare_shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)])
+    do_e = b.prepare_expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
+    nbytes = delta_cost(W, W.row_adapter)["shrink_bytes"]
+    big = torch.ones(256 << 20, dtype=torch.int32, device="cuda")
+    out = {}
+    for name in ("after a 1 GiB fill", "after a 1 GiB read", "after its own expand"):
+        ts = []
+        for rep in range(12):
+            if name == "after a 1 GiB fill":
+                big.fill_(rep)
+            elif name == "after a 1 GiB read":
+                big.max()
+            else:
+                do_e()
+            e0, e1 = HipEvent(timing=True), HipEvent(timing=True)
+            e0.record()
+            do_s()
+            e1.record()
+            e1.synchronize()
+            if rep >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(ts))
+        out[name] = {"us_median": round(us, 2), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    # the decode layer's heterogeneous batch: one fused lora_apply (77.6 MB)
+    Wd = workloads.gen_config(1)
+    dd = to_device(Wd)
+    ra = Wd.batches["hetero"]
+    bd = Batch(Wd.n_rows, Wd.adapter_rank, 4096, 4096, inline=True).refresh(ra)
+    ldvd = -(-int(Wd.adapter_rank.max()) // 4) * 4
+    do_a = bd.prepare_apply([(d.x, Rows(dd.pool, d.A_off, p.A.n_adapters, p.A.max_rank, p.A.row_len, p.A.chunk_len),
+                              bd.new_v(ldvd), Rows(dd.pool, d.B_off, p.B.n_adapters, p.B.max_rank, p.B.row_len,
+                                                    p.B.chunk_len), d.y, Wd.scale)
+                             for p, d in zip(Wd.projections, dd.projections)])
+    nd = delta_cost(Wd, ra)
+    nd = nd["shrink_bytes"] + nd["expand_bytes"]
+    dec = {}
+    for name in ("after a 1 GiB fill", "after a 1 GiB read"):
+        ts = []
+        for rep in range(12):
+            if name == "after a 1 GiB fill":
+                big.fill_(rep)
+            else:
+                big.max()
+            e0, e1 = HipEvent(timing=True), HipEvent(timing=True)
+            e0.record()
+            do_a()
+            e1.record()
+            e1.synchronize()
+            if rep >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(ts))
+        dec[name] = {"us_median": round(us, 2), "hbm_frac": round(nd / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    print(json.dumps({"study": "a kernel's time after three cache states",
+                      "prefill lora_shrink (326 MB)": out,
+                      "decode heterogeneous lora_apply, fused (%.1f MB)" % (nd / 1e6): dec}), flush=True)
 
 
 KERNELS_SRC = os.path.join(ROOT, "heterogeneous_adapter_batching_amd", "csrc", "kernels.hip")
@@ -279,6 +375,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shared-x", action="store_true",
                     help="with --workload prefill|vision: q, k and v take one x (the layer input), o its own")
+    ap.add_argument("--flush-study", action="store_true",
+                    help="time the prefill shrink after a write-based and a read-based cache flush and after its "
+                         "own expand, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy (counter calibration under rocprofv3 --pmc) and exit")
     ap.add_argument("--rmw-ceiling", action="store_true",
@@ -290,6 +389,8 @@ def main():
     args = ap.parse_args()
     if args.traffic_record:
         return traffic_record(args)
+    if args.flush_study:
+        return flush_study()
     if args.copy_calibration:
         return copy_calibration()
     if args.rmw_ceiling:
@@ -848,7 +949,8 @@ def headline(args):
     as merge and unmerge µs per layer, each phase cold (it streams 4.3 GB of
     W); and the heterogeneous / homogeneous time ratio against the mix's
     homogeneous twin (the same rows on one adapter of the token-weighted
-    mean rank), both cold (a 512 MB fill before each timed call)."""
+    mean rank), both cold (a 512 MB read before each timed call evicts the
+    Infinity Cache: ColdCache)."""
     import torch
     import workloads
     from heterogeneous_adapter_batching_amd.session import Batch, HipEvent, Rows, prepare_merge
@@ -964,8 +1066,8 @@ def headline(args):
     kernel_label = dname.split(" ")[0]
     traffic = recorded_traffic(MIX70B_TRAFFIC_FILE, kernel_label)
 
-    # homogeneous twin, cold: lora_apply between an event pair after a 512 MB fill
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # homogeneous twin, cold: lora_apply between an event pair after a cache flush
+    flush = ColdCache(dev)
     Wt = workloads.gen_twin(4)
     dwt = to_device(Wt)
     bt = Batch(Wt.n_rows, Wt.adapter_rank, d_in, d_out, inline=True).refresh(Wt.row_adapter)
@@ -977,7 +1079,7 @@ def headline(args):
     cold = {"hetero": [], "homo": []}
     for it in range(args.warmup + args.steps):
         for name, fn in (("hetero", copies[0]["run"]), ("homo", run_t)):
-            flush.fill_(it & 0xFF)
+            flush()
             e = new_events(2)
             e[0].record(stream); fn(); e[1].record(stream)
             torch.cuda.synchronize()
@@ -1100,7 +1202,7 @@ def other_workload(args):
     if getattr(args, "shared_x", False):
         assert k in (2, 3), "--shared-x applies to the prefill and vision workloads (q/k/v share x)"
         kw["shared_qkv"] = True
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")   # Infinity Cache flush between steps
+    flush = ColdCache("cuda")   # Infinity Cache flush between steps
 
     def setup(W):
         dw = to_device(W)
@@ -1115,14 +1217,14 @@ def other_workload(args):
 
     def time_split(W, dw, A, B, b, ldv, cold=True):
         """Shrink and expand µs over the timed steps: cold (a cache-flushing
-        fill before each step) or warm (the same launches back to back)."""
+        read before each step: ColdCache) or warm (the same launches back to back)."""
         v = [b.new_v(ldv) for _ in W.projections]
         do_s = b.prepare_shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)])
         do_e = b.prepare_expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
         res = {"shrink": [], "expand": []}
         for it in range(args.warmup + args.steps):
             if cold:
-                flush.fill_(it & 0xFF)
+                flush()
             e = [HipEvent(timing=True) for _ in range(3)]
             e[0].record(); do_s(); e[1].record(); do_e(); e[2].record()
             torch.cuda.synchronize()
@@ -1181,9 +1283,9 @@ def other_workload(args):
         r2 = {"apply_host_plan": [], "build": [], "apply_device_plan": []}
         for it in range(args.warmup + args.steps):
             e = [HipEvent(timing=True) for _ in range(5)]
-            flush.fill_(it & 0xFF)
+            flush()
             e[0].record(); do_a(); e[1].record()
-            flush.fill_((it + 1) & 0xFF)
+            flush()
             e[2].record(); db.build(ra_d, rk_d); e[3].record(); do_d(); e[4].record()
             torch.cuda.synchronize()
             if it >= args.warmup:
@@ -1235,7 +1337,7 @@ def mixture_workload(args):
     +s x A_x^T B_x - s x A_0^T B_0 through composite adapters in one
     lora_apply (the fused kernel), timed next to the plain heterogeneous
     lora_apply of the same rows (no adapter merged); HIP events, medians,
-    a 512 MB fill between steps to evict the Infinity Cache."""
+    a 512 MB read between steps (ColdCache) to evict the Infinity Cache."""
     import torch
     import workloads
     from heterogeneous_adapter_batching_amd import lora_mixture_row_adapter
@@ -1263,11 +1365,11 @@ def mixture_workload(args):
     vp = [bp.new_v(r_max) for _ in plain]
     run_mix = bm.prepare_apply([(d.x, A, v, B, d.y, W.scale) for (d, A, B, _), v in zip(mix, vm)])
     run_plain = bp.prepare_apply([(d.x, A, v, B, d.y, W.scale) for (d, A, B), v in zip(plain, vp)])
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = ColdCache("cuda")
     res = {"mixture_apply": [], "unmerged_apply": []}
     for it in range(args.warmup + args.steps):
         for name, fn in (("mixture_apply", run_mix), ("unmerged_apply", run_plain)):
-            flush.fill_(it & 0xFF)
+            flush()
             e = [HipEvent(timing=True) for _ in range(2)]
             e[0].record(); fn(); e[1].record()
             torch.cuda.synchronize()
@@ -1332,14 +1434,14 @@ def swap_workload(args):
     do_s = b.prepare_shrink([(d.x, A[i], v[i]) for i, d in enumerate(dw.projections)])
     do_e = b.prepare_expand([(v[i], B[i], d.y, W.scale) for i, d in enumerate(dw.projections)])
     compute = torch.cuda.current_stream()
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = ColdCache("cuda")
     sets = [np.arange(0, 16), np.arange(16, 32)]
     cur = 1  # the set resident last (none yet): each acquire below loads the other one
     for it in range(args.warmup + args.steps):
         for _ in range(2):
             cur = 1 - cur
             S = sets[cur]
-            flush.fill_(it & 0xFF)
+            flush()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             load = pool.acquire(S, W.adapter_rank[S])
@@ -1365,7 +1467,7 @@ def swap_workload(args):
                 res["scatter_16"].append(e[0].elapsed_time(e[1]) * 1e3)
         # compute alone, then with the copy-in of the set not resident
         for name in ("compute_alone", "compute_with_copy_in"):
-            flush.fill_(it & 0xFF)
+            flush()
             torch.cuda.synchronize()
             if name == "compute_with_copy_in":
                 # the copy-in is enqueued (host packing done) before the compute starts
@@ -1422,10 +1524,10 @@ def heads_workload(args):
     b = Batch(W.n_rows, W.adapter_rank, 4096, 64).refresh(W.row_adapter)
     v = [b.new_v(128)]
     run = b.prepare_shrink([(d.x, H, v[0])])
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = ColdCache("cuda")
     ts = []
     for it in range(args.warmup + args.steps):
-        flush.fill_(it & 0xFF)
+        flush()
         e = [HipEvent(timing=True) for _ in range(2)]
         e[0].record()
         run()

@@ -36,7 +36,7 @@ caller's table) and the library as built, in two phases:
    has its own tail.
 2. Other buckets.  A bucket no batch above reaches is timed alone: a batch of
    segments of one length, rank and width inside it (8192 rows, 256 segments
-   at most, one projection), cold (a 512 MB fill evicts the Infinity Cache
+   at most, one projection), cold (a 512 MB read evicts the Infinity Cache
    before each call), the op the bucket serves only.
 
 In the workload phase a candidate replaces the current choice only when it is
@@ -154,7 +154,7 @@ def _median_us(call, stream, reps, flush=None):
     ts = []
     for k in range(reps + 1):
         if flush is not None:
-            flush.fill_(k & 0xFF)
+            flush.max()  # a read evicts the Infinity Cache without leaving dirty lines behind
         e0, e1 = HipEvent(timing=True), HipEvent(timing=True)
         e0.record(stream)
         call()
@@ -208,7 +208,7 @@ class Case:
                     LORA_OP_EXPAND: (lora_expand_proj_t * n)(*self.ep),
                     LORA_OP_APPLY: (lora_apply_proj_t * n)(*self.ap)}
         self.fn = {LORA_OP_SHRINK: _lib.lora_shrink, LORA_OP_EXPAND: _lib.lora_expand, LORA_OP_APPLY: _lib.lora_apply}
-        self.flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
+        self.flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda") if cold else None
         self.n_proj = n
 
     def buckets(self):
