@@ -81,7 +81,16 @@ __device__ __forceinline__ f32x4_t ldf4_if(bool ok, const float* p) {
     return v;
 }
 __device__ __forceinline__ f32x4_t ldf4(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
-__device__ __forceinline__ void stf4(float* p, f32x4_t v) { *reinterpret_cast<f32x4_t*>(p) = v; }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Stores of y: a launch writes each y element once and does not read it back,
+// so they go out as nontemporal (streaming) stores, which measured ~1% faster
+// on the MFMA expand than plain stores
+__device__ __forceinline__ void stf4(float* p, f32x4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void stf2(float* p, f32x2_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x2_t*>(p));
+}
 __device__ __forceinline__ u32x4_t sel(bool ok, u32x4_t v) {
     const u32x4_t z = {0u, 0u, 0u, 0u};
     return ok ? v : z;
@@ -1066,10 +1075,8 @@ __device__ __forceinline__ void bgmv_item(const ExpandArgs& args, const int bx, 
             sum.x += (part & 1) ? v[2] : v[0];
             sum.y += (part & 1) ? v[3] : v[1];
         }
-        float2 o;
-        o.x = __builtin_fmaf(P.scale, sum.x, y0[p].x);
-        o.y = __builtin_fmaf(P.scale, sum.y, y0[p].y);
-        *reinterpret_cast<float2*>(P.y + (int64_t)yidx[p] * P.ldy + nq) = o;
+        stf2(P.y + (int64_t)yidx[p] * P.ldy + nq,
+             f32x2_t{__builtin_fmaf(P.scale, sum.x, y0[p].x), __builtin_fmaf(P.scale, sum.y, y0[p].y)});
     }
 }
 template <bool UNI>
