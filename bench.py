@@ -84,7 +84,9 @@ def flush_study():
     1 GiB fill (the Infinity Cache left full of dirty lines), after a 1 GiB
     read (evicted, clean), and right after the batch's own lora_expand (y
     just written: the state a step leaves behind); and the decode layer's
-    heterogeneous lora_apply (the fused kernel) after the first two."""
+    heterogeneous lora_apply (the fused kernel) after the first two; and
+    every launch of the 70B mix's lora_apply, alone after a 1 GiB read and
+    inside a step that follows a whole step."""
     import torch
     import workloads
     from heterogeneous_adapter_batching_amd.session import Batch, HipEvent, Rows
@@ -152,9 +154,52 @@ def flush_study():
                 ts.append(e0.elapsed_time(e1) * 1e3)
         us = float(np.median(ts))
         dec[name] = {"us_median": round(us, 2), "hbm_frac": round(nd / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del dd, bd, do_a, dw, b, do_s, do_e
+    # the 70B mix's lora_apply split at its launch boundaries: each piece
+    # alone after a 1 GiB read, and the same pieces in a step that follows a
+    # whole step (the state the bench line's steps run in)
+    Wm = workloads.gen_config(4)
+    dm = to_device(Wm)
+    bm = Batch(Wm.n_rows, Wm.adapter_rank, max(p.d_in for p in Wm.projections),
+               max(p.d_out for p in Wm.projections), inline=True).refresh(Wm.row_adapter)
+    ldvm = -(-int(Wm.adapter_rank.max()) // 4) * 4
+    pm = apply_pieces(bm, [(d.x, Rows(dm.pool, d.A_off, p.A.n_adapters, p.A.max_rank, p.A.row_len, p.A.chunk_len),
+                            bm.new_v(ldvm), Rows(dm.pool, d.B_off, p.B.n_adapters, p.B.max_rank, p.B.row_len,
+                                                  p.B.chunk_len), d.y, Wm.scale)
+                           for p, d in zip(Wm.projections, dm.projections)])
+    clean = {i: [] for i in range(len(pm))}
+    stepped = {i: [] for i in range(len(pm))}
+    for rep in range(12):
+        for i, (_, _, fn, _) in enumerate(pm):
+            big.max()
+            e0, e1 = HipEvent(timing=True), HipEvent(timing=True)
+            e0.record(); fn(); e1.record()
+            e1.synchronize()
+            if rep >= 2:
+                clean[i].append(e0.elapsed_time(e1) * 1e3)
+        ev = [HipEvent(timing=True) for _ in range(len(pm) + 1)]
+        for _, _, fn, _ in pm:
+            fn()
+        for i, (_, _, fn, _) in enumerate(pm):
+            ev[i].record(); fn()
+        ev[len(pm)].record()
+        ev[-1].synchronize()
+        if rep >= 2:
+            for i in range(len(pm)):
+                stepped[i].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
+    mix = {}
+    for i, (name, _, _, items) in enumerate(pm):
+        parts = ("shrink",) if name == "shrink" else ("expand",)
+        nb, _ = piece_cost(Wm, items, parts)
+        c_us, s_us = float(np.median(clean[i])), float(np.median(stepped[i]))
+        mix["%s (%d items)" % (name, items.shape[0])] = {
+            "alg_MB": round(nb / 1e6, 1),
+            "after a 1 GiB read": {"us_median": round(c_us, 2), "hbm_frac": round(nb / c_us / 1e3 / HBM_PEAK_GBS, 4)},
+            "in a step after a step": {"us_median": round(s_us, 2), "hbm_frac": round(nb / s_us / 1e3 / HBM_PEAK_GBS, 4)}}
     print(json.dumps({"study": "a kernel's time after three cache states",
                       "prefill lora_shrink (326 MB)": out,
-                      "decode heterogeneous lora_apply, fused (%.1f MB)" % (nd / 1e6): dec}), flush=True)
+                      "decode heterogeneous lora_apply, fused (%.1f MB)" % (nd / 1e6): dec,
+                      "70B mix lora_apply, launch by launch": mix}), flush=True)
 
 
 KERNELS_SRC = os.path.join(ROOT, "heterogeneous_adapter_batching_amd", "csrc", "kernels.hip")
