@@ -837,8 +837,10 @@ def apply_pieces(batch, projs):
     lora_apply does), then every expand range alone, then the fused range.
     lora_apply itself makes the same launches in the same order (one launch
     per expand range), so the pieces are the call split at its launch
-    boundaries, which lets events sit between them.  Returns [(name,
-    range indices, fn, items)]."""
+    boundaries, which lets events sit between them.  The pieces keep the
+    ranges of the plan current when they are made (the same batch is
+    refreshed with the same rows every step) and read its buffers at each
+    call.  Returns [(name, range indices, fn, items)]."""
     import ctypes
     from heterogeneous_adapter_batching_amd import lora_apply_proj_t, lora_launch_t, call_apply
     from heterogeneous_adapter_batching_amd.session import stream_handle
@@ -870,6 +872,10 @@ def apply_pieces(batch, projs):
         items = np.concatenate([work[ranges[i][1]:ranges[i][1] + ranges[i][2]] for i in idx])
 
         def fn(sub=sub):
+            # the plan's buffers of the batch's latest refresh (a batch with a
+            # side-stream upload alternates between two staging slots)
+            sub.row_index, sub.work, sub.live = L.row_index, L.work, L.live
+            sub.host_work, sub.host_row_index = L.host_work, L.host_row_index
             call_apply(sub, arr, len(projs), h)
         fn.keep = (sub, arr, projs)
         out.append((name, idx, fn, items))
@@ -987,7 +993,9 @@ def headline(args):
     active rows, gathering adapter rows through the page table.  Steps
     alternate between two device copies of the inputs (same values, other
     addresses), so no step finds the previous one's data in the Infinity
-    Cache.  Inputs are resident in HBM before the timed region.
+    Cache.  Inputs are resident in HBM before the timed region.  The plan's
+    upload runs on a side stream (Batch's copy_stream: two staging slots),
+    so a step's copy overlaps the previous step's launches.
 
     Beside it, in the same line: the vision workload's mode switch (merge of
     its rank-64 adapter into 32 layers x q/k/v/o W[4096x4096], then unmerge),
@@ -1011,7 +1019,9 @@ def headline(args):
     d_out = max(p.d_out for p in W.projections)
     ldv = -(-int(W.adapter_rank.max()) // 4) * 4
     dw0 = to_device(W)
-    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out, inline=True).refresh(W.row_adapter)
+    # the plan's upload runs on a side stream, beside the previous step's launches
+    copy_stream = torch.cuda.Stream()
+    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out, inline=True, copy_stream=copy_stream).refresh(W.row_adapter)
     copies = []
     for c in range(2):
         if c == 0:
@@ -1115,7 +1125,7 @@ def headline(args):
     flush = ColdCache(dev)
     Wt = workloads.gen_twin(4)
     dwt = to_device(Wt)
-    bt = Batch(Wt.n_rows, Wt.adapter_rank, d_in, d_out, inline=True).refresh(Wt.row_adapter)
+    bt = Batch(Wt.n_rows, Wt.adapter_rank, d_in, d_out, inline=True, copy_stream=copy_stream).refresh(Wt.row_adapter)
     ldvt = -(-int(Wt.adapter_rank.max()) // 4) * 4
     twin_runs = []
     for c in range(2):

@@ -1,0 +1,62 @@
+"""Plan upload on a side stream (GPU): a Batch built with ``copy_stream``
+keeps two staging slots and copies batch k's plan while the compute stream
+still runs batch k-1.  A run of refresh + lora_apply steps over changing row
+maps, with the host never waiting between steps, must leave y bit for bit as
+the same steps with the upload on the compute stream; a slot reused too early
+(a copy overwriting a plan that a launch still reads) would change it."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from heterogeneous_adapter_batching_amd.session import Batch
+from workloads.device import to_device
+
+from gpu_helpers import rows_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _maps(ra, n, seed):
+    """n row maps with the same segment shapes: row permutations of ra."""
+    rng = np.random.default_rng(seed)
+    return [np.ascontiguousarray(ra if k == 0 else ra[rng.permutation(ra.shape[0])], np.int32) for k in range(n)]
+
+
+def _run(W, maps, steps, inline, side):
+    dw = to_device(W)
+    d_in = max(p.d_in for p in W.projections)
+    d_out = max(p.d_out for p in W.projections)
+    stream = torch.cuda.current_stream()
+    copy_stream = torch.cuda.Stream() if side else None
+    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out, inline=inline, copy_stream=copy_stream)
+    b.refresh(maps[0], stream)
+    ldv = -(-int(W.adapter_rank.max()) // 4) * 4
+    vs = [b.new_v(ldv) for _ in W.projections]
+    run = b.prepare_apply([(dp.x, rows_of(dw.pool, p.A, dp.A_off), v, rows_of(dw.pool, p.B, dp.B_off), dp.y,
+                            W.scale) for p, dp, v in zip(W.projections, dw.projections, vs)])
+    run()
+    for k in range(1, steps):
+        b.refresh(maps[k % len(maps)], stream)
+        run()
+    torch.cuda.synchronize()
+    return [dp.y.cpu().numpy() for dp in dw.projections]
+
+
+@pytest.mark.parametrize("inline", [False, True])
+def test_side_stream_upload_matches(inline):
+    if inline:
+        # one-token rows and short low-rank segments: an all-fused plan (inline)
+        ra = np.repeat([0, 1, -1, 2, 3, 4, 5], [1, 1, 2, 1, 3, 1, 1])
+        W = workloads.gen_custom(71, ra, [16, 8, 32, 16, 64, 8], 1024, 768, n_proj=2)
+    else:
+        # long and short segments, one-row ones and released rows: a copied plan
+        ra = np.repeat([0, -1, 1, 2, 3, -1, 4], [1, 3, 1, 12, 300, 2, 140])
+        W = workloads.gen_custom(72, ra, [16, 64, 8, 32, 40], 1024, 960, n_proj=2)
+    maps = _maps(np.asarray(W.row_adapter, np.int32), 3, 7)
+    y0 = [p.y0.copy() for p in W.projections]
+    ref = _run(W, maps, 9, inline, side=False)
+    got = _run(W, maps, 9, inline, side=True)
+    for pi, (r, g) in enumerate(zip(ref, got)):
+        assert not np.array_equal(r, y0[pi]), "the steps left y unchanged"
+        assert np.array_equal(r.view(np.uint32), g.view(np.uint32)), "projection %d differs" % pi
