@@ -23,13 +23,13 @@ def _maps(ra, n, seed):
     return [np.ascontiguousarray(ra if k == 0 else ra[rng.permutation(ra.shape[0])], np.int32) for k in range(n)]
 
 
-def _run(W, maps, steps, inline, side):
+def _run(W, maps, steps, inline, side, n_rows_max=None):
     dw = to_device(W)
     d_in = max(p.d_in for p in W.projections)
     d_out = max(p.d_out for p in W.projections)
     stream = torch.cuda.current_stream()
     copy_stream = torch.cuda.Stream() if side else None
-    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out, inline=inline, copy_stream=copy_stream)
+    b = Batch(n_rows_max or W.n_rows, W.adapter_rank, d_in, d_out, inline=inline, copy_stream=copy_stream)
     b.refresh(maps[0], stream)
     ldv = -(-int(W.adapter_rank.max()) // 4) * 4
     vs = [b.new_v(ldv) for _ in W.projections]
@@ -43,8 +43,10 @@ def _run(W, maps, steps, inline, side):
     return [dp.y.cpu().numpy() for dp in dw.projections]
 
 
-@pytest.mark.parametrize("inline", [False, True])
-def test_side_stream_upload_matches(inline):
+@pytest.mark.parametrize("inline,grow", [(False, False), (True, False), (False, True)])
+def test_side_stream_upload_matches(inline, grow):
+    """grow: the batch starts with room for 8 rows, so the first refresh on
+    each staging slot grows that slot's buffers (and the segment arrays)."""
     if inline:
         # one-token rows and short low-rank segments: an all-fused plan (inline)
         ra = np.repeat([0, 1, -1, 2, 3, 4, 5], [1, 1, 2, 1, 3, 1, 1])
@@ -56,7 +58,7 @@ def test_side_stream_upload_matches(inline):
     maps = _maps(np.asarray(W.row_adapter, np.int32), 3, 7)
     y0 = [p.y0.copy() for p in W.projections]
     ref = _run(W, maps, 9, inline, side=False)
-    got = _run(W, maps, 9, inline, side=True)
+    got = _run(W, maps, 9, inline, side=True, n_rows_max=8 if grow else None)
     for pi, (r, g) in enumerate(zip(ref, got)):
         assert not np.array_equal(r, y0[pi]), "the steps left y unchanged"
         assert np.array_equal(r.view(np.uint32), g.view(np.uint32)), "projection %d differs" % pi
