@@ -248,28 +248,35 @@ def copy_calibration():
 
 
 def rmw_ceiling(reps=24):
-    """The rate at which this device streams an in-place read-modify-write of
-    the merge's size (4 x W[4096x4096] bf16 = 128 MiB read and written), with
-    a plain library kernel (torch's elementwise add) and the Infinity Cache
-    cold: launches rotate over 4 such buffers (512 MiB).  The merge cannot
-    beat this stream by much: it moves the same bytes in the same pattern."""
+    """The rate at which this device streams an in-place read-modify-write,
+    with a plain library kernel (torch's elementwise add), launches back to
+    back: (1) of the merge's size (4 x W[4096x4096] bf16 = 128 MiB read and
+    written), rotating over 4 such buffers so that the reads find nothing in
+    the Infinity Cache; its writes (128 MiB) still fit in that cache, and part
+    of their write-back falls to the next launch.  (2) sustained: fp32
+    buffers of 2.95 GB (the 70B step's y rows twice over), rotating over 2,
+    where every launch pays for its own writes except the last ~256 MB."""
     import torch
     from heterogeneous_adapter_batching_amd.session import HipEvent
-    n = 4 * 4096 * 4096
-    bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
-    for k in range(8):
-        bufs[k % 4].add_(1.0)
-    torch.cuda.synchronize()
-    ev = [HipEvent(timing=True) for _ in range(reps + 1)]
-    for k in range(reps):
-        ev[k].record()
-        bufs[k % 4].add_(1.0)
-    ev[reps].record()
-    torch.cuda.synchronize()
-    us = float(np.median([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(reps)]))
-    nbytes = 2 * n * 2
-    print(json.dumps({"rmw_bytes": nbytes, "us_median": round(us, 2), "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
-                      "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+    out = {}
+    for name, n, dtype, nbuf, k_reps in (("merge-sized", 4 * 4096 * 4096, torch.bfloat16, 4, reps),
+                                         ("sustained", 16384 * 45056, torch.float32, 2, 8)):
+        bufs = [torch.zeros(n, dtype=dtype, device="cuda") for _ in range(nbuf)]
+        for k in range(2 * nbuf):
+            bufs[k % nbuf].add_(1.0)
+        torch.cuda.synchronize()
+        ev = [HipEvent(timing=True) for _ in range(k_reps + 1)]
+        for k in range(k_reps):
+            ev[k].record()
+            bufs[k % nbuf].add_(1.0)
+        ev[k_reps].record()
+        torch.cuda.synchronize()
+        us = float(np.median([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(k_reps)]))
+        nbytes = 2 * n * bufs[0].element_size()
+        out[name] = {"rmw_bytes": nbytes, "us_median": round(us, 2), "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del bufs
+    print(json.dumps(out), flush=True)
 
 
 def delta_cost(W, row_adapter):
