@@ -879,8 +879,8 @@ def apply_pieces(batch, projs):
         items = np.concatenate([work[ranges[i][1]:ranges[i][1] + ranges[i][2]] for i in idx])
 
         def fn(sub=sub):
-            # the plan's buffers of the batch's latest refresh (a batch with a
-            # side-stream upload alternates between two staging slots)
+            # the plan's buffers of the batch's latest refresh (they move when
+            # a refresh grows them)
             sub.row_index, sub.work, sub.live = L.row_index, L.work, L.live
             sub.host_work, sub.host_row_index = L.host_work, L.host_row_index
             call_apply(sub, arr, len(projs), h)
@@ -1000,9 +1000,7 @@ def headline(args):
     active rows, gathering adapter rows through the page table.  Steps
     alternate between two device copies of the inputs (same values, other
     addresses), so no step finds the previous one's data in the Infinity
-    Cache.  Inputs are resident in HBM before the timed region.  The plan's
-    upload runs on a side stream (Batch's copy_stream: two staging slots),
-    so a step's copy overlaps the previous step's launches.
+    Cache.  Inputs are resident in HBM before the timed region.
 
     Beside it, in the same line: the vision workload's mode switch (merge of
     its rank-64 adapter into 32 layers x q/k/v/o W[4096x4096], then unmerge),
@@ -1026,9 +1024,7 @@ def headline(args):
     d_out = max(p.d_out for p in W.projections)
     ldv = -(-int(W.adapter_rank.max()) // 4) * 4
     dw0 = to_device(W)
-    # the plan's upload runs on a side stream, beside the previous step's launches
-    copy_stream = torch.cuda.Stream()
-    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out, inline=True, copy_stream=copy_stream).refresh(W.row_adapter)
+    b = Batch(W.n_rows, W.adapter_rank, d_in, d_out, inline=True).refresh(W.row_adapter)
     copies = []
     for c in range(2):
         if c == 0:
@@ -1132,7 +1128,7 @@ def headline(args):
     flush = ColdCache(dev)
     Wt = workloads.gen_twin(4)
     dwt = to_device(Wt)
-    bt = Batch(Wt.n_rows, Wt.adapter_rank, d_in, d_out, inline=True, copy_stream=copy_stream).refresh(Wt.row_adapter)
+    bt = Batch(Wt.n_rows, Wt.adapter_rank, d_in, d_out, inline=True).refresh(Wt.row_adapter)
     ldvt = -(-int(Wt.adapter_rank.max()) // 4) * 4
     twin_runs = []
     for c in range(2):

@@ -112,19 +112,9 @@ class Batch:
     ``inline=True`` plans the apply op only, with LORA_PREPARE_INLINE: a
     small all-fused plan (decode batches) is then not copied at all but
     handed to the kernel in its launch arguments; a larger plan is copied as
-    usual.  The shrink and expand launches are then unavailable.
+    usual.  The shrink and expand launches are then unavailable."""
 
-    ``copy_stream`` (a torch stream) moves the upload off the compute
-    stream: the batch keeps two staging slots (pinned host + device) and
-    uses them in turn, the copy of batch k runs on ``copy_stream`` while the
-    compute stream still runs the launches of batch k-1, and the compute
-    stream waits for that copy only.  A slot is written again two refreshes
-    later, after the compute stream has passed every launch enqueued before
-    the refresh that followed its use (an event recorded at that refresh);
-    so each refresh must come after the launches of the previous batch are
-    enqueued, as in refresh, run, refresh, run."""
-
-    def __init__(self, n_rows_max, adapter_rank, d_in, d_out, device="cuda", inline=False, copy_stream=None):
+    def __init__(self, n_rows_max, adapter_rank, d_in, d_out, device="cuda", inline=False):
         self.adapter_rank = np.ascontiguousarray(adapter_rank, dtype=np.int32)
         self.d_in, self.d_out = int(d_in), int(d_out)
         self.device = torch.device(device)
@@ -134,20 +124,12 @@ class Batch:
         self._b = lora_batch_t()
         self._b_ref = ctypes.byref(self._b)
         self._launch = [self._b.launch[op] for op in (LORA_OP_SHRINK, LORA_OP_EXPAND, LORA_OP_APPLY)]
+        self._copied = HipEvent()   # the last staging copy
+        self._pending = False
         self._stream, self._stream_h = None, None
-        self._copy_stream = copy_stream
         self._n_active, self._v_slices, self._op_slices = 0, 1, [0, 0, 0]
         self._op_mask = ((1 << LORA_OP_APPLY) | LORA_PREPARE_INLINE) if inline else 7
-        # staging slots: host/dev buffers, the event after the slot's last
-        # copy, and (side-stream uploads) the event after the launches that
-        # read the slot's device buffer
-        self._slots = [dict(copied=HipEvent(), pending=False, released=HipEvent(), held=False)
-                       for _ in range(2 if copy_stream is not None else 1)]
-        self._slot = 0
-        for i in range(len(self._slots)):
-            self._slot = i
-            self._alloc(n + WORK_INTS * 10 * n)  # grown on demand
-        self._slot = len(self._slots) - 1   # the first refresh takes slot 0
+        self._alloc(n + WORK_INTS * 10 * n)  # grown on demand
 
     def _alloc_segs(self, cap):
         self._seg_cap = cap
@@ -155,21 +137,12 @@ class Batch:
         self._seg_ptr = tuple(a.ctypes.data for a in self._seg)
 
     def _alloc(self, cap):
-        S = self._slots[self._slot]
-        if S["pending"]:
-            S["copied"].synchronize()
-            S["pending"] = False
-        if S["held"]:
-            S["released"].synchronize()   # launches still reading the old device buffer
-            S["held"] = False
-        S["host"] = torch.empty(cap, dtype=torch.int32, pin_memory=True)
-        S["dev"] = torch.empty(cap, dtype=torch.int32, device=self.device)
-        self._use_slot()
-
-    def _use_slot(self):
-        S = self._slots[self._slot]
-        self._host, self._dev = S["host"], S["dev"]
+        if self._pending:
+            self._copied.synchronize()
+            self._pending = False
+        self._host = torch.empty(cap, dtype=torch.int32, pin_memory=True)
         self._hnp = self._host.numpy()
+        self._dev = torch.empty(cap, dtype=torch.int32, device=self.device)
         self._host_ptr, self._dev_ptr = self._host.data_ptr(), self._dev.data_ptr()
 
     def refresh(self, row_adapter, stream=None):
@@ -180,27 +153,13 @@ class Batch:
             stream = torch.cuda.current_stream()
         if stream is not self._stream:
             self._stream, self._stream_h = stream, stream.cuda_stream
-        side = self._copy_stream is not None
-        if side:
-            # the launches enqueued so far read the slot of the previous
-            # refresh: its release event follows them
-            prev = self._slots[self._slot]
-            prev["released"].record(stream)
-            prev["held"] = True
-            self._slot ^= 1
-            self._use_slot()
-        S = self._slots[self._slot]
-        if S["pending"]:
-            S["copied"].synchronize()   # the staging buffer may still be in flight
-            S["pending"] = False
-        copy_stream = self._copy_stream if side else stream
-        if side and S["held"]:
-            S["released"].wait(copy_stream)   # the launches that read this slot's device buffer
-            S["held"] = False
+        if self._pending:
+            self._copied.synchronize()   # the staging buffer may still be in flight
+            self._pending = False
         while True:
             st = batch_prepare(ra.shape[0], ra.ctypes.data, self.adapter_rank.shape[0], self._rank_ptr,
                                self.d_in, self.d_out, self._op_mask, self._seg_cap, *self._seg_ptr, self._host_ptr,
-                               self._host.shape[0], self._dev_ptr, copy_stream.cuda_stream, self._b_ref)
+                               self._host.shape[0], self._dev_ptr, self._stream_h, self._b_ref)
             if st != LORA_ECAPACITY:
                 break
             if self._b.n_seg > self._seg_cap:
@@ -213,10 +172,8 @@ class Batch:
         # an inline plan stays on the host (lora_apply copies it into the
         # launch arguments), so nothing is in flight to wait for next time
         if not (self._op_mask & LORA_PREPARE_INLINE) or self._launch[LORA_OP_APPLY].work:
-            S["copied"].record(copy_stream)
-            S["pending"] = True
-            if side:
-                S["copied"].wait(stream)
+            self._copied.record(stream)
+            self._pending = True
         self._n_active = self._b.n_active
         # v buffers from new_v serve every planned op (the library trusts the
         # size of v, so each call checks its own plan's slices below)
