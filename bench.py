@@ -611,6 +611,27 @@ def decode_workload(args):
         step(pevs[k], args.warmup + args.steps + k, True)
     torch.cuda.synchronize()
 
+    # the two batches' calls alone, back to back over the layer copies (no
+    # mode switch between them, as in a run of decode steps): each call then
+    # follows the other batch's, not an unmerge's 128 MB of fresh W writes
+    loop_us = None
+    if not on_device:
+        n_calls = len(layers[0]["calls"][0]) + len(layers[0]["calls"][1])
+        lev = [new_events(n_calls + 1) for _ in range(args.steps + args.warmup)]
+        for k, ev in enumerate(lev):
+            L = layers[k % len(layers)]
+            bh.refresh(het, stream)
+            bo.refresh(homo, stream)
+            g = 0
+            ev[0].record(stream)
+            for fns in L["calls"]:
+                for fn in fns:
+                    fn()
+                    g += 1
+                    ev[g].record(stream)
+        torch.cuda.synchronize()
+        loop_us = [[ev[i].elapsed_time(ev[i + 1]) * 1e3 for ev in lev[args.warmup:]] for i in range(n_calls)]
+
     # launch floor: one near-empty kernel (a 1-element fill) between the same
     # kind of events, on the same stream
     tiny = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -691,6 +712,15 @@ def decode_workload(args):
         "launch_floor_us": round(float(np.median(floor)), 3),
         "step_alg_bytes": int(step_bytes),
     }
+    if loop_us is not None:
+        # the same groups as the step's (minus the mode switch), timed in the
+        # loop of calls alone
+        lg = [g for g in groups if g not in ("merge_unmerge", "metadata")]
+        out["calls_back_to_back"] = {}
+        for g, t in zip(lg, loop_us):
+            b, _ = alg[g]
+            m = float(np.median(t))
+            out["calls_back_to_back"][g] = {"us_median": round(m, 3), "hbm_frac": round(b / (m * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, {"hetero": het, "homo": homo}, merge_host, gpu_results)
     print(json.dumps(out), flush=True)
