@@ -41,7 +41,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --workload prefill|vision|mix70b --twin        (shrink/expand tables and the twin ratio)
        python bench.py --workload prefill|vision|mix70b --metadata device  (apply: host- vs device-built plan)
        python bench.py --copy-calibration                             (counter calibration under rocprofv3)
-       python bench.py --flush-study                                  (the prefill shrink after a write or read cache flush)
+       python bench.py --flush-study                                  (kernel times after a write or a read cache flush, and in a step)
        python bench.py --traffic-record PMC_DIR --traffic-grid N      (write the dominant launch's traffic record)
        python bench.py --rmw-ceiling                                  (in-place streaming rate of this HBM)
 """
