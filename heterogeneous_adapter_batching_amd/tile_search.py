@@ -30,7 +30,10 @@ caller's table) and the library as built, in two phases:
    table: the bucket's candidates are tried in turn with the rest of the table
    fixed, each judged by the summed time of lora_apply, lora_shrink and
    lora_expand (over all projections, one call each, warm, median of
-   ``--reps``) on the batches that touch the bucket.  Judging a choice inside
+   ``--reps``) on the batches that touch the bucket.  Each pass first tries
+   block moves: the buckets that share one launch (same op, d bucket, launch
+   class and shape) set to one candidate at once, which a move of one
+   bucket cannot reach when moving it alone would split that launch.  Judging a choice inside
    the whole batch, not alone, sees what a choice costs its neighbours: two
    buckets on different kernel shapes are separate launches, and each launch
    has its own tail.
@@ -40,8 +43,8 @@ caller's table) and the library as built, in two phases:
    before each call), the op the bucket serves only.
 
 In the workload phase a candidate replaces the current choice only when it is
-faster by more than ``--min-gain`` (1%) and stays so when both are timed
-again; in the isolated phase, whose single-projection timings are noisier, when
+faster by more than ``--min-gain`` (1%; block moves ``--min-gain-block``,
+0.5%) and stays so when both are timed again; in the isolated phase, whose single-projection timings are noisier, when
 it is faster by more than ``--min-gain-alone`` (3%).  Re-running on an
 unchanged device then changes little by noise.  The descent repeats (at most
 ``--passes`` times) until a pass changes nothing.
@@ -301,6 +304,76 @@ def search_workloads(cases, st_tab, ex_tab, reps, min_gain, log, report, pass_no
     return set(touch)
 
 
+def _launch_class(op, r):
+    """Rank buckets whose segments one launch runs together: the expand's
+    rank classes (ranks <= 32 share the one-K-step kernel), the shrink's
+    ranks <= 64 (one launch per shape) against rank 128."""
+    if op == "expand":
+        return 0 if r <= 1 else r - 1
+    return 0 if r <= 2 else 1
+
+
+def search_blocks(cases, st_tab, ex_tab, reps, min_gain, log, report, pass_no):
+    """Block moves: the buckets the batches touch that now share one launch
+    (same op, d bucket, launch class and shape) set to one candidate
+    together.  One bucket at a time,
+    the descent cannot move segments that share a launch to another shape
+    without splitting that launch first, which costs more than the move
+    gains; together they may move as one launch."""
+    touch = {}
+    for c in cases:
+        for bk in c.buckets():
+            touch.setdefault(bk, []).append(c)
+    groups = {}
+    for op, l, r, d in touch:
+        shape = int(st_tab[l, r, d][0]) if op == "shrink" else int(ex_tab[l, r, d])
+        groups.setdefault((op, d, _launch_class(op, r), shape), []).append((op, l, r, d))
+
+    def cost(cs, st, ex):
+        return sum(sum(c.total(st, ex, reps).values()) for c in cs)
+    for key in sorted(groups):
+        bks = sorted(groups[key])
+        if len(bks) < 2:
+            continue
+        op, d = key[0], key[1]
+        cs = sorted({id(c): c for bk in bks for c in touch[bk]}.values(), key=lambda c: c.label)
+        res = {"current": (cost(cs, st_tab, ex_tab), st_tab.copy(), ex_tab.copy())}
+        for cand in (SHRINK_CAND if op == "shrink" else EXPAND_CAND):
+            st, ex = st_tab.copy(), ex_tab.copy()
+            if op == "shrink":
+                if cand[1] > D_IN_REP[d] // 64:
+                    continue
+                for _, l, r, _ in bks:
+                    st[l, r, d] = cand
+            else:
+                if cand == 4 and any(l > 1 for _, l, _, _ in bks):
+                    continue
+                for _, l, r, _ in bks:
+                    ex[l, r, d] = cand
+            if np.array_equal(st, st_tab) and np.array_equal(ex, ex_tab):
+                continue
+            res[cand] = (cost(cs, st, ex), st, ex)
+        best = min(res, key=lambda k: res[k][0])
+        t_cur = res["current"][0]
+        chosen = "current"
+        if best != "current" and res[best][0] < (1 - min_gain) * t_cur:
+            t2c = cost(cs, *res["current"][1:])
+            t2b = cost(cs, *res[best][1:])
+            if t2b < (1 - min_gain) * t2c:
+                chosen = best
+        where = "block, pass %d: %s" % (pass_no, "+".join(c.label for c in cs))
+        for _, l, r, _ in bks:
+            cur = tuple(int(v) for v in st_tab[l, r, d]) if op == "shrink" else int(ex_tab[l, r, d])
+            new = cur if chosen == "current" else chosen
+            report.append((op, l, r, d, where, cur, t_cur, new, res[chosen][0]))
+        if chosen != "current":
+            st_tab[...] = res[chosen][1]
+            ex_tab[...] = res[chosen][2]
+        log("block %d: %s d %d class %d shape %d (%s) on %s: current %.1f us, chosen %s %.1f us (best %s %.1f)"
+            % (pass_no, op, d, key[2], key[3], ", ".join("%s/%d" % (LEN_NAMES[l].strip(), RANK_REP[r]) for _, l, r, _ in bks),
+               "+".join(c.label for c in cs), t_cur, chosen, res[chosen][0], best, res[best][0]))
+
+
 def search_isolated(st_tab, ex_tab, skip, reps, min_gain, log, report):
     for l in range(8):
         for r in range(4):
@@ -353,6 +426,8 @@ def main():
     ap.add_argument("--reps", type=int, default=9)
     ap.add_argument("--min-gain", type=float, default=0.01)
     ap.add_argument("--min-gain-alone", type=float, default=0.03)
+    ap.add_argument("--min-gain-block", type=float, default=0.005,
+                    help="block moves are judged on sums over whole batches, steadier than one bucket's")
     ap.add_argument("--passes", type=int, default=3, help="coordinate-descent passes at most (stops when one "
                     "changes nothing)")
     ap.add_argument("--out", default=TABLE)
@@ -373,6 +448,7 @@ def main():
     report = []
     for k in range(args.passes):
         before_pass = (st_tab.copy(), ex_tab.copy())
+        search_blocks(cases, st_tab, ex_tab, args.reps, args.min_gain_block, log, report, k + 1)
         touched = search_workloads(cases, st_tab, ex_tab, args.reps, args.min_gain, log, report, k + 1)
         if np.array_equal(before_pass[0], st_tab) and np.array_equal(before_pass[1], ex_tab):
             break
@@ -401,8 +477,9 @@ def _summary(args, dev, before, after, again, report):
                 "search):\n\n")
         f.write("    python -m heterogeneous_adapter_batching_amd.tile_search %s\n\n" % " ".join(sys.argv[1:]))
         f.write("Device: %s.  Median of %d calls per timing; a choice changes only when faster by more than "
-                "%.0f%% twice (buckets timed in the batches) or %.0f%% (buckets timed alone).\n\n"
-                % (dev, args.reps, 100 * args.min_gain, 100 * args.min_gain_alone))
+                "%.0f%% twice (buckets timed in the batches; %.1f%% for block moves) or %.0f%% (buckets timed "
+                "alone).\n\n" % (dev, args.reps, 100 * args.min_gain, 100 * args.min_gain_block,
+                                   100 * args.min_gain_alone))
         f.write("## Measured batches, whole (us per call over all projections, warm)\n\n")
         f.write("| batch | op | table before | table after | table before, timed again at the end |\n"
                 "|---|---|---|---|---|\n")
@@ -410,7 +487,8 @@ def _summary(args, dev, before, after, again, report):
             for o in OPS:
                 f.write("| %s | %s | %.1f | %.1f | %.1f |\n" % (k, OP_NAMES[o], before[k][o], after[k][o], again[k][o]))
         f.write("\n## Buckets\n\n`where`: the descent pass and the batches a bucket was judged on (sum of apply + shrink + "
-                "expand over them), or `alone` (the op alone on a batch of that bucket's segments, cold).  Shrink entries are "
+                "expand over them; `block`: the bucket moved together with the others of its launch, the times are the "
+                "block's), or `alone` (the op alone on a batch of that bucket's segments, cold).  Shrink entries are "
                 "(shape, K slices); expand entries the shape.\n\n")
         f.write("| op | length | rank | d | where | current | us | chosen | us |\n|---|---|---|---|---|---|---|---|---|\n")
         for op, l, r, d, where, cur, t_cur, chosen, t_ch in report:

@@ -212,20 +212,23 @@ def test_apply_device_padded_rows_untouched():
 
 
 def test_apply_device_more_items_than_resident_workgroups():
-    """Each grid-stride kernel walks several items per workgroup: 1500 rows on
-    400 adapters (segments of ~4 rows).  At d 1024 every segment is fused
-    (1500 fused rows); with d_in 8192 none is, so the split-K short shrink
-    (8 K slices), the BGMV expand and the 16-row expand take them."""
+    """Each grid-stride kernel walks several items per workgroup: 3000 rows on
+    800 adapters (segments of ~4 rows).  At d 1024 every segment is fused
+    (3000 fused rows); with d_in 8192 none is, so the shrink and expand
+    launch groups the tile table picks for such segments take them, each
+    with more items than a CU-filling grid has workgroups."""
     rng = np.random.default_rng(77)
-    ra = rng.integers(0, 400, 1500).astype(np.int32)
-    ranks = rng.choice([4, 8, 16], 400).astype(np.int32)
+    ra = rng.integers(0, 800, 3000).astype(np.int32)
+    ranks = rng.choice([4, 8, 16], 800).astype(np.int32)
     W = workloads.gen_custom(35, ra, ranks, 1024, 1024, n_proj=2)
     hb, _ = _same_as_host(W)
-    assert sum(c for v, b, c, m in hb.info_apply.range_list() if v == 32) == 1500
+    assert sum(c for v, b, c, m in hb.info_apply.range_list() if v == 32) == 3000
     W = workloads.gen_custom(36, ra, ranks, 8192, 1024, n_proj=2)
     hb, _ = _same_as_host(W)
     variants = {v: c for v, b, c, m in hb.info_apply.range_list()}
-    assert 32 not in variants and sum(c for v, c in variants.items() if v < 4) > 1000
+    assert 32 not in variants
+    assert sum(c for v, c in variants.items() if v < 12) > 1000      # shrink items
+    assert sum(c for v, c in variants.items() if 12 <= v < 32) > 1000  # expand items
 
 
 def test_apply_device_shared_x_bit_identical():
