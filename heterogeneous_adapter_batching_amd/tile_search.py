@@ -316,10 +316,11 @@ def _launch_class(op, r):
 def search_blocks(cases, st_tab, ex_tab, reps, min_gain, log, report, pass_no):
     """Block moves: the buckets the batches touch that now share one launch
     (same op, d bucket, launch class and shape) set to one candidate
-    together.  One bucket at a time,
-    the descent cannot move segments that share a launch to another shape
-    without splitting that launch first, which costs more than the move
-    gains; together they may move as one launch."""
+    together.  One bucket at a time, the descent cannot move segments that
+    share a launch to another shape without splitting that launch first,
+    which costs more than the move gains; together they move as one launch.
+    The groups are disjoint, so each is formed from the table as the pass
+    found it."""
     touch = {}
     for c in cases:
         for bk in c.buckets():
