@@ -18,7 +18,7 @@ import workloads
 from workloads import Projection, RowsDesc, Workload, build_pool, to_bf16_bits
 from workloads.device import to_device
 
-from gpu_helpers import UNMERGE_MIN_EQUAL, check_delta, check_merge_bits, run_delta, run_merge, ulp_compare, rows_of
+from gpu_helpers import UNMERGE_MIN_EQUAL, check_delta, check_merge_bits, run_apply, run_delta, run_merge, ulp_compare, rows_of
 
 pytestmark = pytest.mark.gpu
 
@@ -204,6 +204,31 @@ def test_random_shapes_parity(seed):
     _say("random", seed, "rows", W.n_rows, "ranks", ranks.tolist(), "d", d_in, d_out, layout)
     batch, vs, ys = run_delta(W)
     _say(check_delta(W, batch, vs, ys))
+
+
+@pytest.mark.parametrize("seed", range(200, 216))
+def test_random_wide_shapes_parity(seed):
+    """The tile table's large-d buckets: d_in up to 16384 and d_out up to
+    28672 with every length and rank bucket, through the shrink + expand
+    path and lora_apply, dense and paged; every row of a batch up to 300
+    rows, else a seeded sample of 300 (released rows among them checked
+    untouched)."""
+    rng = np.random.default_rng(seed)
+    n_ad = int(rng.integers(1, 12))
+    ranks = rng.integers(1, 129, size=n_ad)
+    lens = rng.choice([1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64, 65, 200, 256, 257, 600], size=int(rng.integers(1, 10)))
+    ra = np.repeat(rng.integers(-1, n_ad, size=len(lens)), lens)
+    d_in = int(rng.choice([1024, 2048, 4096, 6144, 8192, 12288, 16384]))
+    d_out = int(rng.choice([1024, 4096, 8192, 12288, 16384, 28672]))
+    layout = "paged" if seed % 2 else "dense"
+    W = workloads.gen_custom(seed, ra, ranks, d_in, d_out, n_proj=1 + seed % 2, layout=layout,
+                             page_elems=64 * int(rng.choice([16, 64, 128])))
+    rows = None if W.n_rows <= 300 else sorted(rng.choice(W.n_rows, 300, replace=False).tolist())
+    _say("wide", seed, "rows", W.n_rows, "ranks", ranks.tolist(), "d", d_in, d_out, layout)
+    batch, vs, ys = run_delta(W)
+    _say(check_delta(W, batch, vs, ys, rows=rows))
+    batch, ys = run_apply(W)
+    _say(check_delta(W, batch, None, ys, rows=rows, check_v=False))
 
 
 @pytest.mark.parametrize("d_out,d_in,r", [(64, 192, 1), (576, 320, 17), (1024, 512, 64), (256, 704, 128)])
