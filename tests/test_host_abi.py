@@ -184,6 +184,43 @@ def test_table_plans_follow_the_given_table():
     assert status == hl.LORA_ESHAPE
 
 
+def test_block_moves_group_the_segments_one_launch_runs():
+    """The tile search's block moves treat the buckets of one op, d bucket,
+    launch class and shape as one launch.  Against the planner: with one
+    shape everywhere, segments whose ranks share a launch class get the same
+    expand variant (a host plan runs one launch per expand range), and
+    shrink variants of the same shape whose classes the launcher runs
+    together (ranks up to 64) or apart (rank 128); different classes get
+    different expand variants."""
+    from heterogeneous_adapter_batching_amd.tile_search import RANK_REP, _launch_class, read_table
+    st0, ex0 = read_table()
+    for shape in (0, 1, 2):
+        st, ex = st0.copy(), ex0.copy()
+        st[...] = (shape, 1)
+        ex[...] = shape
+        ranks = np.array(RANK_REP, np.int32)            # one adapter per rank bucket
+        ra = np.repeat(np.arange(4), [40, 40, 40, 40]).astype(np.int32)
+        segs = hl.lora_build_segments(ra, ranks)
+        for op in (hl.LORA_OP_SHRINK, hl.LORA_OP_EXPAND):
+            work, info = hl.lora_plan_table(op, segs, 1024, 1024, st, ex)
+            var_of_rank = {}
+            for v, b, c, _ in info.range_list():
+                for w in work[b:b + c]:
+                    var_of_rank.setdefault(int(w[3]), set()).add(v)
+            assert all(len(vs) == 1 for vs in var_of_rank.values())
+            var = {r: next(iter(var_of_rank[RANK_REP[r]])) for r in range(4)}
+            name = "shrink" if op == hl.LORA_OP_SHRINK else "expand"
+            for r1 in range(4):
+                for r2 in range(4):
+                    same = _launch_class(name, r1) == _launch_class(name, r2)
+                    v1, v2 = var[r1], var[r2]
+                    assert v1 // 4 == v2 // 4 == shape
+                    if op == hl.LORA_OP_EXPAND:
+                        assert (v1 == v2) == same
+                    else:   # the launcher runs shrink classes 0-2 of a shape together, class 3 alone
+                        assert ((v1 % 4 < 3) == (v2 % 4 < 3)) == same
+
+
 def test_tile_table_source_round_trips(tmp_path):
     """The tile search reads the compiled-in table's source and writes it back
     unchanged but for its note line."""
