@@ -730,7 +730,7 @@ def decode_workload(args):
 # The benchmark line: the 70B-shaped paged mix, plus the vision mode switch
 # ---------------------------------------------------------------------------
 APPLY_EXPAND0, APPLY_FUSED = 3 * 4, 3 * 4 + 5 * 4   # apply-plan variant numbering (shrink, expand, fused)
-EXPAND_SHAPES = {0: 16, 1: 64, 2: 128, 3: 128, 4: 2}
+EXPAND_SHAPES = {0: 16, 1: 64, 2: 128, 3: 32, 4: 2}
 MIX70B_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mix70b_dominant_traffic.json")
 
 

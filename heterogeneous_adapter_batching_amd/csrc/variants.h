@@ -28,15 +28,14 @@
 #define LV_S_ROWS128 2
 #define LV_S_SHAPES 3
 
-// Expand shapes: the MFMA kernel with work items of 16 / 64 / 128 rows
+// Expand shapes: the MFMA kernel with work items of 16 / 64 / 128 / 32 rows
 // (more rows reuse each B column strip more, fewer rows give more
-// workgroups), and the VALU kernel for decode items of at most 2 rows (BGMV),
-// which has a single rank class.  Shape 3 is a spare MFMA shape (items of
-// 128 rows, the kernel's maximum); the table does not use it.
+// workgroups and a y stream of shorter columns), and the VALU kernel for
+// decode items of at most 2 rows (BGMV), which has a single rank class.
 #define LV_E_ROWS16 0
 #define LV_E_ROWS64 1
 #define LV_E_ROWS128 2
-#define LV_E_SPARE 3
+#define LV_E_ROWS32 3
 #define LV_E_BGMV 4
 #define LV_E_SHAPES 5
 
@@ -44,7 +43,7 @@ static inline LV_HD int32_t lv_shrink_rows(int shape) {
     return shape == LV_S_SPLITK16 ? 16 : shape == LV_S_ROWS64 ? 64 : 128;
 }
 static inline LV_HD int32_t lv_expand_rows(int shape) {
-    return shape == LV_E_ROWS16 ? 16 : shape == LV_E_ROWS64 ? 64 : shape == LV_E_BGMV ? 2 : 128;
+    return shape == LV_E_ROWS16 ? 16 : shape == LV_E_ROWS32 ? 32 : shape == LV_E_ROWS64 ? 64 : shape == LV_E_BGMV ? 2 : 128;
 }
 // Variant ids of an apply plan: the shrink variants, then the expand
 // variants shifted by LV_APPLY_EXPAND0, then the fused one-row kernel.
@@ -78,8 +77,8 @@ static inline LV_HD int lv_group_member(int key, int i) {
         const int n = key % LV_RANK_CLASSES == 0 ? LV_RANK_CLASSES - 1 : 1;
         return i < n ? key + i : -1;
     }
-    if (key < LV_APPLY_EXPAND0 + LV_RANK_CLASSES)  // MFMA expand of one rank class: shapes 0 .. LV_E_SPARE
-        return i <= LV_E_SPARE ? key + i * LV_RANK_CLASSES : -1;
+    if (key < LV_APPLY_EXPAND0 + LV_RANK_CLASSES)  // MFMA expand of one rank class: shapes 0 .. LV_E_ROWS32
+        return i <= LV_E_ROWS32 ? key + i * LV_RANK_CLASSES : -1;
     return i == 0 ? key : -1;
 }
 

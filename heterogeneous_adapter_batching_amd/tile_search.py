@@ -86,7 +86,7 @@ LEN_NAMES = ["len 1     ", "len 2-4   ", "len 5-8   ", "len 9-16  ", "len 17-32 
 ROWS_TARGET = 8192       # rows per timed batch of the isolated phase
 MAX_SEGMENTS = 256
 SHRINK_CAND = [(s, k) for s in (0, 1, 2) for k in (1, 2, 4, 8, 16)]
-EXPAND_CAND = [0, 1, 2, 4]
+EXPAND_CAND = [0, 3, 1, 2, 4]   # items of 16, 32, 64, 128 rows; the VALU decode kernel
 FUSED_MAX_D, FUSED_MAX_ROWRANK = 4096, 1024   # lv_fused: such segments never read the table in an apply plan
 OPS = (LORA_OP_APPLY, LORA_OP_SHRINK, LORA_OP_EXPAND)
 OP_NAMES = {LORA_OP_SHRINK: "shrink", LORA_OP_EXPAND: "expand", LORA_OP_APPLY: "apply"}
@@ -127,7 +127,7 @@ def write_table(shrink, expand, path, note):
              "//   rank buckets:   <=16, <=32, <=64, <=128",
              "//   d buckets (d_in for the shrink, d_out for the expand): <=1024, <=4096, <=8192, larger",
              "// Shrink shapes: 0 = 4 waves split K over 16 rows, 1 = 4 x 16 rows, 2 = 4 x 32 rows.",
-             "// Expand shapes: 0/1/2 = MFMA work items of 16/64/128 rows (3: spare), 4 = VALU",
+             "// Expand shapes: 0/1/2/3 = MFMA work items of 16/64/128/32 rows, 4 = VALU",
              "// decode items of at most 2 rows.",
              "// " + note,
              "struct ShrinkCfg {",

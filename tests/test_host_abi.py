@@ -145,7 +145,7 @@ def test_table_plans_follow_the_given_table():
             w0, i0 = hl.lora_plan(op, segs, d_in, d_out)
             w1, i1 = hl.lora_plan_table(op, segs, d_in, d_out, st0, ex0)
             assert np.array_equal(w0, w1) and i0.range_list() == i1.range_list() and i0.v_slices == i1.v_slices
-    rows = {hl.LORA_OP_SHRINK: {0: 16, 1: 64, 2: 128}, hl.LORA_OP_EXPAND: {0: 16, 1: 64, 2: 128, 4: 2}}
+    rows = {hl.LORA_OP_SHRINK: {0: 16, 1: 64, 2: 128}, hl.LORA_OP_EXPAND: {0: 16, 1: 64, 2: 128, 3: 32, 4: 2}}
     for op, shapes in rows.items():
         for shape, mt in shapes.items():
             for sl in (1, 2, 4, 8, 16):
