@@ -418,7 +418,8 @@ def main():
                     help="apply (default): lora_apply, one-row segments fused; split: lora_shrink then lora_expand")
     ap.add_argument("--metadata", default="inline", choices=["host", "inline", "device"],
                     help="decode: inline (default) prepares each batch with lora_batch_prepare on the host and "
-                         "passes the small all-fused plan in the kernel's launch arguments (no copy); host "
+                         "passes the small all-fused plan in the kernel's launch arguments (no copy; with "
+                         "--path split, whose plans are not all fused, the plans are copied as with host); host "
                          "copies the prepared metadata to the device instead; device builds it on the GPU (lora_batch_build_device) "
                          "from device-resident row maps")
     ap.add_argument("--twin", action="store_true",
@@ -501,8 +502,8 @@ def decode_workload(args):
         bh = DeviceBatch(64, len(W.adapter_rank), max_rank, 4096, 4096).build(het_d, rk_d)
         bo = DeviceBatch(64, len(W.adapter_rank), max_rank, 4096, 4096).build(homo_d, rk_d)
     else:
-        inline = args.metadata == "inline"
-        assert not inline or args.path == "apply", "inline plans are apply plans"
+        # inline plans are apply plans: the split path copies its plans
+        inline = args.metadata == "inline" and args.path == "apply"
         bh = Batch(64, W.adapter_rank, 4096, 4096, inline=inline).refresh(het)
         bo = Batch(64, W.adapter_rank, 4096, 4096, inline=inline).refresh(homo)
         # both decode plans are all fused and small: they must travel inline
@@ -707,7 +708,7 @@ def decode_workload(args):
         "hetero_over_homo": round(sum(med[g] for g in groups if g.startswith("hetero")) /
                                   sum(med[g] for g in groups if g.startswith("homo")), 3),
         "path": args.path,
-        "metadata": args.metadata,
+        "metadata": "host" if (args.metadata == "inline" and split) else args.metadata,
         "merge_us_per_layer": round(mavg, 3),
         "launch_floor_us": round(float(np.median(floor)), 3),
         "step_alg_bytes": int(step_bytes),
